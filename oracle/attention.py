@@ -1,0 +1,124 @@
+"""write_decode_kv, gather through the block table, paged GQA decode attention.
+
+Test infrastructure only. Everything is float64; the only roundings are the
+bf16 stores the definition itself makes (the cache and the boundary outputs).
+
+Pages followed:
+
+* mini-infer README, "decode_batch key steps": gather each request's cached
+  K/V from the block tensor through its BlockTable, run the batched forward,
+  write the new token's K/V back into the block tensor (write_decode_kv).
+* Course project, section 2.1: RoPE; grouped-query attention, where the KV
+  heads are shared by groups of query heads (sdpa with enable_gqa, or
+  repeat_interleave of the KV heads): query head h reads KV head h // G with
+  G = Hq / Hkv; the KV cache grows by appending one token per decode step.
+* nxmr.cn inference-techniques article, section 5.1: the numerically stable
+  softmax -- subtract the row max, exponentiate, divide by the row sum, then
+  weight V; section 4.1: attention scores are kept in FP32 or better.
+
+Readings where the pages are silent:
+
+* context_lens[b] counts tokens cached BEFORE this step; the new token is
+  written at logical position ctx_b (also its RoPE position) and attention
+  covers L_b = ctx_b + 1 tokens, the new one included.
+* RoPE rotates q and the new k, never v; cached K is stored rotated.
+* softmax scale 1 / sqrt(D) unless given.
+"""
+import numpy as np
+
+from . import bf16
+from . import paged
+from . import rope
+
+
+def write_decode_kv(k_pool, v_pool, q, k, v, block_table, context_lens,
+                    block_size, theta):
+    """Append the new token's rotated K and its V; rotate q.
+
+    k_pool, v_pool : uint16 bf16 bits [N, Hkv, bs, D] (not modified)
+    q              : uint16 [B, Hq, D];  k, v : uint16 [B, Hkv, D]
+    block_table    : int [B, MB];        context_lens : int [B] (pre-step)
+
+    Returns (k_pool_new, v_pool_new, q_rot_bits, q_rot_f64). q_rot_f64 is the
+    unrounded rotation (what a fused layer keeps internally).
+    """
+    k_new = np.array(k_pool, dtype=np.uint16, copy=True)
+    v_new = np.array(v_pool, dtype=np.uint16, copy=True)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    q_rot = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        pos = int(context_lens[b])
+        blk, off = paged.slot(block_table[b], pos, block_size)
+        for g in range(Hkv):
+            k_new[blk, g, off, :] = bf16.encode(rope.apply(bf16.decode(k[b, g]), pos, theta))
+            v_new[blk, g, off, :] = v[b, g]
+        for h in range(Hq):
+            q_rot[b, h] = rope.apply(bf16.decode(q[b, h]), pos, theta)
+    return k_new, v_new, bf16.encode(q_rot), q_rot
+
+
+def gather_kv(k_pool, v_pool, block_table, block_size, b, g, length):
+    """Contiguous copies of K and V of sequence b, kv head g, positions [0, length).
+
+    Bit copies (uint16) in logical order -- the gather_batch_kv step.
+    """
+    D = k_pool.shape[-1]
+    ks = np.empty((length, D), dtype=np.uint16)
+    vs = np.empty((length, D), dtype=np.uint16)
+    for p in range(length):
+        blk, off = paged.slot(block_table[b], p, block_size)
+        ks[p] = k_pool[blk, g, off]
+        vs[p] = v_pool[blk, g, off]
+    return ks, vs
+
+
+def attend(q_vec, K, V, scale):
+    """One query against L keys: softmax(K q * scale) V, the stable form.
+
+    q_vec [D], K [L, D], V [L, D], all float64.
+    """
+    s = (K @ q_vec) * scale
+    m = np.max(s)
+    p = np.exp(s - m)
+    return (p @ V) / np.sum(p)
+
+
+def paged_gqa_decode(q_rot, k_pool, v_pool, block_table, context_lens, block_size,
+                     scale=None, q_is_bits=True):
+    """Paged GQA decode attention: every query head of every sequence attends
+    over the L_b = ctx_b + 1 cached tokens of its KV head.
+
+    q_rot : [B, Hq, D] bf16 bits (or float64 if q_is_bits is False)
+    k_pool, v_pool : bf16 bits [N, Hkv, bs, D] (already holding the new token)
+    Returns float64 [B, Hq, D].
+    """
+    qf = bf16.decode(q_rot) if q_is_bits else np.asarray(q_rot, dtype=np.float64)
+    B, Hq, D = qf.shape
+    Hkv = k_pool.shape[1]
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(np.float64(D))
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b]) + 1
+        for g in range(Hkv):
+            ks, vs = gather_kv(k_pool, v_pool, block_table, block_size, b, g, L)
+            K = bf16.decode(ks)
+            V = bf16.decode(vs)
+            for h in range(g * G, (g + 1) * G):
+                out[b, h] = attend(qf[b, h], K, V, scale)
+    return out
+
+
+def decode_step(k_pool, v_pool, q, k, v, block_table, context_lens, block_size,
+                theta, scale=None):
+    """write_decode_kv followed by paged attention (the attention half of a
+    decoder-layer decode step). Returns (out_f64, k_pool_new, v_pool_new, q_rot_bits)."""
+    k_new, v_new, q_rot_bits, _ = write_decode_kv(
+        k_pool, v_pool, q, k, v, block_table, context_lens, block_size, theta)
+    out = paged_gqa_decode(q_rot_bits, k_new, v_new, block_table, context_lens,
+                           block_size, scale)
+    return out, k_new, v_new, q_rot_bits
