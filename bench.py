@@ -1,0 +1,266 @@
+"""Benchmark of the paged-KV GQA decode step on one MI355X.
+
+A step is one pass of the hot path over one batch: write_decode_kv (RoPE,
+append) then paged GQA decode attention, on the Qwen3-8B-shaped long-context
+workload (batch 32, 32 query / 8 KV heads, head_dim 128, 16-token blocks,
+contexts log-uniform in [1024, 16384], 40000-block pool). Inputs are seeded
+synthetic bf16 N(0, 1) draws, resident in HBM before timing starts. The full
+decoder-layer step (Qwen3-8B-shaped, batch 8) is timed in the same run and
+reported as layer-step tokens/s.
+
+Prints ONE JSON line. `value` = algorithmic bytes of the step / step time.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+METRIC = "paged GQA decode attention: KV GB/s & % HBM peak; layer-step tokens/s"
+
+
+def _dev(a, torch, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+
+def run_attention_bench(args, torch, mk, workloads):
+    dev = "cuda:0"
+    cfg = workloads.CONFIGS["qwen3_8b_long"]
+    case = workloads.make_decode_case(cfg, pool="bench")
+    B, Hq, Hkv, D = len(case.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    kp, vp = _dev(case.k_pool, torch, dev), _dev(case.v_pool, torch, dev)
+    q, k, v = _dev(case.q, torch, dev), _dev(case.k, torch, dev), _dev(case.v, torch, dev)
+    q_rot, out = torch.empty_like(q), torch.empty_like(q)
+    table = torch.from_numpy(case.block_table).to(dev)
+    ctx = torch.from_numpy(case.context_lens).to(dev)
+    mbps, max_ctx = case.block_table.shape[1], int(case.context_lens.max())
+    pool = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp, vp)
+    ws_bytes = mk.mi_paged_gqa_decode_split_workspace_bytes(pool, B, Hq, max_ctx, args.split)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+
+    def step(ev=None):
+        mk.mi_write_decode_kv(pool, q, k, v, q_rot, table, mbps, ctx, B, Hq, cfg.rope_theta, st)
+        if ev is not None:
+            ev[0].record(stream)
+        mk.mi_paged_gqa_decode_split(pool, q_rot, out, table, mbps, ctx, B, Hq, 0.0, max_ctx,
+                                     args.split, ws, ws_bytes, st)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    faults = mk.mi_kv_pool_check_errors(pool)
+    mk.mi_kv_pool_destroy(pool)
+    if faults:
+        raise RuntimeError("device fault bits %#x during the benchmark" % faults)
+
+    ctx_np = case.context_lens
+    attn_bytes = workloads.attention_bytes(ctx_np, Hq, Hkv, D, 16)
+    write_bytes = workloads.write_bytes(B, Hq, Hkv, D)
+    return dict(
+        case=case, cfg=cfg, ms_step=ms_step, wall=wall, attn_ms=attn_ms,
+        attn_bytes=attn_bytes, step_bytes=attn_bytes + write_bytes,
+        tokens=int(ctx_np.sum()) + B,
+        split=args.split or None,
+    )
+
+
+def run_layer_bench(args, torch, mk, workloads):
+    dev = "cuda:0"
+    cfg = workloads.CONFIGS["qwen3_8b_layer"]
+    case = workloads.make_decode_case(cfg, pool="bench")
+    w = workloads.make_layer_weights(cfg)
+    x = workloads.make_layer_input(cfg)
+    B = len(case.context_lens)
+    kp, vp = _dev(case.k_pool, torch, dev), _dev(case.v_pool, torch, dev)
+    wd = {n: _dev(a, torch, dev) for n, a in w.items()}
+    xd = _dev(x, torch, dev)
+    xo = torch.empty_like(xd)
+    table = torch.from_numpy(case.block_table).to(dev)
+    ctx = torch.from_numpy(case.context_lens).to(dev)
+    mbps, max_ctx = case.block_table.shape[1], int(case.context_lens.max())
+    pool = mk.mi_kv_pool_init(case.num_blocks, 16, cfg.num_kv_heads, cfg.head_dim, kp, vp)
+    lc = mk.layer_config(cfg.hidden, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                         cfg.intermediate, cfg.rms_eps, cfg.rope_theta)
+    lw = mk.layer_weights(**wd)
+    ws_bytes = mk.mi_decoder_layer_workspace_bytes(lc, pool, B, max_ctx)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+
+    def step():
+        mk.mi_decoder_layer_decode(pool, lc, lw, xd, xo, table, mbps, ctx, B, max_ctx, ws,
+                                   ws_bytes, st)
+
+    for _ in range(args.warmup):
+        step()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    faults = mk.mi_kv_pool_check_errors(pool)
+    mk.mi_kv_pool_destroy(pool)
+    if faults:
+        raise RuntimeError("device fault bits %#x during the layer benchmark" % faults)
+    nbytes = workloads.layer_bytes(cfg, case.context_lens)
+    flops = workloads.layer_flops(cfg, case.context_lens)
+    return {
+        "workload": "qwen3-8b-shaped decoder layer, batch 8, H 4096, I 12288, ctx U[512,4096]",
+        "ms_per_step": round(ms, 5),
+        "tokens_per_s": round(B / (ms * 1e-3), 1),
+        "algorithmic_bytes": int(nbytes),
+        "achieved_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "achieved_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+    }
+
+
+def cpu_baseline(case, cfg, workloads, budget_s):
+    """The fp64 oracle as it stands, timed on whole sequences of the same
+    workload (write then attention) until about budget_s seconds elapse."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oatt
+
+    B = len(case.context_lens)
+    order = list(range(B))
+    done_bytes, done_tokens, t_total, n = 0, 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for b in order:
+            ctx = case.context_lens[b:b + 1]
+            need = -(-(int(ctx[0]) + 1) // 16)
+            ids = case.block_table[b, :need]
+            kp = case.k_pool[ids]                       # compact pool of this sequence
+            vp = case.v_pool[ids]
+            table = np.arange(need, dtype=np.int32)[None, :]
+            t0 = time.perf_counter()
+            oatt.decode_step(kp, vp, case.q[b:b + 1], case.k[b:b + 1], case.v[b:b + 1], table,
+                             ctx, 16, cfg.rope_theta)
+            t_total += time.perf_counter() - t0
+            n += 1
+            done_tokens += int(ctx[0]) + 1
+            done_bytes += (workloads.attention_bytes(ctx, cfg.num_q_heads, cfg.num_kv_heads,
+                                                     cfg.head_dim, 16)
+                           + workloads.write_bytes(1, cfg.num_q_heads, cfg.num_kv_heads,
+                                                   cfg.head_dim))
+            if t_total >= budget_s:
+                break
+    return {
+        "value": round(done_bytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d of %d sequences (%d tokens, write + attention, fp64 numpy, 1 thread), %.1f s"
+                  % (n, B, done_tokens, t_total),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--split", type=int, default=0, help="split-K tokens (0: library default)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-layer", action="store_true", help="skip the full-layer step")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the paged decode path is single-GPU "
+              "(no collectives); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_246_amd as mk
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mk.lib()
+
+    r = run_attention_bench(args, torch, mk, workloads)
+    ms = r["ms_step"]
+    value = r["step_bytes"] / (ms * 1e-3) / 1e9
+    attn_ms = float(np.mean(r["attn_ms"]))
+    achieved = r["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1) K/V, q, k, v; no dataset)",
+        "config": {
+            "workload": "qwen3-8b-shaped long-context paged GQA decode step "
+                        "(write_decode_kv + attention)",
+            "batch": len(r["case"].context_lens),
+            "num_q_heads": r["cfg"].num_q_heads,
+            "num_kv_heads": r["cfg"].num_kv_heads,
+            "head_dim": r["cfg"].head_dim,
+            "block_size": 16,
+            "context_lens": "log-uniform [1024, 16384], seed 4",
+            "tokens_attended": r["tokens"],
+            "pool_blocks": r["case"].num_blocks,
+            "split_tokens": r["split"],
+        },
+        "hbm_frac": round(value / PEAK_HBM_GBPS, 4),
+        "layer_step_tokens_per_s_attention_only": round(len(r["case"].context_lens) / (ms * 1e-3), 1),
+        "roofline": {
+            "kernel": "mi_paged_gqa_decode (split-K partial + combine)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "avg_launch_ms": round(attn_ms, 5),
+            "algorithmic_bytes": int(r["attn_bytes"]),
+            "traffic": None,
+        },
+    }
+    if not args.no_layer:
+        try:
+            line["layer_step"] = run_layer_bench(args, torch, mk, workloads)
+        except mk.MikvError as e:
+            line["layer_step"] = {"error": str(e)}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(r["case"], r["cfg"], workloads, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,303 @@
+/*
+ * mikv -- paged-KV grouped-query-attention decode for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmikv.so. Everything crossing this boundary is a plain pointer
+ * (host or device, as stated per argument), an integer or a float. bf16
+ * tensors are passed as uint16_t bit patterns; every tensor is row-major and
+ * contiguous. No call synchronises the device unless its comment says so.
+ *
+ * The operations follow the pages this library implements:
+ *  - mini-infer README, "Project overview": the KV cache is a pool of
+ *    fixed-size blocks with a free-block pool and one BlockTable per request;
+ *    "decode_batch key steps": gather each request's K/V through its
+ *    BlockTable, run the batched forward, write the new token's K/V back
+ *    (write_decode_kv).
+ *  - On-device LLM inference course project, section 2.1: RMSNorm, RoPE,
+ *    QKV projection with grouped-query attention (query head h reads KV head
+ *    h / (Hq / Hkv), as repeat_interleave of the KV heads gives), SwiGLU MLP,
+ *    decoder layer with residuals and two norms, KV-cache append.
+ *  - nxmr.cn inference-techniques article: section 2.1, a request of n
+ *    tokens holds ceil(n / block_size) pages popped from a free list;
+ *    section 5.1, the numerically stable softmax; section 4.1, attention
+ *    scores in FP32.
+ *  - MegEngine/InferLLM article, section 4.2 "problem two": KV bytes =
+ *    2 * batch * layers * seq_len * hidden * sizeof(dtype).
+ *
+ * Conventions (readings where the pages are silent):
+ *  - Pool layout: per layer one K pool and one V pool, each
+ *    [num_blocks, num_kv_heads, block_size, head_dim] bf16.
+ *  - block_table: int32 [batch, max_blocks_per_seq], device memory. Row b
+ *    maps logical block j of sequence b to a physical block id in
+ *    [0, num_blocks). Entries at j >= ceil((context_lens[b] + 1) / block_size)
+ *    are never read (tests fill them with -1).
+ *  - context_lens: int32 [batch], device memory, the number of tokens cached
+ *    BEFORE this step. The new token goes to logical position context_lens[b],
+ *    which is also its RoPE position; attention covers context_lens[b] + 1
+ *    tokens, the new one included. Both per-step calls take the same array;
+ *    the caller advances it afterwards.
+ *  - RoPE pairs dimension i with i + head_dim/2, inv_freq_i =
+ *    theta^(-2i/head_dim), integer positions; q and the new k are rotated,
+ *    v never. Cached K is stored already rotated.
+ *  - Supported shapes: block_size 16, head_dim 64 or 128, num_q_heads a
+ *    multiple of num_kv_heads with group size 1..8. Others return
+ *    MI_ERR_UNSUPPORTED.
+ *
+ * Ownership: every device pointer argument (q, k, v, outputs, tables,
+ * lengths, workspaces, weights) is owned by the caller and must stay valid
+ * until the work queued on `stream` has finished; the library keeps no
+ * reference after the call returns. A pool handle is owned by the library
+ * and freed by mi_kv_pool_destroy. A pool handle is not thread-safe.
+ *
+ * Errors: every call returns MI_OK or a negative status, never aborts and
+ * never prints. Device-resident values (block ids, lengths) cannot be checked
+ * without a sync: the kernels range-check every block id and length they
+ * read, skip the access when it is out of range, and record the fault in a
+ * per-pool device error word that mi_kv_pool_check_errors reads back.
+ *
+ * `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ */
+#ifndef MIKV_H
+#define MIKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MI_OK = 0,
+    MI_ERR_INVALID_ARG = -1,          /* null pointer, negative size, bad flag */
+    MI_ERR_OUT_OF_MEMORY = -2,        /* host or device allocation failed */
+    MI_ERR_NO_FREE_BLOCKS = -3,       /* free-block pool cannot satisfy the request */
+    MI_ERR_HIP = -4,                  /* a HIP runtime call or kernel launch failed */
+    MI_ERR_UNSUPPORTED = -5,          /* valid but unsupported shape */
+    MI_ERR_WORKSPACE_TOO_SMALL = -6,  /* workspace_bytes below the size query */
+    MI_ERR_DEVICE_FAULT = -7          /* mi_kv_pool_check_errors found a recorded fault */
+};
+
+/* Device error-word bits (mi_kv_pool_check_errors). */
+enum {
+    MI_FAULT_BLOCK_ID = 1u,           /* a block-table entry outside [0, num_blocks) */
+    MI_FAULT_CONTEXT_LEN = 2u         /* a length < 0, beyond the table row or beyond max_context_len */
+};
+
+/* Pool flags. */
+enum {
+    MI_POOL_HOST_ONLY = 1u            /* block bookkeeping only: no device memory, no kernels */
+};
+
+/* Static description of a status code. Never NULL. */
+const char* mi_status_string(int status);
+
+typedef struct mi_kv_pool_s* mi_kv_pool_t;
+
+/*
+ * Create a paged KV pool of one layer (mini-infer "KVCacheManager": block
+ * tensor plus free-block pool).
+ *  out          host pointer receiving the handle
+ *  num_blocks   > 0
+ *  block_size   must be 16
+ *  num_kv_heads > 0
+ *  head_dim     64 or 128
+ *  k_cache, v_cache  both NULL: the library allocates both pools in device
+ *               memory (contents undefined) and frees them on destroy. Both
+ *               non-NULL: caller-owned device buffers of
+ *               num_blocks*num_kv_heads*block_size*head_dim bf16 each, never
+ *               freed by the library. One NULL and one not: MI_ERR_INVALID_ARG.
+ *  flags        0 or MI_POOL_HOST_ONLY (then k_cache/v_cache must be NULL and
+ *               every kernel call on the pool returns MI_ERR_INVALID_ARG).
+ * The free-block stack starts full; the first allocation returns ids 0, 1, ...
+ * The current HIP device at this call is the pool's device.
+ */
+int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim,
+                    void* k_cache, void* v_cache, uint32_t flags);
+
+/* Free the handle, library-owned pools and the error word. NULL is a no-op. */
+int mi_kv_pool_destroy(mi_kv_pool_t pool);
+
+/* Device pointers of the K and V pools (NULL for a host-only pool). */
+int mi_kv_pool_get(mi_kv_pool_t pool, void** k_cache, void** v_cache);
+
+/* Shape query: any output pointer may be NULL. */
+int mi_kv_pool_shape(mi_kv_pool_t pool, int32_t* num_blocks, int32_t* block_size,
+                     int32_t* num_kv_heads, int32_t* head_dim);
+
+/*
+ * Free-block pool (nxmr.cn article, section 2.1: pop one free page per page
+ * needed). A LIFO stack: freed ids are handed out again last-in first-out.
+ *  mi_kv_alloc_blocks  pops n ids into host array out_ids[n]; if fewer than n
+ *                      are free, returns MI_ERR_NO_FREE_BLOCKS and pops none.
+ *  mi_kv_free_blocks   pushes host array ids[n] back in order; an id out of
+ *                      range, not allocated, or repeated returns
+ *                      MI_ERR_INVALID_ARG and frees none.
+ *  mi_kv_num_free_blocks  free count, or a negative status for a NULL pool.
+ *  mi_kv_blocks_needed ceil(num_tokens / block_size) for num_tokens >= 0.
+ */
+int mi_kv_alloc_blocks(mi_kv_pool_t pool, int32_t n, int32_t* out_ids);
+int mi_kv_free_blocks(mi_kv_pool_t pool, int32_t n, const int32_t* ids);
+int32_t mi_kv_num_free_blocks(mi_kv_pool_t pool);
+int32_t mi_kv_blocks_needed(int32_t num_tokens, int32_t block_size);
+
+/*
+ * Bytes of the K and V caches by the InferLLM article's formula, section 4.2
+ * problem two, with hidden = num_kv_heads * head_dim and 2-byte elements.
+ */
+uint64_t mi_kv_cache_bytes(int64_t batch, int64_t layers, int64_t max_seq_len,
+                           int64_t num_kv_heads, int64_t head_dim);
+
+/*
+ * Read and clear the pool's device error word (MI_FAULT_* bits) into
+ * *fault_bits (host pointer, may be NULL). Synchronises the device. Returns
+ * MI_ERR_DEVICE_FAULT if any bit was set, else MI_OK.
+ */
+int mi_kv_pool_check_errors(mi_kv_pool_t pool, uint32_t* fault_bits);
+
+/*
+ * write_decode_kv: RoPE, then append (mini-infer "decode_batch" step 4;
+ * course project 2.1 RoPE and KV-cache append).
+ *  q      device bf16 [batch, num_q_heads, head_dim]
+ *  k, v   device bf16 [batch, num_kv_heads, head_dim]
+ *  q_rot  device bf16 [batch, num_q_heads, head_dim]; may alias q exactly
+ *  For each sequence b at pos = context_lens[b]: K[slot] = bf16(RoPE(k, pos)),
+ *  V[slot] = v (bit copy) for every kv head, q_rot = bf16(RoPE(q, pos)), where
+ *  slot = (block_table[b][pos / 16], pos % 16). The angle and the rotation are
+ *  computed in float64 and rounded once to bf16 (nearest, ties to even).
+ *  batch == 0 is a no-op.
+ */
+int mi_write_decode_kv(mi_kv_pool_t pool,
+                       const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       uint16_t* q_rot,
+                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t batch,
+                       int32_t num_q_heads, double rope_theta, void* stream);
+
+/*
+ * Workspace bytes needed by mi_paged_gqa_decode for this batch when every
+ * context_lens[b] <= max_context_len (fp32 split-K partials plus padding).
+ */
+size_t mi_paged_gqa_decode_workspace_bytes(mi_kv_pool_t pool, int32_t batch,
+                                           int32_t num_q_heads,
+                                           int32_t max_context_len);
+
+/*
+ * Paged GQA decode attention (mini-infer gather + attention, fused: the
+ * gather through the block table is never materialised). For each sequence b
+ * and query head h, with g = h / (num_q_heads / num_kv_heads) and
+ * L = context_lens[b] + 1:
+ *     s_t = scale * <q_rot[b,h], K[slot(b,t), g]>,  t < L
+ *     out[b,h] = sum_t softmax(s)_t V[slot(b,t), g]
+ * computed as split-K online softmax in fp32 and rounded once to bf16.
+ *  q_rot   device bf16 [batch, num_q_heads, head_dim] (as written by
+ *          mi_write_decode_kv)
+ *  out     device bf16 [batch, num_q_heads, head_dim]; must not alias q_rot
+ *  softmax_scale  <= 0 selects 1/sqrt(head_dim)
+ *  max_context_len  host-side upper bound of context_lens[b]; sizes the grid
+ *          and the workspace. A larger length is a fault (error word) and
+ *          that sequence's output is undefined.
+ *  workspace  device buffer of at least the queried bytes (caller-owned,
+ *          contents need not be initialised).
+ * Tail slots of the last block and blocks past the sequence may hold any
+ * bits (NaN included): they are excluded by selection, never by
+ * multiplication with zero. The reduction order depends only on logical
+ * positions, so results are bit-identical under any relabelling of physical
+ * blocks.
+ */
+int mi_paged_gqa_decode(mi_kv_pool_t pool, const uint16_t* q_rot, uint16_t* out,
+                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t batch,
+                        int32_t num_q_heads, float softmax_scale,
+                        int32_t max_context_len,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Same as mi_paged_gqa_decode with an explicit split size: split_tokens is
+ * the number of tokens per split-K chunk (a positive multiple of 16), or 0
+ * for the library's choice. The workspace query for an explicit split size
+ * is mi_paged_gqa_decode_split_workspace_bytes.
+ */
+int mi_paged_gqa_decode_split(mi_kv_pool_t pool, const uint16_t* q_rot, uint16_t* out,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t batch,
+                              int32_t num_q_heads, float softmax_scale,
+                              int32_t max_context_len, int32_t split_tokens,
+                              void* workspace, size_t workspace_bytes, void* stream);
+size_t mi_paged_gqa_decode_split_workspace_bytes(mi_kv_pool_t pool, int32_t batch,
+                                                 int32_t num_q_heads,
+                                                 int32_t max_context_len,
+                                                 int32_t split_tokens);
+
+/*
+ * Debug export of the gather step (mini-infer gather_batch_kv): bit copies of
+ * K and V of positions [0, context_lens[b] + len_extra) of every sequence and
+ * kv head into k_out / v_out, device bf16 [batch, num_kv_heads, l_max,
+ * head_dim]. Positions at or beyond that length are not written.
+ * len_extra is 0 or 1; every context_lens[b] + len_extra must be <= l_max.
+ */
+int mi_gather_kv(mi_kv_pool_t pool, const int32_t* block_table,
+                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                 int32_t batch, int32_t len_extra,
+                 uint16_t* k_out, uint16_t* v_out, int32_t l_max, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Full decoder-layer decode step (course project 2.1: RMSNorm, QKV with
+ * GQA, RoPE, KV append, attention, o_proj, residual, RMSNorm, SwiGLU,
+ * residual), pre-norm:
+ *   r1 = RMSNorm(x) * ln1_w;  [q|k|v] = r1 W_qkv^T
+ *   write_decode_kv (RoPE, append);  o = paged GQA attention
+ *   x2 = x + o W_o^T;  r2 = RMSNorm(x2) * ln2_w
+ *   x_out = x2 + (silu(r2 W_gate^T) * (r2 W_up^T)) W_down^T
+ * Weights are device bf16 in nn.Linear layout [out_features, in_features];
+ * w_qkv rows are q (num_q_heads*head_dim), then k, then v
+ * (num_kv_heads*head_dim each). The projections run on bf16 MFMA with fp32
+ * accumulation; norms, RoPE angle and softmax in fp32/fp64 as above.
+ * Supported: hidden and intermediate multiples of 256, batch 1..32.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t hidden;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t intermediate;
+    float rms_eps;
+    double rope_theta;
+} mi_layer_config;
+
+typedef struct {
+    const uint16_t* ln1_w;    /* [hidden] */
+    const uint16_t* w_qkv;    /* [(num_q_heads + 2*num_kv_heads)*head_dim, hidden] */
+    const uint16_t* w_o;      /* [hidden, num_q_heads*head_dim] */
+    const uint16_t* ln2_w;    /* [hidden] */
+    const uint16_t* w_gate;   /* [intermediate, hidden] */
+    const uint16_t* w_up;     /* [intermediate, hidden] */
+    const uint16_t* w_down;   /* [hidden, intermediate] */
+} mi_layer_weights;
+
+/* Workspace bytes needed by mi_decoder_layer_decode (host-side query). */
+size_t mi_decoder_layer_workspace_bytes(const mi_layer_config* cfg, mi_kv_pool_t pool,
+                                        int32_t batch, int32_t max_context_len);
+
+/*
+ * One decode step of one layer for `batch` sequences.
+ *  cfg, w    host pointers to the structs above (read during the call only)
+ *  x_in      device bf16 [batch, hidden]
+ *  x_out     device bf16 [batch, hidden]; must not alias x_in
+ *  block_table, max_blocks_per_seq, context_lens, max_context_len: as for
+ *            mi_paged_gqa_decode (the new token is appended at context_lens[b])
+ *  workspace device buffer of at least mi_decoder_layer_workspace_bytes
+ */
+int mi_decoder_layer_decode(mi_kv_pool_t pool, const mi_layer_config* cfg,
+                            const mi_layer_weights* w,
+                            const uint16_t* x_in, uint16_t* x_out,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch,
+                            int32_t max_context_len,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIKV_H */

@@ -1,0 +1,254 @@
+"""Python binding of libmikv.so (paged-KV GQA decode for MI355X / gfx950).
+
+Argument marshalling only: every function below forwards to the C entry
+point of the same name declared in include/mikv.h. Device buffers are given
+as torch tensors (or raw integer addresses); PyTorch supplies device memory
+and the current HIP stream. No computation happens here, and there is no
+fallback: if the shared library is missing the import of any entry point
+raises.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmikv.so")
+
+MI_OK = 0
+MI_ERR_INVALID_ARG = -1
+MI_ERR_OUT_OF_MEMORY = -2
+MI_ERR_NO_FREE_BLOCKS = -3
+MI_ERR_HIP = -4
+MI_ERR_UNSUPPORTED = -5
+MI_ERR_WORKSPACE_TOO_SMALL = -6
+MI_ERR_DEVICE_FAULT = -7
+
+MI_FAULT_BLOCK_ID = 1
+MI_FAULT_CONTEXT_LEN = 2
+MI_POOL_HOST_ONLY = 1
+
+_c = ctypes
+_vp = _c.c_void_p
+_i32 = _c.c_int32
+_u32 = _c.c_uint32
+_i64 = _c.c_int64
+_sz = _c.c_size_t
+
+# name -> (restype, argtypes); the same list as include/mikv.h
+SIGNATURES = {
+    "mi_status_string": (_c.c_char_p, [_c.c_int]),
+    "mi_kv_pool_init": (_c.c_int, [_c.POINTER(_vp), _i32, _i32, _i32, _i32, _vp, _vp, _u32]),
+    "mi_kv_pool_destroy": (_c.c_int, [_vp]),
+    "mi_kv_pool_get": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp)]),
+    "mi_kv_pool_shape": (_c.c_int, [_vp, _c.POINTER(_i32), _c.POINTER(_i32), _c.POINTER(_i32),
+                                    _c.POINTER(_i32)]),
+    "mi_kv_alloc_blocks": (_c.c_int, [_vp, _i32, _c.POINTER(_i32)]),
+    "mi_kv_free_blocks": (_c.c_int, [_vp, _i32, _c.POINTER(_i32)]),
+    "mi_kv_num_free_blocks": (_i32, [_vp]),
+    "mi_kv_blocks_needed": (_i32, [_i32, _i32]),
+    "mi_kv_cache_bytes": (_c.c_uint64, [_i64, _i64, _i64, _i64, _i64]),
+    "mi_kv_pool_check_errors": (_c.c_int, [_vp, _c.POINTER(_u32)]),
+    "mi_write_decode_kv": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                      _c.c_double, _vp]),
+    "mi_paged_gqa_decode_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
+    "mi_paged_gqa_decode": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _c.c_float,
+                                       _i32, _vp, _sz, _vp]),
+    "mi_paged_gqa_decode_split": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                             _c.c_float, _i32, _i32, _vp, _sz, _vp]),
+    "mi_paged_gqa_decode_split_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32]),
+    "mi_gather_kv": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp]),
+    "mi_decoder_layer_workspace_bytes": (_sz, [_vp, _vp, _i32, _i32]),
+    "mi_decoder_layer_decode": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                           _vp, _sz, _vp]),
+}
+
+
+class MiLayerConfig(ctypes.Structure):
+    _fields_ = [("hidden", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
+                ("head_dim", _i32), ("intermediate", _i32), ("rms_eps", _c.c_float),
+                ("rope_theta", _c.c_double)]
+
+
+class MiLayerWeights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("ln1_w", "w_qkv", "w_o", "ln2_w", "w_gate", "w_up", "w_down")]
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libmikv.so with argument types set. Raises if it is not built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmikv.so is not built (%s); run "
+                              "`python -m paged_kv_cache_246_amd.build`" % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+class MikvError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__("%s failed: %d (%s)" % (fn, status, status_string(status)))
+        self.status = status
+
+
+def status_string(status):
+    return lib().mi_status_string(status).decode()
+
+
+def _check(fn, rc):
+    if rc != MI_OK:
+        raise MikvError(fn, rc)
+    return rc
+
+
+def _ptr(x):
+    """Device/host address of a torch tensor, or an integer address, or None -> NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ------------------------------------------------------------------ pool
+def mi_kv_pool_init(num_blocks, block_size, num_kv_heads, head_dim, k_cache=None,
+                    v_cache=None, flags=0):
+    h = _vp()
+    _check("mi_kv_pool_init", lib().mi_kv_pool_init(
+        ctypes.byref(h), num_blocks, block_size, num_kv_heads, head_dim,
+        _ptr(k_cache), _ptr(v_cache), flags))
+    return h.value
+
+
+def mi_kv_pool_destroy(pool):
+    return _check("mi_kv_pool_destroy", lib().mi_kv_pool_destroy(pool))
+
+
+def mi_kv_pool_get(pool):
+    k, v = _vp(), _vp()
+    _check("mi_kv_pool_get", lib().mi_kv_pool_get(pool, ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
+
+
+def mi_kv_pool_shape(pool):
+    vals = [_i32() for _ in range(4)]
+    _check("mi_kv_pool_shape", lib().mi_kv_pool_shape(pool, *[ctypes.byref(x) for x in vals]))
+    return tuple(x.value for x in vals)
+
+
+def mi_kv_alloc_blocks(pool, n):
+    ids = (_i32 * max(n, 1))()
+    _check("mi_kv_alloc_blocks", lib().mi_kv_alloc_blocks(pool, n, ids))
+    return [ids[i] for i in range(n)]
+
+
+def mi_kv_free_blocks(pool, ids):
+    ids = list(ids)
+    arr = (_i32 * max(len(ids), 1))(*ids)
+    return _check("mi_kv_free_blocks", lib().mi_kv_free_blocks(pool, len(ids), arr))
+
+
+def mi_kv_num_free_blocks(pool):
+    n = lib().mi_kv_num_free_blocks(pool)
+    if n < 0:
+        raise MikvError("mi_kv_num_free_blocks", n)
+    return n
+
+
+def mi_kv_blocks_needed(num_tokens, block_size):
+    n = lib().mi_kv_blocks_needed(num_tokens, block_size)
+    if n < 0:
+        raise MikvError("mi_kv_blocks_needed", n)
+    return n
+
+
+def mi_kv_cache_bytes(batch, layers, max_seq_len, num_kv_heads, head_dim):
+    return lib().mi_kv_cache_bytes(batch, layers, max_seq_len, num_kv_heads, head_dim)
+
+
+def mi_kv_pool_check_errors(pool):
+    """Returns the fault bits (0 if none). Synchronises the device."""
+    bits = _u32()
+    rc = lib().mi_kv_pool_check_errors(pool, ctypes.byref(bits))
+    if rc not in (MI_OK, MI_ERR_DEVICE_FAULT):
+        raise MikvError("mi_kv_pool_check_errors", rc)
+    return bits.value
+
+
+# ------------------------------------------------------------- decode step
+def mi_write_decode_kv(pool, q, k, v, q_rot, block_table, max_blocks_per_seq, context_lens,
+                       batch, num_q_heads, rope_theta, stream=None):
+    return _check("mi_write_decode_kv", lib().mi_write_decode_kv(
+        pool, _ptr(q), _ptr(k), _ptr(v), _ptr(q_rot), _ptr(block_table), max_blocks_per_seq,
+        _ptr(context_lens), batch, num_q_heads, float(rope_theta), _stream(stream)))
+
+
+def mi_paged_gqa_decode_workspace_bytes(pool, batch, num_q_heads, max_context_len):
+    return lib().mi_paged_gqa_decode_workspace_bytes(pool, batch, num_q_heads, max_context_len)
+
+
+def mi_paged_gqa_decode_split_workspace_bytes(pool, batch, num_q_heads, max_context_len,
+                                              split_tokens):
+    return lib().mi_paged_gqa_decode_split_workspace_bytes(pool, batch, num_q_heads,
+                                                           max_context_len, split_tokens)
+
+
+def mi_paged_gqa_decode(pool, q_rot, out, block_table, max_blocks_per_seq, context_lens, batch,
+                        num_q_heads, softmax_scale, max_context_len, workspace,
+                        workspace_bytes, stream=None):
+    return _check("mi_paged_gqa_decode", lib().mi_paged_gqa_decode(
+        pool, _ptr(q_rot), _ptr(out), _ptr(block_table), max_blocks_per_seq,
+        _ptr(context_lens), batch, num_q_heads, float(softmax_scale), max_context_len,
+        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mi_paged_gqa_decode_split(pool, q_rot, out, block_table, max_blocks_per_seq, context_lens,
+                              batch, num_q_heads, softmax_scale, max_context_len, split_tokens,
+                              workspace, workspace_bytes, stream=None):
+    return _check("mi_paged_gqa_decode_split", lib().mi_paged_gqa_decode_split(
+        pool, _ptr(q_rot), _ptr(out), _ptr(block_table), max_blocks_per_seq,
+        _ptr(context_lens), batch, num_q_heads, float(softmax_scale), max_context_len,
+        split_tokens, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mi_gather_kv(pool, block_table, max_blocks_per_seq, context_lens, batch, len_extra, k_out,
+                 v_out, l_max, stream=None):
+    return _check("mi_gather_kv", lib().mi_gather_kv(
+        pool, _ptr(block_table), max_blocks_per_seq, _ptr(context_lens), batch, len_extra,
+        _ptr(k_out), _ptr(v_out), l_max, _stream(stream)))
+
+
+# -------------------------------------------------------------- full layer
+def layer_config(hidden, num_q_heads, num_kv_heads, head_dim, intermediate, rms_eps, rope_theta):
+    return MiLayerConfig(hidden, num_q_heads, num_kv_heads, head_dim, intermediate,
+                         rms_eps, rope_theta)
+
+
+def layer_weights(ln1_w, w_qkv, w_o, ln2_w, w_gate, w_up, w_down):
+    return MiLayerWeights(*[_ptr(x) for x in (ln1_w, w_qkv, w_o, ln2_w, w_gate, w_up, w_down)])
+
+
+def mi_decoder_layer_workspace_bytes(cfg, pool, batch, max_context_len):
+    return lib().mi_decoder_layer_workspace_bytes(ctypes.byref(cfg), pool, batch, max_context_len)
+
+
+def mi_decoder_layer_decode(pool, cfg, weights, x_in, x_out, block_table, max_blocks_per_seq,
+                            context_lens, batch, max_context_len, workspace, workspace_bytes,
+                            stream=None):
+    return _check("mi_decoder_layer_decode", lib().mi_decoder_layer_decode(
+        pool, ctypes.byref(cfg), ctypes.byref(weights), _ptr(x_in), _ptr(x_out),
+        _ptr(block_table), max_blocks_per_seq, _ptr(context_lens), batch, max_context_len,
+        _ptr(workspace), workspace_bytes, _stream(stream)))

@@ -1,0 +1,655 @@
+// Paged-KV decode kernels for gfx950 (CDNA4): write_decode_kv (RoPE, then
+// append), split-K paged GQA decode attention with its combine, and the
+// gather-through-the-block-table export used by tests.
+//
+// Pages: mini-infer README, "decode_batch key steps" (gather through the
+// BlockTable, forward, write_decode_kv); course project section 2.1 (RoPE,
+// GQA with KV heads shared by groups of query heads, KV-cache append);
+// nxmr.cn inference-techniques article, section 5.1 (stable softmax: subtract
+// the maximum, exponentiate, normalise by the sum) and section 4.1 (scores in
+// FP32 or better).
+//
+// Data layout: K and V pools [num_blocks, Hkv, 16, D] bf16. One (block, kv
+// head) tile is 16 * D * 2 bytes (4 KiB at D = 128), contiguous.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "internal.h"
+
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int BS = 16;                // tokens per KV block
+constexpr float kNegInf = -INFINITY;
+constexpr float kRescaleSlack = 8.0f; // log2 units: running max may lag by 2^8
+
+// ---------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// float64 -> bf16, nearest-even, a single rounding: truncate to float32 with a
+// sticky bit (round-to-odd keeps 16 guard bits), then round that to bf16.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+    if (x != x) return 0x7fc0;
+    const float f = __double2float_rz(x);
+    uint32_t u = __float_as_uint(f);
+    if (static_cast<double>(f) != x) u |= 1u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ double bf16_to_f64(uint16_t h) {
+    return static_cast<double>(__uint_as_float(static_cast<uint32_t>(h) << 16));
+}
+
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
+                                          __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
+                                          __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
+                                          __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
+                                          __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+    return acc;
+}
+
+// DPP lane exchanges inside a row of 16 lanes.
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7-i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;    // lane i <- lane 15-i within each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 8 consecutive lanes that share one token row; every lane of
+// the 8 ends with the same bits (each step adds a commutative pair).
+__device__ __forceinline__ float sum8(float x) {
+    x += dpp<kDppQuadSwap1>(x);
+    x += dpp<kDppQuadSwap2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    return x;
+}
+
+__device__ __forceinline__ uint4 ld16(const char* base, uint32_t off) {
+    return *reinterpret_cast<const uint4*>(base + off);
+}
+
+// ============================================================== write_decode_kv
+// One workgroup per sequence. The D/2 angles pos * theta^(-2i/D) and their
+// sines and cosines are float64 (fp32 loses ~1e-3 rad at pos 16K); each
+// rotated pair is computed in float64 with separately rounded products and
+// rounded once to bf16.
+template <int D>
+__global__ __launch_bounds__(256) void write_decode_kv_kernel(
+    const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* q_rot, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
+    int32_t hq, int32_t hkv, int32_t num_blocks, double theta, uint32_t* __restrict__ err) {
+    constexpr int H2 = D / 2;
+    __shared__ double cs[H2];
+    __shared__ double sn[H2];
+    const int b = blockIdx.x;
+    const int pos = ctx_lens[b];
+    const bool pos_ok = pos >= 0 && pos / BS < mbps;
+    const int32_t blk = pos_ok ? table[static_cast<size_t>(b) * mbps + pos / BS] : -1;
+    const bool blk_ok = pos_ok && blk >= 0 && blk < num_blocks;
+    if (threadIdx.x == 0) {
+        if (!pos_ok) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+        else if (!blk_ok) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+    }
+    if (!pos_ok) return;
+    for (int i = threadIdx.x; i < H2; i += blockDim.x) {
+        const double inv_freq = pow(theta, -2.0 * i / D);
+        const double a = static_cast<double>(pos) * inv_freq;
+        double s, c;
+        sincos(a, &s, &c);
+        cs[i] = c;
+        sn[i] = s;
+    }
+    __syncthreads();
+    const int nh = hq + (blk_ok ? hkv : 0);
+    const int off = pos % BS;
+    for (int idx = threadIdx.x; idx < nh * H2; idx += blockDim.x) {
+        const int h = idx / H2;
+        const int i = idx - h * H2;
+        const uint16_t* src;
+        uint16_t* dst;
+        if (h < hq) {
+            src = q + (static_cast<size_t>(b) * hq + h) * D;
+            dst = q_rot + (static_cast<size_t>(b) * hq + h) * D;
+        } else {
+            const int g = h - hq;
+            src = k + (static_cast<size_t>(b) * hkv + g) * D;
+            dst = kc + ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
+        }
+        const double x1 = bf16_to_f64(src[i]);
+        const double x2 = bf16_to_f64(src[i + H2]);
+        const double y1 = __dsub_rn(__dmul_rn(x1, cs[i]), __dmul_rn(x2, sn[i]));
+        const double y2 = __dadd_rn(__dmul_rn(x2, cs[i]), __dmul_rn(x1, sn[i]));
+        dst[i] = f64_to_bf16_rne(y1);
+        dst[i + H2] = f64_to_bf16_rne(y2);
+    }
+    if (blk_ok) {
+        // V is a bit copy, 16 bytes per thread
+        const int n16 = hkv * D / 8;
+        for (int idx = threadIdx.x; idx < n16; idx += blockDim.x) {
+            const int g = idx / (D / 8);
+            const int e = (idx - g * (D / 8)) * 8;
+            const uint4 val = *reinterpret_cast<const uint4*>(v + (static_cast<size_t>(b) * hkv + g) * D + e);
+            *reinterpret_cast<uint4*>(vc + ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D + e) = val;
+        }
+    }
+}
+
+// Lane layout of a 16-token (block, kv head) tile for LAM lanes per token row:
+// lane = LAM * r + c holds tokens r, r + TPI, r + 2 TPI, ... (TPI = 64 / LAM
+// tokens per load instruction) and, of each token, the 16-byte pieces
+// c + LAM * j (j < NJ) of its row. Each 128-bit load instruction then covers
+// TPI whole row segments of LAM * 16 bytes (>= one 128-byte line).
+template <int D, int LAM>
+struct TileShape {
+    static constexpr int TPI = 64 / LAM;          // tokens per load instruction
+    static constexpr int NT = BS / TPI;           // tokens per lane per tile
+    static constexpr int NJ = D / (8 * LAM);      // 16-byte pieces per lane per token
+    static_assert(NJ >= 1 && NJ * 8 * LAM == D, "head_dim / lane split mismatch");
+};
+
+template <int NT, int NJ>
+__device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, size_t blk_stride,
+                                          int32_t id, const uint32_t (&loff)[NT][NJ],
+                                          uint4 (&kr)[NT][NJ], uint4 (&vr)[NT][NJ]) {
+    const char* kb = kbase + static_cast<size_t>(id) * blk_stride;
+    const char* vb = vbase + static_cast<size_t>(id) * blk_stride;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) kr[t][j] = ld16(kb, loff[t][j]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) vr[t][j] = ld16(vb, loff[t][j]);
+}
+
+// Sum over the LAM consecutive lanes of one token row.
+template <int LAM>
+__device__ __forceinline__ float row_sum(float x) {
+    x = sum8(x);
+    if (LAM == 16) x += dpp<kDppRowMirror>(x);
+    return x;
+}
+
+// One 16-token tile: scores of the lane's NT tokens for the G heads,
+// online-softmax update, weighted V accumulation. With TAIL, token rows >=
+// valid_rows are excluded by selection (their K/V bits may be NaN).
+template <int LAM, int NT, int NJ, int G, bool TAIL>
+__device__ __forceinline__ void consume_tile(uint4 (&kr)[NT][NJ], uint4 (&vr)[NT][NJ],
+                                             const uint4 (&qv)[G][NJ], float scale_log2,
+                                             int valid_rows, int r, float (&m)[G], float (&l)[G],
+                                             float (&acc)[G][NJ][8]) {
+    constexpr int TPI = 64 / LAM;
+    float s[NT][G];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float a = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) a = dot8_bf16(qv[h][j], kr[t][j], a);
+            s[t][h] = row_sum<LAM>(a) * scale_log2;
+        }
+    bool valid[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        valid[t] = true;
+        if (TAIL) {
+            valid[t] = t * TPI + r < valid_rows;
+            if (!valid[t]) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) s[t][h] = kNegInf;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) vr[t][j] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float mx = s[0][h];
+#pragma unroll
+        for (int t = 1; t < NT; ++t) mx = fmaxf(mx, s[t][h]);
+        if (mx > m[h] + kRescaleSlack) {
+            const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
+            m[h] = mx;
+            l[h] *= alpha;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][j][e] *= alpha;
+        }
+        float p[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            p[t] = __builtin_amdgcn_exp2f(s[t][h] - m[h]);
+            if (TAIL) p[t] = valid[t] ? p[t] : 0.f;
+            l[h] += p[t];
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint32_t w[4] = {vr[t][j].x, vr[t][j].y, vr[t][j].z, vr[t][j].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[h][j][2 * e] = fmaf(p[t], bf16_lo(w[e]), acc[h][j][2 * e]);
+                    acc[h][j][2 * e + 1] = fmaf(p[t], bf16_hi(w[e]), acc[h][j][2 * e + 1]);
+                }
+            }
+    }
+}
+
+// ====================================================== paged GQA decode, split-K
+// One wavefront per (split-K chunk, kv head, sequence); a chunk is
+// chunk_blocks consecutive logical blocks. The wave's G query heads share
+// every K/V tile; q.k runs on packed bf16 dot products with fp32
+// accumulation, summed over the lanes of a token row by DPP. Every lane keeps
+// an online softmax over its own token stream (running max m, sum l,
+// weighted V sum acc); the token rows are merged once at the end of the
+// chunk and written as an fp32 partial (m, l, acc).
+template <int D, int G, int LAM>
+__global__ __launch_bounds__(64) void paged_attn_partial_kernel(
+    const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
+    const int32_t* __restrict__ ctx_lens, int32_t hkv, int32_t num_blocks, int32_t max_ctx,
+    int32_t chunk_blocks, int32_t S, float scale_log2, float* __restrict__ part_acc,
+    float2* __restrict__ part_ml, uint32_t* __restrict__ err) {
+    using TS = TileShape<D, LAM>;
+    constexpr int NT = TS::NT;
+    constexpr int NJ = TS::NJ;
+    constexpr int TPI = TS::TPI;
+    constexpr uint32_t ROW = D * 2;            // bytes per token row
+    constexpr size_t TILE = BS * D * 2;        // bytes per (block, head) tile
+    const int chunk = blockIdx.x;
+    const int g = blockIdx.y;
+    const int b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int r = lane / LAM;
+    const int c = lane % LAM;
+
+    const int ctx = ctx_lens[b];
+    if (ctx < 0 || ctx > max_ctx || ctx + 1 > mbps * BS) {
+        if (chunk == 0 && g == 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+        return;
+    }
+    const int L = ctx + 1;
+    const int t_begin = chunk * chunk_blocks * BS;
+    if (t_begin >= L) return;
+    const int t_end = min(L, t_begin + chunk_blocks * BS);
+    const int nblk = (t_end - t_begin + BS - 1) / BS;
+    const int lb0 = chunk * chunk_blocks;
+
+    // q of the group's G heads: this lane's pieces
+    uint4 qv[G][NJ];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            qv[h][j] = *reinterpret_cast<const uint4*>(
+                q_rot + (static_cast<size_t>(b) * hkv * G + g * G + h) * D + (c + LAM * j) * 8);
+
+    // this chunk's block ids, one per lane (chunk_blocks <= 64)
+    int32_t my_id = 0;
+    if (lane < nblk) my_id = table[static_cast<size_t>(b) * mbps + lb0 + lane];
+    const bool bad_id = lane < nblk && (my_id < 0 || my_id >= num_blocks);
+    if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+    if (bad_id) my_id = 0;
+
+    float m[G], l[G];
+    float acc[G][NJ][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = kNegInf;
+        l[h] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][j][e] = 0.f;
+    }
+
+    const char* kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
+    const char* vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
+    const size_t blk_stride = static_cast<size_t>(hkv) * TILE;
+    uint32_t loff[NT][NJ];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) loff[t][j] = (t * TPI + r) * ROW + (c + LAM * j) * 16;
+
+    uint4 kr[NT][NJ], vr[NT][NJ];
+    load_tile<NT, NJ>(kbase, vbase, blk_stride, __builtin_amdgcn_readfirstlane(my_id), loff, kr, vr);
+    // Steady state: the next block's loads are always in flight while the
+    // current one is consumed (an unconditional prefetch keeps the waitcnt
+    // exact). Only the last block of a chunk can be partial.
+    for (int i = 0; i + 1 < nblk; ++i) {
+        uint4 kn[NT][NJ], vn[NT][NJ];
+        load_tile<NT, NJ>(kbase, vbase, blk_stride, __builtin_amdgcn_readlane(my_id, i + 1), loff, kn, vn);
+        consume_tile<LAM, NT, NJ, G, false>(kr, vr, qv, scale_log2, 0, r, m, l, acc);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                kr[t][j] = kn[t][j];
+                vr[t][j] = vn[t][j];
+            }
+    }
+    {
+        const int valid_rows = t_end - (t_begin + (nblk - 1) * BS);   // 1..16
+        if (valid_rows == BS)
+            consume_tile<LAM, NT, NJ, G, false>(kr, vr, qv, scale_log2, BS, r, m, l, acc);
+        else
+            consume_tile<LAM, NT, NJ, G, true>(kr, vr, qv, scale_log2, valid_rows, r, m, l, acc);
+    }
+
+    // merge the TPI token rows (lanes c, c + LAM, ... hold the same dims)
+    const size_t unit = (static_cast<size_t>(b) * hkv + g) * S + chunk;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float M = m[h];
+#pragma unroll
+        for (int x = LAM; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
+        const float f = (m[h] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m[h] - M);
+        float lt = l[h] * f;
+#pragma unroll
+        for (int x = LAM; x < 64; x *= 2) lt += __shfl_xor(lt, x);
+        float out[NJ][8];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = acc[h][j][e] * f;
+#pragma unroll
+                for (int x = LAM; x < 64; x *= 2) a += __shfl_xor(a, x);
+                out[j][e] = a;
+            }
+        if (r == 0) {
+            float* dst = part_acc + (unit * G + h) * D;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                float4* d4 = reinterpret_cast<float4*>(dst + (c + LAM * j) * 8);
+                d4[0] = make_float4(out[j][0], out[j][1], out[j][2], out[j][3]);
+                d4[1] = make_float4(out[j][4], out[j][5], out[j][6], out[j][7]);
+            }
+            if (c == 0) part_ml[unit * G + h] = make_float2(M, lt);
+        }
+    }
+}
+
+// Combine the split-K partials of one (sequence, kv head): weights
+// 2^(m_i - max m), normalised by the weighted sum of l_i; round once to bf16.
+template <int D, int G>
+__global__ __launch_bounds__(D) void paged_attn_combine_kernel(
+    const float* __restrict__ part_acc, const float2* __restrict__ part_ml,
+    const int32_t* __restrict__ ctx_lens, int32_t mbps, int32_t hkv, int32_t max_ctx,
+    int32_t chunk_tokens, int32_t S, uint16_t* __restrict__ out) {
+    const int g = blockIdx.x;
+    const int b = blockIdx.y;
+    const int d = threadIdx.x;
+    const int ctx = ctx_lens[b];
+    uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + g * G) * D;
+    if (ctx < 0 || ctx > max_ctx || ctx + 1 > mbps * BS) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) o[h * D + d] = 0x7fc0;
+        return;
+    }
+    const int nch = (ctx + 1 + chunk_tokens - 1) / chunk_tokens;
+    const size_t unit0 = (static_cast<size_t>(b) * hkv + g) * S;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float M = kNegInf;
+        for (int i = 0; i < nch; ++i) M = fmaxf(M, part_ml[(unit0 + i) * G + h].x);
+        float lsum = 0.f, a = 0.f;
+        for (int i = 0; i < nch; ++i) {
+            const float2 ml = part_ml[(unit0 + i) * G + h];
+            const float w = __builtin_amdgcn_exp2f(ml.x - M);
+            lsum = fmaf(w, ml.y, lsum);
+            a = fmaf(w, part_acc[((unit0 + i) * G + h) * D + d], a);
+        }
+        o[h * D + d] = f32_to_bf16_rne(a / lsum);
+    }
+}
+
+// ===================================================================== gather
+template <int D>
+__global__ __launch_bounds__(256) void gather_kv_kernel(
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
+    int32_t hkv, int32_t num_blocks, int32_t len_extra, int32_t l_max,
+    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, uint32_t* __restrict__ err) {
+    const int lb = blockIdx.x;       // logical block
+    const int g = blockIdx.y;
+    const int b = blockIdx.z;
+    const int n = ctx_lens[b] + len_extra;
+    if (n < 0 || n > l_max || (n + BS - 1) / BS > mbps) {
+        if (lb == 0 && g == 0 && threadIdx.x == 0)
+            atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+        return;
+    }
+    if (lb * BS >= n) return;
+    const int32_t blk = table[static_cast<size_t>(b) * mbps + lb];
+    if (blk < 0 || blk >= num_blocks) {
+        if (threadIdx.x == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+        return;
+    }
+    constexpr int PER_TOK = D / 8;   // 16-byte pieces per token row
+    for (int idx = threadIdx.x; idx < BS * PER_TOK; idx += blockDim.x) {
+        const int t = idx / PER_TOK;
+        const int e = (idx - t * PER_TOK) * 8;
+        const int p = lb * BS + t;
+        if (p >= n) continue;
+        const size_t src = ((static_cast<size_t>(blk) * hkv + g) * BS + t) * D + e;
+        const size_t dst = ((static_cast<size_t>(b) * hkv + g) * l_max + p) * D + e;
+        *reinterpret_cast<uint4*>(k_out + dst) = *reinterpret_cast<const uint4*>(kc + src);
+        *reinterpret_cast<uint4*>(v_out + dst) = *reinterpret_cast<const uint4*>(vc + src);
+    }
+}
+
+template <int D, int G>
+void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                 const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
+                 float scale_log2, int32_t max_ctx, int32_t chunk_tokens, int32_t S,
+                 float* part_acc, float2* part_ml, hipStream_t st) {
+    const int hkv = p->num_kv_heads;
+    // 8 lanes per token row keeps 2 tokens per lane; from G = 5 at D = 128 the
+    // accumulators need the 16-lane split (1 piece per token) to stay in VGPRs.
+    constexpr int LAM = (D == 128 && G > 4) ? 16 : 8;
+    const dim3 grid1(S, hkv, batch);
+    hipLaunchKernelGGL((paged_attn_partial_kernel<D, G, LAM>), grid1, dim3(64), 0, st, q_rot, p->k, p->v,
+                       table, mbps, ctx, hkv, p->num_blocks, max_ctx, chunk_tokens / BS, S,
+                       scale_log2, part_acc, part_ml, p->err);
+    const dim3 grid2(hkv, batch);
+    hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), grid2, dim3(D), 0, st, part_acc, part_ml,
+                       ctx, mbps, hkv, max_ctx, chunk_tokens, S, out);
+}
+
+template <int D>
+int dispatch_group(int G, const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                   const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
+                   float scale_log2, int32_t max_ctx, int32_t chunk_tokens, int32_t S,
+                   float* pa, float2* pm, hipStream_t st) {
+#define MIKV_G(GG)                                                                             \
+    case GG:                                                                                   \
+        launch_attn<D, GG>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,        \
+                           chunk_tokens, S, pa, pm, st);                                       \
+        return MI_OK;
+    switch (G) {
+        MIKV_G(1)
+        MIKV_G(2)
+        MIKV_G(3)
+        MIKV_G(4)
+        MIKV_G(5)
+        MIKV_G(6)
+        MIKV_G(7)
+        MIKV_G(8)
+        default: return MI_ERR_UNSUPPORTED;
+    }
+#undef MIKV_G
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+namespace mikv {
+
+int32_t default_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len) {
+    // Aim for about eight resident waves per CU on 256 CUs, in chunks of
+    // 64..1024 tokens (whole 16-token blocks).
+    const int64_t tokens = static_cast<int64_t>(batch) * num_kv_heads * (max_context_len + 1);
+    const int64_t target_units = 2048;
+    int64_t c = (tokens + target_units - 1) / target_units;
+    c = (c + BS - 1) / BS * BS;
+    c = std::max<int64_t>(64, std::min<int64_t>(1024, c));
+    return static_cast<int32_t>(c);
+}
+
+size_t attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t split_tokens) {
+    const size_t S = (static_cast<size_t>(max_context_len) + split_tokens) / split_tokens;
+    const size_t units = static_cast<size_t>(batch) * num_q_heads * S;   // (b, kv head, chunk, h)
+    return align_up(units * head_dim * sizeof(float), 256) + align_up(units * sizeof(float2), 256);
+}
+
+int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, uint16_t* q_rot, const int32_t* table, int32_t mbps,
+                           const int32_t* ctx, int32_t batch, int32_t hq, double theta,
+                           void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p->head_dim == 128)
+        hipLaunchKernelGGL(write_decode_kv_kernel<128>, dim3(batch), dim3(256), 0, st, q, k, v, q_rot,
+                           p->k, p->v, table, mbps, ctx, hq, p->num_kv_heads, p->num_blocks, theta,
+                           p->err);
+    else
+        hipLaunchKernelGGL(write_decode_kv_kernel<64>, dim3(batch), dim3(256), 0, st, q, k, v, q_rot,
+                           p->k, p->v, table, mbps, ctx, hq, p->num_kv_heads, p->num_blocks, theta,
+                           p->err);
+    return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                            const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
+                            int32_t hq, float scale, int32_t max_ctx, int32_t split_tokens,
+                            void* ws, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int G = hq / p->num_kv_heads;
+    const int32_t S = (max_ctx + split_tokens) / split_tokens;
+    const size_t units = static_cast<size_t>(batch) * hq * S;
+    float* pa = static_cast<float*>(ws);
+    float2* pm = reinterpret_cast<float2*>(static_cast<char*>(ws) +
+                                           align_up(units * p->head_dim * sizeof(float), 256));
+    const float scale_log2 = scale * 1.4426950408889634f;
+    int rc;
+    if (p->head_dim == 128)
+        rc = dispatch_group<128>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
+                                 split_tokens, S, pa, pm, st);
+    else
+        rc = dispatch_group<64>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
+                                split_tokens, S, pa, pm, st);
+    if (rc != MI_OK) return rc;
+    return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+}  // namespace mikv
+
+// ============================================================== C entry points
+namespace {
+
+int check_common(const mi_kv_pool_s* p, int32_t batch, int32_t hq, int32_t mbps) {
+    if (!p || batch < 0 || mbps <= 0) return MI_ERR_INVALID_ARG;
+    if (!mikv::pool_has_device(p)) return MI_ERR_INVALID_ARG;
+    if (!mikv::supported_group(hq, p->num_kv_heads)) return MI_ERR_UNSUPPORTED;
+    return MI_OK;
+}
+
+}  // namespace
+
+extern "C" int mi_write_decode_kv(mi_kv_pool_t p, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, uint16_t* q_rot, const int32_t* table,
+                                  int32_t mbps, const int32_t* ctx, int32_t batch, int32_t hq,
+                                  double theta, void* stream) {
+    int rc = check_common(p, batch, hq, mbps);
+    if (rc != MI_OK) return rc;
+    if (batch == 0) return MI_OK;
+    if (!q || !k || !v || !q_rot || !table || !ctx || !(theta > 0.0)) return MI_ERR_INVALID_ARG;
+    return mikv::launch_write_decode_kv(p, q, k, v, q_rot, table, mbps, ctx, batch, hq, theta, stream);
+}
+
+extern "C" size_t mi_paged_gqa_decode_split_workspace_bytes(mi_kv_pool_t p, int32_t batch,
+                                                            int32_t hq, int32_t max_ctx,
+                                                            int32_t split_tokens) {
+    if (!p || batch < 0 || hq <= 0 || max_ctx < 0) return 0;
+    if (split_tokens == 0) split_tokens = mikv::default_split_tokens(batch, p->num_kv_heads, max_ctx);
+    if (split_tokens <= 0 || split_tokens % BS || split_tokens > 64 * BS) return 0;
+    return mikv::attention_workspace_bytes(batch, hq, p->head_dim, max_ctx, split_tokens);
+}
+
+extern "C" size_t mi_paged_gqa_decode_workspace_bytes(mi_kv_pool_t p, int32_t batch, int32_t hq,
+                                                      int32_t max_ctx) {
+    return mi_paged_gqa_decode_split_workspace_bytes(p, batch, hq, max_ctx, 0);
+}
+
+extern "C" int mi_paged_gqa_decode_split(mi_kv_pool_t p, const uint16_t* q_rot, uint16_t* out,
+                                         const int32_t* table, int32_t mbps, const int32_t* ctx,
+                                         int32_t batch, int32_t hq, float scale, int32_t max_ctx,
+                                         int32_t split_tokens, void* ws, size_t ws_bytes,
+                                         void* stream) {
+    int rc = check_common(p, batch, hq, mbps);
+    if (rc != MI_OK) return rc;
+    if (max_ctx < 0 || split_tokens < 0) return MI_ERR_INVALID_ARG;
+    if (split_tokens == 0) split_tokens = mikv::default_split_tokens(batch, p->num_kv_heads, max_ctx);
+    if (split_tokens % BS || split_tokens > 64 * BS) return MI_ERR_UNSUPPORTED;
+    if (batch == 0) return MI_OK;
+    if (!q_rot || !out || !table || !ctx || !ws || q_rot == out) return MI_ERR_INVALID_ARG;
+    if (ws_bytes < mikv::attention_workspace_bytes(batch, hq, p->head_dim, max_ctx, split_tokens))
+        return MI_ERR_WORKSPACE_TOO_SMALL;
+    if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(p->head_dim));
+    return mikv::launch_paged_gqa_decode(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx,
+                                         split_tokens, ws, stream);
+}
+
+extern "C" int mi_paged_gqa_decode(mi_kv_pool_t p, const uint16_t* q_rot, uint16_t* out,
+                                   const int32_t* table, int32_t mbps, const int32_t* ctx,
+                                   int32_t batch, int32_t hq, float scale, int32_t max_ctx,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    return mi_paged_gqa_decode_split(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx, 0,
+                                     ws, ws_bytes, stream);
+}
+
+extern "C" int mi_gather_kv(mi_kv_pool_t p, const int32_t* table, int32_t mbps, const int32_t* ctx,
+                            int32_t batch, int32_t len_extra, uint16_t* k_out, uint16_t* v_out,
+                            int32_t l_max, void* stream) {
+    if (!p || !mikv::pool_has_device(p) || batch < 0 || mbps <= 0 || l_max < 0) return MI_ERR_INVALID_ARG;
+    if (len_extra != 0 && len_extra != 1) return MI_ERR_INVALID_ARG;
+    if (batch == 0 || l_max == 0) return MI_OK;
+    if (!table || !ctx || !k_out || !v_out) return MI_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid((l_max + BS - 1) / BS, p->num_kv_heads, batch);
+    if (p->head_dim == 128)
+        hipLaunchKernelGGL(gather_kv_kernel<128>, grid, dim3(256), 0, st, p->k, p->v, table, mbps, ctx,
+                           p->num_kv_heads, p->num_blocks, len_extra, l_max, k_out, v_out, p->err);
+    else
+        hipLaunchKernelGGL(gather_kv_kernel<64>, grid, dim3(256), 0, st, p->k, p->v, table, mbps, ctx,
+                           p->num_kv_heads, p->num_blocks, len_extra, l_max, k_out, v_out, p->err);
+    return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
+}

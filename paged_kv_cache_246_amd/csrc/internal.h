@@ -1,0 +1,54 @@
+// Internal declarations shared by the host sources of libmikv.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "mikv.h"
+
+struct mi_kv_pool_s {
+    int32_t num_blocks = 0;
+    int32_t block_size = 0;
+    int32_t num_kv_heads = 0;
+    int32_t head_dim = 0;
+    uint32_t flags = 0;
+    int device = -1;
+    uint16_t* k = nullptr;           // device [N, Hkv, bs, D]
+    uint16_t* v = nullptr;
+    bool owns_cache = false;
+    uint32_t* err = nullptr;         // device error word (MI_FAULT_* bits)
+    std::vector<int32_t> stack;      // free-block LIFO; back() is handed out next
+    std::vector<uint8_t> allocated;  // 1 if the id is currently handed out
+};
+
+namespace mikv {
+
+constexpr int kBlockSize = 16;
+
+inline bool pool_has_device(const mi_kv_pool_s* p) {
+    return p && !(p->flags & MI_POOL_HOST_ONLY) && p->k && p->v && p->err;
+}
+
+inline bool supported_group(int32_t hq, int32_t hkv) {
+    return hq > 0 && hkv > 0 && hq % hkv == 0 && hq / hkv >= 1 && hq / hkv <= 8;
+}
+
+// Tokens per split-K chunk chosen by the library for a given workload.
+int32_t default_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len);
+
+// Workspace bytes of the attention split-K partials.
+size_t attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t split_tokens);
+
+// Launches (attention.hip). Arguments are validated by the caller.
+int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, uint16_t* q_rot, const int32_t* table,
+                           int32_t mbps, const int32_t* ctx, int32_t batch, int32_t hq,
+                           double theta, void* stream);
+int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                            const int32_t* table, int32_t mbps, const int32_t* ctx,
+                            int32_t batch, int32_t hq, float scale, int32_t max_ctx,
+                            int32_t split_tokens, void* ws, void* stream);
+
+}  // namespace mikv

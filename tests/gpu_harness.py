@@ -1,0 +1,93 @@
+"""Helpers for the GPU tests: move seeded workloads onto the device and run the
+library's entry points through the C ABI. Tolerance checks live here too."""
+import numpy as np
+import torch
+
+import paged_kv_cache_246_amd as mk
+
+DEV = "cuda:0"
+
+
+def bits_to_dev(a):
+    """uint16 bf16 bit patterns -> int16 device tensor holding the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def dev_to_bits(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def bf16_bits_to_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class DeviceCase:
+    """A DecodeCase on the GPU with a pool over caller-owned K/V buffers."""
+
+    def __init__(self, case):
+        self.case = case
+        cfg = case.cfg
+        self.B = len(case.context_lens)
+        self.Hq, self.Hkv, self.D = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+        self.k_pool = bits_to_dev(case.k_pool)
+        self.v_pool = bits_to_dev(case.v_pool)
+        self.q = bits_to_dev(case.q)
+        self.k = bits_to_dev(case.k)
+        self.v = bits_to_dev(case.v)
+        self.q_rot = torch.empty_like(self.q)
+        self.out = torch.empty_like(self.q)
+        self.table = torch.from_numpy(case.block_table.astype(np.int32)).to(DEV)
+        self.ctx = torch.from_numpy(case.context_lens.astype(np.int32)).to(DEV)
+        self.mbps = case.block_table.shape[1]
+        self.max_ctx = int(case.context_lens.max()) if self.B else 0
+        self.pool = mk.mi_kv_pool_init(case.num_blocks, cfg.block_size, self.Hkv, self.D,
+                                       self.k_pool, self.v_pool)
+
+    def close(self):
+        if self.pool:
+            mk.mi_kv_pool_destroy(self.pool)
+            self.pool = None
+
+    def write(self, theta=None):
+        mk.mi_write_decode_kv(self.pool, self.q, self.k, self.v, self.q_rot, self.table,
+                              self.mbps, self.ctx, self.B, self.Hq,
+                              self.case.cfg.rope_theta if theta is None else theta)
+
+    def attend(self, split_tokens=0, scale=0.0, max_ctx=None, out=None, q=None):
+        max_ctx = self.max_ctx if max_ctx is None else max_ctx
+        ws_bytes = mk.mi_paged_gqa_decode_split_workspace_bytes(
+            self.pool, self.B, self.Hq, max_ctx, split_tokens)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
+        out = self.out if out is None else out
+        mk.mi_paged_gqa_decode_split(self.pool, self.q_rot if q is None else q, out, self.table,
+                                     self.mbps, self.ctx, self.B, self.Hq, scale, max_ctx,
+                                     split_tokens, ws, ws_bytes)
+        return out
+
+    def faults(self):
+        return mk.mi_kv_pool_check_errors(self.pool)
+
+
+def check_tolerance(got_bits, ref, label=""):
+    """bf16 GPU output vs float64 oracle: |d| <= 2e-2 + 2^-8 |ref| per element
+    and relative L2 <= 5e-3. Returns (max_abs, rel_l2)."""
+    got = bf16_bits_to_f64(got_bits)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), label + ": non-finite output"
+    d = np.abs(got - ref)
+    bound = 2e-2 + 2.0 ** -8 * np.abs(ref)
+    worst = np.unravel_index(np.argmax(d - bound), d.shape)
+    assert np.all(d <= bound), "%s: |d|=%g at %s (ref %g)" % (label, d[worst], worst, ref[worst])
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= 5e-3, "%s: relative L2 %g" % (label, rel)
+    return float(d.max()), float(rel)
+
+
+def ulp_diff_bf16(a_bits, b_bits):
+    """Distance in bf16 units in the last place between two finite bit arrays."""
+    def ordered(x):      # monotone integer ordering of bf16 values
+        x = np.asarray(x, np.uint16).astype(np.int64)
+        mag = x & 0x7FFF
+        return np.where(x & 0x8000, -mag, mag)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
