@@ -84,15 +84,20 @@ __device__ __forceinline__ float sum8(float x) {
     return x;
 }
 
-__device__ __forceinline__ uint4 ld16(const char* base, uint32_t off) {
-    return *reinterpret_cast<const uint4*>(base + off);
+// K/V tiles are streamed once per call: non-temporal loads keep them from
+// displacing reusable lines in the caches.
+__device__ __forceinline__ uint4 ld16_stream(const char* base, uint32_t off) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+    return make_uint4(t.x, t.y, t.z, t.w);
 }
 
 // ============================================================== write_decode_kv
-// One workgroup per sequence. The D/2 angles pos * theta^(-2i/D) and their
-// sines and cosines are float64 (fp32 loses ~1e-3 rad at pos 16K); each
-// rotated pair is computed in float64 with separately rounded products and
-// rounded once to bf16.
+// One thread per rotated pair (i, i + D/2) of one head, q heads first, then
+// the new k heads, then 16-byte pieces of the V copy; workgroups of 256
+// threads tile that index space (grid.y) for each sequence (grid.x). The
+// angle pos * theta^(-2i/D), its sine and cosine and the rotation are float64
+// with separately rounded products, rounded once to bf16.
 template <int D>
 __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -100,30 +105,20 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
     int32_t hq, int32_t hkv, int32_t num_blocks, double theta, uint32_t* __restrict__ err) {
     constexpr int H2 = D / 2;
-    __shared__ double cs[H2];
-    __shared__ double sn[H2];
     const int b = blockIdx.x;
     const int pos = ctx_lens[b];
     const bool pos_ok = pos >= 0 && pos / BS < mbps;
     const int32_t blk = pos_ok ? table[static_cast<size_t>(b) * mbps + pos / BS] : -1;
     const bool blk_ok = pos_ok && blk >= 0 && blk < num_blocks;
-    if (threadIdx.x == 0) {
+    if (blockIdx.y == 0 && threadIdx.x == 0) {
         if (!pos_ok) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
         else if (!blk_ok) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
     }
     if (!pos_ok) return;
-    for (int i = threadIdx.x; i < H2; i += blockDim.x) {
-        const double inv_freq = pow(theta, -2.0 * i / D);
-        const double a = static_cast<double>(pos) * inv_freq;
-        double s, c;
-        sincos(a, &s, &c);
-        cs[i] = c;
-        sn[i] = s;
-    }
-    __syncthreads();
-    const int nh = hq + (blk_ok ? hkv : 0);
     const int off = pos % BS;
-    for (int idx = threadIdx.x; idx < nh * H2; idx += blockDim.x) {
+    const int n_rot = (hq + hkv) * H2;
+    const int idx = blockIdx.y * blockDim.x + threadIdx.x;
+    if (idx < n_rot) {
         const int h = idx / H2;
         const int i = idx - h * H2;
         const uint16_t* src;
@@ -132,26 +127,29 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
             src = q + (static_cast<size_t>(b) * hq + h) * D;
             dst = q_rot + (static_cast<size_t>(b) * hq + h) * D;
         } else {
+            if (!blk_ok) return;
             const int g = h - hq;
             src = k + (static_cast<size_t>(b) * hkv + g) * D;
             dst = kc + ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
         }
         const double x1 = bf16_to_f64(src[i]);
         const double x2 = bf16_to_f64(src[i + H2]);
-        const double y1 = __dsub_rn(__dmul_rn(x1, cs[i]), __dmul_rn(x2, sn[i]));
-        const double y2 = __dadd_rn(__dmul_rn(x2, cs[i]), __dmul_rn(x1, sn[i]));
+        const double inv_freq = pow(theta, -2.0 * i / D);
+        const double a = static_cast<double>(pos) * inv_freq;
+        double sn, cs;
+        sincos(a, &sn, &cs);
+        const double y1 = __dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn));
+        const double y2 = __dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn));
         dst[i] = f64_to_bf16_rne(y1);
         dst[i + H2] = f64_to_bf16_rne(y2);
-    }
-    if (blk_ok) {
+    } else if (blk_ok) {
         // V is a bit copy, 16 bytes per thread
-        const int n16 = hkv * D / 8;
-        for (int idx = threadIdx.x; idx < n16; idx += blockDim.x) {
-            const int g = idx / (D / 8);
-            const int e = (idx - g * (D / 8)) * 8;
-            const uint4 val = *reinterpret_cast<const uint4*>(v + (static_cast<size_t>(b) * hkv + g) * D + e);
-            *reinterpret_cast<uint4*>(vc + ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D + e) = val;
-        }
+        const int piece = idx - n_rot;
+        if (piece >= hkv * (D / 8)) return;
+        const int g = piece / (D / 8);
+        const int e = (piece - g * (D / 8)) * 8;
+        const uint4 val = *reinterpret_cast<const uint4*>(v + (static_cast<size_t>(b) * hkv + g) * D + e);
+        *reinterpret_cast<uint4*>(vc + ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D + e) = val;
     }
 }
 
@@ -177,11 +175,11 @@ __device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, 
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) kr[t][j] = ld16(kb, loff[t][j]);
+        for (int j = 0; j < NJ; ++j) kr[t][j] = ld16_stream(kb, loff[t][j]);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) vr[t][j] = ld16(vb, loff[t][j]);
+        for (int j = 0; j < NJ; ++j) vr[t][j] = ld16_stream(vb, loff[t][j]);
 }
 
 // Sum over the LAM consecutive lanes of one token row.
@@ -260,6 +258,64 @@ __device__ __forceinline__ void consume_tile(uint4 (&kr)[NT][NJ], uint4 (&vr)[NT
     }
 }
 
+// Ring of PF + 1 K/V tiles in registers for one wave (see the partial kernel).
+template <int D, int G, int LAM, int PF>
+struct TileRing {
+    static constexpr int NT = TileShape<D, LAM>::NT;
+    static constexpr int NJ = TileShape<D, LAM>::NJ;
+    uint4 kr[PF + 1][NT][NJ];
+    uint4 vr[PF + 1][NT][NJ];
+    const char* kbase;
+    const char* vbase;
+    size_t blk_stride;
+    uint32_t loff[NT][NJ];
+    int32_t my_id;   // lane i holds the chunk's i-th block id
+
+    template <int S>
+    __device__ __forceinline__ void load(int tile) {
+        load_tile<NT, NJ>(kbase, vbase, blk_stride, __builtin_amdgcn_readlane(my_id, tile), loff,
+                          kr[S], vr[S]);
+    }
+    // tiles 0 .. PF-1 into slots 0 .. PF-1
+    template <int S>
+    __device__ __forceinline__ void prologue(int nblk) {
+        if constexpr (S < PF) {
+            load<S>(min(S, nblk - 1));
+            prologue<S + 1>(nblk);
+        }
+    }
+    // PF + 1 full tiles i .. i+PF; tile i+U prefetches tile i+U+PF
+    template <int U>
+    __device__ __forceinline__ void steady(int i, int nblk, const uint4 (&qv)[G][NJ], float sl2,
+                                           int r, float (&m)[G], float (&l)[G],
+                                           float (&acc)[G][NJ][8]) {
+        if constexpr (U <= PF) {
+            load<(U + PF) % (PF + 1)>(min(i + U + PF, nblk - 1));
+            consume_tile<LAM, NT, NJ, G, false>(kr[U], vr[U], qv, sl2, 0, r, m, l, acc);
+            steady<U + 1>(i, nblk, qv, sl2, r, m, l, acc);
+        }
+    }
+    // the last nblk - i (1 .. PF+1) tiles, all already requested; the final
+    // one may be partial (valid_rows < 16)
+    template <int U>
+    __device__ __forceinline__ void rest(int i, int nblk, int valid_rows, const uint4 (&qv)[G][NJ],
+                                         float sl2, int r, float (&m)[G], float (&l)[G],
+                                         float (&acc)[G][NJ][8]) {
+        if constexpr (U <= PF) {
+            const int tile = i + U;
+            if (tile < nblk - 1) {
+                consume_tile<LAM, NT, NJ, G, false>(kr[U], vr[U], qv, sl2, 0, r, m, l, acc);
+            } else if (tile == nblk - 1) {
+                if (valid_rows == BS)
+                    consume_tile<LAM, NT, NJ, G, false>(kr[U], vr[U], qv, sl2, BS, r, m, l, acc);
+                else
+                    consume_tile<LAM, NT, NJ, G, true>(kr[U], vr[U], qv, sl2, valid_rows, r, m, l, acc);
+            }
+            rest<U + 1>(i, nblk, valid_rows, qv, sl2, r, m, l, acc);
+        }
+    }
+};
+
 // ====================================================== paged GQA decode, split-K
 // One wavefront per (split-K chunk, kv head, sequence); a chunk is
 // chunk_blocks consecutive logical blocks. The wave's G query heads share
@@ -268,13 +324,13 @@ __device__ __forceinline__ void consume_tile(uint4 (&kr)[NT][NJ], uint4 (&vr)[NT
 // an online softmax over its own token stream (running max m, sum l,
 // weighted V sum acc); the token rows are merged once at the end of the
 // chunk and written as an fp32 partial (m, l, acc).
-template <int D, int G, int LAM>
+template <int D, int G, int LAM, int PF>
 __global__ __launch_bounds__(64) void paged_attn_partial_kernel(
     const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
     const int32_t* __restrict__ ctx_lens, int32_t hkv, int32_t num_blocks, int32_t max_ctx,
     int32_t chunk_blocks, int32_t S, float scale_log2, float* __restrict__ part_acc,
-    float2* __restrict__ part_ml, uint32_t* __restrict__ err) {
+    float2* __restrict__ part_ml, uint16_t* __restrict__ out, uint32_t* __restrict__ err) {
     using TS = TileShape<D, LAM>;
     constexpr int NT = TS::NT;
     constexpr int NJ = TS::NJ;
@@ -337,33 +393,31 @@ __global__ __launch_bounds__(64) void paged_attn_partial_kernel(
 #pragma unroll
         for (int j = 0; j < NJ; ++j) loff[t][j] = (t * TPI + r) * ROW + (c + LAM * j) * 16;
 
-    uint4 kr[NT][NJ], vr[NT][NJ];
-    load_tile<NT, NJ>(kbase, vbase, blk_stride, __builtin_amdgcn_readfirstlane(my_id), loff, kr, vr);
-    // Steady state: the next block's loads are always in flight while the
-    // current one is consumed (an unconditional prefetch keeps the waitcnt
-    // exact). Only the last block of a chunk can be partial.
-    for (int i = 0; i + 1 < nblk; ++i) {
-        uint4 kn[NT][NJ], vn[NT][NJ];
-        load_tile<NT, NJ>(kbase, vbase, blk_stride, __builtin_amdgcn_readlane(my_id, i + 1), loff, kn, vn);
-        consume_tile<LAM, NT, NJ, G, false>(kr, vr, qv, scale_log2, 0, r, m, l, acc);
+    // Register ring of PF + 1 tiles: tile t lives in slot t % (PF + 1) and
+    // the PF tiles after the one being consumed are in flight. The loop is
+    // unrolled by PF + 1 so ring slots are compile-time registers (no copies
+    // that would wait on in-flight loads), and every prefetch in it is
+    // unconditional (clamped to the chunk's last block, a cache hit), so the
+    // wait before each tile covers exactly the older loads.
+    TileRing<D, G, LAM, PF> ring;
+    ring.kbase = kbase;
+    ring.vbase = vbase;
+    ring.blk_stride = blk_stride;
+    ring.my_id = my_id;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                kr[t][j] = kn[t][j];
-                vr[t][j] = vn[t][j];
-            }
-    }
-    {
-        const int valid_rows = t_end - (t_begin + (nblk - 1) * BS);   // 1..16
-        if (valid_rows == BS)
-            consume_tile<LAM, NT, NJ, G, false>(kr, vr, qv, scale_log2, BS, r, m, l, acc);
-        else
-            consume_tile<LAM, NT, NJ, G, true>(kr, vr, qv, scale_log2, valid_rows, r, m, l, acc);
-    }
+        for (int j = 0; j < NJ; ++j) ring.loff[t][j] = loff[t][j];
+    ring.template prologue<0>(nblk);
+    int i = 0;
+    for (; i + PF + 1 < nblk; i += PF + 1) ring.template steady<0>(i, nblk, qv, scale_log2, r, m, l, acc);
+    ring.template load<PF>(min(i + PF, nblk - 1));
+    ring.template rest<0>(i, nblk, t_end - (t_begin + (nblk - 1) * BS), qv, scale_log2, r, m, l, acc);
 
     // merge the TPI token rows (lanes c, c + LAM, ... hold the same dims)
+    const int nch = (L + chunk_blocks * BS - 1) / (chunk_blocks * BS);
     const size_t unit = (static_cast<size_t>(b) * hkv + g) * S + chunk;
+    uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + g * G) * D;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float M = m[h];
@@ -373,7 +427,7 @@ __global__ __launch_bounds__(64) void paged_attn_partial_kernel(
         float lt = l[h] * f;
 #pragma unroll
         for (int x = LAM; x < 64; x *= 2) lt += __shfl_xor(lt, x);
-        float out[NJ][8];
+        float red[NJ][8];
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -381,52 +435,111 @@ __global__ __launch_bounds__(64) void paged_attn_partial_kernel(
                 float a = acc[h][j][e] * f;
 #pragma unroll
                 for (int x = LAM; x < 64; x *= 2) a += __shfl_xor(a, x);
-                out[j][e] = a;
+                red[j][e] = a;
             }
-        if (r == 0) {
+        if (r != 0) continue;
+        if (nch == 1) {
+            // the whole sequence is this chunk: normalise and store bf16
+            const float inv = 1.0f / lt;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e] * inv)) |
+                           (static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e + 1] * inv)) << 16);
+                *reinterpret_cast<uint4*>(o + h * D + (c + LAM * j) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        } else {
             float* dst = part_acc + (unit * G + h) * D;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 float4* d4 = reinterpret_cast<float4*>(dst + (c + LAM * j) * 8);
-                d4[0] = make_float4(out[j][0], out[j][1], out[j][2], out[j][3]);
-                d4[1] = make_float4(out[j][4], out[j][5], out[j][6], out[j][7]);
+                d4[0] = make_float4(red[j][0], red[j][1], red[j][2], red[j][3]);
+                d4[1] = make_float4(red[j][4], red[j][5], red[j][6], red[j][7]);
             }
             if (c == 0) part_ml[unit * G + h] = make_float2(M, lt);
         }
     }
 }
 
-// Combine the split-K partials of one (sequence, kv head): weights
-// 2^(m_i - max m), normalised by the weighted sum of l_i; round once to bf16.
+// Combine kernel: one workgroup per (query head, sequence) with more than
+// one chunk. Thread t covers head dim t % D for the chunks i = t / D mod NCG;
+// weights 2^(m_i - max m), normalised by the weighted sum of the l_i, sums in
+// a fixed order (deterministic), one rounding to bf16.
 template <int D, int G>
-__global__ __launch_bounds__(D) void paged_attn_combine_kernel(
+__global__ __launch_bounds__(256) void paged_attn_combine_kernel(
     const float* __restrict__ part_acc, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ ctx_lens, int32_t mbps, int32_t hkv, int32_t max_ctx,
     int32_t chunk_tokens, int32_t S, uint16_t* __restrict__ out) {
-    const int g = blockIdx.x;
+    constexpr int NCG = 256 / D;        // chunk groups
+    constexpr int NW = 256 / 64;        // waves
+    __shared__ float red[NCG][D];
+    __shared__ float wred[2][NW];
+    const int hq_idx = blockIdx.x;      // query head
     const int b = blockIdx.y;
-    const int d = threadIdx.x;
+    const int g = hq_idx / G;
+    const int h = hq_idx - g * G;
+    const int t = threadIdx.x;
     const int ctx = ctx_lens[b];
-    uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + g * G) * D;
     if (ctx < 0 || ctx > max_ctx || ctx + 1 > mbps * BS) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) o[h * D + d] = 0x7fc0;
+        if (t < D) out[(static_cast<size_t>(b) * hkv * G + hq_idx) * D + t] = 0x7fc0;
         return;
     }
     const int nch = (ctx + 1 + chunk_tokens - 1) / chunk_tokens;
+    if (nch == 1) return;              // the partial kernel stored this output itself
     const size_t unit0 = (static_cast<size_t>(b) * hkv + g) * S;
+    const int lane = t & 63;
+    const int wv = t >> 6;
+
+    float M = kNegInf;
+    for (int i = t; i < nch; i += 256) M = fmaxf(M, part_ml[(unit0 + i) * G + h].x);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float M = kNegInf;
-        for (int i = 0; i < nch; ++i) M = fmaxf(M, part_ml[(unit0 + i) * G + h].x);
-        float lsum = 0.f, a = 0.f;
-        for (int i = 0; i < nch; ++i) {
-            const float2 ml = part_ml[(unit0 + i) * G + h];
-            const float w = __builtin_amdgcn_exp2f(ml.x - M);
-            lsum = fmaf(w, ml.y, lsum);
-            a = fmaf(w, part_acc[((unit0 + i) * G + h) * D + d], a);
+    for (int x = 1; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
+    if (lane == 0) wred[0][wv] = M;
+    __syncthreads();
+    M = wred[0][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, wred[0][w]);
+
+    float lsum = 0.f;
+    for (int i = t; i < nch; i += 256) {
+        const float2 ml = part_ml[(unit0 + i) * G + h];
+        lsum = fmaf(__builtin_amdgcn_exp2f(ml.x - M), ml.y, lsum);
+    }
+#pragma unroll
+    for (int x = 1; x < 64; x *= 2) lsum += __shfl_xor(lsum, x);
+    if (lane == 0) wred[1][wv] = lsum;
+
+    const int d = t % D;
+    const int cg = t / D;
+    float a = 0.f;
+    int i = cg;
+    for (; i + 3 * NCG < nch; i += 4 * NCG) {
+        float2 ml[4];
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            ml[u] = part_ml[(unit0 + i + u * NCG) * G + h];
+            v[u] = part_acc[((unit0 + i + u * NCG) * G + h) * D + d];
         }
-        o[h * D + d] = f32_to_bf16_rne(a / lsum);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a = fmaf(__builtin_amdgcn_exp2f(ml[u].x - M), v[u], a);
+    }
+    for (; i < nch; i += NCG) {
+        const float2 ml = part_ml[(unit0 + i) * G + h];
+        a = fmaf(__builtin_amdgcn_exp2f(ml.x - M), part_acc[((unit0 + i) * G + h) * D + d], a);
+    }
+    red[cg][d] = a;
+    __syncthreads();
+    if (t < D) {
+        float tot = red[0][t];
+#pragma unroll
+        for (int c2 = 1; c2 < NCG; ++c2) tot += red[c2][t];
+        float l = wred[1][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) l += wred[1][w];
+        out[(static_cast<size_t>(b) * hkv * G + hq_idx) * D + t] = f32_to_bf16_rne(tot / l);
     }
 }
 
@@ -466,21 +579,34 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
 }
 
 template <int D, int G>
+struct AttnTuning {
+#if defined(MIKV_TUNE_LAM) && defined(MIKV_TUNE_PF)
+    static constexpr int LAM = (D == 128) ? MIKV_TUNE_LAM : 8;
+    static constexpr int PF = MIKV_TUNE_PF;
+#else
+    static constexpr int LAM = (D == 128 && G > 2) ? 16 : 8;
+    static constexpr int PF = (D == 128 && G > 4) ? 1 : 2;
+#endif
+};
+
+template <int D, int G>
 void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                  const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                  float scale_log2, int32_t max_ctx, int32_t chunk_tokens, int32_t S,
                  float* part_acc, float2* part_ml, hipStream_t st) {
+    // Lanes per token row and prefetch depth, sized so that the accumulators
+    // (G * D / LAM floats per lane) and PF + 1 tiles stay in VGPRs.
+    constexpr int LAM = AttnTuning<D, G>::LAM;
+    constexpr int PF = AttnTuning<D, G>::PF;
     const int hkv = p->num_kv_heads;
-    // 8 lanes per token row keeps 2 tokens per lane; from G = 5 at D = 128 the
-    // accumulators need the 16-lane split (1 piece per token) to stay in VGPRs.
-    constexpr int LAM = (D == 128 && G > 4) ? 16 : 8;
-    const dim3 grid1(S, hkv, batch);
-    hipLaunchKernelGGL((paged_attn_partial_kernel<D, G, LAM>), grid1, dim3(64), 0, st, q_rot, p->k, p->v,
+    const dim3 grid(S, hkv, batch);
+    hipLaunchKernelGGL((paged_attn_partial_kernel<D, G, LAM, PF>), grid, dim3(64), 0, st, q_rot, p->k, p->v,
                        table, mbps, ctx, hkv, p->num_blocks, max_ctx, chunk_tokens / BS, S,
-                       scale_log2, part_acc, part_ml, p->err);
-    const dim3 grid2(hkv, batch);
-    hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), grid2, dim3(D), 0, st, part_acc, part_ml,
-                       ctx, mbps, hkv, max_ctx, chunk_tokens, S, out);
+                       scale_log2, part_acc, part_ml, out, p->err);
+    // every split sequence (more than one chunk) is merged by the combine kernel
+    if (max_ctx + 1 > chunk_tokens)
+        hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), dim3(hkv * G, batch), dim3(256), 0, st,
+                           part_acc, part_ml, ctx, mbps, hkv, max_ctx, chunk_tokens, S, out);
 }
 
 template <int D>
@@ -536,14 +662,15 @@ int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint1
                            const int32_t* ctx, int32_t batch, int32_t hq, double theta,
                            void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const int hkv = p->num_kv_heads;
+    const int items = (hq + hkv) * (p->head_dim / 2) + hkv * (p->head_dim / 8);
+    const dim3 grid(batch, (items + 255) / 256);
     if (p->head_dim == 128)
-        hipLaunchKernelGGL(write_decode_kv_kernel<128>, dim3(batch), dim3(256), 0, st, q, k, v, q_rot,
-                           p->k, p->v, table, mbps, ctx, hq, p->num_kv_heads, p->num_blocks, theta,
-                           p->err);
+        hipLaunchKernelGGL(write_decode_kv_kernel<128>, grid, dim3(256), 0, st, q, k, v, q_rot,
+                           p->k, p->v, table, mbps, ctx, hq, hkv, p->num_blocks, theta, p->err);
     else
-        hipLaunchKernelGGL(write_decode_kv_kernel<64>, dim3(batch), dim3(256), 0, st, q, k, v, q_rot,
-                           p->k, p->v, table, mbps, ctx, hq, p->num_kv_heads, p->num_blocks, theta,
-                           p->err);
+        hipLaunchKernelGGL(write_decode_kv_kernel<64>, grid, dim3(256), 0, st, q, k, v, q_rot,
+                           p->k, p->v, table, mbps, ctx, hq, hkv, p->num_blocks, theta, p->err);
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 

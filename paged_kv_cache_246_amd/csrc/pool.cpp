@@ -78,7 +78,7 @@ extern "C" int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t bl
             p->owns_cache = true;
         }
         if (hipMalloc(reinterpret_cast<void**>(&p->err), 256) != hipSuccess ||
-            hipMemset(p->err, 0, 256) != hipSuccess) {
+            hipMemset(p->err, 0, 256) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
             if (p->err) (void)hipFree(p->err);
             if (p->owns_cache) {
                 (void)hipFree(p->k);
