@@ -316,20 +316,88 @@ struct TileRing {
     }
 };
 
-// ====================================================== paged GQA decode, split-K
-// One wavefront per (split-K chunk, kv head, sequence); a chunk is
-// chunk_blocks consecutive logical blocks. The wave's G query heads share
-// every K/V tile; q.k runs on packed bf16 dot products with fp32
-// accumulation, summed over the lanes of a token row by DPP. Every lane keeps
-// an online softmax over its own token stream (running max m, sum l,
-// weighted V sum acc); the token rows are merged once at the end of the
-// chunk and written as an fp32 partial (m, l, acc).
+// ================================================= work partition (stream-K)
+// The work of one call is the list of 16-token tiles of every segment
+// (sequence b, kv head g), g fastest; segment (b, g) has nt_b =
+// ceil((ctx_b + 1) / 16) tiles, and a sequence whose length is out of range
+// has none. W waves split the list into W equal contiguous ranges,
+// [floor(w T / W), floor((w + 1) T / W)), so every wave streams the same
+// number of tiles whatever the length mix. A segment cut by a range boundary
+// leaves one fp32 partial per piece; a segment inside one range is finished by
+// that wave. W = min(grid, ceil(T / min_tiles)).
+constexpr int kMaxBatch = 1024;      // sequences per call (LDS prefix table)
+
+// TP[b] = first global tile of sequence b, TP[batch] = T. One wave; every lane
+// of the wave returns T. Records a length fault in *bad.
+__device__ __forceinline__ int build_tile_prefix(const int32_t* __restrict__ ctx_lens, int batch,
+                                                 int mbps, int max_ctx, int hkv, int* TP,
+                                                 bool* bad, int lane) {
+    int carry = 0;
+    bool any_bad = false;
+    for (int base = 0; base < batch; base += 64) {
+        const int b = base + lane;
+        int v = 0;
+        if (b < batch) {
+            const int c = ctx_lens[b];
+            const bool badb = c < 0 || c > max_ctx || c + 1 > mbps * BS;
+            any_bad |= badb;
+            v = badb ? 0 : (c + BS) / BS * hkv;
+        }
+#pragma unroll
+        for (int x = 1; x < 64; x *= 2) {
+            const int y = __shfl_up(v, x);
+            if (lane >= x) v += y;
+        }
+        if (b < batch) TP[b + 1] = carry + v;
+        carry += __shfl(v, 63);
+    }
+    if (lane == 0) TP[0] = 0;
+    *bad = __ballot(any_bad) != 0;
+    return carry;
+}
+
+__device__ __forceinline__ int active_waves(int T, int grid_waves, int min_tiles) {
+    return max(1, min(grid_waves, (T + min_tiles - 1) / min_tiles));
+}
+
+__device__ __forceinline__ int range_start(int w, int T, int W) {
+    return static_cast<int>(static_cast<int64_t>(w) * T / W);
+}
+
+// The wave whose range holds tile x (0 <= x < T): the largest w with
+// floor(w T / W) <= x, i.e. floor(((x + 1) W - 1) / T).
+__device__ __forceinline__ int wave_of_tile(int x, int T, int W) {
+    const int w = static_cast<int>((static_cast<int64_t>(x + 1) * W - 1) / T);
+    return min(max(w, 0), W - 1);
+}
+
+// Largest b with TP[b] <= x (that segment is non-empty for x < T).
+__device__ __forceinline__ int find_sequence(const int* TP, int batch, int x) {
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (TP[mid] <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ====================================================== paged GQA decode
+// One wavefront per work range (see above). For each segment piece in its
+// range the wave streams the piece's K/V tiles in logical order; the G query
+// heads of the segment share every tile; q.k runs on packed bf16 dot
+// products with fp32 accumulation, summed over the lanes of a token row by
+// DPP. Every lane keeps an online softmax over its own token stream (running
+// max m, sum l, weighted V sum acc); the token rows are merged at the end of
+// the piece, which is then either stored as the final bf16 output (the whole
+// segment) or as an fp32 partial (m, l, acc) in slot 2w (first piece of the
+// range) or 2w + 1 (last piece).
 template <int D, int G, int LAM, int PF>
 __global__ __launch_bounds__(64) void paged_attn_partial_kernel(
     const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
-    const int32_t* __restrict__ ctx_lens, int32_t hkv, int32_t num_blocks, int32_t max_ctx,
-    int32_t chunk_blocks, int32_t S, float scale_log2, float* __restrict__ part_acc,
+    const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t hkv, int32_t num_blocks,
+    int32_t max_ctx, int32_t min_tiles, float scale_log2, float* __restrict__ part_acc,
     float2* __restrict__ part_ml, uint16_t* __restrict__ out, uint32_t* __restrict__ err) {
     using TS = TileShape<D, LAM>;
     constexpr int NT = TS::NT;
@@ -337,143 +405,159 @@ __global__ __launch_bounds__(64) void paged_attn_partial_kernel(
     constexpr int TPI = TS::TPI;
     constexpr uint32_t ROW = D * 2;            // bytes per token row
     constexpr size_t TILE = BS * D * 2;        // bytes per (block, head) tile
-    const int chunk = blockIdx.x;
-    const int g = blockIdx.y;
-    const int b = blockIdx.z;
+    __shared__ int TP[kMaxBatch + 1];
+    const int w = blockIdx.x;
     const int lane = threadIdx.x;
     const int r = lane / LAM;
     const int c = lane % LAM;
 
-    const int ctx = ctx_lens[b];
-    if (ctx < 0 || ctx > max_ctx || ctx + 1 > mbps * BS) {
-        if (chunk == 0 && g == 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
-        return;
-    }
-    const int L = ctx + 1;
-    const int t_begin = chunk * chunk_blocks * BS;
-    if (t_begin >= L) return;
-    const int t_end = min(L, t_begin + chunk_blocks * BS);
-    const int nblk = (t_end - t_begin + BS - 1) / BS;
-    const int lb0 = chunk * chunk_blocks;
+    bool bad_len;
+    const int T = build_tile_prefix(ctx_lens, batch, mbps, max_ctx, hkv, TP, &bad_len, lane);
+    __syncthreads();
+    if (bad_len && w == 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+    if (T == 0) return;
+    const int W = active_waves(T, gridDim.x, min_tiles);
+    if (w >= W) return;
+    const int start = range_start(w, T, W);
+    const int end = range_start(w + 1, T, W);
 
-    // q of the group's G heads: this lane's pieces
-    uint4 qv[G][NJ];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            qv[h][j] = *reinterpret_cast<const uint4*>(
-                q_rot + (static_cast<size_t>(b) * hkv * G + g * G + h) * D + (c + LAM * j) * 8);
-
-    // this chunk's block ids, one per lane (chunk_blocks <= 64)
-    int32_t my_id = 0;
-    if (lane < nblk) my_id = table[static_cast<size_t>(b) * mbps + lb0 + lane];
-    const bool bad_id = lane < nblk && (my_id < 0 || my_id >= num_blocks);
-    if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
-    if (bad_id) my_id = 0;
-
-    float m[G], l[G];
-    float acc[G][NJ][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = kNegInf;
-        l[h] = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][j][e] = 0.f;
-    }
-
-    const char* kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
-    const char* vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
-    const size_t blk_stride = static_cast<size_t>(hkv) * TILE;
     uint32_t loff[NT][NJ];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) loff[t][j] = (t * TPI + r) * ROW + (c + LAM * j) * 16;
+    const size_t blk_stride = static_cast<size_t>(hkv) * TILE;
 
-    // Register ring of PF + 1 tiles: tile t lives in slot t % (PF + 1) and
-    // the PF tiles after the one being consumed are in flight. The loop is
-    // unrolled by PF + 1 so ring slots are compile-time registers (no copies
-    // that would wait on in-flight loads), and every prefetch in it is
-    // unconditional (clamped to the chunk's last block, a cache hit), so the
-    // wait before each tile covers exactly the older loads.
-    TileRing<D, G, LAM, PF> ring;
-    ring.kbase = kbase;
-    ring.vbase = vbase;
-    ring.blk_stride = blk_stride;
-    ring.my_id = my_id;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) ring.loff[t][j] = loff[t][j];
-    ring.template prologue<0>(nblk);
-    int i = 0;
-    for (; i + PF + 1 < nblk; i += PF + 1) ring.template steady<0>(i, nblk, qv, scale_log2, r, m, l, acc);
-    ring.template load<PF>(min(i + PF, nblk - 1));
-    ring.template rest<0>(i, nblk, t_end - (t_begin + (nblk - 1) * BS), qv, scale_log2, r, m, l, acc);
+    int pos = start;
+    int b = find_sequence(TP, batch, pos);
+    bool first_piece = true;
+    while (pos < end) {
+        while (__builtin_amdgcn_readfirstlane(TP[b + 1]) <= pos) ++b;
+        const int seg0 = __builtin_amdgcn_readfirstlane(TP[b]);
+        const int nt = (__builtin_amdgcn_readfirstlane(TP[b + 1]) - seg0) / hkv;
+        const int rel = pos - seg0;
+        const int g = rel / nt;
+        const int t0 = rel - g * nt;
+        const int t1 = min(nt, t0 + (end - pos));
+        const int L = ctx_lens[b] + 1;
 
-    // merge the TPI token rows (lanes c, c + LAM, ... hold the same dims)
-    const int nch = (L + chunk_blocks * BS - 1) / (chunk_blocks * BS);
-    const size_t unit = (static_cast<size_t>(b) * hkv + g) * S + chunk;
-    uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + g * G) * D;
+        uint4 qv[G][NJ];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float M = m[h];
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int x = LAM; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
-        const float f = (m[h] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m[h] - M);
-        float lt = l[h] * f;
+            for (int j = 0; j < NJ; ++j)
+                qv[h][j] = *reinterpret_cast<const uint4*>(
+                    q_rot + (static_cast<size_t>(b) * hkv * G + g * G + h) * D + (c + LAM * j) * 8);
+        float m[G], l[G];
+        float acc[G][NJ][8];
 #pragma unroll
-        for (int x = LAM; x < 64; x *= 2) lt += __shfl_xor(lt, x);
-        float red[NJ][8];
+        for (int h = 0; h < G; ++h) {
+            m[h] = kNegInf;
+            l[h] = 0.f;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = acc[h][j][e] * f;
-#pragma unroll
-                for (int x = LAM; x < 64; x *= 2) a += __shfl_xor(a, x);
-                red[j][e] = a;
-            }
-        if (r != 0) continue;
-        if (nch == 1) {
-            // the whole sequence is this chunk: normalise and store bf16
-            const float inv = 1.0f / lt;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                uint32_t w[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e] * inv)) |
-                           (static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e + 1] * inv)) << 16);
-                *reinterpret_cast<uint4*>(o + h * D + (c + LAM * j) * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-            }
-        } else {
-            float* dst = part_acc + (unit * G + h) * D;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                float4* d4 = reinterpret_cast<float4*>(dst + (c + LAM * j) * 8);
-                d4[0] = make_float4(red[j][0], red[j][1], red[j][2], red[j][3]);
-                d4[1] = make_float4(red[j][4], red[j][5], red[j][6], red[j][7]);
-            }
-            if (c == 0) part_ml[unit * G + h] = make_float2(M, lt);
+                for (int e = 0; e < 8; ++e) acc[h][j][e] = 0.f;
         }
+
+        TileRing<D, G, LAM, PF> ring;
+        ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
+        ring.vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
+        ring.blk_stride = blk_stride;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ring.loff[t][j] = loff[t][j];
+
+        // sub-chunks of at most 64 tiles: one block id per lane
+        for (int s0 = t0; s0 < t1; s0 += 64) {
+            const int nblk = min(64, t1 - s0);
+            int32_t id = 0;
+            if (lane < nblk) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
+            const bool bad_id = lane < nblk && (id < 0 || id >= num_blocks);
+            if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+            ring.my_id = bad_id ? 0 : id;
+            // Register ring of PF + 1 tiles: tile i lives in slot i % (PF + 1)
+            // and the PF tiles after the one being consumed are in flight.
+            // The loop is unrolled by PF + 1 so ring slots are compile-time
+            // registers (no copies that would wait on in-flight loads), and
+            // every prefetch in it is unconditional (clamped to the last
+            // tile, a cache hit), so the wait before each tile covers exactly
+            // the older loads.
+            const int last_rows = (s0 + nblk == nt) ? L - (nt - 1) * BS : BS;
+            ring.template prologue<0>(nblk);
+            int i = 0;
+            for (; i + PF + 1 < nblk; i += PF + 1)
+                ring.template steady<0>(i, nblk, qv, scale_log2, r, m, l, acc);
+            ring.template load<PF>(min(i + PF, nblk - 1));
+            ring.template rest<0>(i, nblk, last_rows, qv, scale_log2, r, m, l, acc);
+        }
+
+        // merge the TPI token rows (lanes c, c + LAM, ... hold the same dims)
+        const bool whole = (t0 == 0 && t1 == nt);
+        const size_t slot = 2 * static_cast<size_t>(w) + (first_piece ? 0 : 1);
+        uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + g * G) * D;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float M = m[h];
+#pragma unroll
+            for (int x = LAM; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
+            const float f = (m[h] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m[h] - M);
+            float lt = l[h] * f;
+#pragma unroll
+            for (int x = LAM; x < 64; x *= 2) lt += __shfl_xor(lt, x);
+            float red[NJ][8];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float a = acc[h][j][e] * f;
+#pragma unroll
+                    for (int x = LAM; x < 64; x *= 2) a += __shfl_xor(a, x);
+                    red[j][e] = a;
+                }
+            if (r != 0) continue;
+            if (whole) {
+                const float inv = 1.0f / lt;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    uint32_t wd[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        wd[e] = static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e] * inv)) |
+                                (static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e + 1] * inv)) << 16);
+                    *reinterpret_cast<uint4*>(o + h * D + (c + LAM * j) * 8) =
+                        make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                }
+            } else {
+                float* dst = part_acc + (slot * G + h) * D;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    float4* d4 = reinterpret_cast<float4*>(dst + (c + LAM * j) * 8);
+                    d4[0] = make_float4(red[j][0], red[j][1], red[j][2], red[j][3]);
+                    d4[1] = make_float4(red[j][4], red[j][5], red[j][6], red[j][7]);
+                }
+                if (c == 0) part_ml[slot * G + h] = make_float2(M, lt);
+            }
+        }
+        pos += t1 - t0;
+        first_piece = false;
     }
 }
 
-// Combine kernel: one workgroup per (query head, sequence) with more than
-// one chunk. Thread t covers head dim t % D for the chunks i = t / D mod NCG;
-// weights 2^(m_i - max m), normalised by the weighted sum of the l_i, sums in
-// a fixed order (deterministic), one rounding to bf16.
+// Combine kernel: one workgroup per (query head, sequence). It rebuilds the
+// same partition, and if the segment was cut into pieces, merges their
+// partials in range order: weights 2^(m_i - max m), normalised by the
+// weighted sum of the l_i, one rounding to bf16. Sequences with an
+// out-of-range length get NaN outputs.
 template <int D, int G>
 __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
     const float* __restrict__ part_acc, const float2* __restrict__ part_ml,
-    const int32_t* __restrict__ ctx_lens, int32_t mbps, int32_t hkv, int32_t max_ctx,
-    int32_t chunk_tokens, int32_t S, uint16_t* __restrict__ out) {
-    constexpr int NCG = 256 / D;        // chunk groups
+    const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t mbps, int32_t hkv,
+    int32_t max_ctx, int32_t grid_waves, int32_t min_tiles, uint16_t* __restrict__ out) {
+    constexpr int NCG = 256 / D;        // piece groups
     constexpr int NW = 256 / 64;        // waves
+    __shared__ int TP[kMaxBatch + 1];
     __shared__ float red[NCG][D];
     __shared__ float wred[2][NW];
     const int hq_idx = blockIdx.x;      // query head
@@ -481,30 +565,46 @@ __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
     const int g = hq_idx / G;
     const int h = hq_idx - g * G;
     const int t = threadIdx.x;
-    const int ctx = ctx_lens[b];
-    if (ctx < 0 || ctx > max_ctx || ctx + 1 > mbps * BS) {
-        if (t < D) out[(static_cast<size_t>(b) * hkv * G + hq_idx) * D + t] = 0x7fc0;
-        return;
-    }
-    const int nch = (ctx + 1 + chunk_tokens - 1) / chunk_tokens;
-    if (nch == 1) return;              // the partial kernel stored this output itself
-    const size_t unit0 = (static_cast<size_t>(b) * hkv + g) * S;
     const int lane = t & 63;
     const int wv = t >> 6;
+    uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + hq_idx) * D;
+
+    const int ctx = ctx_lens[b];
+    if (ctx < 0 || ctx > max_ctx || ctx + 1 > mbps * BS) {
+        if (t < D) o[t] = 0x7fc0;
+        return;
+    }
+    int T = 0;
+    if (wv == 0) {
+        bool bad;
+        T = build_tile_prefix(ctx_lens, batch, mbps, max_ctx, hkv, TP, &bad, lane);
+    }
+    __syncthreads();
+    T = TP[batch];
+    const int W = active_waves(T, grid_waves, min_tiles);
+    const int nt = (ctx + BS) / BS;
+    const int A = TP[b] + g * nt;                  // first tile of the segment
+    const int w_first = wave_of_tile(A, T, W);
+    const int w_last = wave_of_tile(A + nt - 1, T, W);
+    if (w_first == w_last) return;                 // finished by one wave
+    const int npieces = w_last - w_first + 1;
+    const int first_slot = 2 * w_first + (range_start(w_first, T, W) < A ? 1 : 0);
+    // piece k (0 .. npieces-1) lives in slot first_slot for k = 0, 2 (w_first + k) after
+    auto slot_of = [&](int k) { return k == 0 ? first_slot : 2 * (w_first + k); };
 
     float M = kNegInf;
-    for (int i = t; i < nch; i += 256) M = fmaxf(M, part_ml[(unit0 + i) * G + h].x);
+    for (int k = t; k < npieces; k += 256) M = fmaxf(M, part_ml[static_cast<size_t>(slot_of(k)) * G + h].x);
 #pragma unroll
     for (int x = 1; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
     if (lane == 0) wred[0][wv] = M;
     __syncthreads();
     M = wred[0][0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, wred[0][w]);
+    for (int v = 1; v < NW; ++v) M = fmaxf(M, wred[0][v]);
 
     float lsum = 0.f;
-    for (int i = t; i < nch; i += 256) {
-        const float2 ml = part_ml[(unit0 + i) * G + h];
+    for (int k = t; k < npieces; k += 256) {
+        const float2 ml = part_ml[static_cast<size_t>(slot_of(k)) * G + h];
         lsum = fmaf(__builtin_amdgcn_exp2f(ml.x - M), ml.y, lsum);
     }
 #pragma unroll
@@ -514,21 +614,10 @@ __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
     const int d = t % D;
     const int cg = t / D;
     float a = 0.f;
-    int i = cg;
-    for (; i + 3 * NCG < nch; i += 4 * NCG) {
-        float2 ml[4];
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            ml[u] = part_ml[(unit0 + i + u * NCG) * G + h];
-            v[u] = part_acc[((unit0 + i + u * NCG) * G + h) * D + d];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a = fmaf(__builtin_amdgcn_exp2f(ml[u].x - M), v[u], a);
-    }
-    for (; i < nch; i += NCG) {
-        const float2 ml = part_ml[(unit0 + i) * G + h];
-        a = fmaf(__builtin_amdgcn_exp2f(ml.x - M), part_acc[((unit0 + i) * G + h) * D + d], a);
+    for (int k = cg; k < npieces; k += NCG) {
+        const size_t sl = static_cast<size_t>(slot_of(k));
+        const float2 ml = part_ml[sl * G + h];
+        a = fmaf(__builtin_amdgcn_exp2f(ml.x - M), part_acc[(sl * G + h) * D + d], a);
     }
     red[cg][d] = a;
     __syncthreads();
@@ -536,10 +625,10 @@ __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
         float tot = red[0][t];
 #pragma unroll
         for (int c2 = 1; c2 < NCG; ++c2) tot += red[c2][t];
-        float l = wred[1][0];
+        float lt = wred[1][0];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) l += wred[1][w];
-        out[(static_cast<size_t>(b) * hkv * G + hq_idx) * D + t] = f32_to_bf16_rne(tot / l);
+        for (int v = 1; v < NW; ++v) lt += wred[1][v];
+        o[t] = f32_to_bf16_rne(tot / lt);
     }
 }
 
@@ -589,35 +678,51 @@ struct AttnTuning {
 #endif
 };
 
+// Resident 64-lane workgroups of the attention kernel on the current device
+// (CUs x waves per CU at the kernel's register budget), cached per device.
+template <typename K>
+int resident_waves(K kernel) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return mikv::kMaxAttnWaves;
+    if (cached[dev] > 0) return cached[dev];
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu <= 0 || cus <= 0)
+        return mikv::kMaxAttnWaves;
+    cached[dev] = std::min(mikv::kMaxAttnWaves, per_cu * cus);
+    return cached[dev];
+}
+
 template <int D, int G>
 void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                  const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
-                 float scale_log2, int32_t max_ctx, int32_t chunk_tokens, int32_t S,
-                 float* part_acc, float2* part_ml, hipStream_t st) {
+                 float scale_log2, int32_t max_ctx, int32_t min_tiles, float* part_acc,
+                 float2* part_ml, hipStream_t st) {
     // Lanes per token row and prefetch depth, sized so that the accumulators
     // (G * D / LAM floats per lane) and PF + 1 tiles stay in VGPRs.
     constexpr int LAM = AttnTuning<D, G>::LAM;
     constexpr int PF = AttnTuning<D, G>::PF;
     const int hkv = p->num_kv_heads;
-    const dim3 grid(S, hkv, batch);
-    hipLaunchKernelGGL((paged_attn_partial_kernel<D, G, LAM, PF>), grid, dim3(64), 0, st, q_rot, p->k, p->v,
-                       table, mbps, ctx, hkv, p->num_blocks, max_ctx, chunk_tokens / BS, S,
-                       scale_log2, part_acc, part_ml, out, p->err);
-    // every split sequence (more than one chunk) is merged by the combine kernel
-    if (max_ctx + 1 > chunk_tokens)
-        hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), dim3(hkv * G, batch), dim3(256), 0, st,
-                           part_acc, part_ml, ctx, mbps, hkv, max_ctx, chunk_tokens, S, out);
+    auto kern = paged_attn_partial_kernel<D, G, LAM, PF>;
+    const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, resident_waves(kern));
+    hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot, p->k, p->v, table, mbps, ctx, batch,
+                       hkv, p->num_blocks, max_ctx, min_tiles, scale_log2, part_acc, part_ml, out,
+                       p->err);
+    hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), dim3(hkv * G, batch), dim3(256), 0, st,
+                       part_acc, part_ml, ctx, batch, mbps, hkv, max_ctx, waves, min_tiles, out);
 }
 
 template <int D>
 int dispatch_group(int G, const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                    const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
-                   float scale_log2, int32_t max_ctx, int32_t chunk_tokens, int32_t S,
-                   float* pa, float2* pm, hipStream_t st) {
+                   float scale_log2, int32_t max_ctx, int32_t min_tiles, float* pa, float2* pm,
+                   hipStream_t st) {
 #define MIKV_G(GG)                                                                             \
     case GG:                                                                                   \
         launch_attn<D, GG>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,        \
-                           chunk_tokens, S, pa, pm, st);                                       \
+                           min_tiles, pa, pm, st);                                             \
         return MI_OK;
     switch (G) {
         MIKV_G(1)
@@ -639,22 +744,22 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 namespace mikv {
 
-int32_t default_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len) {
-    // Aim for about eight resident waves per CU on 256 CUs, in chunks of
-    // 64..1024 tokens (whole 16-token blocks).
-    const int64_t tokens = static_cast<int64_t>(batch) * num_kv_heads * (max_context_len + 1);
-    const int64_t target_units = 2048;
-    int64_t c = (tokens + target_units - 1) / target_units;
-    c = (c + BS - 1) / BS * BS;
-    c = std::max<int64_t>(64, std::min<int64_t>(1024, c));
-    return static_cast<int32_t>(c);
+int32_t default_split_tokens(int32_t, int32_t, int32_t) { return kDefaultSplitTokens; }
+
+int attention_grid_waves(int32_t batch, int32_t hkv, int32_t max_ctx, int32_t min_tiles,
+                         int resident) {
+    // upper bound of the tile count: every sequence at max_context_len
+    const int64_t t_upper = static_cast<int64_t>(batch) * hkv * ((max_ctx + BS) / BS);
+    const int64_t by_work = (t_upper + min_tiles - 1) / min_tiles;
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(resident, by_work)));
 }
 
-size_t attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t split_tokens) {
-    const size_t S = (static_cast<size_t>(max_context_len) + split_tokens) / split_tokens;
-    const size_t units = static_cast<size_t>(batch) * num_q_heads * S;   // (b, kv head, chunk, h)
-    return align_up(units * head_dim * sizeof(float), 256) + align_up(units * sizeof(float2), 256);
+size_t attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t split_tokens) {
+    const int waves = attention_grid_waves(batch, num_kv_heads, max_context_len, split_tokens / BS,
+                                           kMaxAttnWaves);
+    const size_t slots = 2 * static_cast<size_t>(waves) * (num_q_heads / num_kv_heads);
+    return align_up(slots * head_dim * sizeof(float), 256) + align_up(slots * sizeof(float2), 256);
 }
 
 int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
@@ -680,19 +785,20 @@ int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16
                             void* ws, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int G = hq / p->num_kv_heads;
-    const int32_t S = (max_ctx + split_tokens) / split_tokens;
-    const size_t units = static_cast<size_t>(batch) * hq * S;
+    const int min_tiles = split_tokens / BS;
+    const int waves_bound = attention_grid_waves(batch, p->num_kv_heads, max_ctx, min_tiles, kMaxAttnWaves);
+    const size_t slots = 2 * static_cast<size_t>(waves_bound) * G;
     float* pa = static_cast<float*>(ws);
     float2* pm = reinterpret_cast<float2*>(static_cast<char*>(ws) +
-                                           align_up(units * p->head_dim * sizeof(float), 256));
+                                           align_up(slots * p->head_dim * sizeof(float), 256));
     const float scale_log2 = scale * 1.4426950408889634f;
     int rc;
     if (p->head_dim == 128)
         rc = dispatch_group<128>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                 split_tokens, S, pa, pm, st);
+                                 min_tiles, pa, pm, st);
     else
         rc = dispatch_group<64>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                split_tokens, S, pa, pm, st);
+                                min_tiles, pa, pm, st);
     if (rc != MI_OK) return rc;
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
@@ -727,8 +833,10 @@ extern "C" size_t mi_paged_gqa_decode_split_workspace_bytes(mi_kv_pool_t p, int3
                                                             int32_t split_tokens) {
     if (!p || batch < 0 || hq <= 0 || max_ctx < 0) return 0;
     if (split_tokens == 0) split_tokens = mikv::default_split_tokens(batch, p->num_kv_heads, max_ctx);
-    if (split_tokens <= 0 || split_tokens % BS || split_tokens > 64 * BS) return 0;
-    return mikv::attention_workspace_bytes(batch, hq, p->head_dim, max_ctx, split_tokens);
+    if (split_tokens <= 0 || split_tokens % BS) return 0;
+    if (!mikv::supported_group(hq, p->num_kv_heads) || batch > mikv::kMaxBatch) return 0;
+    return mikv::attention_workspace_bytes(batch, hq, p->num_kv_heads, p->head_dim, max_ctx,
+                                           split_tokens);
 }
 
 extern "C" size_t mi_paged_gqa_decode_workspace_bytes(mi_kv_pool_t p, int32_t batch, int32_t hq,
@@ -745,10 +853,12 @@ extern "C" int mi_paged_gqa_decode_split(mi_kv_pool_t p, const uint16_t* q_rot, 
     if (rc != MI_OK) return rc;
     if (max_ctx < 0 || split_tokens < 0) return MI_ERR_INVALID_ARG;
     if (split_tokens == 0) split_tokens = mikv::default_split_tokens(batch, p->num_kv_heads, max_ctx);
-    if (split_tokens % BS || split_tokens > 64 * BS) return MI_ERR_UNSUPPORTED;
+    if (split_tokens % BS) return MI_ERR_UNSUPPORTED;
+    if (batch > mikv::kMaxBatch) return MI_ERR_UNSUPPORTED;
     if (batch == 0) return MI_OK;
     if (!q_rot || !out || !table || !ctx || !ws || q_rot == out) return MI_ERR_INVALID_ARG;
-    if (ws_bytes < mikv::attention_workspace_bytes(batch, hq, p->head_dim, max_ctx, split_tokens))
+    if (ws_bytes < mikv::attention_workspace_bytes(batch, hq, p->num_kv_heads, p->head_dim, max_ctx,
+                                                   split_tokens))
         return MI_ERR_WORKSPACE_TOO_SMALL;
     if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(p->head_dim));
     return mikv::launch_paged_gqa_decode(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx,

@@ -34,12 +34,19 @@ inline bool supported_group(int32_t hq, int32_t hkv) {
     return hq > 0 && hkv > 0 && hq % hkv == 0 && hq / hkv >= 1 && hq / hkv <= 8;
 }
 
-// Tokens per split-K chunk chosen by the library for a given workload.
+constexpr int kMaxBatch = 1024;            // sequences per attention call
+constexpr int kMaxAttnWaves = 4096;        // upper bound of the attention grid
+constexpr int kDefaultSplitTokens = 128;   // minimum tokens per wave's share
+
+// Minimum tokens per attention wave's share chosen by the library.
 int32_t default_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len);
 
-// Workspace bytes of the attention split-K partials.
-size_t attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t split_tokens);
+// Attention grid size: resident waves, capped by the work bound.
+int attention_grid_waves(int32_t batch, int32_t hkv, int32_t max_ctx, int32_t min_tiles, int resident);
+
+// Workspace bytes of the attention partials (two slots per wave).
+size_t attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t split_tokens);
 
 // Launches (attention.hip). Arguments are validated by the caller.
 int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,

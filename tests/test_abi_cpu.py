@@ -136,10 +136,12 @@ def test_blocks_needed_and_size_formula_match_oracle():
 def test_workspace_queries_are_host_only():
     pool = _host_pool()
     try:
-        ws = mk.mi_paged_gqa_decode_split_workspace_bytes(pool, 32, 32, 16384, 512)
-        S = (16384 + 512) // 512
-        assert ws >= 32 * 32 * S * (128 * 4 + 8)
-        assert mk.mi_paged_gqa_decode_split_workspace_bytes(pool, 32, 32, 16384, 24) == 0
-        assert mk.mi_paged_gqa_decode_workspace_bytes(pool, 32, 32, 16384) > 0
+        ws = mk.mi_paged_gqa_decode_split_workspace_bytes(pool, 32, 8, 16384, 512)
+        assert ws >= 2 * 4 * (128 * 4 + 8)                 # at least one wave's two slots
+        assert mk.mi_paged_gqa_decode_split_workspace_bytes(pool, 64, 8, 16384, 512) >= ws
+        assert mk.mi_paged_gqa_decode_split_workspace_bytes(pool, 32, 8, 16384, 24) == 0
+        assert mk.mi_paged_gqa_decode_split_workspace_bytes(pool, 32, 18, 16384, 512) == 0  # group of 9
+        assert mk.mi_paged_gqa_decode_workspace_bytes(pool, 32, 8, 16384) > 0
+        assert mk.mi_paged_gqa_decode_workspace_bytes(pool, 2000, 8, 100) == 0          # batch above the limit
     finally:
         mk.mi_kv_pool_destroy(pool)
