@@ -547,88 +547,90 @@ __global__ __launch_bounds__(64) void paged_attn_partial_kernel(
 
 // Combine kernel: one workgroup per (query head, sequence). It rebuilds the
 // same partition, and if the segment was cut into pieces, merges their
-// partials in range order: weights 2^(m_i - max m), normalised by the
-// weighted sum of the l_i, one rounding to bf16. Sequences with an
-// out-of-range length get NaN outputs.
+// partials in range order. Thread (d, cg) folds the pieces cg, cg + NCG, ...
+// of head dim d into a running (max, sum, weighted acc) with 2^(m - max)
+// rescaling; the NCG groups are then merged in order. One memory round trip
+// for the partition, one per four pieces; a single rounding to bf16.
+// Sequences with an out-of-range length (no tiles) get NaN outputs.
 template <int D, int G>
 __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
     const float* __restrict__ part_acc, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t mbps, int32_t hkv,
     int32_t max_ctx, int32_t grid_waves, int32_t min_tiles, uint16_t* __restrict__ out) {
     constexpr int NCG = 256 / D;        // piece groups
-    constexpr int NW = 256 / 64;        // waves
     __shared__ int TP[kMaxBatch + 1];
-    __shared__ float red[NCG][D];
-    __shared__ float wred[2][NW];
+    __shared__ float sm[NCG][D], sl[NCG][D], sa[NCG][D];
     const int hq_idx = blockIdx.x;      // query head
     const int b = blockIdx.y;
     const int g = hq_idx / G;
     const int h = hq_idx - g * G;
     const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int wv = t >> 6;
     uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + hq_idx) * D;
 
-    const int ctx = ctx_lens[b];
-    if (ctx < 0 || ctx > max_ctx || ctx + 1 > mbps * BS) {
+    if (t < 64) {
+        bool bad;
+        build_tile_prefix(ctx_lens, batch, mbps, max_ctx, hkv, TP, &bad, t);
+    }
+    __syncthreads();
+    const int T = TP[batch];
+    const int nt = (TP[b + 1] - TP[b]) / hkv;
+    if (nt == 0) {                                  // length out of range
         if (t < D) o[t] = 0x7fc0;
         return;
     }
-    int T = 0;
-    if (wv == 0) {
-        bool bad;
-        T = build_tile_prefix(ctx_lens, batch, mbps, max_ctx, hkv, TP, &bad, lane);
-    }
-    __syncthreads();
-    T = TP[batch];
     const int W = active_waves(T, grid_waves, min_tiles);
-    const int nt = (ctx + BS) / BS;
     const int A = TP[b] + g * nt;                  // first tile of the segment
     const int w_first = wave_of_tile(A, T, W);
     const int w_last = wave_of_tile(A + nt - 1, T, W);
     if (w_first == w_last) return;                 // finished by one wave
     const int npieces = w_last - w_first + 1;
     const int first_slot = 2 * w_first + (range_start(w_first, T, W) < A ? 1 : 0);
-    // piece k (0 .. npieces-1) lives in slot first_slot for k = 0, 2 (w_first + k) after
-    auto slot_of = [&](int k) { return k == 0 ? first_slot : 2 * (w_first + k); };
-
-    float M = kNegInf;
-    for (int k = t; k < npieces; k += 256) M = fmaxf(M, part_ml[static_cast<size_t>(slot_of(k)) * G + h].x);
-#pragma unroll
-    for (int x = 1; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
-    if (lane == 0) wred[0][wv] = M;
-    __syncthreads();
-    M = wred[0][0];
-#pragma unroll
-    for (int v = 1; v < NW; ++v) M = fmaxf(M, wred[0][v]);
-
-    float lsum = 0.f;
-    for (int k = t; k < npieces; k += 256) {
-        const float2 ml = part_ml[static_cast<size_t>(slot_of(k)) * G + h];
-        lsum = fmaf(__builtin_amdgcn_exp2f(ml.x - M), ml.y, lsum);
-    }
-#pragma unroll
-    for (int x = 1; x < 64; x *= 2) lsum += __shfl_xor(lsum, x);
-    if (lane == 0) wred[1][wv] = lsum;
+    // piece k lives in slot first_slot for k = 0, else 2 (w_first + k)
 
     const int d = t % D;
     const int cg = t / D;
-    float a = 0.f;
-    for (int k = cg; k < npieces; k += NCG) {
-        const size_t sl = static_cast<size_t>(slot_of(k));
-        const float2 ml = part_ml[sl * G + h];
-        a = fmaf(__builtin_amdgcn_exp2f(ml.x - M), part_acc[(sl * G + h) * D + d], a);
+    float m = kNegInf, l = 0.f, a = 0.f;
+    for (int k0 = cg; k0 < npieces; k0 += 4 * NCG) {
+        float2 ml[4];
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k = k0 + u * NCG;
+            ml[u] = make_float2(kNegInf, 0.f);
+            v[u] = 0.f;
+            if (k < npieces) {
+                const size_t sl_idx = static_cast<size_t>(k == 0 ? first_slot : 2 * (w_first + k));
+                ml[u] = part_ml[sl_idx * G + h];
+                v[u] = part_acc[(sl_idx * G + h) * D + d];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (k0 + u * NCG >= npieces) break;
+            const float mn = fmaxf(m, ml[u].x);
+            const float fo = __builtin_amdgcn_exp2f(m - mn);     // 0 while m = -inf
+            const float fn = __builtin_amdgcn_exp2f(ml[u].x - mn);
+            l = l * fo + ml[u].y * fn;
+            a = a * fo + v[u] * fn;
+            m = mn;
+        }
     }
-    red[cg][d] = a;
+    sm[cg][d] = m;
+    sl[cg][d] = l;
+    sa[cg][d] = a;
     __syncthreads();
     if (t < D) {
-        float tot = red[0][t];
+        float M = sm[0][t];
 #pragma unroll
-        for (int c2 = 1; c2 < NCG; ++c2) tot += red[c2][t];
-        float lt = wred[1][0];
+        for (int c2 = 1; c2 < NCG; ++c2) M = fmaxf(M, sm[c2][t]);
+        float lt = 0.f, at = 0.f;
 #pragma unroll
-        for (int v = 1; v < NW; ++v) lt += wred[1][v];
-        o[t] = f32_to_bf16_rne(tot / lt);
+        for (int c2 = 0; c2 < NCG; ++c2) {
+            const float f = (sm[c2][t] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sm[c2][t] - M);
+            lt = fmaf(sl[c2][t], f, lt);
+            at = fmaf(sa[c2][t], f, at);
+        }
+        o[t] = f32_to_bf16_rne(at / lt);
     }
 }
 

@@ -37,6 +37,8 @@ inline bool supported_group(int32_t hq, int32_t hkv) {
 constexpr int kMaxBatch = 1024;            // sequences per attention call
 constexpr int kMaxAttnWaves = 4096;        // upper bound of the attention grid
 constexpr int kDefaultSplitTokens = 128;   // minimum tokens per wave's share
+constexpr int kMaxLayerBatch = 32;         // rows of the decoder-layer projections
+constexpr int kLayerDimMultiple = 256;     // hidden, intermediate, Hq * D multiples
 
 // Minimum tokens per attention wave's share chosen by the library.
 int32_t default_split_tokens(int32_t batch, int32_t num_kv_heads, int32_t max_context_len);

@@ -1,0 +1,138 @@
+"""GPU parity of the full decoder-layer decode step against the fp64 oracle,
+through the C ABI (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_246_amd as mk
+import workloads
+from oracle import bf16 as obf16
+from oracle import layer as olayer
+from tests.gpu_harness import DEV, bits_to_dev, check_tolerance, dev_to_bits, ulp_diff_bf16
+
+pytestmark = pytest.mark.gpu
+
+SMALL = workloads.DecodeConfig(
+    "small_layer", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+    num_blocks=64, rope_theta=1e4, ctx_draw="fixed", ctx_fixed=(0, 20, 47), seed=11,
+    hidden=256, intermediate=512, rms_eps=1e-6)
+
+WIDE = workloads.DecodeConfig(
+    "wide_layer", batch=20, num_q_heads=4, num_kv_heads=4, head_dim=128, block_size=16,
+    num_blocks=512, rope_theta=1e6, ctx_draw="uniform", ctx_lo=0, ctx_hi=200, seed=12,
+    hidden=512, intermediate=768, rms_eps=1e-5)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mk.lib()
+
+
+def _run_layer(cfg, case, w, x):
+    B = len(case.context_lens)
+    kp, vp = bits_to_dev(case.k_pool), bits_to_dev(case.v_pool)
+    wd = {n: bits_to_dev(a) for n, a in w.items()}
+    xd = bits_to_dev(x)
+    xo = torch.empty_like(xd)
+    table = torch.from_numpy(case.block_table).to(DEV)
+    ctx = torch.from_numpy(case.context_lens).to(DEV)
+    mbps, max_ctx = case.block_table.shape[1], int(case.context_lens.max())
+    pool = mk.mi_kv_pool_init(case.num_blocks, 16, cfg.num_kv_heads, cfg.head_dim, kp, vp)
+    try:
+        lc = mk.layer_config(cfg.hidden, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                             cfg.intermediate, cfg.rms_eps, cfg.rope_theta)
+        lw = mk.layer_weights(**wd)
+        need = mk.mi_decoder_layer_workspace_bytes(lc, pool, B, max_ctx)
+        assert need > 0
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        mk.mi_decoder_layer_decode(pool, lc, lw, xd, xo, table, mbps, ctx, B, max_ctx, ws, need)
+        torch.cuda.synchronize()
+        assert mk.mi_kv_pool_check_errors(pool) == 0
+    finally:
+        mk.mi_kv_pool_destroy(pool)
+    return dev_to_bits(xo), dev_to_bits(kp), dev_to_bits(vp)
+
+
+def _oracle(cfg, case, w, x):
+    return olayer.decoder_layer_decode(x, w, case.k_pool, case.v_pool, case.block_table,
+                                       case.context_lens, cfg.block_size, cfg.num_q_heads,
+                                       cfg.num_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.rope_theta)
+
+
+def _check_cache(case, cfg, gk, gv, kn, vn):
+    """Written slots: same places as the oracle, values within one bf16 ulp
+    (the GPU projection accumulates in fp32); every other slot untouched."""
+    slots = np.zeros(case.k_pool.shape[:3], dtype=bool)
+    for b, ctx in enumerate(case.context_lens):
+        slots[case.block_table[b, ctx // 16], :, ctx % 16] = True
+    sel = slots[..., None].repeat(cfg.head_dim, -1)
+    assert np.array_equal(gk[~sel], case.k_pool[~sel])
+    assert np.array_equal(gv[~sel], case.v_pool[~sel])
+    uk, uv = ulp_diff_bf16(gk[sel], kn[sel]), ulp_diff_bf16(gv[sel], vn[sel])
+    assert uk.max() <= 2 and uv.max() <= 2, (uk.max(), uv.max())
+
+
+@pytest.mark.parametrize("cfg", [SMALL, WIDE], ids=["small", "wide_b20"])
+def test_layer_small_shapes(cfg):
+    print("layer", cfg.name, flush=True)
+    case = workloads.make_decode_case(cfg, pool="poison")
+    w = workloads.make_layer_weights(cfg, std=0.05)
+    x = workloads.make_layer_input(cfg)
+    out, gk, gv = _run_layer(cfg, case, w, x)
+    ref, kn, vn = _oracle(cfg, case, w, x)
+    mx, rel = check_tolerance(out, ref, cfg.name)
+    print("  max|d| %.3g relL2 %.3g" % (mx, rel), flush=True)
+    _check_cache(case, cfg, gk, gv, kn, vn)
+
+
+def test_layer_zero_output_projections_return_input_bit_exact():
+    cfg = SMALL
+    case = workloads.make_decode_case(cfg, pool="poison")
+    w = dict(workloads.make_layer_weights(cfg, std=0.05))
+    w["w_o"] = np.zeros_like(w["w_o"])
+    w["w_down"] = np.zeros_like(w["w_down"])
+    x = workloads.make_layer_input(cfg)
+    out, _, _ = _run_layer(cfg, case, w, x)
+    assert np.array_equal(out, x)
+
+
+def test_layer_qwen3_8b_shape_full_size():
+    """Qwen3-8B-shaped layer, batch 8, contexts U[512, 4096], full oracle."""
+    cfg = workloads.CONFIGS["qwen3_8b_layer"]
+    print("layer qwen3_8b_layer", flush=True)
+    case = workloads.make_decode_case(cfg, pool="poison")
+    w = workloads.make_layer_weights(cfg)
+    x = workloads.make_layer_input(cfg)
+    out, gk, gv = _run_layer(cfg, case, w, x)
+    ref, kn, vn = _oracle(cfg, case, w, x)
+    mx, rel = check_tolerance(out, ref, "qwen3_8b_layer")
+    print("  max|d| %.3g relL2 %.3g" % (mx, rel), flush=True)
+    _check_cache(case, cfg, gk, gv, kn, vn)
+
+
+def test_layer_argument_errors():
+    cfg = SMALL
+    case = workloads.make_decode_case(cfg, pool="poison")
+    kp, vp = bits_to_dev(case.k_pool), bits_to_dev(case.v_pool)
+    pool = mk.mi_kv_pool_init(case.num_blocks, 16, cfg.num_kv_heads, cfg.head_dim, kp, vp)
+    try:
+        lc = mk.layer_config(300, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                             cfg.intermediate, cfg.rms_eps, cfg.rope_theta)
+        assert mk.mi_decoder_layer_workspace_bytes(lc, pool, 3, 100) == 0     # hidden % 256
+        lc = mk.layer_config(cfg.hidden, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                             cfg.intermediate, cfg.rms_eps, cfg.rope_theta)
+        assert mk.mi_decoder_layer_workspace_bytes(lc, pool, 33, 100) == 0    # batch > 32
+        need = mk.mi_decoder_layer_workspace_bytes(lc, pool, 3, 100)
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        x = torch.zeros(3, cfg.hidden, dtype=torch.int16, device=DEV)
+        lw = mk.layer_weights(*([x] * 7))
+        with pytest.raises(mk.MikvError) as e:
+            mk.mi_decoder_layer_decode(pool, lc, lw, x, x, x, 4, x, 3, 100, ws, need)
+        assert e.value.status == mk.MI_ERR_INVALID_ARG                    # x_in aliases x_out
+        with pytest.raises(mk.MikvError) as e:
+            mk.mi_decoder_layer_decode(pool, lc, lw, x, x.clone(), x, 4, x, 3, 100, ws, need - 1)
+        assert e.value.status == mk.MI_ERR_WORKSPACE_TOO_SMALL
+    finally:
+        mk.mi_kv_pool_destroy(pool)
