@@ -26,6 +26,22 @@ PEAK_BF16_TFLOPS = 2500.0
 METRIC = "paged GQA decode attention: KV GB/s & % HBM peak; layer-step tokens/s"
 
 
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed counter summary, if it
+    was taken on the current kernel source (else None)."""
+    import hashlib
+    src = os.path.join(ROOT, "paged_kv_cache_246_amd", "csrc", "attention.hip")
+    summ = os.path.join(ROOT, "profiles", "attention_qwen3_8b_long_hbm_counters.md")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        fields = dict(ln.split(": ", 1) for ln in open(summ).read().splitlines() if ": " in ln)
+        if fields.get("source_sha256_prefix", "").strip() == sha:
+            return int(fields["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
 def _dev(a, torch, dev):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 
@@ -190,7 +206,11 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="split-K tokens (0: library default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-layer", action="store_true", help="skip the full-layer step")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time only the full-layer step (for its kernel profile)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the paged decode path is single-GPU "
@@ -205,7 +225,25 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        # A plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it
+        # scales the counters taken on the attention kernel.
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
     mk.lib()
+
+    if args.layer_only:
+        lay = run_layer_bench(args, torch, mk, workloads)
+        print(json.dumps({"metric": "layer-step tokens/s", "value": lay["tokens_per_s"],
+                          "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "layer_step": lay}), flush=True)
+        return
 
     r = run_attention_bench(args, torch, mk, workloads)
     ms = r["ms_step"]
@@ -241,7 +279,7 @@ def main():
         "hbm_frac": round(value / PEAK_HBM_GBPS, 4),
         "layer_step_tokens_per_s_attention_only": round(len(r["case"].context_lens) / (ms * 1e-3), 1),
         "roofline": {
-            "kernel": "mi_paged_gqa_decode (split-K partial + combine)",
+            "kernel": "mi_paged_gqa_decode (attention partial kernel + combine kernel)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
@@ -249,7 +287,7 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "avg_launch_ms": round(attn_ms, 5),
             "algorithmic_bytes": int(r["attn_bytes"]),
-            "traffic": None,
+            "traffic": recorded_traffic(),
         },
     }
     if not args.no_layer:
