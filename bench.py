@@ -104,6 +104,55 @@ def run_attention_bench(args, torch, mk, workloads):
     )
 
 
+def run_small_workloads(args, torch, mk, workloads):
+    """Decode step (write + attention) on the other decode workloads: step time,
+    algorithmic GB/s and fraction of the HBM peak (most are launch-latency bound)."""
+    dev = "cuda:0"
+    res = {}
+    for name in ["tiny", "qwen3_1p7b", "qwen2p5_7b_b1", "qwen2p5_7b_b4", "qwen2p5_7b_b8"]:
+        cfg = workloads.CONFIGS[name]
+        case = workloads.make_decode_case(cfg, pool="bench")
+        B, Hq, Hkv, D = len(case.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+        kp, vp = _dev(case.k_pool, torch, dev), _dev(case.v_pool, torch, dev)
+        q, k, v = _dev(case.q, torch, dev), _dev(case.k, torch, dev), _dev(case.v, torch, dev)
+        q_rot, out = torch.empty_like(q), torch.empty_like(q)
+        table = torch.from_numpy(case.block_table).to(dev)
+        ctx = torch.from_numpy(case.context_lens).to(dev)
+        mbps, max_ctx = case.block_table.shape[1], int(case.context_lens.max())
+        pool = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp, vp)
+        ws_bytes = mk.mi_paged_gqa_decode_workspace_bytes(pool, B, Hq, max_ctx)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream()
+        st = stream.cuda_stream
+
+        def step():
+            mk.mi_write_decode_kv(pool, q, k, v, q_rot, table, mbps, ctx, B, Hq, cfg.rope_theta, st)
+            mk.mi_paged_gqa_decode(pool, q_rot, out, table, mbps, ctx, B, Hq, 0.0, max_ctx, ws,
+                                   ws_bytes, st)
+
+        for _ in range(args.warmup):
+            step()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        faults = mk.mi_kv_pool_check_errors(pool)
+        mk.mi_kv_pool_destroy(pool)
+        if faults:
+            raise RuntimeError("device fault bits %#x on %s" % (faults, name))
+        nbytes = (workloads.attention_bytes(case.context_lens, Hq, Hkv, D, 16)
+                  + workloads.write_bytes(B, Hq, Hkv, D))
+        res[name] = {"ms_per_step": round(ms, 5), "algorithmic_bytes": int(nbytes),
+                     "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "tokens_per_s": round(B / (ms * 1e-3), 1)}
+    return res
+
+
 def run_layer_bench(args, torch, mk, workloads):
     dev = "cuda:0"
     cfg = workloads.CONFIGS["qwen3_8b_layer"]
@@ -206,6 +255,7 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="split-K tokens (0: library default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-layer", action="store_true", help="skip the full-layer step")
+    ap.add_argument("--no-small", action="store_true", help="skip the smaller decode workloads")
     ap.add_argument("--layer-only", action="store_true",
                     help="time only the full-layer step (for its kernel profile)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -295,6 +345,8 @@ def main():
             line["layer_step"] = run_layer_bench(args, torch, mk, workloads)
         except mk.MikvError as e:
             line["layer_step"] = {"error": str(e)}
+    if not args.no_small:
+        line["other_workloads"] = run_small_workloads(args, torch, mk, workloads)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(r["case"], r["cfg"], workloads, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -119,17 +119,31 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 // tiles. load() only issues memory reads (activations, then weights); the
 // activation's conversion to bf16 (hi, lo) happens in mma(), so prefetching
 // the next batch never waits on its own loads.
-template <int MT, int NW, int ACT, int KB>
+//
+// Weight loads come in one of two layouts. Direct (TR = false): each lane
+// loads exactly its MFMA B-operand piece, i.e. 16 rows x 64 bytes per load
+// instruction. Transposed (TR = true): 4 KB lanes share a row, so one
+// instruction reads 64 / (4 KB) whole row segments of 64 KB bytes (full
+// 128-byte lines at KB = 2); mma() writes the batch to the wave's LDS tile and
+// reads it back in the MFMA layout (rows padded by 16 bytes).
+template <int MT, int NW, int ACT, int KB, bool TR>
 struct GemmBatch {
     static constexpr int AE = (ACT == kActF32Split) ? 4 : 2;   // activation element bytes
-    uint4 w[KB][NW];
+    static constexpr int LPR = 4 * KB;                         // transposed: lanes per row
+    static constexpr int RPI = 64 / LPR;                       // transposed: rows per load
+    static constexpr int ROWB = 64 * KB + 16;                  // LDS bytes per row (padded)
+    static constexpr int LDS_BYTES = TR ? 16 * NW * ROWB : 16;
+    uint4 w[KB][NW];       // direct: [step][tile]; transposed: flat [KB * NW] loads
     uint4 a0[KB][MT];      // bf16 activations, or fp32 elements 0..3
     uint4 a1[KB][MT];      // gain (kActGainSplit) or fp32 elements 4..7
 
-    // kbyte: byte offset of the batch's first K column in a bf16 row
+    // kbyte: byte offset of the batch's first K column in a bf16 row.
+    // Direct: woff[j] = lane's offset in tile j. Transposed: woff[0] = lane's
+    // offset in load 0, wstep = bytes between consecutive loads (RPI rows).
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rw, const uint32_t (&woff)[NW],
-                                         __amdgpu_buffer_rsrc_t ra, const uint32_t (&aoff)[MT],
-                                         __amdgpu_buffer_rsrc_t rg, uint32_t goff, uint32_t kbyte) {
+                                         uint32_t wstep, __amdgpu_buffer_rsrc_t ra,
+                                         const uint32_t (&aoff)[MT], __amdgpu_buffer_rsrc_t rg,
+                                         uint32_t goff, uint32_t kbyte) {
 #pragma unroll
         for (int u = 0; u < KB; ++u)
 #pragma unroll
@@ -140,13 +154,27 @@ struct GemmBatch {
                 else if constexpr (ACT == kActGainSplit) a1[u][mt] = bload<0>(rg, goff, kbyte + u * kKStep * 2);
                 else a1[u][mt] = make_uint4(0, 0, 0, 0);
             }
+        if constexpr (TR) {
 #pragma unroll
-        for (int u = 0; u < KB; ++u)
+            for (int i = 0; i < KB * NW; ++i)
+                w[i / NW][i % NW] = bload<kAuxStream>(rw, woff[0], kbyte + i * wstep);
+        } else {
 #pragma unroll
-            for (int j = 0; j < NW; ++j) w[u][j] = bload<kAuxStream>(rw, woff[j], kbyte + u * kKStep * 2);
+            for (int u = 0; u < KB; ++u)
+#pragma unroll
+                for (int j = 0; j < NW; ++j) w[u][j] = bload<kAuxStream>(rw, woff[j], kbyte + u * kKStep * 2);
+        }
     }
 
-    __device__ __forceinline__ void mma(f32x4_t (&acc)[NW][MT]) const {
+    // lds: the wave's tile; wr = lane's write offset of load 0 (bytes),
+    // rd = lane's read offset for step 0 of tile 0
+    __device__ __forceinline__ void mma(f32x4_t (&acc)[NW][MT], char* lds, uint32_t wr,
+                                        uint32_t rd) const {
+        if constexpr (TR) {
+#pragma unroll
+            for (int i = 0; i < KB * NW; ++i)
+                *reinterpret_cast<uint4*>(lds + wr + i * RPI * ROWB) = w[i / NW][i % NW];
+        }
 #pragma unroll
         for (int u = 0; u < KB; ++u)
 #pragma unroll
@@ -175,13 +203,15 @@ struct GemmBatch {
                 }
 #pragma unroll
                 for (int j = 0; j < NW; ++j) {
+                    uint4 wv;
+                    if constexpr (TR) wv = *reinterpret_cast<const uint4*>(lds + rd + j * 16 * ROWB + u * 64);
+                    else wv = w[u][j];
                     acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, hi), __builtin_bit_cast(bf16x8_t, w[u][j]), acc[j][mt],
-                        0, 0, 0);
+                        __builtin_bit_cast(bf16x8_t, hi), __builtin_bit_cast(bf16x8_t, wv), acc[j][mt], 0, 0, 0);
                     if constexpr (ACT != kActBf16)
                         acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, lo), __builtin_bit_cast(bf16x8_t, w[u][j]),
-                            acc[j][mt], 0, 0, 0);
+                            __builtin_bit_cast(bf16x8_t, lo), __builtin_bit_cast(bf16x8_t, wv), acc[j][mt],
+                            0, 0, 0);
                 }
             }
     }
@@ -192,13 +222,14 @@ struct GemmBatch {
 // next batch is in flight while the current one is multiplied (the loop is
 // unrolled by two so the slots are fixed registers). A group never straddles
 // the W0/W1 boundary (n_split is a multiple of 16 NW).
-template <int MT, int NW, int ACT>
+template <int MT, int NW, int ACT, bool TR>
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(
     const void* __restrict__ Aptr, const uint16_t* __restrict__ gain, int M, int K,
     const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int n_split, int N,
     int k_chunk, float* __restrict__ P) {
     constexpr int KB = batch_steps(NW);        // MFMA steps per batch
-    using Batch = GemmBatch<MT, NW, ACT, KB>;
+    using Batch = GemmBatch<MT, NW, ACT, KB, TR>;
+    __shared__ __align__(16) char lds[Batch::LDS_BYTES];
     const int grp = blockIdx.x;
     const int s = blockIdx.y;
     const int lane = threadIdx.x;
@@ -213,8 +244,19 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(Aptr, static_cast<uint32_t>(static_cast<size_t>(M) * K * Batch::AE));
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(gain, gain ? static_cast<uint32_t>(K) * 2 : 0u);
     uint32_t woff[NW];
+    uint32_t wstep = 0, wr = 0, rd = 0;
+    if constexpr (TR) {
+        const int r_in = lane / Batch::LPR, piece = lane % Batch::LPR;
+        woff[0] = (static_cast<uint32_t>(row0 + r_in) * K) * 2 + piece * 16;
 #pragma unroll
-    for (int j = 0; j < NW; ++j) woff[j] = (static_cast<uint32_t>(row0 + j * 16 + col) * K + kq * 8) * 2;
+        for (int j = 1; j < NW; ++j) woff[j] = 0;
+        wstep = static_cast<uint32_t>(Batch::RPI) * K * 2;
+        wr = r_in * Batch::ROWB + piece * 16;
+        rd = col * Batch::ROWB + kq * 16;
+    } else {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) woff[j] = (static_cast<uint32_t>(row0 + j * 16 + col) * K + kq * 8) * 2;
+    }
     // Rows m >= M of the MFMA tile only feed output rows that are never
     // stored, so those lanes read row M - 1 again.
     uint32_t aoff[MT];
@@ -233,20 +275,20 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(
     const int nb = k_chunk / (KB * kKStep);   // batches (>= 1)
     const uint32_t kb0 = static_cast<uint32_t>(s) * k_chunk * 2;
     Batch b0, b1;
-    b0.load(rw, woff, ra, aoff, rg, goff, kb0);
+    b0.load(rw, woff, wstep, ra, aoff, rg, goff, kb0);
     int i = 0;
     for (; i + 2 < nb; i += 2) {
-        b1.load(rw, woff, ra, aoff, rg, goff, kb0 + (i + 1) * STEP_BYTES);
-        b0.mma(acc);
-        b0.load(rw, woff, ra, aoff, rg, goff, kb0 + (i + 2) * STEP_BYTES);
-        b1.mma(acc);
+        b1.load(rw, woff, wstep, ra, aoff, rg, goff, kb0 + (i + 1) * STEP_BYTES);
+        b0.mma(acc, lds, wr, rd);
+        b0.load(rw, woff, wstep, ra, aoff, rg, goff, kb0 + (i + 2) * STEP_BYTES);
+        b1.mma(acc, lds, wr, rd);
     }
     if (i + 1 < nb) {
-        b1.load(rw, woff, ra, aoff, rg, goff, kb0 + (i + 1) * STEP_BYTES);
-        b0.mma(acc);
-        b1.mma(acc);
+        b1.load(rw, woff, wstep, ra, aoff, rg, goff, kb0 + (i + 1) * STEP_BYTES);
+        b0.mma(acc, lds, wr, rd);
+        b1.mma(acc, lds, wr, rd);
     } else {
-        b0.mma(acc);
+        b0.mma(acc, lds, wr, rd);
     }
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
@@ -411,19 +453,18 @@ __global__ __launch_bounds__(256) void residual_out_kernel(const float* __restri
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Shape of a projection's grid: NW column tiles per wave and S K splits.
-// Measured on MI355X (8-row activations): wide projections stream best with
-// 8 tiles (128 weight rows) per wave and ~768 waves, the others with 4 tiles
-// per wave and ~1536 waves. S is the largest divisor of the K batches that
-// keeps the wave count within that target.
+// Measured on MI355X (8-row activations, transposed weight loads): 4 tiles
+// (64 weight rows) per wave and about 1536 waves stream best; S is the
+// largest divisor of the K batches that keeps the wave count within that.
 struct GemmShape {
     int nw, splits;
 };
 GemmShape gemm_shape(int N, int K, int n_split) {
     const int tiles = N / 16;
     const int split_tiles = n_split / 16;
-    int nw = (tiles >= 1024) ? 8 : 4;
+    int nw = 4;
     while (nw > 1 && (tiles % nw || split_tiles % nw)) nw /= 2;
-    const int target = (nw == 8) ? 768 : 1536;
+    const int target = 1536;
     const int groups = tiles / nw;
     const int units = K / (kKStep * batch_steps(nw));
     int best = 1;
@@ -493,23 +534,28 @@ int check_layer(const mi_layer_config* c, const mi_kv_pool_s* p, int batch, int 
     return MI_OK;
 }
 
+#ifndef MIKV_GEMM_TRANSPOSED
+#define MIKV_GEMM_TRANSPOSED true
+#endif
+
 template <int MT, int ACT>
 void launch_gemm_mt(const void* A, const uint16_t* gain, int M, int K, const uint16_t* W0,
                     const uint16_t* W1, int n_split, int N, GemmShape g, float* P, hipStream_t st) {
+    constexpr bool TR = MIKV_GEMM_TRANSPOSED;
     const dim3 grid(N / 16 / g.nw, g.splits);
     const int k_chunk = K / g.splits;
     if (g.nw == 8)
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 8, ACT>), grid, dim3(64), 0, st, A, gain, M, K, W0, W1,
-                           n_split, N, k_chunk, P);
+        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 8, ACT, TR>), grid, dim3(64), 0, st, A, gain, M, K, W0,
+                           W1, n_split, N, k_chunk, P);
     else if (g.nw == 4)
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 4, ACT>), grid, dim3(64), 0, st, A, gain, M, K, W0, W1,
-                           n_split, N, k_chunk, P);
+        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 4, ACT, TR>), grid, dim3(64), 0, st, A, gain, M, K, W0,
+                           W1, n_split, N, k_chunk, P);
     else if (g.nw == 2)
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 2, ACT>), grid, dim3(64), 0, st, A, gain, M, K, W0, W1,
-                           n_split, N, k_chunk, P);
+        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 2, ACT, TR>), grid, dim3(64), 0, st, A, gain, M, K, W0,
+                           W1, n_split, N, k_chunk, P);
     else
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 1, ACT>), grid, dim3(64), 0, st, A, gain, M, K, W0, W1,
-                           n_split, N, k_chunk, P);
+        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 1, ACT, TR>), grid, dim3(64), 0, st, A, gain, M, K, W0,
+                           W1, n_split, N, k_chunk, P);
 }
 
 template <int ACT>
