@@ -96,14 +96,15 @@ __device__ __forceinline__ uint4 ld16_stream(const char* base, uint32_t off) {
 // One thread per rotated pair (i, i + D/2) of one head, q heads first, then
 // the new k heads, then 16-byte pieces of the V copy; workgroups of 256
 // threads tile that index space (grid.y) for each sequence (grid.x). The
-// angle pos * theta^(-2i/D), its sine and cosine and the rotation are float64
-// with separately rounded products, rounded once to bf16.
+// angle pos * theta^(-2i/D) (inverse frequencies from the host table), its
+// sine and cosine and the rotation are float64 with separately rounded
+// products, rounded once to bf16.
 template <int D>
 __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* q_rot, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
-    int32_t hq, int32_t hkv, int32_t num_blocks, double theta, uint32_t* __restrict__ err) {
+    int32_t hq, int32_t hkv, int32_t num_blocks, mikv::RopeTable rope, uint32_t* __restrict__ err) {
     constexpr int H2 = D / 2;
     const int b = blockIdx.x;
     const int pos = ctx_lens[b];
@@ -134,8 +135,7 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
         }
         const double x1 = bf16_to_f64(src[i]);
         const double x2 = bf16_to_f64(src[i + H2]);
-        const double inv_freq = pow(theta, -2.0 * i / D);
-        const double a = static_cast<double>(pos) * inv_freq;
+        const double a = static_cast<double>(pos) * rope.inv_freq[i];
         double sn, cs;
         sincos(a, &sn, &cs);
         const double y1 = __dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn));
@@ -190,25 +190,16 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
-// One 16-token tile: scores of the lane's NT tokens for the G heads,
-// online-softmax update, weighted V accumulation. With TAIL, token rows >=
-// valid_rows are excluded by selection (their K/V bits may be NaN).
+// One 16-token tile: for each of the G heads in turn, scores of the lane's
+// NT tokens, online-softmax update and weighted V accumulation (one head's
+// scores live at a time). With TAIL, token rows >= valid_rows are excluded by
+// selection (their K/V bits may be NaN).
 template <int LAM, int NT, int NJ, int G, bool TAIL>
 __device__ __forceinline__ void consume_tile(uint4 (&kr)[NT][NJ], uint4 (&vr)[NT][NJ],
                                              const uint4 (&qv)[G][NJ], float scale_log2,
                                              int valid_rows, int r, float (&m)[G], float (&l)[G],
                                              float (&acc)[G][NJ][8]) {
     constexpr int TPI = 64 / LAM;
-    float s[NT][G];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float a = 0.f;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) a = dot8_bf16(qv[h][j], kr[t][j], a);
-            s[t][h] = row_sum<LAM>(a) * scale_log2;
-        }
     bool valid[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -217,17 +208,24 @@ __device__ __forceinline__ void consume_tile(uint4 (&kr)[NT][NJ], uint4 (&vr)[NT
             valid[t] = t * TPI + r < valid_rows;
             if (!valid[t]) {
 #pragma unroll
-                for (int h = 0; h < G; ++h) s[t][h] = kNegInf;
-#pragma unroll
                 for (int j = 0; j < NJ; ++j) vr[t][j] = make_uint4(0, 0, 0, 0);
             }
         }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float mx = s[0][h];
+        float s[NT];
 #pragma unroll
-        for (int t = 1; t < NT; ++t) mx = fmaxf(mx, s[t][h]);
+        for (int t = 0; t < NT; ++t) {
+            float a = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) a = dot8_bf16(qv[h][j], kr[t][j], a);
+            s[t] = row_sum<LAM>(a) * scale_log2;
+            if (TAIL && !valid[t]) s[t] = kNegInf;
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int t = 1; t < NT; ++t) mx = fmaxf(mx, s[t]);
         if (mx > m[h] + kRescaleSlack) {
             const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
             m[h] = mx;
@@ -240,7 +238,7 @@ __device__ __forceinline__ void consume_tile(uint4 (&kr)[NT][NJ], uint4 (&vr)[NT
         float p[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            p[t] = __builtin_amdgcn_exp2f(s[t][h] - m[h]);
+            p[t] = __builtin_amdgcn_exp2f(s[t] - m[h]);
             if (TAIL) p[t] = valid[t] ? p[t] : 0.f;
             l[h] += p[t];
         }
@@ -324,7 +322,9 @@ struct TileRing {
 // [floor(w T / W), floor((w + 1) T / W)), so every wave streams the same
 // number of tiles whatever the length mix. A segment cut by a range boundary
 // leaves one fp32 partial per piece; a segment inside one range is finished by
-// that wave. W = min(grid, ceil(T / min_tiles)).
+// that wave. W = min(grid, ceil(T / min_tiles)): small workloads get many
+// short ranges (a tile fetch costs a memory round trip), large ones are
+// capped by the resident waves.
 constexpr int kMaxBatch = 1024;      // sequences per call (LDS prefix table)
 
 // TP[b] = first global tile of sequence b, TP[batch] = T. One wave; every lane
@@ -772,12 +772,13 @@ int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint1
     const int hkv = p->num_kv_heads;
     const int items = (hq + hkv) * (p->head_dim / 2) + hkv * (p->head_dim / 8);
     const dim3 grid(batch, (items + 255) / 256);
+    const RopeTable rope = make_rope_table(theta, p->head_dim);
     if (p->head_dim == 128)
         hipLaunchKernelGGL(write_decode_kv_kernel<128>, grid, dim3(256), 0, st, q, k, v, q_rot,
-                           p->k, p->v, table, mbps, ctx, hq, hkv, p->num_blocks, theta, p->err);
+                           p->k, p->v, table, mbps, ctx, hq, hkv, p->num_blocks, rope, p->err);
     else
         hipLaunchKernelGGL(write_decode_kv_kernel<64>, grid, dim3(256), 0, st, q, k, v, q_rot,
-                           p->k, p->v, table, mbps, ctx, hq, hkv, p->num_blocks, theta, p->err);
+                           p->k, p->v, table, mbps, ctx, hq, hkv, p->num_blocks, rope, p->err);
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 

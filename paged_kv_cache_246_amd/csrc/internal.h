@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cstddef>
+#include <cmath>
 #include <cstdint>
 #include <vector>
 
@@ -26,6 +27,17 @@ namespace mikv {
 
 constexpr int kBlockSize = 16;
 
+// RoPE inverse frequencies theta^(-2i/D), i < D/2, computed on the host in
+// float64 and passed to the kernels by value.
+struct RopeTable {
+    double inv_freq[64];
+};
+inline RopeTable make_rope_table(double theta, int head_dim) {
+    RopeTable t{};
+    for (int i = 0; i < head_dim / 2 && i < 64; ++i) t.inv_freq[i] = std::pow(theta, -2.0 * i / head_dim);
+    return t;
+}
+
 inline bool pool_has_device(const mi_kv_pool_s* p) {
     return p && !(p->flags & MI_POOL_HOST_ONLY) && p->k && p->v && p->err;
 }
@@ -36,7 +48,7 @@ inline bool supported_group(int32_t hq, int32_t hkv) {
 
 constexpr int kMaxBatch = 1024;            // sequences per attention call
 constexpr int kMaxAttnWaves = 4096;        // upper bound of the attention grid
-constexpr int kDefaultSplitTokens = 128;   // minimum tokens per wave's share
+constexpr int kDefaultSplitTokens = 32;    // minimum tokens per wave's share
 constexpr int kMaxLayerBatch = 32;         // rows of the decoder-layer projections
 constexpr int kLayerDimMultiple = 256;     // hidden, intermediate, Hq * D multiples
 

@@ -303,15 +303,19 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(
     }
 }
 
-// 1 / sqrt(mean(x^2) + eps) of row b of a bf16 or fp32 matrix, by one block.
-template <typename T>
-__device__ float block_inv_rms(const T* row, int H, float eps, float* red) {
+// 1 / sqrt(mean(x^2) + eps) of a bf16 row (H a multiple of 8), by one block.
+__device__ float block_inv_rms(const uint16_t* row, int H, float eps, float* red) {
     float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) {
-        float v;
-        if constexpr (sizeof(T) == 2) v = bf16_to_f32(row[i]);
-        else v = row[i];
-        ss = fmaf(v, v, ss);
+    for (int i = threadIdx.x * 8; i < H; i += blockDim.x * 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(row + i);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = bf16_to_f32(static_cast<uint16_t>(ws[e]));
+            const float hi = bf16_to_f32(static_cast<uint16_t>(ws[e] >> 16));
+            ss = fmaf(lo, lo, ss);
+            ss = fmaf(hi, hi, ss);
+        }
     }
 #pragma unroll
     for (int x = 1; x < 64; x *= 2) ss += __shfl_xor(ss, x);
@@ -323,19 +327,18 @@ __device__ float block_inv_rms(const T* row, int H, float eps, float* red) {
     return 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
 }
 
-// Sum of the K-split partials of one output, in split order.
+// Sum of the K-split partials of one output, in split order; the loads are
+// issued eight at a time so the sum costs few memory round trips.
 __device__ __forceinline__ float sum_splits(const float* P, int S, size_t stride, size_t idx) {
     float v = 0.f;
-    int s = 0;
-    for (; s + 4 <= S; s += 4) {
-        const float a0 = P[s * stride + idx], a1 = P[(s + 1) * stride + idx];
-        const float a2 = P[(s + 2) * stride + idx], a3 = P[(s + 3) * stride + idx];
-        v += a0;
-        v += a1;
-        v += a2;
-        v += a3;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = (s0 + u < S) ? P[(s0 + u) * stride + idx] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < S) v += t[u];
     }
-    for (; s < S; ++s) v += P[s * stride + idx];
     return v;
 }
 
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     const float* __restrict__ P, int S, const uint16_t* __restrict__ x, int H, float eps,
     uint16_t* __restrict__ q_rot, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
-    int32_t batch, int32_t hq, int32_t hkv, int32_t num_blocks, double theta,
+    int32_t batch, int32_t hq, int32_t hkv, int32_t num_blocks, mikv::RopeTable rope,
     uint32_t* __restrict__ err) {
     constexpr int H2 = D / 2;
     __shared__ float red[4];
@@ -381,8 +384,7 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
         }
         const double x1 = static_cast<double>(inv * sum_splits(Pb, S, stride, h * D + i));
         const double x2 = static_cast<double>(inv * sum_splits(Pb, S, stride, h * D + i + H2));
-        const double inv_freq = pow(theta, -2.0 * i / D);
-        const double a = static_cast<double>(pos) * inv_freq;
+        const double a = static_cast<double>(pos) * rope.inv_freq[i];
         double sn, cs;
         sincos(a, &sn, &cs);
         dst[i] = f64_to_bf16(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
@@ -428,8 +430,7 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
     const int b = blockIdx.y;
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= I) return;
-    float tot = 0.f;
-    for (int c = 0; c < nssq; ++c) tot += ssq[static_cast<size_t>(b) * nssq + c];
+    const float tot = sum_splits(ssq + static_cast<size_t>(b) * nssq, nssq, 1, 0);
     const float inv = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
     const size_t stride = static_cast<size_t>(batch) * 2 * I;
     const size_t row = static_cast<size_t>(b) * 2 * I;
@@ -611,14 +612,15 @@ extern "C" int mi_decoder_layer_decode(mi_kv_pool_t p, const mi_layer_config* cf
     {
         const int items = (hq + hkv) * (D / 2) + hkv * D;
         const dim3 grid(batch, (items + 255) / 256);
+        const mikv::RopeTable rope = mikv::make_rope_table(cfg->rope_theta, D);
         if (D == 128)
             hipLaunchKernelGGL(rope_append_kernel<128>, grid, dim3(256), 0, st, p_qkv, pl.s_qkv, x_in, H,
                                cfg->rms_eps, q_rot, p->k, p->v, table, mbps, ctx, batch, hq, hkv,
-                               p->num_blocks, cfg->rope_theta, p->err);
+                               p->num_blocks, rope, p->err);
         else
             hipLaunchKernelGGL(rope_append_kernel<64>, grid, dim3(256), 0, st, p_qkv, pl.s_qkv, x_in, H,
                                cfg->rms_eps, q_rot, p->k, p->v, table, mbps, ctx, batch, hq, hkv,
-                               p->num_blocks, cfg->rope_theta, p->err);
+                               p->num_blocks, rope, p->err);
     }
     // 3. paged GQA decode attention
     rc = mikv::launch_paged_gqa_decode(p, q_rot, o, table, mbps, ctx, batch, hq,
