@@ -545,6 +545,335 @@ __global__ __launch_bounds__(64) void paged_attn_partial_kernel(
     }
 }
 
+// ================================================ paged GQA decode on MFMA
+// Same work partition, ring and partial format as the kernel above, with
+// both contractions of a tile on the matrix cores. Lane l = 16 q + n
+// (n = l % 16, q = l / 16) of the wave:
+//  - scores S^T = K Q^T by 16x16x32 bf16 MFMAs: rows are the 16 tokens of
+//    the tile, columns the query heads (n < G; the other columns are
+//    padding), the D dims split in slices of 32. The lane holds token row n
+//    of K and column n of Q^T for its 8 dims of each slice and receives the
+//    scores of tokens 4q .. 4q + 3 for head n;
+//  - O^T += V^T P^T by 16x16x16 bf16 MFMAs: B = P^T is exactly the score
+//    layout (tokens 4q .. 4q + 3 of head n, rounded to bf16), A = V^T takes
+//    dim psi of tokens 4q .. 4q + 3, built by 16-bit permutes from the four
+//    token rows the lane loads (D / 16 dims each). Output dims of MFMA jj
+//    in row 4q + r are psi = (D / 16)(4q + r) + jj, so every lane owns D / 4
+//    consecutive dims of its head.
+// Softmax state is per head: the running max m is shared by the 4 lanes of
+// a head, each lane keeps the sum of its own p; a tile raises m only when
+// some score exceeds it by more than the slack (one wave vote), then the 4
+// lanes agree on the new maximum through two lane exchanges.
+// With an 8-bit cache (E4M3) the codes are widened to bf16 exactly by the
+// hardware conversion; the per-head scales multiply the scores and the
+// weighted V sum.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kFmtBf16 = 0;
+constexpr int kFmtFp8 = 1;
+
+template <int D, int FMT>
+struct MfmaTile {
+    static constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1;       // bytes per element
+    static constexpr int ROW = D * ESZ;                         // bytes per token row
+    static constexpr int NQK = D / 32;                          // score MFMAs
+    static constexpr int NKL = FMT == kFmtBf16 ? NQK : NQK / 2; // 16-byte K loads per lane
+    static constexpr int NPV = D / 16;                          // output MFMAs
+    static constexpr int VB = D * ESZ / 16;                     // V bytes per lane per row
+    static constexpr int VW = VB / 4;                           // ... in 32-bit words
+    static constexpr int BW = D / 32;                           // bf16 words per lane per row
+    static_assert(NKL >= 1 && VW >= 1, "head_dim");
+};
+
+template <int NB>
+__device__ __forceinline__ void ld_stream_words(const char* base, uint32_t off, uint32_t (&w)[NB / 4]) {
+    if constexpr (NB == 16) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+    } else if constexpr (NB == 8) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + off));
+        w[0] = t.x; w[1] = t.y;
+    } else {
+        w[0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned int*>(base + off));
+    }
+}
+
+// Two E4M3 codes (bytes 0-1 or 2-3 of w) -> two bf16 (exact).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                            static_cast<int>(w), 1.0f, HI));
+}
+
+struct MfmaSoftmax {
+    float m;      // running max of head n (log2 units), shared by its 4 lanes
+    float l;      // this lane's sum of 2^(s - m)
+};
+
+template <int D, int FMT, int NPV = MfmaTile<D, FMT>::NPV>
+__device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>::NKL],
+                                             uint32_t (&vr)[4][MfmaTile<D, FMT>::VW],
+                                             const uint4 (&qb)[MfmaTile<D, FMT>::NQK], float sl2,
+                                             bool head_ok, int q4, int valid_rows, bool tail,
+                                             MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
+    using TL = MfmaTile<D, FMT>;
+    // ---- scores of tokens 4q4 .. 4q4+3 for head n
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < TL::NQK; ++j) {
+        uint4 a;
+        if constexpr (FMT == kFmtBf16) {
+            a = kr[j];
+        } else {
+            const uint4 w = kr[j / 2];
+            const uint32_t w0 = (j & 1) ? w.z : w.x;
+            const uint32_t w1 = (j & 1) ? w.w : w.y;
+            a = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                           fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
+        }
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, qb[j]), s, 0, 0, 0);
+    }
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sc[i] = s[i] * sl2;
+        const bool ok = head_ok && (!tail || 4 * q4 + i < valid_rows);
+        sc[i] = ok ? sc[i] : kNegInf;
+    }
+    const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    if (__ballot(mx > sm.m + kRescaleSlack) != 0) {
+        float hm = fmaxf(mx, __shfl_xor(mx, 16));
+        hm = fmaxf(hm, __shfl_xor(hm, 32));
+        const float mn = fmaxf(sm.m, hm);
+        const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
+        sm.m = mn;
+        sm.l *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < NPV; ++jj) o[jj] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(sc[i] - sm.m);
+        sm.l += p[i];
+    }
+    const bf16x4_t pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                         static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+    // ---- V rows 4q4 .. 4q4+3 as bf16 words (masked rows zeroed: their bits
+    // may be NaN and 0 * NaN would reach the sum)
+    uint32_t bw[4][TL::BW];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool ok = !tail || 4 * q4 + r < valid_rows;
+#pragma unroll
+        for (int e = 0; e < TL::BW; ++e) {
+            uint32_t x;
+            if constexpr (FMT == kFmtBf16) x = vr[r][e];
+            else x = (e & 1) ? fp8x2_to_bf16x2<true>(vr[r][e / 2]) : fp8x2_to_bf16x2<false>(vr[r][e / 2]);
+            bw[r][e] = ok ? x : 0u;
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < NPV; ++jj) {
+        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+        const int e = jj / 2;
+        const uint32_t lo = __builtin_amdgcn_perm(bw[1][e], bw[0][e], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(bw[3][e], bw[2][e], sel);
+        const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
+        o[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4_t, pb), o[jj], 0, 0, 0);
+    }
+}
+
+template <int D, int FMT, int PF>
+struct MfmaRing {
+    using TL = MfmaTile<D, FMT>;
+    static constexpr int NPV = TL::NPV;
+    uint4 kr[PF + 1][TL::NKL];
+    uint32_t vr[PF + 1][4][TL::VW];
+    const char* kbase;
+    const char* vbase;
+    size_t blk_stride;
+    uint32_t koff[TL::NKL];
+    uint32_t voff[4];
+    int32_t my_id;   // lane i holds the chunk's i-th block id
+
+    template <int S>
+    __device__ __forceinline__ void load(int tile) {
+        const int32_t id = __builtin_amdgcn_readlane(my_id, tile);
+        const char* kb = kbase + static_cast<size_t>(id) * blk_stride;
+        const char* vb = vbase + static_cast<size_t>(id) * blk_stride;
+#pragma unroll
+        for (int j = 0; j < TL::NKL; ++j) kr[S][j] = ld16_stream(kb, koff[j]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ld_stream_words<TL::VB>(vb, voff[r], vr[S][r]);
+    }
+    template <int S>
+    __device__ __forceinline__ void prologue(int nblk) {
+        if constexpr (S < PF) {
+            load<S>(min(S, nblk - 1));
+            prologue<S + 1>(nblk);
+        }
+    }
+    template <int U>
+    __device__ __forceinline__ void steady(int i, int nblk, const uint4 (&qb)[TL::NQK], float sl2,
+                                           bool head_ok, int q4, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
+        if constexpr (U <= PF) {
+            load<(U + PF) % (PF + 1)>(min(i + U + PF, nblk - 1));
+            mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, head_ok, q4, BS, false, sm, o);
+            steady<U + 1>(i, nblk, qb, sl2, head_ok, q4, sm, o);
+        }
+    }
+    template <int U>
+    __device__ __forceinline__ void rest(int i, int nblk, int valid_rows, const uint4 (&qb)[TL::NQK],
+                                         float sl2, bool head_ok, int q4, MfmaSoftmax& sm,
+                                         f32x4_t (&o)[NPV]) {
+        if constexpr (U <= PF) {
+            const int tile = i + U;
+            if (tile < nblk - 1) {
+                mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, head_ok, q4, BS, false, sm, o);
+            } else if (tile == nblk - 1) {
+                if (valid_rows == BS)
+                    mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, head_ok, q4, BS, false, sm, o);
+                else
+                    mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, head_ok, q4, valid_rows, true, sm, o);
+            }
+            rest<U + 1>(i, nblk, valid_rows, qb, sl2, head_ok, q4, sm, o);
+        }
+    }
+};
+
+template <int D, int G, int FMT, int PF>
+__global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
+    const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
+    const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
+    const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t hkv, int32_t num_blocks,
+    int32_t max_ctx, int32_t min_tiles, float scale_log2, const float* __restrict__ kv_scales,
+    float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
+    uint32_t* __restrict__ err) {
+    using TL = MfmaTile<D, FMT>;
+    constexpr int NPV = TL::NPV;
+    constexpr size_t TILE = static_cast<size_t>(BS) * TL::ROW;   // bytes per (block, head) tile
+    __shared__ int TP[kMaxBatch + 1];
+    const int w = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int n = lane & 15;
+    const int q4 = lane >> 4;
+    const bool head_ok = n < G;
+
+    bool bad_len;
+    const int T = build_tile_prefix(ctx_lens, batch, mbps, max_ctx, hkv, TP, &bad_len, lane);
+    __syncthreads();
+    if (bad_len && w == 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+    if (T == 0) return;
+    const int W = active_waves(T, gridDim.x, min_tiles);
+    if (w >= W) return;
+    const int start = range_start(w, T, W);
+    const int end = range_start(w + 1, T, W);
+    const size_t blk_stride = static_cast<size_t>(hkv) * TILE;
+
+    int pos = start;
+    int b = find_sequence(TP, batch, pos);
+    bool first_piece = true;
+    while (pos < end) {
+        while (__builtin_amdgcn_readfirstlane(TP[b + 1]) <= pos) ++b;
+        const int seg0 = __builtin_amdgcn_readfirstlane(TP[b]);
+        const int nt = (__builtin_amdgcn_readfirstlane(TP[b + 1]) - seg0) / hkv;
+        const int rel = pos - seg0;
+        const int g = rel / nt;
+        const int t0 = rel - g * nt;
+        const int t1 = min(nt, t0 + (end - pos));
+        const int L = ctx_lens[b] + 1;
+
+        // Q^T operand: head n, the lane's 8 dims of each 32-dim slice (the
+        // same dims its K row supplies)
+        uint4 qb[TL::NQK];
+        const uint16_t* qh = q_rot + (static_cast<size_t>(b) * hkv * G + g * G + (head_ok ? n : 0)) * D;
+#pragma unroll
+        for (int j = 0; j < TL::NQK; ++j) {
+            const int d0 = FMT == kFmtBf16 ? 32 * j + 8 * q4 : 64 * (j / 2) + 16 * q4 + 8 * (j & 1);
+            qb[j] = head_ok ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
+        }
+        float sl2 = scale_log2;
+        float vscale = 1.f;
+        if constexpr (FMT == kFmtFp8) {
+            sl2 *= kv_scales[g];
+            vscale = kv_scales[hkv + g];
+        }
+        MfmaSoftmax sm{head_ok ? kNegInf : 0.f, 0.f};
+        f32x4_t o[NPV];
+#pragma unroll
+        for (int jj = 0; jj < NPV; ++jj) o[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        MfmaRing<D, FMT, PF> ring;
+        ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
+        ring.vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
+        ring.blk_stride = blk_stride;
+#pragma unroll
+        for (int j = 0; j < TL::NKL; ++j) ring.koff[j] = n * TL::ROW + 64 * j + 16 * q4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ring.voff[r] = (4 * q4 + r) * TL::ROW + TL::VB * n;
+
+        for (int s0 = t0; s0 < t1; s0 += 64) {
+            const int nblk = min(64, t1 - s0);
+            int32_t id = 0;
+            if (lane < nblk) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
+            const bool bad_id = lane < nblk && (id < 0 || id >= num_blocks);
+            if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+            ring.my_id = bad_id ? 0 : id;
+            const int last_rows = (s0 + nblk == nt) ? L - (nt - 1) * BS : BS;
+            ring.template prologue<0>(nblk);
+            int i = 0;
+            for (; i + PF + 1 < nblk; i += PF + 1)
+                ring.template steady<0>(i, nblk, qb, sl2, head_ok, q4, sm, o);
+            ring.template load<PF>(min(i + PF, nblk - 1));
+            ring.template rest<0>(i, nblk, last_rows, qb, sl2, head_ok, q4, sm, o);
+        }
+
+        // head totals of the lane sums (same bits in the 4 lanes of a head)
+        float lt = sm.l + __shfl_xor(sm.l, 16);
+        lt += __shfl_xor(lt, 32);
+        const bool whole = (t0 == 0 && t1 == nt);
+        const size_t slot = 2 * static_cast<size_t>(w) + (first_piece ? 0 : 1);
+        if (head_ok) {
+            const int dbase = NPV * 4 * q4;     // first of the lane's D/4 dims
+            if (whole) {
+                const float inv = vscale / lt;
+                uint16_t* oh = out + (static_cast<size_t>(b) * hkv * G + g * G + n) * D + dbase;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    uint32_t wd[NPV / 2];
+#pragma unroll
+                    for (int e = 0; e < NPV / 2; ++e)
+                        wd[e] = static_cast<uint32_t>(f32_to_bf16_rne(o[2 * e][r] * inv)) |
+                                (static_cast<uint32_t>(f32_to_bf16_rne(o[2 * e + 1][r] * inv)) << 16);
+                    if constexpr (NPV == 8)
+                        *reinterpret_cast<uint4*>(oh + NPV * r) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                    else
+                        *reinterpret_cast<uint2*>(oh + NPV * r) = make_uint2(wd[0], wd[1]);
+                }
+            } else {
+                float* dst = part_acc + (slot * G + n) * D + dbase;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int e = 0; e < NPV / 4; ++e)
+                        reinterpret_cast<float4*>(dst + NPV * r)[e] =
+                            make_float4(o[4 * e][r] * vscale, o[4 * e + 1][r] * vscale,
+                                        o[4 * e + 2][r] * vscale, o[4 * e + 3][r] * vscale);
+                if (q4 == 0) part_ml[slot * G + n] = make_float2(sm.m, lt);
+            }
+        }
+        pos += t1 - t0;
+        first_piece = false;
+    }
+}
+
 // Combine kernel: one workgroup per (query head, sequence). It rebuilds the
 // same partition, and if the segment was cut into pieces, merges their
 // partials in range order. Thread (d, cg) folds the pieces cg, cg + NCG, ...
@@ -678,6 +1007,11 @@ struct AttnTuning {
     static constexpr int LAM = (D == 128 && G > 2) ? 16 : 8;
     static constexpr int PF = (D == 128 && G > 4) ? 1 : 2;
 #endif
+#ifdef MIKV_TUNE_MFMA_PF
+    static constexpr int MFMA_PF = MIKV_TUNE_MFMA_PF;
+#else
+    static constexpr int MFMA_PF = 2;
+#endif
 };
 
 // Resident 64-lane workgroups of the attention kernel on the current device
@@ -707,11 +1041,23 @@ void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
     constexpr int LAM = AttnTuning<D, G>::LAM;
     constexpr int PF = AttnTuning<D, G>::PF;
     const int hkv = p->num_kv_heads;
+#ifdef MIKV_ATTN_DOT
     auto kern = paged_attn_partial_kernel<D, G, LAM, PF>;
     const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, resident_waves(kern));
     hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot, p->k, p->v, table, mbps, ctx, batch,
                        hkv, p->num_blocks, max_ctx, min_tiles, scale_log2, part_acc, part_ml, out,
                        p->err);
+#else
+    (void)LAM;
+    (void)PF;
+    constexpr int MPF = AttnTuning<D, G>::MFMA_PF;
+    auto kern = paged_attn_mfma_kernel<D, G, kFmtBf16, MPF>;
+    const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, resident_waves(kern));
+    hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot,
+                       reinterpret_cast<const uint8_t*>(p->k), reinterpret_cast<const uint8_t*>(p->v),
+                       table, mbps, ctx, batch, hkv, p->num_blocks, max_ctx, min_tiles, scale_log2,
+                       static_cast<const float*>(nullptr), part_acc, part_ml, out, p->err);
+#endif
     hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), dim3(hkv * G, batch), dim3(256), 0, st,
                        part_acc, part_ml, ctx, batch, mbps, hkv, max_ctx, waves, min_tiles, out);
 }
