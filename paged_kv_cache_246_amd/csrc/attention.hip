@@ -20,7 +20,6 @@
 
 namespace {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BS = 16;                // tokens per KV block
 constexpr float kNegInf = -INFINITY;
@@ -50,38 +49,6 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
     return static_cast<double>(__uint_as_float(static_cast<uint32_t>(h) << 16));
-}
-
-__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
-                                          __builtin_bit_cast(bf16x2_t, b.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
-                                          __builtin_bit_cast(bf16x2_t, b.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
-                                          __builtin_bit_cast(bf16x2_t, b.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
-                                          __builtin_bit_cast(bf16x2_t, b.w), acc, false);
-    return acc;
-}
-
-// DPP lane exchanges inside a row of 16 lanes.
-constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7-i within each 8 lanes
-constexpr int kDppRowMirror = 0x140;    // lane i <- lane 15-i within each 16 lanes
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 8 consecutive lanes that share one token row; every lane of
-// the 8 ends with the same bits (each step adds a commutative pair).
-__device__ __forceinline__ float sum8(float x) {
-    x += dpp<kDppQuadSwap1>(x);
-    x += dpp<kDppQuadSwap2>(x);
-    x += dpp<kDppHalfMirror>(x);
-    return x;
 }
 
 // K/V tiles are streamed once per call: non-temporal loads keep them from
@@ -153,167 +120,6 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     }
 }
 
-// Lane layout of a 16-token (block, kv head) tile for LAM lanes per token row:
-// lane = LAM * r + c holds tokens r, r + TPI, r + 2 TPI, ... (TPI = 64 / LAM
-// tokens per load instruction) and, of each token, the 16-byte pieces
-// c + LAM * j (j < NJ) of its row. Each 128-bit load instruction then covers
-// TPI whole row segments of LAM * 16 bytes (>= one 128-byte line).
-template <int D, int LAM>
-struct TileShape {
-    static constexpr int TPI = 64 / LAM;          // tokens per load instruction
-    static constexpr int NT = BS / TPI;           // tokens per lane per tile
-    static constexpr int NJ = D / (8 * LAM);      // 16-byte pieces per lane per token
-    static_assert(NJ >= 1 && NJ * 8 * LAM == D, "head_dim / lane split mismatch");
-};
-
-template <int NT, int NJ>
-__device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, size_t blk_stride,
-                                          int32_t id, const uint32_t (&loff)[NT][NJ],
-                                          uint4 (&kr)[NT][NJ], uint4 (&vr)[NT][NJ]) {
-    const char* kb = kbase + static_cast<size_t>(id) * blk_stride;
-    const char* vb = vbase + static_cast<size_t>(id) * blk_stride;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) kr[t][j] = ld16_stream(kb, loff[t][j]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) vr[t][j] = ld16_stream(vb, loff[t][j]);
-}
-
-// Sum over the LAM consecutive lanes of one token row.
-template <int LAM>
-__device__ __forceinline__ float row_sum(float x) {
-    x = sum8(x);
-    if (LAM == 16) x += dpp<kDppRowMirror>(x);
-    return x;
-}
-
-// One 16-token tile: for each of the G heads in turn, scores of the lane's
-// NT tokens, online-softmax update and weighted V accumulation (one head's
-// scores live at a time). With TAIL, token rows >= valid_rows are excluded by
-// selection (their K/V bits may be NaN).
-template <int LAM, int NT, int NJ, int G, bool TAIL>
-__device__ __forceinline__ void consume_tile(uint4 (&kr)[NT][NJ], uint4 (&vr)[NT][NJ],
-                                             const uint4 (&qv)[G][NJ], float scale_log2,
-                                             int valid_rows, int r, float (&m)[G], float (&l)[G],
-                                             float (&acc)[G][NJ][8]) {
-    constexpr int TPI = 64 / LAM;
-    bool valid[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        valid[t] = true;
-        if (TAIL) {
-            valid[t] = t * TPI + r < valid_rows;
-            if (!valid[t]) {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) vr[t][j] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float s[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            float a = 0.f;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) a = dot8_bf16(qv[h][j], kr[t][j], a);
-            s[t] = row_sum<LAM>(a) * scale_log2;
-            if (TAIL && !valid[t]) s[t] = kNegInf;
-        }
-        float mx = s[0];
-#pragma unroll
-        for (int t = 1; t < NT; ++t) mx = fmaxf(mx, s[t]);
-        if (mx > m[h] + kRescaleSlack) {
-            const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
-            m[h] = mx;
-            l[h] *= alpha;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][j][e] *= alpha;
-        }
-        float p[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            p[t] = __builtin_amdgcn_exp2f(s[t] - m[h]);
-            if (TAIL) p[t] = valid[t] ? p[t] : 0.f;
-            l[h] += p[t];
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const uint32_t w[4] = {vr[t][j].x, vr[t][j].y, vr[t][j].z, vr[t][j].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[h][j][2 * e] = fmaf(p[t], bf16_lo(w[e]), acc[h][j][2 * e]);
-                    acc[h][j][2 * e + 1] = fmaf(p[t], bf16_hi(w[e]), acc[h][j][2 * e + 1]);
-                }
-            }
-    }
-}
-
-// Ring of PF + 1 K/V tiles in registers for one wave (see the partial kernel).
-template <int D, int G, int LAM, int PF>
-struct TileRing {
-    static constexpr int NT = TileShape<D, LAM>::NT;
-    static constexpr int NJ = TileShape<D, LAM>::NJ;
-    uint4 kr[PF + 1][NT][NJ];
-    uint4 vr[PF + 1][NT][NJ];
-    const char* kbase;
-    const char* vbase;
-    size_t blk_stride;
-    uint32_t loff[NT][NJ];
-    int32_t my_id;   // lane i holds the chunk's i-th block id
-
-    template <int S>
-    __device__ __forceinline__ void load(int tile) {
-        load_tile<NT, NJ>(kbase, vbase, blk_stride, __builtin_amdgcn_readlane(my_id, tile), loff,
-                          kr[S], vr[S]);
-    }
-    // tiles 0 .. PF-1 into slots 0 .. PF-1
-    template <int S>
-    __device__ __forceinline__ void prologue(int nblk) {
-        if constexpr (S < PF) {
-            load<S>(min(S, nblk - 1));
-            prologue<S + 1>(nblk);
-        }
-    }
-    // PF + 1 full tiles i .. i+PF; tile i+U prefetches tile i+U+PF
-    template <int U>
-    __device__ __forceinline__ void steady(int i, int nblk, const uint4 (&qv)[G][NJ], float sl2,
-                                           int r, float (&m)[G], float (&l)[G],
-                                           float (&acc)[G][NJ][8]) {
-        if constexpr (U <= PF) {
-            load<(U + PF) % (PF + 1)>(min(i + U + PF, nblk - 1));
-            consume_tile<LAM, NT, NJ, G, false>(kr[U], vr[U], qv, sl2, 0, r, m, l, acc);
-            steady<U + 1>(i, nblk, qv, sl2, r, m, l, acc);
-        }
-    }
-    // the last nblk - i (1 .. PF+1) tiles, all already requested; the final
-    // one may be partial (valid_rows < 16)
-    template <int U>
-    __device__ __forceinline__ void rest(int i, int nblk, int valid_rows, const uint4 (&qv)[G][NJ],
-                                         float sl2, int r, float (&m)[G], float (&l)[G],
-                                         float (&acc)[G][NJ][8]) {
-        if constexpr (U <= PF) {
-            const int tile = i + U;
-            if (tile < nblk - 1) {
-                consume_tile<LAM, NT, NJ, G, false>(kr[U], vr[U], qv, sl2, 0, r, m, l, acc);
-            } else if (tile == nblk - 1) {
-                if (valid_rows == BS)
-                    consume_tile<LAM, NT, NJ, G, false>(kr[U], vr[U], qv, sl2, BS, r, m, l, acc);
-                else
-                    consume_tile<LAM, NT, NJ, G, true>(kr[U], vr[U], qv, sl2, valid_rows, r, m, l, acc);
-            }
-            rest<U + 1>(i, nblk, valid_rows, qv, sl2, r, m, l, acc);
-        }
-    }
-};
-
 // ================================================= work partition (stream-K)
 // The work of one call is the list of 16-token tiles of every segment
 // (sequence b, kv head g), g fastest; segment (b, g) has nt_b =
@@ -382,172 +188,15 @@ __device__ __forceinline__ int find_sequence(const int* TP, int batch, int x) {
     return lo;
 }
 
-// ====================================================== paged GQA decode
-// One wavefront per work range (see above). For each segment piece in its
-// range the wave streams the piece's K/V tiles in logical order; the G query
-// heads of the segment share every tile; q.k runs on packed bf16 dot
-// products with fp32 accumulation, summed over the lanes of a token row by
-// DPP. Every lane keeps an online softmax over its own token stream (running
-// max m, sum l, weighted V sum acc); the token rows are merged at the end of
-// the piece, which is then either stored as the final bf16 output (the whole
+// ======================================================= paged GQA decode
+// One wavefront per work range (see the partition above). For each segment
+// piece in its range the wave streams the piece's K/V tiles in logical order
+// through a register ring (tile i in slot i % (PF + 1), the PF tiles after
+// the one being consumed in flight); the G query heads of the segment share
+// every tile. The piece ends either as the final bf16 output (the whole
 // segment) or as an fp32 partial (m, l, acc) in slot 2w (first piece of the
-// range) or 2w + 1 (last piece).
-template <int D, int G, int LAM, int PF>
-__global__ __launch_bounds__(64) void paged_attn_partial_kernel(
-    const uint16_t* __restrict__ q_rot, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
-    const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t hkv, int32_t num_blocks,
-    int32_t max_ctx, int32_t min_tiles, float scale_log2, float* __restrict__ part_acc,
-    float2* __restrict__ part_ml, uint16_t* __restrict__ out, uint32_t* __restrict__ err) {
-    using TS = TileShape<D, LAM>;
-    constexpr int NT = TS::NT;
-    constexpr int NJ = TS::NJ;
-    constexpr int TPI = TS::TPI;
-    constexpr uint32_t ROW = D * 2;            // bytes per token row
-    constexpr size_t TILE = BS * D * 2;        // bytes per (block, head) tile
-    __shared__ int TP[kMaxBatch + 1];
-    const int w = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int r = lane / LAM;
-    const int c = lane % LAM;
-
-    bool bad_len;
-    const int T = build_tile_prefix(ctx_lens, batch, mbps, max_ctx, hkv, TP, &bad_len, lane);
-    __syncthreads();
-    if (bad_len && w == 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
-    if (T == 0) return;
-    const int W = active_waves(T, gridDim.x, min_tiles);
-    if (w >= W) return;
-    const int start = range_start(w, T, W);
-    const int end = range_start(w + 1, T, W);
-
-    uint32_t loff[NT][NJ];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) loff[t][j] = (t * TPI + r) * ROW + (c + LAM * j) * 16;
-    const size_t blk_stride = static_cast<size_t>(hkv) * TILE;
-
-    int pos = start;
-    int b = find_sequence(TP, batch, pos);
-    bool first_piece = true;
-    while (pos < end) {
-        while (__builtin_amdgcn_readfirstlane(TP[b + 1]) <= pos) ++b;
-        const int seg0 = __builtin_amdgcn_readfirstlane(TP[b]);
-        const int nt = (__builtin_amdgcn_readfirstlane(TP[b + 1]) - seg0) / hkv;
-        const int rel = pos - seg0;
-        const int g = rel / nt;
-        const int t0 = rel - g * nt;
-        const int t1 = min(nt, t0 + (end - pos));
-        const int L = ctx_lens[b] + 1;
-
-        uint4 qv[G][NJ];
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                qv[h][j] = *reinterpret_cast<const uint4*>(
-                    q_rot + (static_cast<size_t>(b) * hkv * G + g * G + h) * D + (c + LAM * j) * 8);
-        float m[G], l[G];
-        float acc[G][NJ][8];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            m[h] = kNegInf;
-            l[h] = 0.f;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][j][e] = 0.f;
-        }
-
-        TileRing<D, G, LAM, PF> ring;
-        ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
-        ring.vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
-        ring.blk_stride = blk_stride;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) ring.loff[t][j] = loff[t][j];
-
-        // sub-chunks of at most 64 tiles: one block id per lane
-        for (int s0 = t0; s0 < t1; s0 += 64) {
-            const int nblk = min(64, t1 - s0);
-            int32_t id = 0;
-            if (lane < nblk) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
-            const bool bad_id = lane < nblk && (id < 0 || id >= num_blocks);
-            if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
-            ring.my_id = bad_id ? 0 : id;
-            // Register ring of PF + 1 tiles: tile i lives in slot i % (PF + 1)
-            // and the PF tiles after the one being consumed are in flight.
-            // The loop is unrolled by PF + 1 so ring slots are compile-time
-            // registers (no copies that would wait on in-flight loads), and
-            // every prefetch in it is unconditional (clamped to the last
-            // tile, a cache hit), so the wait before each tile covers exactly
-            // the older loads.
-            const int last_rows = (s0 + nblk == nt) ? L - (nt - 1) * BS : BS;
-            ring.template prologue<0>(nblk);
-            int i = 0;
-            for (; i + PF + 1 < nblk; i += PF + 1)
-                ring.template steady<0>(i, nblk, qv, scale_log2, r, m, l, acc);
-            ring.template load<PF>(min(i + PF, nblk - 1));
-            ring.template rest<0>(i, nblk, last_rows, qv, scale_log2, r, m, l, acc);
-        }
-
-        // merge the TPI token rows (lanes c, c + LAM, ... hold the same dims)
-        const bool whole = (t0 == 0 && t1 == nt);
-        const size_t slot = 2 * static_cast<size_t>(w) + (first_piece ? 0 : 1);
-        uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + g * G) * D;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float M = m[h];
-#pragma unroll
-            for (int x = LAM; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
-            const float f = (m[h] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m[h] - M);
-            float lt = l[h] * f;
-#pragma unroll
-            for (int x = LAM; x < 64; x *= 2) lt += __shfl_xor(lt, x);
-            float red[NJ][8];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float a = acc[h][j][e] * f;
-#pragma unroll
-                    for (int x = LAM; x < 64; x *= 2) a += __shfl_xor(a, x);
-                    red[j][e] = a;
-                }
-            if (r != 0) continue;
-            if (whole) {
-                const float inv = 1.0f / lt;
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    uint32_t wd[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        wd[e] = static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e] * inv)) |
-                                (static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e + 1] * inv)) << 16);
-                    *reinterpret_cast<uint4*>(o + h * D + (c + LAM * j) * 8) =
-                        make_uint4(wd[0], wd[1], wd[2], wd[3]);
-                }
-            } else {
-                float* dst = part_acc + (slot * G + h) * D;
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    float4* d4 = reinterpret_cast<float4*>(dst + (c + LAM * j) * 8);
-                    d4[0] = make_float4(red[j][0], red[j][1], red[j][2], red[j][3]);
-                    d4[1] = make_float4(red[j][4], red[j][5], red[j][6], red[j][7]);
-                }
-                if (c == 0) part_ml[slot * G + h] = make_float2(M, lt);
-            }
-        }
-        pos += t1 - t0;
-        first_piece = false;
-    }
-}
-
-// ================================================ paged GQA decode on MFMA
-// Same work partition, ring and partial format as the kernel above, with
-// both contractions of a tile on the matrix cores. Lane l = 16 q + n
+// range) or 2w + 1 (last piece), merged by the combine kernel.
+// Both contractions of a tile run on the matrix cores. Lane l = 16 q + n
 // (n = l % 16, q = l / 16) of the wave:
 //  - scores S^T = K Q^T by 16x16x32 bf16 MFMAs: rows are the 16 tokens of
 //    the tile, columns the query heads (n < G; the other columns are
@@ -826,6 +475,11 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
             const bool bad_id = lane < nblk && (id < 0 || id >= num_blocks);
             if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
             ring.my_id = bad_id ? 0 : id;
+            // The loop is unrolled by PF + 1 so ring slots are compile-time
+            // registers (no copies that would wait on in-flight loads), and
+            // every prefetch in it is unconditional (clamped to the last
+            // tile, a cache hit), so the wait before each tile covers exactly
+            // the older loads.
             const int last_rows = (s0 + nblk == nt) ? L - (nt - 1) * BS : BS;
             ring.template prologue<0>(nblk);
             int i = 0;
@@ -998,26 +652,22 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
     }
 }
 
-template <int D, int G>
-struct AttnTuning {
-#if defined(MIKV_TUNE_LAM) && defined(MIKV_TUNE_PF)
-    static constexpr int LAM = (D == 128) ? MIKV_TUNE_LAM : 8;
-    static constexpr int PF = MIKV_TUNE_PF;
-#else
-    static constexpr int LAM = (D == 128 && G > 2) ? 16 : 8;
-    static constexpr int PF = (D == 128 && G > 4) ? 1 : 2;
-#endif
+// Prefetch depth of the attention tile ring and waves per CU of its grid.
+// One wave per SIMD with one tile in flight beyond the one being consumed
+// measured fastest on MI355X (long contexts and short batches alike): more
+// or deeper streams only add pieces to combine.
 #ifdef MIKV_TUNE_MFMA_PF
-    static constexpr int MFMA_PF = MIKV_TUNE_MFMA_PF;
+constexpr int kAttnPrefetch = MIKV_TUNE_MFMA_PF;
 #else
-    static constexpr int MFMA_PF = 2;
+constexpr int kAttnPrefetch = 1;
 #endif
-};
+constexpr int kAttnWavesPerCU = 4;
 
-// Resident 64-lane workgroups of the attention kernel on the current device
-// (CUs x waves per CU at the kernel's register budget), cached per device.
+// Grid of the attention kernel on the current device: CUs x min(waves per
+// CU, resident workgroups per CU at the kernel's register budget), cached
+// per device (the kernels differ only in G, all fit kAttnWavesPerCU).
 template <typename K>
-int resident_waves(K kernel) {
+int attention_waves(K kernel) {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return mikv::kMaxAttnWaves;
@@ -1027,7 +677,7 @@ int resident_waves(K kernel) {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         per_cu <= 0 || cus <= 0)
         return mikv::kMaxAttnWaves;
-    cached[dev] = std::min(mikv::kMaxAttnWaves, per_cu * cus);
+    cached[dev] = std::min(mikv::kMaxAttnWaves, std::min(per_cu, kAttnWavesPerCU) * cus);
     return cached[dev];
 }
 
@@ -1036,28 +686,13 @@ void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                  const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                  float scale_log2, int32_t max_ctx, int32_t min_tiles, float* part_acc,
                  float2* part_ml, hipStream_t st) {
-    // Lanes per token row and prefetch depth, sized so that the accumulators
-    // (G * D / LAM floats per lane) and PF + 1 tiles stay in VGPRs.
-    constexpr int LAM = AttnTuning<D, G>::LAM;
-    constexpr int PF = AttnTuning<D, G>::PF;
     const int hkv = p->num_kv_heads;
-#ifdef MIKV_ATTN_DOT
-    auto kern = paged_attn_partial_kernel<D, G, LAM, PF>;
-    const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, resident_waves(kern));
-    hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot, p->k, p->v, table, mbps, ctx, batch,
-                       hkv, p->num_blocks, max_ctx, min_tiles, scale_log2, part_acc, part_ml, out,
-                       p->err);
-#else
-    (void)LAM;
-    (void)PF;
-    constexpr int MPF = AttnTuning<D, G>::MFMA_PF;
-    auto kern = paged_attn_mfma_kernel<D, G, kFmtBf16, MPF>;
-    const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, resident_waves(kern));
+    auto kern = paged_attn_mfma_kernel<D, G, kFmtBf16, kAttnPrefetch>;
+    const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, attention_waves(kern));
     hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot,
                        reinterpret_cast<const uint8_t*>(p->k), reinterpret_cast<const uint8_t*>(p->v),
                        table, mbps, ctx, batch, hkv, p->num_blocks, max_ctx, min_tiles, scale_log2,
                        static_cast<const float*>(nullptr), part_acc, part_ml, out, p->err);
-#endif
     hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), dim3(hkv * G, batch), dim3(256), 0, st,
                        part_acc, part_ml, ctx, batch, mbps, hkv, max_ctx, waves, min_tiles, out);
 }
