@@ -19,15 +19,20 @@ Pages followed (cited by title and section in every function):
 * nxmr.cn inference-techniques article -- section 2.1 (page-table
   allocation, ceil(seq_len / PAGE_SIZE) pages), section 4.1 (attention scores
   in FP32), section 5.1 (numerically stable softmax: row max, exp, row sum).
+* vLLM-based inference-framework project report (gitlink.org.cn) -- the
+  "FP8 KV Cache quantisation" exploration (an 8-bit KV cache to cut the bytes
+  moved); nxmr.cn article section 2.2 (per-head quantisation scales).
 * MegEngine/InferLLM article (lnwmold.com) -- section 4.2 "problem two"
   (KV-cache size formula and its ~1 GB worked example), section 3.4
   (preallocated contiguous per-layer K/V cache).
 
 Modules:
   bf16       bf16 <-> float64 codec (definition of round-to-nearest-even)
+  fp8        E4M3 codec, per-head static-scale quantise / dequantise
   paged      block counts, slot mapping, free-block stack, size formula
   rope       rotary position embedding, half-split pairing
-  attention  write_decode_kv, gather, paged GQA decode attention
+  attention  write_decode_kv, gather, paged GQA decode attention (bf16 and
+             8-bit caches)
   layer      RMSNorm, SiLU, SwiGLU, full decoder-layer decode step
 
 Every function is pinned by the ``-m "not gpu"`` tests against closed forms,

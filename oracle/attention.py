@@ -27,6 +27,7 @@ Readings where the pages are silent:
 import numpy as np
 
 from . import bf16
+from . import fp8
 from . import paged
 from . import rope
 
@@ -61,11 +62,12 @@ def write_decode_kv(k_pool, v_pool, q, k, v, block_table, context_lens,
 def gather_kv(k_pool, v_pool, block_table, block_size, b, g, length):
     """Contiguous copies of K and V of sequence b, kv head g, positions [0, length).
 
-    Bit copies (uint16) in logical order -- the gather_batch_kv step.
+    Bit copies (the pool's element type: bf16 bits or 8-bit codes) in logical
+    order -- the gather_batch_kv step.
     """
     D = k_pool.shape[-1]
-    ks = np.empty((length, D), dtype=np.uint16)
-    vs = np.empty((length, D), dtype=np.uint16)
+    ks = np.empty((length, D), dtype=k_pool.dtype)
+    vs = np.empty((length, D), dtype=v_pool.dtype)
     for p in range(length):
         blk, off = paged.slot(block_table[b], p, block_size)
         ks[p] = k_pool[blk, g, off]
@@ -121,4 +123,74 @@ def decode_step(k_pool, v_pool, q, k, v, block_table, context_lens, block_size,
         k_pool, v_pool, q, k, v, block_table, context_lens, block_size, theta)
     out = paged_gqa_decode(q_rot_bits, k_new, v_new, block_table, context_lens,
                            block_size, scale)
+    return out, k_new, v_new, q_rot_bits
+
+
+# ---------------------------------------------------------------- 8-bit cache
+# vLLM-based inference-framework project report, "FP8 KV Cache quantisation":
+# the cache holds FP8 codes; the attention reads them back dequantised. Codec
+# and scale convention in oracle.fp8.
+
+def write_decode_kv_fp8(k_pool8, v_pool8, q, k, v, block_table, context_lens,
+                        block_size, theta, k_scales, v_scales):
+    """write_decode_kv into an 8-bit cache: the new token's K is rotated and
+    rounded to bf16 exactly as for the bf16 cache, then K and V are quantised
+    with their KV head's scale (oracle.fp8.quantize) and stored at the slot.
+
+    k_pool8, v_pool8 : uint8 codes [N, Hkv, bs, D] (not modified)
+    k_scales, v_scales : [Hkv] float32 scales
+    Returns (k_pool_new, v_pool_new, q_rot_bits, q_rot_f64).
+    """
+    k_new = np.array(k_pool8, dtype=np.uint8, copy=True)
+    v_new = np.array(v_pool8, dtype=np.uint8, copy=True)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    q_rot = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        pos = int(context_lens[b])
+        blk, off = paged.slot(block_table[b], pos, block_size)
+        for g in range(Hkv):
+            k_rot = bf16.decode(bf16.encode(rope.apply(bf16.decode(k[b, g]), pos, theta)))
+            k_new[blk, g, off, :] = fp8.quantize(k_rot, k_scales[g])
+            v_new[blk, g, off, :] = fp8.quantize(bf16.decode(v[b, g]), v_scales[g])
+        for h in range(Hq):
+            q_rot[b, h] = rope.apply(bf16.decode(q[b, h]), pos, theta)
+    return k_new, v_new, bf16.encode(q_rot), q_rot
+
+
+def paged_gqa_decode_fp8(q_rot, k_pool8, v_pool8, block_table, context_lens, block_size,
+                         k_scales, v_scales, scale=None, q_is_bits=True):
+    """Paged GQA decode attention over an 8-bit cache: gather the codes through
+    the block table, dequantise them with their KV head's scales, then the
+    same stable softmax attention as paged_gqa_decode. Returns float64
+    [B, Hq, D]."""
+    qf = bf16.decode(q_rot) if q_is_bits else np.asarray(q_rot, dtype=np.float64)
+    B, Hq, D = qf.shape
+    Hkv = k_pool8.shape[1]
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(np.float64(D))
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b]) + 1
+        for g in range(Hkv):
+            ks, vs = gather_kv(k_pool8, v_pool8, block_table, block_size, b, g, L)
+            K = fp8.dequantize(ks, k_scales[g])
+            V = fp8.dequantize(vs, v_scales[g])
+            for h in range(g * G, (g + 1) * G):
+                out[b, h] = attend(qf[b, h], K, V, scale)
+    return out
+
+
+def decode_step_fp8(k_pool8, v_pool8, q, k, v, block_table, context_lens, block_size,
+                    theta, k_scales, v_scales, scale=None):
+    """write_decode_kv_fp8 followed by paged_gqa_decode_fp8.
+    Returns (out_f64, k_pool_new, v_pool_new, q_rot_bits)."""
+    k_new, v_new, q_rot_bits, _ = write_decode_kv_fp8(
+        k_pool8, v_pool8, q, k, v, block_table, context_lens, block_size, theta,
+        k_scales, v_scales)
+    out = paged_gqa_decode_fp8(q_rot_bits, k_new, v_new, block_table, context_lens,
+                               block_size, k_scales, v_scales, scale)
     return out, k_new, v_new, q_rot_bits

@@ -20,6 +20,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 NAN_BF16 = np.uint16(0x7FC0)
+NAN_FP8 = np.uint8(0x7F)
 
 
 def f32_to_bf16_bits(a):
@@ -34,6 +35,20 @@ def bf16_normal(rng, shape, std=1.0):
     if std != 1.0:
         a *= np.float32(std)
     return f32_to_bf16_bits(a)
+
+
+def fp8_normal_like(rng, shape):
+    """Random 8-bit E4M3 bit patterns with N(0, 1)-like magnitudes: the exponent
+    field is floor(log2|x|) + 7 of a normal draw x (clipped to 0..15, field 0
+    being the subnormal range), the 3 significand bits are uniform and the
+    sign is that of x. Plain bit construction -- no rounding of values -- and
+    the NaN patterns 0x7F / 0xFF are never drawn."""
+    x = rng.standard_normal(shape)
+    e = np.clip(np.floor(np.log2(np.maximum(np.abs(x), 1e-30))).astype(np.int64) + 7, 0, 15)
+    m = rng.integers(0, 8, shape)
+    m = np.where((e == 15) & (m == 7), 6, m)
+    s = (x < 0).astype(np.int64) << 7
+    return (s | (e << 3) | m).astype(np.uint8)
 
 
 @dataclass
@@ -151,7 +166,7 @@ def make_block_table(rng, ctx, bs, num_blocks, mode):
 
 
 def make_decode_case(cfg, pool="poison", seed=None, context_lens=None, num_blocks=None,
-                     table_mode=None):
+                     table_mode=None, kv_format="bf16"):
     """Draw one decode step.
 
     pool = "poison": cached slots [0, ctx) hold N(0,1); the write slot, the tail
@@ -159,6 +174,8 @@ def make_decode_case(cfg, pool="poison", seed=None, context_lens=None, num_block
     pool = "bench":  every slot of every allocated block holds N(0,1);
            unallocated blocks are zero (never read).
     pool = "full":   every element of the pool holds N(0,1).
+    kv_format = "bf16": pools of bf16 bits; "fp8": pools of E4M3 codes drawn by
+           fp8_normal_like (q, k, v stay bf16).
     """
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
     ctx = (np.asarray(context_lens, dtype=np.int32) if context_lens is not None
@@ -175,22 +192,28 @@ def make_decode_case(cfg, pool="poison", seed=None, context_lens=None, num_block
     v = bf16_normal(rng, (B, Hkv, D))
 
     shape = (N, Hkv, bs, D)
+    if kv_format == "bf16":
+        draw, nan, dt = bf16_normal, NAN_BF16, np.uint16
+    elif kv_format == "fp8":
+        draw, nan, dt = fp8_normal_like, NAN_FP8, np.uint8
+    else:
+        raise ValueError(kv_format)
     if pool == "full":
-        k_pool = bf16_normal(rng, shape)
-        v_pool = bf16_normal(rng, shape)
+        k_pool = draw(rng, shape)
+        v_pool = draw(rng, shape)
     else:
         ids = np.concatenate([table[b, :need[b]] for b in range(B)]) if B else np.zeros(0, np.int32)
-        fill = NAN_BF16 if pool == "poison" else np.uint16(0)
-        k_pool = np.full(shape, fill, dtype=np.uint16)
-        v_pool = np.full(shape, fill, dtype=np.uint16)
-        k_pool[ids] = bf16_normal(rng, (len(ids), Hkv, bs, D))
-        v_pool[ids] = bf16_normal(rng, (len(ids), Hkv, bs, D))
+        fill = nan if pool == "poison" else dt(0)
+        k_pool = np.full(shape, fill, dtype=dt)
+        v_pool = np.full(shape, fill, dtype=dt)
+        k_pool[ids] = draw(rng, (len(ids), Hkv, bs, D))
+        v_pool[ids] = draw(rng, (len(ids), Hkv, bs, D))
     if pool == "poison":
         for b in range(B):
             last = table[b, need[b] - 1]
             first_bad = int(ctx[b]) % bs       # write slot, then the tail
-            k_pool[last, :, first_bad:, :] = NAN_BF16
-            v_pool[last, :, first_bad:, :] = NAN_BF16
+            k_pool[last, :, first_bad:, :] = nan
+            v_pool[last, :, first_bad:, :] = nan
     return DecodeCase(cfg, ctx, table, N, q, k, v, k_pool, v_pool)
 
 
@@ -218,22 +241,26 @@ def make_layer_input(cfg, seed=None):
 
 # ---------------------------------------------------------------- byte counts
 def attention_bytes(context_lens, num_q_heads, num_kv_heads, head_dim, block_size,
-                    elem_bytes=2):
+                    kv_elem_bytes=2):
     """Algorithmic HBM bytes of one paged decode attention call: K and V of the
-    L = ctx + 1 attended tokens once per (sequence, kv head), q in and out
-    once, the used block-table entries and the lengths."""
+    L = ctx + 1 attended tokens once per (sequence, kv head) at kv_elem_bytes
+    per element (2 for bf16, 1 for an 8-bit cache, which adds its two fp32
+    scales per kv head), bf16 q in and out once, the used block-table entries
+    and the lengths."""
     L = np.asarray(context_lens, dtype=np.int64) + 1
-    kv = 2 * elem_bytes * num_kv_heads * head_dim * int(L.sum())
-    qo = 2 * elem_bytes * len(L) * num_q_heads * head_dim
+    kv = 2 * kv_elem_bytes * num_kv_heads * head_dim * int(L.sum())
+    qo = 2 * 2 * len(L) * num_q_heads * head_dim
     table = 4 * int(sum(nblocks(x, block_size) for x in L))
-    return kv + qo + table + 4 * len(L)
+    scales = 8 * num_kv_heads if kv_elem_bytes == 1 else 0
+    return kv + qo + table + 4 * len(L) + scales
 
 
-def write_bytes(batch, num_q_heads, num_kv_heads, head_dim, elem_bytes=2):
-    """Algorithmic bytes of write_decode_kv: q in and q_rot out, k and v in, the
-    new K and V rows out, one table entry and one length per sequence."""
-    return (2 * elem_bytes * batch * head_dim * (num_q_heads + 2 * num_kv_heads)
-            + 8 * batch)
+def write_bytes(batch, num_q_heads, num_kv_heads, head_dim, kv_elem_bytes=2):
+    """Algorithmic bytes of write_decode_kv: bf16 q in and q_rot out, bf16 k
+    and v in, the new K and V rows out at kv_elem_bytes per element, one
+    table entry and one length per sequence."""
+    return (2 * 2 * batch * head_dim * (num_q_heads + num_kv_heads)
+            + 2 * kv_elem_bytes * batch * head_dim * num_kv_heads + 8 * batch)
 
 
 def layer_weight_bytes(cfg):
