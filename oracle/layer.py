@@ -17,12 +17,14 @@ of the Qwen models they run:
     out = x2 + a W_d^T
 
 Weights use the nn.Linear layout [out_features, in_features] (y = x W^T).
-Everything is float64; the only roundings are the bf16 cache stores.
+Everything is float64; the only roundings are the cache stores (bf16, or the
+E4M3 codes of those bf16 values for an 8-bit cache).
 """
 import numpy as np
 
 from . import attention
 from . import bf16
+from . import fp8
 from . import paged
 from . import rope
 
@@ -47,13 +49,17 @@ def swiglu(r, w_gate, w_up, w_down):
 
 def decoder_layer_decode(x_bits, weights, k_pool, v_pool, block_table, context_lens,
                          block_size, num_q_heads, num_kv_heads, head_dim,
-                         rms_eps, theta, return_intermediates=False):
+                         rms_eps, theta, return_intermediates=False, kv_scales=None):
     """One decode step of one layer for a batch of sequences.
 
     x_bits  : uint16 bf16 bits [B, H]
     weights : dict of uint16 bf16 bits: ln1_w [H], w_qkv [(Hq+2Hkv)D, H],
               w_o [H, Hq D], ln2_w [H], w_gate [I, H], w_up [I, H], w_down [H, I]
-    k_pool, v_pool : uint16 [N, Hkv, bs, D] (not modified)
+    k_pool, v_pool : uint16 [N, Hkv, bs, D] (not modified); with kv_scales =
+              (k_scales [Hkv], v_scales [Hkv]) they are uint8 E4M3 codes of an
+              8-bit cache: the stores become fp8.quantize of the bf16 values
+              and the attention reads fp8.dequantize (vLLM-based
+              inference-framework report, "FP8 KV Cache quantisation").
     Returns (out_f64 [B, H], k_pool_new, v_pool_new[, intermediates]).
     """
     x = bf16.decode(x_bits)
@@ -68,15 +74,22 @@ def decoder_layer_decode(x_bits, weights, k_pool, v_pool, block_table, context_l
     k = qkv[:, Hq * D: (Hq + Hkv) * D].reshape(B, Hkv, D)
     v = qkv[:, (Hq + Hkv) * D:].reshape(B, Hkv, D)
 
-    k_new = np.array(k_pool, dtype=np.uint16, copy=True)
-    v_new = np.array(v_pool, dtype=np.uint16, copy=True)
+    f8 = kv_scales is not None
+    k_new = np.array(k_pool, dtype=np.uint8 if f8 else np.uint16, copy=True)
+    v_new = np.array(v_pool, dtype=np.uint8 if f8 else np.uint16, copy=True)
     q_rot = np.empty_like(q)
     for b in range(B):
         pos = int(context_lens[b])
         blk, off = paged.slot(block_table[b], pos, block_size)
         for g in range(Hkv):
-            k_new[blk, g, off] = bf16.encode(rope.apply(k[b, g], pos, theta))
-            v_new[blk, g, off] = bf16.encode(v[b, g])
+            kb = bf16.encode(rope.apply(k[b, g], pos, theta))
+            vb = bf16.encode(v[b, g])
+            if f8:
+                k_new[blk, g, off] = fp8.quantize(bf16.decode(kb), kv_scales[0][g])
+                v_new[blk, g, off] = fp8.quantize(bf16.decode(vb), kv_scales[1][g])
+            else:
+                k_new[blk, g, off] = kb
+                v_new[blk, g, off] = vb
         q_rot[b] = rope.apply(q[b], pos, theta)
 
     o = np.empty((B, Hq, D), dtype=np.float64)
@@ -85,7 +98,11 @@ def decoder_layer_decode(x_bits, weights, k_pool, v_pool, block_table, context_l
         L = int(context_lens[b]) + 1
         for g in range(Hkv):
             ks, vs = attention.gather_kv(k_new, v_new, block_table, block_size, b, g, L)
-            K, V = bf16.decode(ks), bf16.decode(vs)
+            if f8:
+                K = fp8.dequantize(ks, kv_scales[0][g])
+                V = fp8.dequantize(vs, kv_scales[1][g])
+            else:
+                K, V = bf16.decode(ks), bf16.decode(vs)
             for h in range(g * G, (g + 1) * G):
                 o[b, h] = attention.attend(q_rot[b, h], K, V, scale)
 

@@ -142,3 +142,37 @@ def test_layer_position_zero_sequence_attends_to_itself_only():
     G = Hq // Hkv
     for h in range(Hq):
         assert np.array_equal(inter["o"][0, h], v[h // G])
+
+
+def test_layer_with_8bit_cache_composes_the_pinned_fp8_write_and_attention():
+    """An 8-bit cache changes only the stores and the reads: the projections
+    equal the bf16 layer's; the new slots hold fp8.quantize of the bf16 layer's
+    stored K and V; the attention output equals paged_gqa_decode_fp8 (pinned
+    against the bf16 attention) over the new codes."""
+    from oracle import fp8
+    cfg = SMALL
+    case = workloads.make_decode_case(cfg, pool="poison", kv_format="fp8")
+    w = workloads.make_layer_weights(cfg, std=0.2)
+    x = workloads.make_layer_input(cfg)
+    ks = np.array([0.75, 1.5], np.float32)
+    vs = np.array([2.0, 0.3], np.float32)
+    out8, k8, v8, i8 = _run(case, w, x, return_intermediates=True, kv_scales=(ks, vs))
+    zeros = np.zeros(case.k_pool.shape, np.uint16)
+    case16 = workloads.make_decode_case(cfg, pool="poison")
+    _, kb, vb, ib = layer.decoder_layer_decode(
+        x, w, zeros, zeros.copy(), case16.block_table, case16.context_lens, 16, cfg.num_q_heads,
+        cfg.num_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.rope_theta, return_intermediates=True)
+    assert np.array_equal(case.block_table, case16.block_table)
+    for name in ("r1", "qkv", "q_rot"):
+        assert np.array_equal(i8[name], ib[name])
+    written = np.zeros(case.k_pool.shape[:3], bool)
+    for b, ctx in enumerate(case.context_lens):
+        blk, off = case.block_table[b, ctx // 16], ctx % 16
+        written[blk, :, off] = True
+        for g in range(cfg.num_kv_heads):
+            assert np.array_equal(k8[blk, g, off], fp8.quantize(bf16.decode(kb[blk, g, off]), ks[g]))
+            assert np.array_equal(v8[blk, g, off], fp8.quantize(bf16.decode(vb[blk, g, off]), vs[g]))
+    assert np.array_equal(k8[~written], case.k_pool[~written])
+    o = attention.paged_gqa_decode_fp8(i8["q_rot"], k8, v8, case.block_table, case.context_lens,
+                                       16, ks, vs, q_is_bits=False)
+    assert np.array_equal(i8["o"], o)
