@@ -85,7 +85,8 @@ enum {
 
 /* Pool flags. */
 enum {
-    MI_POOL_HOST_ONLY = 1u            /* block bookkeeping only: no device memory, no kernels */
+    MI_POOL_HOST_ONLY = 1u,           /* block bookkeeping only: no device memory, no kernels */
+    MI_POOL_KV_FP8 = 2u               /* 8-bit cache: E4M3 codes with per-KV-head scales */
 };
 
 /* Static description of a status code. Never NULL. */
@@ -104,16 +105,48 @@ typedef struct mi_kv_pool_s* mi_kv_pool_t;
  *  k_cache, v_cache  both NULL: the library allocates both pools in device
  *               memory (contents undefined) and frees them on destroy. Both
  *               non-NULL: caller-owned device buffers of
- *               num_blocks*num_kv_heads*block_size*head_dim bf16 each, never
+ *               num_blocks*num_kv_heads*block_size*head_dim elements each
+ *               (bf16 bits, or 1-byte E4M3 codes with MI_POOL_KV_FP8), never
  *               freed by the library. One NULL and one not: MI_ERR_INVALID_ARG.
- *  flags        0 or MI_POOL_HOST_ONLY (then k_cache/v_cache must be NULL and
- *               every kernel call on the pool returns MI_ERR_INVALID_ARG).
+ *  flags        any OR of
+ *               MI_POOL_HOST_ONLY: no device memory (k_cache/v_cache must be
+ *                 NULL) and every kernel call on the pool returns
+ *                 MI_ERR_INVALID_ARG;
+ *               MI_POOL_KV_FP8: the cache holds 8-bit E4M3 codes (OCP "FN"
+ *                 variant: bias 7, no infinities, largest finite 448) of
+ *                 value / scale, with one K scale and one V scale per KV head
+ *                 (all 1.0 until mi_kv_pool_set_scales). vLLM-based
+ *                 inference-framework report, "FP8 KV Cache quantisation": the
+ *                 cache is held in FP8 to cut the bytes the attention moves.
  * The free-block stack starts full; the first allocation returns ids 0, 1, ...
  * The current HIP device at this call is the pool's device.
  */
 int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t block_size,
                     int32_t num_kv_heads, int32_t head_dim,
                     void* k_cache, void* v_cache, uint32_t flags);
+
+/*
+ * Per-KV-head scales of an 8-bit pool (nxmr.cn inference-techniques article,
+ * section 2.2: heads with different value ranges need their own scales).
+ * k_scales, v_scales: host arrays [num_kv_heads] of finite values > 0, or
+ * NULL for all 1.0. A bf16 value x is stored as the code nearest to
+ * float32(x) / scale (one float32 division, then round to nearest even,
+ * saturating at +-448, NaN -> 0x7F) and read back as code_value * scale.
+ * Set the scales before anything is written: codes already in the cache are
+ * not converted. Synchronises the device. MI_ERR_INVALID_ARG for a bf16 pool
+ * or a bad scale (nothing changed).
+ */
+int mi_kv_pool_set_scales(mi_kv_pool_t pool, const float* k_scales, const float* v_scales);
+
+/*
+ * Quantise whole bf16 caches into an 8-bit pool: k_src, v_src are device
+ * bf16 pools of the same [num_blocks, num_kv_heads, 16, head_dim] shape
+ * (e.g. filled by a bf16 prefill); every element is stored as its code under
+ * its KV head's scale (the rule of mi_kv_pool_set_scales). Asynchronous on
+ * stream. MI_ERR_INVALID_ARG for a bf16 or host-only pool or NULL sources.
+ */
+int mi_kv_pool_quantize(mi_kv_pool_t pool, const uint16_t* k_src, const uint16_t* v_src,
+                        void* stream);
 
 /* Free the handle, library-owned pools and the error word. NULL is a no-op. */
 int mi_kv_pool_destroy(mi_kv_pool_t pool);
@@ -165,6 +198,8 @@ int mi_kv_pool_check_errors(mi_kv_pool_t pool, uint32_t* fault_bits);
  *  V[slot] = v (bit copy) for every kv head, q_rot = bf16(RoPE(q, pos)), where
  *  slot = (block_table[b][pos / 16], pos % 16). The angle and the rotation are
  *  computed in float64 and rounded once to bf16 (nearest, ties to even).
+ *  With an 8-bit pool (MI_POOL_KV_FP8) the slot receives the E4M3 codes of
+ *  that bf16 K and of v under the head's scales (mi_kv_pool_set_scales).
  *  batch == 0 is a no-op.
  */
 int mi_write_decode_kv(mi_kv_pool_t pool,
@@ -189,7 +224,12 @@ size_t mi_paged_gqa_decode_workspace_bytes(mi_kv_pool_t pool, int32_t batch,
  * L = context_lens[b] + 1:
  *     s_t = scale * <q_rot[b,h], K[slot(b,t), g]>,  t < L
  *     out[b,h] = sum_t softmax(s)_t V[slot(b,t), g]
- * computed as split-K online softmax in fp32 and rounded once to bf16.
+ * (with an 8-bit pool, K and V are the codes times their head's scales). The
+ * work is split over the device in equal shares of tiles (split-K online
+ * softmax): q.K in fp32 from exact bf16 products, the softmax weights
+ * exp2-based in fp32 and rounded to bf16 for the weighted sum of V (fp32
+ * accumulation), partial results merged in fp32, one rounding to bf16.
+ *  batch   0 .. 1024 (more: MI_ERR_UNSUPPORTED)
  *  q_rot   device bf16 [batch, num_q_heads, head_dim] (as written by
  *          mi_write_decode_kv)
  *  out     device bf16 [batch, num_q_heads, head_dim]; must not alias q_rot
@@ -214,8 +254,9 @@ int mi_paged_gqa_decode(mi_kv_pool_t pool, const uint16_t* q_rot, uint16_t* out,
 
 /*
  * Same as mi_paged_gqa_decode with an explicit split size: split_tokens is
- * the number of tokens per split-K chunk (a positive multiple of 16), or 0
- * for the library's choice. The workspace query for an explicit split size
+ * the minimum number of tokens in one wave's share of the work (a positive
+ * multiple of 16; small workloads then use fewer, longer shares), or 0 for
+ * the library's choice (32). The workspace query for an explicit split size
  * is mi_paged_gqa_decode_split_workspace_bytes.
  */
 int mi_paged_gqa_decode_split(mi_kv_pool_t pool, const uint16_t* q_rot, uint16_t* out,
@@ -232,14 +273,15 @@ size_t mi_paged_gqa_decode_split_workspace_bytes(mi_kv_pool_t pool, int32_t batc
 /*
  * Debug export of the gather step (mini-infer gather_batch_kv): bit copies of
  * K and V of positions [0, context_lens[b] + len_extra) of every sequence and
- * kv head into k_out / v_out, device bf16 [batch, num_kv_heads, l_max,
- * head_dim]. Positions at or beyond that length are not written.
+ * kv head into k_out / v_out, device arrays [batch, num_kv_heads, l_max,
+ * head_dim] of the pool's element type (bf16 bits, or E4M3 codes). Positions
+ * at or beyond that length are not written.
  * len_extra is 0 or 1; every context_lens[b] + len_extra must be <= l_max.
  */
 int mi_gather_kv(mi_kv_pool_t pool, const int32_t* block_table,
                  int32_t max_blocks_per_seq, const int32_t* context_lens,
                  int32_t batch, int32_t len_extra,
-                 uint16_t* k_out, uint16_t* v_out, int32_t l_max, void* stream);
+                 void* k_out, void* v_out, int32_t l_max, void* stream);
 
 /* ------------------------------------------------------------------------
  * Full decoder-layer decode step (course project 2.1: RMSNorm, QKV with

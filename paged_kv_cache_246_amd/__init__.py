@@ -25,6 +25,7 @@ MI_ERR_DEVICE_FAULT = -7
 MI_FAULT_BLOCK_ID = 1
 MI_FAULT_CONTEXT_LEN = 2
 MI_POOL_HOST_ONLY = 1
+MI_POOL_KV_FP8 = 2
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -38,6 +39,8 @@ SIGNATURES = {
     "mi_status_string": (_c.c_char_p, [_c.c_int]),
     "mi_kv_pool_init": (_c.c_int, [_c.POINTER(_vp), _i32, _i32, _i32, _i32, _vp, _vp, _u32]),
     "mi_kv_pool_destroy": (_c.c_int, [_vp]),
+    "mi_kv_pool_set_scales": (_c.c_int, [_vp, _vp, _vp]),
+    "mi_kv_pool_quantize": (_c.c_int, [_vp, _vp, _vp, _vp]),
     "mi_kv_pool_get": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp)]),
     "mi_kv_pool_shape": (_c.c_int, [_vp, _c.POINTER(_i32), _c.POINTER(_i32), _c.POINTER(_i32),
                                     _c.POINTER(_i32)]),
@@ -135,6 +138,25 @@ def mi_kv_pool_init(num_blocks, block_size, num_kv_heads, head_dim, k_cache=None
 
 def mi_kv_pool_destroy(pool):
     return _check("mi_kv_pool_destroy", lib().mi_kv_pool_destroy(pool))
+
+
+def mi_kv_pool_set_scales(pool, k_scales=None, v_scales=None):
+    """Per-KV-head scales of an 8-bit pool (host sequences of floats, or None
+    for 1.0)."""
+    def arr(x):
+        if x is None:
+            return None
+        a = (ctypes.c_float * len(x))(*[float(v) for v in x])
+        return a
+    ka, va = arr(k_scales), arr(v_scales)
+    return _check("mi_kv_pool_set_scales", lib().mi_kv_pool_set_scales(
+        pool, ctypes.cast(ka, _vp) if ka is not None else None,
+        ctypes.cast(va, _vp) if va is not None else None))
+
+
+def mi_kv_pool_quantize(pool, k_src, v_src, stream=None):
+    return _check("mi_kv_pool_quantize", lib().mi_kv_pool_quantize(
+        pool, _ptr(k_src), _ptr(v_src), _stream(stream)))
 
 
 def mi_kv_pool_get(pool):

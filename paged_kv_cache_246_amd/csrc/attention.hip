@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "e4m3.h"
 #include "internal.h"
 
 namespace {
@@ -65,13 +66,18 @@ __device__ __forceinline__ uint4 ld16_stream(const char* base, uint32_t off) {
 // threads tile that index space (grid.y) for each sequence (grid.x). The
 // angle pos * theta^(-2i/D) (inverse frequencies from the host table), its
 // sine and cosine and the rotation are float64 with separately rounded
-// products, rounded once to bf16.
-template <int D>
+// products, rounded once to bf16. An 8-bit cache (FMT = kFmtFp8) stores the
+// E4M3 codes of that bf16 K and of v under the head's scales.
+constexpr int kFmtBf16 = 0;
+constexpr int kFmtFp8 = 1;
+
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* q_rot, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+    uint16_t* q_rot, void* __restrict__ kc, void* __restrict__ vc,
     const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
-    int32_t hq, int32_t hkv, int32_t num_blocks, mikv::RopeTable rope, uint32_t* __restrict__ err) {
+    int32_t hq, int32_t hkv, int32_t num_blocks, mikv::RopeTable rope,
+    const float* __restrict__ kv_scales, uint32_t* __restrict__ err) {
     constexpr int H2 = D / 2;
     const int b = blockIdx.x;
     const int pos = ctx_lens[b];
@@ -89,17 +95,10 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     if (idx < n_rot) {
         const int h = idx / H2;
         const int i = idx - h * H2;
-        const uint16_t* src;
-        uint16_t* dst;
-        if (h < hq) {
-            src = q + (static_cast<size_t>(b) * hq + h) * D;
-            dst = q_rot + (static_cast<size_t>(b) * hq + h) * D;
-        } else {
-            if (!blk_ok) return;
-            const int g = h - hq;
-            src = k + (static_cast<size_t>(b) * hkv + g) * D;
-            dst = kc + ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
-        }
+        if (h >= hq && !blk_ok) return;
+        const int g = h - hq;
+        const uint16_t* src = h < hq ? q + (static_cast<size_t>(b) * hq + h) * D
+                                     : k + (static_cast<size_t>(b) * hkv + g) * D;
         const double x1 = bf16_to_f64(src[i]);
         const double x2 = bf16_to_f64(src[i + H2]);
         const double a = static_cast<double>(pos) * rope.inv_freq[i];
@@ -107,16 +106,59 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
         sincos(a, &sn, &cs);
         const double y1 = __dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn));
         const double y2 = __dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn));
-        dst[i] = f64_to_bf16_rne(y1);
-        dst[i + H2] = f64_to_bf16_rne(y2);
+        const uint16_t r1 = f64_to_bf16_rne(y1);
+        const uint16_t r2 = f64_to_bf16_rne(y2);
+        if (h < hq) {
+            uint16_t* dst = q_rot + (static_cast<size_t>(b) * hq + h) * D;
+            dst[i] = r1;
+            dst[i + H2] = r2;
+        } else {
+            const size_t row = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
+            if constexpr (FMT == kFmtBf16) {
+                uint16_t* dst = static_cast<uint16_t*>(kc) + row;
+                dst[i] = r1;
+                dst[i + H2] = r2;
+            } else {
+                uint8_t* dst = static_cast<uint8_t*>(kc) + row;
+                const float s = kv_scales[g];
+                dst[i] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, s));
+                dst[i + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, s));
+            }
+        }
     } else if (blk_ok) {
-        // V is a bit copy, 16 bytes per thread
+        // V: 8 elements (16 input bytes) per thread
         const int piece = idx - n_rot;
         if (piece >= hkv * (D / 8)) return;
         const int g = piece / (D / 8);
         const int e = (piece - g * (D / 8)) * 8;
         const uint4 val = *reinterpret_cast<const uint4*>(v + (static_cast<size_t>(b) * hkv + g) * D + e);
-        *reinterpret_cast<uint4*>(vc + ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D + e) = val;
+        const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D + e;
+        if constexpr (FMT == kFmtBf16)
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(vc) + at) = val;
+        else
+            *reinterpret_cast<uint2*>(static_cast<uint8_t*>(vc) + at) =
+                mikv_dev::e4m3_quantize_bf16x8(val, kv_scales[hkv + g]);
+    }
+}
+
+// Whole-pool quantisation of bf16 caches into an 8-bit pool: 8 elements per
+// thread, grid-stride over the pool (grid.y: 0 = K, 1 = V); the KV head of an
+// element picks its scale.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_pool_kernel(
+    const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, size_t pieces, int32_t hkv,
+    const float* __restrict__ kv_scales) {
+    const bool is_v = blockIdx.y == 1;
+    const uint16_t* src = is_v ? v_src : k_src;
+    uint8_t* dst = is_v ? vc : kc;
+    constexpr size_t kPiecesPerTile = BS * D / 8;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < pieces;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+        const int g = static_cast<int>((i / kPiecesPerTile) % hkv);
+        const float s = kv_scales[(is_v ? hkv : 0) + g];
+        const uint4 w = reinterpret_cast<const uint4*>(src)[i];
+        reinterpret_cast<uint2*>(dst)[i] = mikv_dev::e4m3_quantize_bf16x8(w, s);
     }
 }
 
@@ -220,9 +262,6 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kFmtBf16 = 0;
-constexpr int kFmtFp8 = 1;
 
 template <int D, int FMT>
 struct MfmaTile {
@@ -618,12 +657,13 @@ __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
 }
 
 // ===================================================================== gather
-template <int D>
+// Bit copies of the pool's rows (ESZ bytes per element) in logical order.
+template <int D, int ESZ>
 __global__ __launch_bounds__(256) void gather_kv_kernel(
-    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
     int32_t hkv, int32_t num_blocks, int32_t len_extra, int32_t l_max,
-    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, uint32_t* __restrict__ err) {
+    uint8_t* __restrict__ k_out, uint8_t* __restrict__ v_out, uint32_t* __restrict__ err) {
     const int lb = blockIdx.x;       // logical block
     const int g = blockIdx.y;
     const int b = blockIdx.z;
@@ -639,14 +679,15 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
         if (threadIdx.x == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
         return;
     }
-    constexpr int PER_TOK = D / 8;   // 16-byte pieces per token row
+    constexpr int ROWB = D * ESZ;        // bytes per token row
+    constexpr int PER_TOK = ROWB / 16;   // 16-byte pieces per token row
     for (int idx = threadIdx.x; idx < BS * PER_TOK; idx += blockDim.x) {
         const int t = idx / PER_TOK;
-        const int e = (idx - t * PER_TOK) * 8;
+        const int e = (idx - t * PER_TOK) * 16;
         const int p = lb * BS + t;
         if (p >= n) continue;
-        const size_t src = ((static_cast<size_t>(blk) * hkv + g) * BS + t) * D + e;
-        const size_t dst = ((static_cast<size_t>(b) * hkv + g) * l_max + p) * D + e;
+        const size_t src = ((static_cast<size_t>(blk) * hkv + g) * BS + t) * ROWB + e;
+        const size_t dst = ((static_cast<size_t>(b) * hkv + g) * l_max + p) * ROWB + e;
         *reinterpret_cast<uint4*>(k_out + dst) = *reinterpret_cast<const uint4*>(kc + src);
         *reinterpret_cast<uint4*>(v_out + dst) = *reinterpret_cast<const uint4*>(vc + src);
     }
@@ -687,12 +728,13 @@ void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                  float scale_log2, int32_t max_ctx, int32_t min_tiles, float* part_acc,
                  float2* part_ml, hipStream_t st) {
     const int hkv = p->num_kv_heads;
-    auto kern = paged_attn_mfma_kernel<D, G, kFmtBf16, kAttnPrefetch>;
+    auto kern = mikv::pool_fp8(p) ? paged_attn_mfma_kernel<D, G, kFmtFp8, kAttnPrefetch>
+                                  : paged_attn_mfma_kernel<D, G, kFmtBf16, kAttnPrefetch>;
     const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, attention_waves(kern));
-    hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot,
-                       reinterpret_cast<const uint8_t*>(p->k), reinterpret_cast<const uint8_t*>(p->v),
-                       table, mbps, ctx, batch, hkv, p->num_blocks, max_ctx, min_tiles, scale_log2,
-                       static_cast<const float*>(nullptr), part_acc, part_ml, out, p->err);
+    hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
+                       static_cast<const uint8_t*>(p->v), table, mbps, ctx, batch, hkv,
+                       p->num_blocks, max_ctx, min_tiles, scale_log2,
+                       static_cast<const float*>(p->scales), part_acc, part_ml, out, p->err);
     hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), dim3(hkv * G, batch), dim3(256), 0, st,
                        part_acc, part_ml, ctx, batch, mbps, hkv, max_ctx, waves, min_tiles, out);
 }
@@ -754,12 +796,11 @@ int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint1
     const int items = (hq + hkv) * (p->head_dim / 2) + hkv * (p->head_dim / 8);
     const dim3 grid(batch, (items + 255) / 256);
     const RopeTable rope = make_rope_table(theta, p->head_dim);
-    if (p->head_dim == 128)
-        hipLaunchKernelGGL(write_decode_kv_kernel<128>, grid, dim3(256), 0, st, q, k, v, q_rot,
-                           p->k, p->v, table, mbps, ctx, hq, hkv, p->num_blocks, rope, p->err);
-    else
-        hipLaunchKernelGGL(write_decode_kv_kernel<64>, grid, dim3(256), 0, st, q, k, v, q_rot,
-                           p->k, p->v, table, mbps, ctx, hq, hkv, p->num_blocks, rope, p->err);
+    const bool f8 = pool_fp8(p);
+    auto kern = p->head_dim == 128 ? (f8 ? write_decode_kv_kernel<128, kFmtFp8> : write_decode_kv_kernel<128, kFmtBf16>)
+                                   : (f8 ? write_decode_kv_kernel<64, kFmtFp8> : write_decode_kv_kernel<64, kFmtBf16>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, k, v, q_rot, p->k, p->v, table, mbps, ctx, hq,
+                       hkv, p->num_blocks, rope, static_cast<const float*>(p->scales), p->err);
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 
@@ -858,7 +899,7 @@ extern "C" int mi_paged_gqa_decode(mi_kv_pool_t p, const uint16_t* q_rot, uint16
 }
 
 extern "C" int mi_gather_kv(mi_kv_pool_t p, const int32_t* table, int32_t mbps, const int32_t* ctx,
-                            int32_t batch, int32_t len_extra, uint16_t* k_out, uint16_t* v_out,
+                            int32_t batch, int32_t len_extra, void* k_out, void* v_out,
                             int32_t l_max, void* stream) {
     if (!p || !mikv::pool_has_device(p) || batch < 0 || mbps <= 0 || l_max < 0) return MI_ERR_INVALID_ARG;
     if (len_extra != 0 && len_extra != 1) return MI_ERR_INVALID_ARG;
@@ -866,11 +907,26 @@ extern "C" int mi_gather_kv(mi_kv_pool_t p, const int32_t* table, int32_t mbps, 
     if (!table || !ctx || !k_out || !v_out) return MI_ERR_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid((l_max + BS - 1) / BS, p->num_kv_heads, batch);
-    if (p->head_dim == 128)
-        hipLaunchKernelGGL(gather_kv_kernel<128>, grid, dim3(256), 0, st, p->k, p->v, table, mbps, ctx,
-                           p->num_kv_heads, p->num_blocks, len_extra, l_max, k_out, v_out, p->err);
-    else
-        hipLaunchKernelGGL(gather_kv_kernel<64>, grid, dim3(256), 0, st, p->k, p->v, table, mbps, ctx,
-                           p->num_kv_heads, p->num_blocks, len_extra, l_max, k_out, v_out, p->err);
+    const bool f8 = mikv::pool_fp8(p);
+    auto kern = p->head_dim == 128 ? (f8 ? gather_kv_kernel<128, 1> : gather_kv_kernel<128, 2>)
+                                   : (f8 ? gather_kv_kernel<64, 1> : gather_kv_kernel<64, 2>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, static_cast<const uint8_t*>(p->k),
+                       static_cast<const uint8_t*>(p->v), table, mbps, ctx, p->num_kv_heads,
+                       p->num_blocks, len_extra, l_max, static_cast<uint8_t*>(k_out),
+                       static_cast<uint8_t*>(v_out), p->err);
+    return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+extern "C" int mi_kv_pool_quantize(mi_kv_pool_t p, const uint16_t* k_src, const uint16_t* v_src,
+                                   void* stream) {
+    if (!p || !mikv::pool_has_device(p) || !mikv::pool_fp8(p) || !k_src || !v_src)
+        return MI_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t pieces = static_cast<size_t>(p->num_blocks) * p->num_kv_heads * BS * p->head_dim / 8;
+    const unsigned blocks = static_cast<unsigned>(std::min<size_t>((pieces + 255) / 256, 8192));
+    auto kern = p->head_dim == 128 ? quantize_pool_kernel<128> : quantize_pool_kernel<64>;
+    hipLaunchKernelGGL(kern, dim3(blocks, 2), dim3(256), 0, st, k_src, v_src,
+                       static_cast<uint8_t*>(p->k), static_cast<uint8_t*>(p->v), pieces,
+                       p->num_kv_heads, static_cast<const float*>(p->scales));
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }

@@ -15,8 +15,9 @@ struct mi_kv_pool_s {
     int32_t head_dim = 0;
     uint32_t flags = 0;
     int device = -1;
-    uint16_t* k = nullptr;           // device [N, Hkv, bs, D]
-    uint16_t* v = nullptr;
+    void* k = nullptr;               // device [N, Hkv, bs, D]: bf16 bits, or E4M3 codes
+    void* v = nullptr;
+    float* scales = nullptr;         // device [2 * Hkv] (8-bit pools): K scales, then V scales
     bool owns_cache = false;
     uint32_t* err = nullptr;         // device error word (MI_FAULT_* bits)
     std::vector<int32_t> stack;      // free-block LIFO; back() is handed out next
@@ -37,6 +38,9 @@ inline RopeTable make_rope_table(double theta, int head_dim) {
     for (int i = 0; i < head_dim / 2 && i < 64; ++i) t.inv_freq[i] = std::pow(theta, -2.0 * i / head_dim);
     return t;
 }
+
+inline bool pool_fp8(const mi_kv_pool_s* p) { return (p->flags & MI_POOL_KV_FP8) != 0; }
+inline int pool_elem_bytes(const mi_kv_pool_s* p) { return pool_fp8(p) ? 1 : 2; }
 
 inline bool pool_has_device(const mi_kv_pool_s* p) {
     return p && !(p->flags & MI_POOL_HOST_ONLY) && p->k && p->v && p->err;

@@ -21,6 +21,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "e4m3.h"
 #include "internal.h"
 
 namespace {
@@ -345,14 +346,15 @@ __device__ __forceinline__ float sum_splits(const float* P, int S, size_t stride
 // ------------------------------------------- RoPE + append from the QKV GEMM
 // qkv[b][c] = inv_rms1(x_b) * sum_s P[s][b][c]. Then, at pos = ctx_b, the
 // same float64 RoPE and single rounding as write_decode_kv: K slot gets
-// bf16(RoPE(k)), V slot bf16(v), q_rot bf16(RoPE(q)).
-template <int D>
+// bf16(RoPE(k)), V slot bf16(v), q_rot bf16(RoPE(q)); an 8-bit cache (FP8)
+// stores the E4M3 codes of those bf16 K and V under the head's scales.
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) void rope_append_kernel(
     const float* __restrict__ P, int S, const uint16_t* __restrict__ x, int H, float eps,
-    uint16_t* __restrict__ q_rot, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+    uint16_t* __restrict__ q_rot, void* __restrict__ kc, void* __restrict__ vc,
     const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
     int32_t batch, int32_t hq, int32_t hkv, int32_t num_blocks, mikv::RopeTable rope,
-    uint32_t* __restrict__ err) {
+    const float* __restrict__ kv_scales, uint32_t* __restrict__ err) {
     constexpr int H2 = D / 2;
     __shared__ float red[4];
     const int b = blockIdx.x;
@@ -375,27 +377,43 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     if (idx < n_rot) {
         const int h = idx / H2;
         const int i = idx - h * H2;
-        uint16_t* dst;
-        if (h < hq) {
-            dst = q_rot + (static_cast<size_t>(b) * hq + h) * D;
-        } else {
-            if (!blk_ok) return;
-            dst = kc + ((static_cast<size_t>(blk) * hkv + (h - hq)) * BS + off) * D;
-        }
+        if (h >= hq && !blk_ok) return;
         const double x1 = static_cast<double>(inv * sum_splits(Pb, S, stride, h * D + i));
         const double x2 = static_cast<double>(inv * sum_splits(Pb, S, stride, h * D + i + H2));
         const double a = static_cast<double>(pos) * rope.inv_freq[i];
         double sn, cs;
         sincos(a, &sn, &cs);
-        dst[i] = f64_to_bf16(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
-        dst[i + H2] = f64_to_bf16(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
+        const uint16_t r1 = f64_to_bf16(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
+        const uint16_t r2 = f64_to_bf16(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
+        if (h < hq) {
+            uint16_t* dst = q_rot + (static_cast<size_t>(b) * hq + h) * D;
+            dst[i] = r1;
+            dst[i + H2] = r2;
+        } else {
+            const int g = h - hq;
+            const size_t row = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
+            if constexpr (FP8) {
+                uint8_t* dst = static_cast<uint8_t*>(kc) + row;
+                dst[i] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, kv_scales[g]));
+                dst[i + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, kv_scales[g]));
+            } else {
+                uint16_t* dst = static_cast<uint16_t*>(kc) + row;
+                dst[i] = r1;
+                dst[i + H2] = r2;
+            }
+        }
     } else if (blk_ok) {
         const int e = idx - n_rot;                 // element of the v heads
         if (e >= hkv * D) return;
         const int g = e / D;
         const int d = e - g * D;
         const float v = inv * sum_splits(Pb, S, stride, (hq + hkv) * D + e);
-        vc[((static_cast<size_t>(blk) * hkv + g) * BS + off) * D + d] = f32_to_bf16(v);
+        const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D + d;
+        if constexpr (FP8)
+            static_cast<uint8_t*>(vc)[at] =
+                static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(f32_to_bf16(v), kv_scales[hkv + g]));
+        else
+            static_cast<uint16_t*>(vc)[at] = f32_to_bf16(v);
     }
 }
 
@@ -613,14 +631,12 @@ extern "C" int mi_decoder_layer_decode(mi_kv_pool_t p, const mi_layer_config* cf
         const int items = (hq + hkv) * (D / 2) + hkv * D;
         const dim3 grid(batch, (items + 255) / 256);
         const mikv::RopeTable rope = mikv::make_rope_table(cfg->rope_theta, D);
-        if (D == 128)
-            hipLaunchKernelGGL(rope_append_kernel<128>, grid, dim3(256), 0, st, p_qkv, pl.s_qkv, x_in, H,
-                               cfg->rms_eps, q_rot, p->k, p->v, table, mbps, ctx, batch, hq, hkv,
-                               p->num_blocks, rope, p->err);
-        else
-            hipLaunchKernelGGL(rope_append_kernel<64>, grid, dim3(256), 0, st, p_qkv, pl.s_qkv, x_in, H,
-                               cfg->rms_eps, q_rot, p->k, p->v, table, mbps, ctx, batch, hq, hkv,
-                               p->num_blocks, rope, p->err);
+        const bool f8 = mikv::pool_fp8(p);
+        auto kern = D == 128 ? (f8 ? rope_append_kernel<128, true> : rope_append_kernel<128, false>)
+                             : (f8 ? rope_append_kernel<64, true> : rope_append_kernel<64, false>);
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, p_qkv, pl.s_qkv, x_in, H, cfg->rms_eps, q_rot,
+                           p->k, p->v, table, mbps, ctx, batch, hq, hkv, p->num_blocks, rope,
+                           static_cast<const float*>(p->scales), p->err);
     }
     // 3. paged GQA decode attention
     rc = mikv::launch_paged_gqa_decode(p, q_rot, o, table, mbps, ctx, batch, hq,

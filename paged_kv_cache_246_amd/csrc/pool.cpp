@@ -9,7 +9,9 @@
 // MI_ERR_NO_FREE_BLOCKS instead.
 #include <hip/hip_runtime_api.h>
 
+#include <cmath>
 #include <new>
+#include <vector>
 
 #include "internal.h"
 
@@ -34,7 +36,7 @@ extern "C" int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t bl
     *out = nullptr;
     if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
         return MI_ERR_INVALID_ARG;
-    if (flags & ~static_cast<uint32_t>(MI_POOL_HOST_ONLY)) return MI_ERR_INVALID_ARG;
+    if (flags & ~static_cast<uint32_t>(MI_POOL_HOST_ONLY | MI_POOL_KV_FP8)) return MI_ERR_INVALID_ARG;
     if ((k_cache == nullptr) != (v_cache == nullptr)) return MI_ERR_INVALID_ARG;
     if ((flags & MI_POOL_HOST_ONLY) && k_cache) return MI_ERR_INVALID_ARG;
     if (block_size != mikv::kBlockSize) return MI_ERR_UNSUPPORTED;
@@ -61,25 +63,34 @@ extern "C" int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t bl
             delete p;
             return MI_ERR_HIP;
         }
-        const size_t elems = static_cast<size_t>(num_blocks) * num_kv_heads * block_size * head_dim;
+        const size_t bytes = static_cast<size_t>(num_blocks) * num_kv_heads * block_size *
+                             head_dim * mikv::pool_elem_bytes(p);
         if (k_cache) {
-            p->k = static_cast<uint16_t*>(k_cache);
-            p->v = static_cast<uint16_t*>(v_cache);
+            p->k = k_cache;
+            p->v = v_cache;
         } else {
-            if (hipMalloc(reinterpret_cast<void**>(&p->k), elems * 2) != hipSuccess) {
+            if (hipMalloc(&p->k, bytes) != hipSuccess) {
                 delete p;
                 return MI_ERR_OUT_OF_MEMORY;
             }
-            if (hipMalloc(reinterpret_cast<void**>(&p->v), elems * 2) != hipSuccess) {
+            if (hipMalloc(&p->v, bytes) != hipSuccess) {
                 (void)hipFree(p->k);
                 delete p;
                 return MI_ERR_OUT_OF_MEMORY;
             }
             p->owns_cache = true;
         }
-        if (hipMalloc(reinterpret_cast<void**>(&p->err), 256) != hipSuccess ||
-            hipMemset(p->err, 0, 256) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        bool ok = hipMalloc(reinterpret_cast<void**>(&p->err), 256) == hipSuccess &&
+                  hipMemset(p->err, 0, 256) == hipSuccess;
+        if (ok && mikv::pool_fp8(p)) {
+            const std::vector<float> one(2 * static_cast<size_t>(num_kv_heads), 1.0f);
+            ok = hipMalloc(reinterpret_cast<void**>(&p->scales), one.size() * sizeof(float)) == hipSuccess &&
+                 hipMemcpy(p->scales, one.data(), one.size() * sizeof(float), hipMemcpyHostToDevice) ==
+                     hipSuccess;
+        }
+        if (!ok || hipDeviceSynchronize() != hipSuccess) {
             if (p->err) (void)hipFree(p->err);
+            if (p->scales) (void)hipFree(p->scales);
             if (p->owns_cache) {
                 (void)hipFree(p->k);
                 (void)hipFree(p->v);
@@ -92,10 +103,28 @@ extern "C" int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t bl
     return MI_OK;
 }
 
+extern "C" int mi_kv_pool_set_scales(mi_kv_pool_t p, const float* k_scales, const float* v_scales) {
+    if (!p || !mikv::pool_fp8(p)) return MI_ERR_INVALID_ARG;
+    const int hkv = p->num_kv_heads;
+    std::vector<float> s(2 * static_cast<size_t>(hkv), 1.0f);
+    for (int g = 0; g < hkv; ++g) {
+        if (k_scales) s[g] = k_scales[g];
+        if (v_scales) s[hkv + g] = v_scales[g];
+    }
+    for (float x : s)
+        if (!(x > 0.0f) || !std::isfinite(x)) return MI_ERR_INVALID_ARG;
+    if (!mikv::pool_has_device(p)) return MI_OK;      // host-only pool: nothing on a device
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(p->scales, s.data(), s.size() * sizeof(float), hipMemcpyHostToDevice) != hipSuccess)
+        return MI_ERR_HIP;
+    return MI_OK;
+}
+
 extern "C" int mi_kv_pool_destroy(mi_kv_pool_t p) {
     if (!p) return MI_OK;
     int st = MI_OK;
     if (p->err && hipFree(p->err) != hipSuccess) st = MI_ERR_HIP;
+    if (p->scales && hipFree(p->scales) != hipSuccess) st = MI_ERR_HIP;
     if (p->owns_cache) {
         if (hipFree(p->k) != hipSuccess) st = MI_ERR_HIP;
         if (hipFree(p->v) != hipSuccess) st = MI_ERR_HIP;

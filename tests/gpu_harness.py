@@ -21,16 +21,25 @@ def bf16_bits_to_f64(bits):
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-class DeviceCase:
-    """A DecodeCase on the GPU with a pool over caller-owned K/V buffers."""
+def codes_to_dev(a):
+    """uint8 E4M3 codes -> uint8 device tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
 
-    def __init__(self, case):
+
+class DeviceCase:
+    """A DecodeCase on the GPU with a pool over caller-owned K/V buffers. A case
+    drawn with kv_format="fp8" (uint8 pools) gets an 8-bit pool with the given
+    per-head scales."""
+
+    def __init__(self, case, k_scales=None, v_scales=None):
         self.case = case
         cfg = case.cfg
         self.B = len(case.context_lens)
         self.Hq, self.Hkv, self.D = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
-        self.k_pool = bits_to_dev(case.k_pool)
-        self.v_pool = bits_to_dev(case.v_pool)
+        self.fp8 = case.k_pool.dtype == np.uint8
+        to_dev = codes_to_dev if self.fp8 else bits_to_dev
+        self.k_pool = to_dev(case.k_pool)
+        self.v_pool = to_dev(case.v_pool)
         self.q = bits_to_dev(case.q)
         self.k = bits_to_dev(case.k)
         self.v = bits_to_dev(case.v)
@@ -41,7 +50,10 @@ class DeviceCase:
         self.mbps = case.block_table.shape[1]
         self.max_ctx = int(case.context_lens.max()) if self.B else 0
         self.pool = mk.mi_kv_pool_init(case.num_blocks, cfg.block_size, self.Hkv, self.D,
-                                       self.k_pool, self.v_pool)
+                                       self.k_pool, self.v_pool,
+                                       flags=mk.MI_POOL_KV_FP8 if self.fp8 else 0)
+        if self.fp8:
+            mk.mi_kv_pool_set_scales(self.pool, k_scales, v_scales)
 
     def close(self):
         if self.pool:

@@ -145,3 +145,24 @@ def test_workspace_queries_are_host_only():
         assert mk.mi_paged_gqa_decode_workspace_bytes(pool, 2000, 8, 100) == 0          # batch above the limit
     finally:
         mk.mi_kv_pool_destroy(pool)
+
+
+def test_fp8_pool_scales_validation_on_host_only_pools():
+    p8 = mk.mi_kv_pool_init(8, 16, 2, 128, flags=mk.MI_POOL_HOST_ONLY | mk.MI_POOL_KV_FP8)
+    p16 = _host_pool(8)
+    try:
+        mk.mi_kv_pool_set_scales(p8, [0.5, 2.0], None)
+        mk.mi_kv_pool_set_scales(p8, None, None)
+        for bad in ([0.0, 1.0], [1.0, -2.0], [float("nan"), 1.0], [float("inf"), 1.0]):
+            with pytest.raises(mk.MikvError) as e:
+                mk.mi_kv_pool_set_scales(p8, None, bad)
+            assert e.value.status == mk.MI_ERR_INVALID_ARG
+        with pytest.raises(mk.MikvError) as e:          # bf16 pool has no scales
+            mk.mi_kv_pool_set_scales(p16, [1.0, 1.0], None)
+        assert e.value.status == mk.MI_ERR_INVALID_ARG
+        with pytest.raises(mk.MikvError) as e:          # no device buffers to quantise into
+            mk.mi_kv_pool_quantize(p8, 1, 1, stream=0)
+        assert e.value.status == mk.MI_ERR_INVALID_ARG
+    finally:
+        mk.mi_kv_pool_destroy(p8)
+        mk.mi_kv_pool_destroy(p16)

@@ -1,0 +1,299 @@
+"""GPU parity of the 8-bit (E4M3) KV cache against the fp64 oracle, through
+the C ABI (needs an MI355X): the encoder on every bf16 bit pattern, the
+decode-step write, the gather, paged attention over codes and the full layer."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_246_amd as mk
+import workloads
+from oracle import attention as oatt
+from oracle import bf16 as obf16
+from oracle import fp8 as ofp8
+from oracle import layer as olayer
+from tests.gpu_harness import (DEV, DeviceCase, bf16_bits_to_f64, bits_to_dev, check_tolerance,
+                               codes_to_dev, dev_to_bits, ulp_diff_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mk.lib()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _scales(Hkv, seed):
+    """Per-head scales: a mix of powers of two and arbitrary values."""
+    rng = np.random.default_rng(seed)
+    base = np.array([1.0, 0.37, 2.0, 0.8125, 3.3, 0.5, 1.7, 0.25], np.float32)
+    k = base[rng.permutation(8)[:Hkv] % 8]
+    v = base[rng.permutation(8)[:Hkv] % 8]
+    return k.astype(np.float32), v.astype(np.float32)
+
+
+def _codes(t):
+    return t.cpu().numpy().view(np.uint8)
+
+
+def _code_dist(a, b):
+    """Distance between E4M3 codes in value order (finite codes)."""
+    def ordered(x):
+        x = np.asarray(x, np.uint8).astype(np.int64)
+        return np.where(x & 0x80, -(x & 0x7F), x & 0x7F)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def test_quantize_every_bf16_pattern_bit_exact():
+    """mi_kv_pool_quantize on pools holding all 65536 bf16 patterns per head
+    (NaNs, infinities, subnormals, +-0 included) under per-head scales."""
+    Hkv, D = 4, 128
+    per_head = 65536
+    N = per_head // (16 * D)                               # 32 blocks
+    pat = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    rng = np.random.default_rng(5)
+    src_k = np.empty((N, Hkv, 16, D), np.uint16)
+    src_v = np.empty((N, Hkv, 16, D), np.uint16)
+    for g in range(Hkv):
+        src_k[:, g] = rng.permutation(pat).reshape(N, 16, D)
+        src_v[:, g] = rng.permutation(pat).reshape(N, 16, D)
+    ks = np.array([1.0, 0.37, 3.0, 2.0 ** -7], np.float32)
+    vs = np.array([0.8125, 1.0, 2.0 ** 5, 1.7], np.float32)
+    kd = torch.zeros((N, Hkv, 16, D), dtype=torch.uint8, device=DEV)
+    vd = torch.zeros_like(kd)
+    pool = mk.mi_kv_pool_init(N, 16, Hkv, D, kd, vd, flags=mk.MI_POOL_KV_FP8)
+    try:
+        mk.mi_kv_pool_set_scales(pool, ks, vs)
+        mk.mi_kv_pool_quantize(pool, bits_to_dev(src_k), bits_to_dev(src_v))
+        torch.cuda.synchronize()
+        gk, gv = _codes(kd), _codes(vd)
+    finally:
+        mk.mi_kv_pool_destroy(pool)
+    for g in range(Hkv):
+        ek = ofp8.quantize(obf16.decode(src_k[:, g]), ks[g])
+        ev = ofp8.quantize(obf16.decode(src_v[:, g]), vs[g])
+        nk, nv = int((gk[:, g] != ek).sum()), int((gv[:, g] != ev).sum())
+        _say("head", g, "scales", ks[g], vs[g], "mismatches", nk, nv)
+        assert nk == 0 and nv == 0
+
+
+def _check_write_fp8(case, dc, ks, vs):
+    """Codes after the GPU write vs the oracle's: V codes bit-exact; K codes
+    equal except where the bf16 RoPE value itself may differ by one ulp
+    (then within one code); q_rot within one bf16 ulp; nothing else moved."""
+    cfg = case.cfg
+    kn, vn, qb, _ = oatt.write_decode_kv_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                             case.block_table, case.context_lens, 16,
+                                             cfg.rope_theta, ks, vs)
+    gk, gv = _codes(dc.k_pool), _codes(dc.v_pool)
+    assert np.array_equal(gv, vn)
+    slots = np.zeros(case.k_pool.shape[:3], dtype=bool)
+    for b, ctx in enumerate(case.context_lens):
+        slots[case.block_table[b, ctx // 16], :, ctx % 16] = True
+    assert np.array_equal(gk[~slots], kn[~slots])
+    d = _code_dist(gk[slots], kn[slots])
+    assert d.max() <= 1, d.max()
+    assert ulp_diff_bf16(dev_to_bits(dc.q_rot), qb).max() <= 1
+    return int((d > 0).sum())
+
+
+FP8_CONFIGS = ["tiny", "qwen3_1p7b", "qwen2p5_7b_b1", "qwen2p5_7b_b8"]
+
+
+@pytest.mark.parametrize("name", FP8_CONFIGS)
+def test_fp8_decode_step_parity(name):
+    cfg = workloads.CONFIGS[name]
+    case = workloads.make_decode_case(cfg, pool="poison", kv_format="fp8")
+    ks, vs = _scales(cfg.num_kv_heads, len(name))
+    _say("fp8 decode step", name)
+    ref, _, _, _ = oatt.decode_step_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                        case.block_table, case.context_lens, 16, cfg.rope_theta,
+                                        ks, vs)
+    dc = DeviceCase(case, ks, vs)
+    try:
+        dc.write()
+        torch.cuda.synchronize()
+        off = _check_write_fp8(case, dc, ks, vs)
+        _say("  K codes one step apart:", off)
+        dc.attend()
+        torch.cuda.synchronize()
+        mx, rel = check_tolerance(dev_to_bits(dc.out), ref, name)
+        _say("  max|d| %.3g  relL2 %.3g" % (mx, rel))
+        assert dc.faults() == 0
+    finally:
+        dc.close()
+
+
+GROUPS = [(1, 1), (3, 1), (4, 2), (14, 2), (8, 1)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", GROUPS)
+def test_fp8_group_sizes_head_dims_and_block_boundaries(D, Hq, Hkv):
+    cfg = workloads.DecodeConfig("custom8", batch=0, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                 block_size=16, num_blocks=0, rope_theta=1e4, ctx_draw="fixed",
+                                 seed=D + Hq + 7)
+    ctx = [0, 15, 16, 17, 31, 32, 33, 47, 100]
+    case = workloads.make_decode_case(cfg, pool="poison", context_lens=ctx, num_blocks=96,
+                                      kv_format="fp8")
+    ks, vs = _scales(Hkv, D + Hq)
+    _say("fp8 groups", Hq, Hkv, "D", D)
+    ref, _, _, _ = oatt.decode_step_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                        case.block_table, case.context_lens, 16, cfg.rope_theta,
+                                        ks, vs)
+    dc = DeviceCase(case, ks, vs)
+    try:
+        dc.write()
+        _check_write_fp8(case, dc, ks, vs)
+        for split in (0, 16, 48):
+            dc.attend(split_tokens=split)
+            torch.cuda.synchronize()
+            check_tolerance(dev_to_bits(dc.out), ref, "fp8 G=%d D=%d split=%d" % (Hq // Hkv, D, split))
+        assert dc.faults() == 0
+    finally:
+        dc.close()
+
+
+def test_fp8_permutation_invariance_bit_exact():
+    cfg = workloads.CONFIGS["qwen3_1p7b"]
+    case = workloads.make_decode_case(cfg, pool="poison", kv_format="fp8")
+    ks, vs = _scales(cfg.num_kv_heads, 3)
+    dc = DeviceCase(case, ks, vs)
+    try:
+        dc.write()
+        dc.attend(split_tokens=64)
+        torch.cuda.synchronize()
+        out1 = dev_to_bits(dc.out)
+        pi = np.random.default_rng(9).permutation(case.num_blocks)
+        kp, vp = _codes(dc.k_pool), _codes(dc.v_pool)
+        kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+        kp2[pi] = kp
+        vp2[pi] = vp
+        t2 = np.where(case.block_table >= 0, pi[np.maximum(case.block_table, 0)], -1).astype(np.int32)
+        dc.k_pool.copy_(codes_to_dev(kp2))
+        dc.v_pool.copy_(codes_to_dev(vp2))
+        dc.table.copy_(torch.from_numpy(t2))
+        dc.attend(split_tokens=64)
+        torch.cuda.synchronize()
+        assert np.array_equal(dev_to_bits(dc.out), out1)
+    finally:
+        dc.close()
+
+
+def test_fp8_gather_bit_exact():
+    cfg = workloads.CONFIGS["qwen3_1p7b"]
+    case = workloads.make_decode_case(cfg, pool="poison", kv_format="fp8")
+    dc = DeviceCase(case)
+    try:
+        dc.write()
+        l_max = int(case.context_lens.max()) + 1
+        ko = torch.full((dc.B, dc.Hkv, l_max, dc.D), 0xA5, dtype=torch.uint8, device=DEV)
+        vo = ko.clone()
+        mk.mi_gather_kv(dc.pool, dc.table, dc.mbps, dc.ctx, dc.B, 1, ko, vo, l_max)
+        torch.cuda.synchronize()
+        ko, vo = _codes(ko), _codes(vo)
+        kp, vp = _codes(dc.k_pool), _codes(dc.v_pool)
+        for b in range(dc.B):
+            n = int(case.context_lens[b]) + 1
+            for g in range(dc.Hkv):
+                ksq, vsq = oatt.gather_kv(kp, vp, case.block_table, 16, b, g, n)
+                assert np.array_equal(ko[b, g, :n], ksq)
+                assert np.array_equal(vo[b, g, :n], vsq)
+                assert np.all(ko[b, g, n:] == 0xA5)
+        assert dc.faults() == 0
+    finally:
+        dc.close()
+
+
+def test_fp8_long_context_full_size_sampled():
+    """The long-context workload over an 8-bit cache at full size in the
+    benchmark's launch configuration; sampled (sequence, kv head) pairs from
+    the oracle, which dequantises the codes the GPU wrote."""
+    cfg = workloads.CONFIGS["qwen3_8b_long"]
+    case = workloads.make_decode_case(cfg, pool="poison", kv_format="fp8")
+    _say("fp8 qwen3_8b_long")
+    dc = DeviceCase(case)
+    try:
+        dc.write()
+        dc.attend()
+        torch.cuda.synchronize()
+        out = dev_to_bits(dc.out)
+        assert dc.faults() == 0
+        ctx = case.context_lens
+        ones = np.ones(cfg.num_kv_heads, np.float32)
+        kn, vn, qb, _ = oatt.write_decode_kv_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                                 case.block_table, ctx, 16, cfg.rope_theta,
+                                                 ones, ones)
+        G = cfg.group
+        rng = np.random.default_rng(45)
+        picks = {int(np.argmax(ctx)), int(np.argmin(ctx))} | set(rng.choice(len(ctx), 4, replace=False).tolist())
+        scale = 1.0 / np.sqrt(cfg.head_dim)
+        for b in sorted(picks):
+            g = int(rng.integers(cfg.num_kv_heads))
+            L = int(ctx[b]) + 1
+            ksq, vsq = oatt.gather_kv(kn, vn, case.block_table, 16, b, g, L)
+            K, V = ofp8.dequantize(ksq, 1.0), ofp8.dequantize(vsq, 1.0)
+            ref = np.stack([oatt.attend(obf16.decode(qb[b, h]), K, V, scale)
+                            for h in range(g * G, (g + 1) * G)])
+            check_tolerance(out[b, g * G:(g + 1) * G], ref, "fp8 b=%d g=%d L=%d" % (b, g, L))
+        assert np.all(np.isfinite(bf16_bits_to_f64(out)))
+    finally:
+        dc.close()
+
+
+LAYER_SMALL = workloads.DecodeConfig(
+    "small_layer8", batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+    num_blocks=64, rope_theta=1e4, ctx_draw="fixed", ctx_fixed=(0, 20, 47), seed=11,
+    hidden=256, intermediate=512, rms_eps=1e-6)
+
+
+@pytest.mark.parametrize("cfg_name", ["small", "qwen3_8b_layer"])
+def test_fp8_layer_parity(cfg_name):
+    cfg = LAYER_SMALL if cfg_name == "small" else workloads.CONFIGS["qwen3_8b_layer"]
+    case = workloads.make_decode_case(cfg, pool="poison", kv_format="fp8")
+    w = workloads.make_layer_weights(cfg, std=0.05 if cfg_name == "small" else 0.02)
+    x = workloads.make_layer_input(cfg)
+    ks, vs = _scales(cfg.num_kv_heads, 17)
+    _say("fp8 layer", cfg.name)
+    B = len(case.context_lens)
+    kp, vp = codes_to_dev(case.k_pool), codes_to_dev(case.v_pool)
+    wd = {n: bits_to_dev(a) for n, a in w.items()}
+    xd = bits_to_dev(x)
+    xo = torch.empty_like(xd)
+    table = torch.from_numpy(case.block_table).to(DEV)
+    ctx = torch.from_numpy(case.context_lens).to(DEV)
+    mbps, max_ctx = case.block_table.shape[1], int(case.context_lens.max())
+    pool = mk.mi_kv_pool_init(case.num_blocks, 16, cfg.num_kv_heads, cfg.head_dim, kp, vp,
+                              flags=mk.MI_POOL_KV_FP8)
+    try:
+        mk.mi_kv_pool_set_scales(pool, ks, vs)
+        lc = mk.layer_config(cfg.hidden, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                             cfg.intermediate, cfg.rms_eps, cfg.rope_theta)
+        lw = mk.layer_weights(**wd)
+        need = mk.mi_decoder_layer_workspace_bytes(lc, pool, B, max_ctx)
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        mk.mi_decoder_layer_decode(pool, lc, lw, xd, xo, table, mbps, ctx, B, max_ctx, ws, need)
+        torch.cuda.synchronize()
+        assert mk.mi_kv_pool_check_errors(pool) == 0
+    finally:
+        mk.mi_kv_pool_destroy(pool)
+    ref, kn, vn = olayer.decoder_layer_decode(x, w, case.k_pool, case.v_pool, case.block_table,
+                                              case.context_lens, 16, cfg.num_q_heads,
+                                              cfg.num_kv_heads, cfg.head_dim, cfg.rms_eps,
+                                              cfg.rope_theta, kv_scales=(ks, vs))
+    mx, rel = check_tolerance(dev_to_bits(xo), ref, cfg.name)
+    _say("  max|d| %.3g relL2 %.3g" % (mx, rel))
+    gk, gv = _codes(kp), _codes(vp)
+    slots = np.zeros(case.k_pool.shape[:3], dtype=bool)
+    for b, c in enumerate(case.context_lens):
+        slots[case.block_table[b, c // 16], :, c % 16] = True
+    assert np.array_equal(gk[~slots], case.k_pool[~slots])
+    assert np.array_equal(gv[~slots], case.v_pool[~slots])
+    # the GPU projections accumulate in fp32: new codes within one step of the oracle's
+    assert _code_dist(gk[slots], kn[slots]).max() <= 1
+    assert _code_dist(gv[slots], vn[slots]).max() <= 1

@@ -43,8 +43,8 @@ def fp8_normal_like(rng, shape):
     being the subnormal range), the 3 significand bits are uniform and the
     sign is that of x. Plain bit construction -- no rounding of values -- and
     the NaN patterns 0x7F / 0xFF are never drawn."""
-    x = rng.standard_normal(shape)
-    e = np.clip(np.floor(np.log2(np.maximum(np.abs(x), 1e-30))).astype(np.int64) + 7, 0, 15)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    e = np.clip(np.floor(np.log2(np.maximum(np.abs(x), np.float32(1e-30)))).astype(np.int64) + 7, 0, 15)
     m = rng.integers(0, 8, shape)
     m = np.where((e == 15) & (m == 7), 6, m)
     s = (x < 0).astype(np.int64) << 7
