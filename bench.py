@@ -43,13 +43,18 @@ def recorded_traffic():
 
 
 def _dev(a, torch, dev):
+    if a.dtype == np.uint8:                    # E4M3 codes of an 8-bit cache
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 
 
-def run_attention_bench(args, torch, mk, workloads):
+def run_attention_bench(args, torch, mk, workloads, kv_format="bf16"):
+    """The long-context decode step (write + attention) over a bf16 cache or an
+    8-bit (E4M3, unit scales) cache of the same workload."""
     dev = "cuda:0"
     cfg = workloads.CONFIGS["qwen3_8b_long"]
-    case = workloads.make_decode_case(cfg, pool="bench")
+    case = workloads.make_decode_case(cfg, pool="bench", kv_format=kv_format)
+    kv_elem = 1 if kv_format == "fp8" else 2
     B, Hq, Hkv, D = len(case.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     kp, vp = _dev(case.k_pool, torch, dev), _dev(case.v_pool, torch, dev)
     q, k, v = _dev(case.q, torch, dev), _dev(case.k, torch, dev), _dev(case.v, torch, dev)
@@ -57,7 +62,8 @@ def run_attention_bench(args, torch, mk, workloads):
     table = torch.from_numpy(case.block_table).to(dev)
     ctx = torch.from_numpy(case.context_lens).to(dev)
     mbps, max_ctx = case.block_table.shape[1], int(case.context_lens.max())
-    pool = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp, vp)
+    pool = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp, vp,
+                              flags=mk.MI_POOL_KV_FP8 if kv_elem == 1 else 0)
     ws_bytes = mk.mi_paged_gqa_decode_split_workspace_bytes(pool, B, Hq, max_ctx, args.split)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -94,8 +100,8 @@ def run_attention_bench(args, torch, mk, workloads):
         raise RuntimeError("device fault bits %#x during the benchmark" % faults)
 
     ctx_np = case.context_lens
-    attn_bytes = workloads.attention_bytes(ctx_np, Hq, Hkv, D, 16)
-    write_bytes = workloads.write_bytes(B, Hq, Hkv, D)
+    attn_bytes = workloads.attention_bytes(ctx_np, Hq, Hkv, D, 16, kv_elem_bytes=kv_elem)
+    write_bytes = workloads.write_bytes(B, Hq, Hkv, D, kv_elem_bytes=kv_elem)
     return dict(
         case=case, cfg=cfg, ms_step=ms_step, wall=wall, attn_ms=attn_ms,
         attn_bytes=attn_bytes, step_bytes=attn_bytes + write_bytes,
@@ -256,6 +262,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-layer", action="store_true", help="skip the full-layer step")
     ap.add_argument("--no-small", action="store_true", help="skip the smaller decode workloads")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache variant of the step")
     ap.add_argument("--layer-only", action="store_true",
                     help="time only the full-layer step (for its kernel profile)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -340,6 +347,21 @@ def main():
             "traffic": recorded_traffic(),
         },
     }
+    if not args.no_fp8:
+        r8 = run_attention_bench(args, torch, mk, workloads, kv_format="fp8")
+        ms8 = r8["ms_step"]
+        attn8 = float(np.mean(r8["attn_ms"]))
+        line["kv_fp8"] = {
+            "workload": "same step over an 8-bit E4M3 cache (unit per-head scales)",
+            "ms_per_step": round(ms8, 5),
+            "algorithmic_bytes_per_step": int(r8["step_bytes"]),
+            "GBps": round(r8["step_bytes"] / (ms8 * 1e-3) / 1e9, 1),
+            "hbm_frac": round(r8["step_bytes"] / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "attention_avg_launch_ms": round(attn8, 5),
+            "attention_GBps": round(r8["attn_bytes"] / (attn8 * 1e-3) / 1e9, 1),
+            "attention_hbm_frac": round(r8["attn_bytes"] / (attn8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "step_speedup_vs_bf16": round(ms / ms8, 3),
+        }
     if not args.no_layer:
         try:
             line["layer_step"] = run_layer_bench(args, torch, mk, workloads)

@@ -694,15 +694,25 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
 }
 
 // Prefetch depth of the attention tile ring and waves per CU of its grid.
-// One wave per SIMD with one tile in flight beyond the one being consumed
-// measured fastest on MI355X (long contexts and short batches alike): more
-// or deeper streams only add pieces to combine.
+// One wave per SIMD with one bf16 tile in flight beyond the one being
+// consumed measured fastest on MI355X (long contexts and short batches
+// alike): more or deeper streams only add pieces to combine. 8-bit tiles are
+// half the bytes, so that cache keeps more of them in flight.
 #ifdef MIKV_TUNE_MFMA_PF
 constexpr int kAttnPrefetch = MIKV_TUNE_MFMA_PF;
 #else
 constexpr int kAttnPrefetch = 1;
 #endif
+#ifdef MIKV_TUNE_FP8_PF
+constexpr int kAttnPrefetchFp8 = MIKV_TUNE_FP8_PF;
+#else
+constexpr int kAttnPrefetchFp8 = 2;
+#endif
+#ifdef MIKV_TUNE_WAVES_PER_CU
+constexpr int kAttnWavesPerCU = MIKV_TUNE_WAVES_PER_CU;
+#else
 constexpr int kAttnWavesPerCU = 4;
+#endif
 
 // Grid of the attention kernel on the current device: CUs x min(waves per
 // CU, resident workgroups per CU at the kernel's register budget), cached
@@ -728,7 +738,7 @@ void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                  float scale_log2, int32_t max_ctx, int32_t min_tiles, float* part_acc,
                  float2* part_ml, hipStream_t st) {
     const int hkv = p->num_kv_heads;
-    auto kern = mikv::pool_fp8(p) ? paged_attn_mfma_kernel<D, G, kFmtFp8, kAttnPrefetch>
+    auto kern = mikv::pool_fp8(p) ? paged_attn_mfma_kernel<D, G, kFmtFp8, kAttnPrefetchFp8>
                                   : paged_attn_mfma_kernel<D, G, kFmtBf16, kAttnPrefetch>;
     const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, attention_waves(kern));
     hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
