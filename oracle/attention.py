@@ -194,3 +194,85 @@ def decode_step_fp8(k_pool8, v_pool8, q, k, v, block_table, context_lens, block_
     out = paged_gqa_decode_fp8(q_rot_bits, k_new, v_new, block_table, context_lens,
                                block_size, k_scales, v_scales, scale)
     return out, k_new, v_new, q_rot_bits
+
+
+# -------------------------------------------------------------------- prefill
+# mini-infer README, "Project overview": prefill runs as its own forward for a
+# request's prompt before the request joins the batched decode steps; course
+# project section 2.1: the inference loop is a prefill stage then a decode
+# stage, with the KV cache appended as tokens are processed. A prefill chunk
+# of sequence b holds n_b new tokens at positions ctx_b .. ctx_b + n_b - 1
+# (ctx_b tokens already cached; 0 for a fresh prompt). The new tokens are
+# packed over the batch: token i of sequence b is row cu[b] + i of q, k, v
+# (cu = prefix sums of n_b). Each new token's K/V is written like a decode
+# step's, and each new token attends causally over positions 0 .. its own.
+
+def _prefill_rows(context_lens, cu_seqlens):
+    """(row, sequence, position) of every packed new token."""
+    out = []
+    for b in range(len(context_lens)):
+        for i in range(int(cu_seqlens[b]), int(cu_seqlens[b + 1])):
+            out.append((i, b, int(context_lens[b]) + i - int(cu_seqlens[b])))
+    return out
+
+
+def write_prefill_kv(k_pool, v_pool, q, k, v, block_table, context_lens, cu_seqlens,
+                     block_size, theta):
+    """Append every new token's rotated K and its V at its position; rotate q.
+
+    q : uint16 [T, Hq, D];  k, v : uint16 [T, Hkv, D]  (packed rows)
+    Returns (k_pool_new, v_pool_new, q_rot_bits [T, Hq, D])."""
+    k_new = np.array(k_pool, dtype=np.uint16, copy=True)
+    v_new = np.array(v_pool, dtype=np.uint16, copy=True)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    q_rot = np.empty((T, Hq, D), dtype=np.float64)
+    for i, b, pos in _prefill_rows(context_lens, cu_seqlens):
+        blk, off = paged.slot(block_table[b], pos, block_size)
+        for g in range(Hkv):
+            k_new[blk, g, off, :] = bf16.encode(rope.apply(bf16.decode(k[i, g]), pos, theta))
+            v_new[blk, g, off, :] = v[i, g]
+        for h in range(Hq):
+            q_rot[i, h] = rope.apply(bf16.decode(q[i, h]), pos, theta)
+    return k_new, v_new, bf16.encode(q_rot)
+
+
+def paged_prefill_attention(q_rot, k_pool, v_pool, block_table, context_lens, cu_seqlens,
+                            block_size, scale=None):
+    """Causal paged GQA attention of the packed new tokens: the token at
+    position p of sequence b attends over positions 0 .. p of its sequence
+    (cached prefix and the new tokens, already written). Returns float64
+    [T, Hq, D]."""
+    qf = bf16.decode(q_rot)
+    T, Hq, D = qf.shape
+    Hkv = k_pool.shape[1]
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(np.float64(D))
+    out = np.empty((T, Hq, D), dtype=np.float64)
+    for b in range(len(context_lens)):
+        lo, hi = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        if hi == lo:
+            continue
+        last = int(context_lens[b]) + hi - lo          # keys of the last new token
+        for g in range(Hkv):
+            ks, vs = gather_kv(k_pool, v_pool, block_table, block_size, b, g, last)
+            K, V = bf16.decode(ks), bf16.decode(vs)
+            for i in range(lo, hi):
+                L = int(context_lens[b]) + i - lo + 1
+                for h in range(g * G, (g + 1) * G):
+                    out[i, h] = attend(qf[i, h], K[:L], V[:L], scale)
+    return out
+
+
+def prefill_step(k_pool, v_pool, q, k, v, block_table, context_lens, cu_seqlens, block_size,
+                 theta, scale=None):
+    """write_prefill_kv followed by paged_prefill_attention.
+    Returns (out_f64, k_pool_new, v_pool_new, q_rot_bits)."""
+    k_new, v_new, q_rot_bits = write_prefill_kv(k_pool, v_pool, q, k, v, block_table,
+                                                context_lens, cu_seqlens, block_size, theta)
+    out = paged_prefill_attention(q_rot_bits, k_new, v_new, block_table, context_lens,
+                                  cu_seqlens, block_size, scale)
+    return out, k_new, v_new, q_rot_bits

@@ -287,3 +287,98 @@ def layer_flops(cfg, context_lens):
     gemm = 2 * B * (H * (Hq + 2 * Hkv) * D + Hq * D * H + 3 * H * I)
     L = np.asarray(context_lens, dtype=np.int64) + 1
     return gemm + 4 * Hq * D * int(L.sum())
+
+
+# -------------------------------------------------------------------- prefill
+@dataclass
+class PrefillCase:
+    """One prefill chunk per sequence: n_b new tokens after ctx_b cached ones.
+    q, k, v are packed over the batch ([T, H, D], rows cu[b] .. cu[b+1])."""
+    cfg: DecodeConfig
+    context_lens: np.ndarray      # int32 [B], tokens cached before the chunk
+    new_lens: np.ndarray          # int32 [B]
+    cu_seqlens: np.ndarray        # int32 [B + 1]
+    block_table: np.ndarray       # int32 [B, MB], -1 padded
+    num_blocks: int
+    q: np.ndarray                 # [T, Hq, D]
+    k: np.ndarray                 # [T, Hkv, D]
+    v: np.ndarray
+    k_pool: np.ndarray            # [N, Hkv, bs, D]
+    v_pool: np.ndarray
+
+
+PREFILL_CONFIGS = {
+    "prefill_small": (DecodeConfig("prefill_small", batch=4, num_q_heads=8, num_kv_heads=2,
+                                   head_dim=64, block_size=16, num_blocks=64, rope_theta=1e4,
+                                   ctx_draw="fixed", seed=61),
+                      (0, 5, 40, 16), (37, 1, 16, 50)),
+    "qwen3_8b_prefill": (DecodeConfig("qwen3_8b_prefill", batch=4, num_q_heads=32,
+                                      num_kv_heads=8, head_dim=128, block_size=16,
+                                      num_blocks=4096, rope_theta=1e6, ctx_draw="fixed",
+                                      seed=62),
+                         None, None),
+}
+
+
+def make_prefill_case(cfg, context_lens, new_lens, pool="poison", seed=None):
+    """Draw a prefill chunk. pool = "poison": cached slots [0, ctx) hold N(0,1);
+    the slots the chunk will write, the tail and unallocated blocks hold NaN.
+    pool = "bench": every slot of the allocated blocks holds N(0,1)."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    ctx = np.asarray(context_lens, dtype=np.int32)
+    n = np.asarray(new_lens, dtype=np.int32)
+    B, Hq, Hkv, D, bs = len(ctx), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(n)
+    T = int(cu[-1])
+    total = ctx + n
+    need = [nblocks(t, bs) for t in total]
+    N = cfg.num_blocks
+    table = np.full((B, max(max(need), 1)), -1, dtype=np.int32)
+    perm = rng.permutation(N).astype(np.int32)
+    pos = 0
+    for b, m in enumerate(need):
+        table[b, :m] = perm[pos:pos + m]
+        pos += m
+    if pos > N:
+        raise ValueError("pool too small for the drawn contexts")
+    q = bf16_normal(rng, (T, Hq, D))
+    k = bf16_normal(rng, (T, Hkv, D))
+    v = bf16_normal(rng, (T, Hkv, D))
+    shape = (N, Hkv, bs, D)
+    fill = NAN_BF16 if pool == "poison" else np.uint16(0)
+    k_pool = np.full(shape, fill, dtype=np.uint16)
+    v_pool = np.full(shape, fill, dtype=np.uint16)
+    ids = np.concatenate([table[b, :need[b]] for b in range(B)])
+    k_pool[ids] = bf16_normal(rng, (len(ids), Hkv, bs, D))
+    v_pool[ids] = bf16_normal(rng, (len(ids), Hkv, bs, D))
+    if pool == "poison":
+        for b in range(B):
+            for p in range(int(ctx[b]), need[b] * bs):
+                blk = table[b, p // bs]
+                k_pool[blk, :, p % bs, :] = NAN_BF16
+                v_pool[blk, :, p % bs, :] = NAN_BF16
+    return PrefillCase(cfg, ctx, n, cu, table, N, q, k, v, k_pool, v_pool)
+
+
+def prefill_flops(context_lens, new_lens, num_q_heads, head_dim):
+    """Multiply-add flops of the causal attention of a prefill chunk: each new
+    token at position p scores and weights p + 1 keys (2 * 2 * D per key and
+    query head)."""
+    tot = 0
+    for c, n in zip(context_lens, new_lens):
+        c, n = int(c), int(n)
+        tot += n * c + n * (n + 1) // 2          # sum over new tokens of (p + 1)
+    return 4 * head_dim * num_q_heads * tot
+
+
+def prefill_attention_bytes(context_lens, new_lens, num_q_heads, num_kv_heads, head_dim,
+                            block_size):
+    """Minimum HBM bytes of the prefill attention: each sequence's K and V of
+    its ctx + n tokens once per kv head, q in and out once, table entries."""
+    tot = 0
+    for c, n in zip(context_lens, new_lens):
+        L = int(c) + int(n)
+        tot += 4 * num_kv_heads * head_dim * L + 4 * int(n) * num_q_heads * head_dim
+        tot += 4 * nblocks(L, block_size)
+    return tot + 8 * len(context_lens)
