@@ -210,6 +210,48 @@ int mi_write_decode_kv(mi_kv_pool_t pool,
                        int32_t num_q_heads, double rope_theta, void* stream);
 
 /*
+ * Prefill write (mini-infer README: prefill runs as its own forward before a
+ * request joins the batched decode steps; course project 2.1: prefill stage,
+ * then decode, appending to the KV cache). One chunk of n_b new tokens per
+ * sequence b at positions context_lens[b] .. context_lens[b] + n_b - 1,
+ * packed over the batch:
+ *  q      device bf16 [total_tokens, num_q_heads, head_dim]
+ *  k, v   device bf16 [total_tokens, num_kv_heads, head_dim]
+ *  q_rot  device bf16 [total_tokens, num_q_heads, head_dim]; may alias q
+ *  cu_seqlens  device int32 [batch + 1]: 0 = cu[0] <= cu[1] <= ... <= cu[batch]
+ *         = total_tokens; row i of q/k/v with cu[b] <= i < cu[b+1] is new token
+ *         i - cu[b] of sequence b.
+ *  context_lens  device int32 [batch]: tokens cached before the chunk.
+ * Every new token gets the same RoPE, rounding and store as
+ * mi_write_decode_kv at its position; the table row must cover
+ * context_lens[b] + n_b tokens. 8-bit pools: MI_ERR_UNSUPPORTED.
+ */
+int mi_write_prefill_kv(mi_kv_pool_t pool, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, uint16_t* q_rot, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens,
+                        const int32_t* cu_seqlens, int32_t batch, int32_t total_tokens,
+                        int32_t num_q_heads, double rope_theta, void* stream);
+
+/*
+ * Causal paged GQA attention of a prefill chunk (after mi_write_prefill_kv):
+ * the new token at position p of sequence b attends over positions 0 .. p of
+ * that sequence through its block table (cached prefix and the chunk),
+ *     out[i,h] = sum_{t <= p} softmax(scale * <q_rot[i,h], K[slot(b,t), g]>)_t V[slot(b,t), g]
+ * with g = h / (num_q_heads / num_kv_heads). fp32 accumulation on MFMA, one
+ * rounding to bf16 (same arithmetic as mi_paged_gqa_decode, no split).
+ *  q_rot, out  device bf16 [total_tokens, num_q_heads, head_dim], no aliasing
+ *  max_new_tokens  host-side bound of every n_b (sizes the grid); a larger
+ *         n_b, cu beyond total_tokens or a chunk past the table row is a fault
+ *         (error word) and that sequence's rows are not written.
+ *  batch <= 65535. 8-bit pools: MI_ERR_UNSUPPORTED. No workspace.
+ */
+int mi_paged_prefill_attention(mi_kv_pool_t pool, const uint16_t* q_rot, uint16_t* out,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, const int32_t* cu_seqlens,
+                               int32_t batch, int32_t total_tokens, int32_t max_new_tokens,
+                               int32_t num_q_heads, float softmax_scale, void* stream);
+
+/*
  * Workspace bytes needed by mi_paged_gqa_decode for this batch when every
  * context_lens[b] <= max_context_len (fp32 split-K partials plus padding).
  */

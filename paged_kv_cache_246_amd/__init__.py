@@ -58,6 +58,10 @@ SIGNATURES = {
     "mi_paged_gqa_decode_split": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                              _c.c_float, _i32, _i32, _vp, _sz, _vp]),
     "mi_paged_gqa_decode_split_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32]),
+    "mi_write_prefill_kv": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                       _i32, _c.c_double, _vp]),
+    "mi_paged_prefill_attention": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                              _i32, _i32, _c.c_float, _vp]),
     "mi_gather_kv": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp]),
     "mi_decoder_layer_workspace_bytes": (_sz, [_vp, _vp, _i32, _i32]),
     "mi_decoder_layer_decode": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
@@ -244,6 +248,23 @@ def mi_paged_gqa_decode_split(pool, q_rot, out, block_table, max_blocks_per_seq,
         pool, _ptr(q_rot), _ptr(out), _ptr(block_table), max_blocks_per_seq,
         _ptr(context_lens), batch, num_q_heads, float(softmax_scale), max_context_len,
         split_tokens, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mi_write_prefill_kv(pool, q, k, v, q_rot, block_table, max_blocks_per_seq, context_lens,
+                        cu_seqlens, batch, total_tokens, num_q_heads, rope_theta, stream=None):
+    return _check("mi_write_prefill_kv", lib().mi_write_prefill_kv(
+        pool, _ptr(q), _ptr(k), _ptr(v), _ptr(q_rot), _ptr(block_table), max_blocks_per_seq,
+        _ptr(context_lens), _ptr(cu_seqlens), batch, total_tokens, num_q_heads, rope_theta,
+        _stream(stream)))
+
+
+def mi_paged_prefill_attention(pool, q_rot, out, block_table, max_blocks_per_seq, context_lens,
+                               cu_seqlens, batch, total_tokens, max_new_tokens, num_q_heads,
+                               softmax_scale=0.0, stream=None):
+    return _check("mi_paged_prefill_attention", lib().mi_paged_prefill_attention(
+        pool, _ptr(q_rot), _ptr(out), _ptr(block_table), max_blocks_per_seq, _ptr(context_lens),
+        _ptr(cu_seqlens), batch, total_tokens, max_new_tokens, num_q_heads, softmax_scale,
+        _stream(stream)))
 
 
 def mi_gather_kv(pool, block_table, max_blocks_per_seq, context_lens, batch, len_extra, k_out,

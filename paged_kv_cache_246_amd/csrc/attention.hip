@@ -71,16 +71,32 @@ __device__ __forceinline__ uint4 ld16_stream(const char* base, uint32_t off) {
 constexpr int kFmtBf16 = 0;
 constexpr int kFmtFp8 = 1;
 
-template <int D, int FMT>
+// With PREFILL the rows of q, k, v are the packed new tokens of a prefill
+// chunk (grid.x = total tokens): row i belongs to the sequence b with
+// cu[b] <= i < cu[b + 1] and sits at position ctx_b + i - cu[b].
+template <int D, int FMT, bool PREFILL>
 __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* q_rot, void* __restrict__ kc, void* __restrict__ vc,
     const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
-    int32_t hq, int32_t hkv, int32_t num_blocks, mikv::RopeTable rope,
-    const float* __restrict__ kv_scales, uint32_t* __restrict__ err) {
+    const int32_t* __restrict__ cu, int32_t batch, int32_t hq, int32_t hkv, int32_t num_blocks,
+    mikv::RopeTable rope, const float* __restrict__ kv_scales, uint32_t* __restrict__ err) {
     constexpr int H2 = D / 2;
-    const int b = blockIdx.x;
-    const int pos = ctx_lens[b];
+    const int row = blockIdx.x;               // row of q, k, v
+    int b = row;
+    int pos = 0;
+    if constexpr (PREFILL) {
+        int lo = 0, hi = batch - 1;           // last b with cu[b] <= row
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cu[mid] <= row) lo = mid;
+            else hi = mid - 1;
+        }
+        b = lo;
+        pos = ctx_lens[b] + row - cu[b];
+    } else {
+        pos = ctx_lens[b];
+    }
     const bool pos_ok = pos >= 0 && pos / BS < mbps;
     const int32_t blk = pos_ok ? table[static_cast<size_t>(b) * mbps + pos / BS] : -1;
     const bool blk_ok = pos_ok && blk >= 0 && blk < num_blocks;
@@ -97,8 +113,8 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
         const int i = idx - h * H2;
         if (h >= hq && !blk_ok) return;
         const int g = h - hq;
-        const uint16_t* src = h < hq ? q + (static_cast<size_t>(b) * hq + h) * D
-                                     : k + (static_cast<size_t>(b) * hkv + g) * D;
+        const uint16_t* src = h < hq ? q + (static_cast<size_t>(row) * hq + h) * D
+                                     : k + (static_cast<size_t>(row) * hkv + g) * D;
         const double x1 = bf16_to_f64(src[i]);
         const double x2 = bf16_to_f64(src[i + H2]);
         const double a = static_cast<double>(pos) * rope.inv_freq[i];
@@ -109,17 +125,17 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
         const uint16_t r1 = f64_to_bf16_rne(y1);
         const uint16_t r2 = f64_to_bf16_rne(y2);
         if (h < hq) {
-            uint16_t* dst = q_rot + (static_cast<size_t>(b) * hq + h) * D;
+            uint16_t* dst = q_rot + (static_cast<size_t>(row) * hq + h) * D;
             dst[i] = r1;
             dst[i + H2] = r2;
         } else {
-            const size_t row = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
+            const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
             if constexpr (FMT == kFmtBf16) {
-                uint16_t* dst = static_cast<uint16_t*>(kc) + row;
+                uint16_t* dst = static_cast<uint16_t*>(kc) + at;
                 dst[i] = r1;
                 dst[i + H2] = r2;
             } else {
-                uint8_t* dst = static_cast<uint8_t*>(kc) + row;
+                uint8_t* dst = static_cast<uint8_t*>(kc) + at;
                 const float s = kv_scales[g];
                 dst[i] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, s));
                 dst[i + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, s));
@@ -131,7 +147,7 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
         if (piece >= hkv * (D / 8)) return;
         const int g = piece / (D / 8);
         const int e = (piece - g * (D / 8)) * 8;
-        const uint4 val = *reinterpret_cast<const uint4*>(v + (static_cast<size_t>(b) * hkv + g) * D + e);
+        const uint4 val = *reinterpret_cast<const uint4*>(v + (static_cast<size_t>(row) * hkv + g) * D + e);
         const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D + e;
         if constexpr (FMT == kFmtBf16)
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(vc) + at) = val;
@@ -303,12 +319,17 @@ struct MfmaSoftmax {
     float l;      // this lane's sum of 2^(s - m)
 };
 
+// One 16-token tile. Column n (query head in decode, query token in
+// prefill) is live if col_ok. With tail set, key row t of the tile counts for
+// column n only if t < qlim (the lane's column limit: the rows written so far
+// in decode, the causal limit in prefill), and V rows t >= valid_rows are
+// zeroed (their bits may be NaN).
 template <int D, int FMT, int NPV = MfmaTile<D, FMT>::NPV>
 __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>::NKL],
                                              uint32_t (&vr)[4][MfmaTile<D, FMT>::VW],
                                              const uint4 (&qb)[MfmaTile<D, FMT>::NQK], float sl2,
-                                             bool head_ok, int q4, int valid_rows, bool tail,
-                                             MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
+                                             bool col_ok, int q4, int qlim, int valid_rows,
+                                             bool tail, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
     using TL = MfmaTile<D, FMT>;
     // ---- scores of tokens 4q4 .. 4q4+3 for head n
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -331,7 +352,7 @@ __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>:
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         sc[i] = s[i] * sl2;
-        const bool ok = head_ok && (!tail || 4 * q4 + i < valid_rows);
+        const bool ok = col_ok && (!tail || 4 * q4 + i < qlim);
         sc[i] = ok ? sc[i] : kNegInf;
     }
     const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -410,28 +431,29 @@ struct MfmaRing {
     }
     template <int U>
     __device__ __forceinline__ void steady(int i, int nblk, const uint4 (&qb)[TL::NQK], float sl2,
-                                           bool head_ok, int q4, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
+                                           bool col_ok, int q4, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
         if constexpr (U <= PF) {
             load<(U + PF) % (PF + 1)>(min(i + U + PF, nblk - 1));
-            mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, head_ok, q4, BS, false, sm, o);
-            steady<U + 1>(i, nblk, qb, sl2, head_ok, q4, sm, o);
+            mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, col_ok, q4, BS, BS, false, sm, o);
+            steady<U + 1>(i, nblk, qb, sl2, col_ok, q4, sm, o);
         }
     }
     template <int U>
     __device__ __forceinline__ void rest(int i, int nblk, int valid_rows, const uint4 (&qb)[TL::NQK],
-                                         float sl2, bool head_ok, int q4, MfmaSoftmax& sm,
+                                         float sl2, bool col_ok, int q4, MfmaSoftmax& sm,
                                          f32x4_t (&o)[NPV]) {
         if constexpr (U <= PF) {
             const int tile = i + U;
             if (tile < nblk - 1) {
-                mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, head_ok, q4, BS, false, sm, o);
+                mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, col_ok, q4, BS, BS, false, sm, o);
             } else if (tile == nblk - 1) {
                 if (valid_rows == BS)
-                    mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, head_ok, q4, BS, false, sm, o);
+                    mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, col_ok, q4, BS, BS, false, sm, o);
                 else
-                    mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, head_ok, q4, valid_rows, true, sm, o);
+                    mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, col_ok, q4, valid_rows, valid_rows,
+                                         true, sm, o);
             }
-            rest<U + 1>(i, nblk, valid_rows, qb, sl2, head_ok, q4, sm, o);
+            rest<U + 1>(i, nblk, valid_rows, qb, sl2, col_ok, q4, sm, o);
         }
     }
 };
@@ -564,6 +586,131 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
         }
         pos += t1 - t0;
         first_piece = false;
+    }
+}
+
+// ======================================================== paged prefill
+// Causal attention of a prefill chunk (packed rows, see the PREFILL write).
+// One wave per (block of 16 new tokens, query head): the MFMA tile of the
+// decode kernel with the 16 columns taken by the block's query tokens
+// instead of the group's heads. The wave streams its sequence's K/V tiles
+// 0 .. last in logical order; tiles whose keys all lie at or before the
+// block's first position are unmasked and go through the register ring, the
+// one or two tiles on the diagonal follow with a per-column causal limit.
+// Blocks are issued longest first (largest key range).
+template <int D, int G, int FMT, int PF>
+__global__ __launch_bounds__(64) void paged_prefill_kernel(
+    const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
+    const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu, int32_t hkv,
+    int32_t num_blocks, int32_t total, int32_t max_new, float scale_log2,
+    const float* __restrict__ kv_scales, uint16_t* __restrict__ out, uint32_t* __restrict__ err) {
+    using TL = MfmaTile<D, FMT>;
+    constexpr int NPV = TL::NPV;
+    constexpr size_t TILE = static_cast<size_t>(BS) * TL::ROW;
+    const int lane = threadIdx.x;
+    const int n = lane & 15;
+    const int q4 = lane >> 4;
+    const int h = blockIdx.y;
+    const int b = blockIdx.z;
+    const int g = h / G;
+    const int row0 = cu[b];
+    const int nnew = cu[b + 1] - row0;
+    const int ctx = ctx_lens[b];
+    if (row0 < 0 || nnew < 0 || row0 + nnew > total || nnew > max_new || ctx < 0 ||
+        ctx + nnew > mbps * BS) {
+        if (blockIdx.x == 0 && h == 0 && lane == 0)
+            atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+        return;
+    }
+    const int nqb = (nnew + BS - 1) / BS;
+    if (static_cast<int>(blockIdx.x) >= nqb) return;
+    const int qb = nqb - 1 - static_cast<int>(blockIdx.x);
+    const int j = qb * BS + n;                   // this lane's query token
+    const bool col_ok = j < nnew;
+    const int p_first = ctx + qb * BS;
+    const int p_last = ctx + min(qb * BS + BS, nnew) - 1;
+    const int p_n = ctx + j;
+    const int nkt = p_last / BS + 1;             // tiles holding keys 0 .. p_last
+    const int kt_m = (p_first + 1) / BS;         // tiles below are unmasked for every query
+
+    uint4 qb_op[TL::NQK];
+    const uint16_t* qh = q_rot + (static_cast<size_t>(row0 + (col_ok ? j : 0)) * hkv * G + h) * D;
+#pragma unroll
+    for (int jj = 0; jj < TL::NQK; ++jj) {
+        const int d0 = FMT == kFmtBf16 ? 32 * jj + 8 * q4 : 64 * (jj / 2) + 16 * q4 + 8 * (jj & 1);
+        qb_op[jj] = col_ok ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
+    }
+    float sl2 = scale_log2;
+    float vscale = 1.f;
+    if constexpr (FMT == kFmtFp8) {
+        sl2 *= kv_scales[g];
+        vscale = kv_scales[hkv + g];
+    }
+    MfmaSoftmax sm{col_ok ? kNegInf : 0.f, 0.f};
+    f32x4_t o[NPV];
+#pragma unroll
+    for (int jj = 0; jj < NPV; ++jj) o[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    MfmaRing<D, FMT, PF> ring;
+    ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
+    ring.vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
+    ring.blk_stride = static_cast<size_t>(hkv) * TILE;
+#pragma unroll
+    for (int jj = 0; jj < TL::NKL; ++jj) ring.koff[jj] = n * TL::ROW + 64 * jj + 16 * q4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ring.voff[r] = (4 * q4 + r) * TL::ROW + TL::VB * n;
+
+    // block ids of the sub-chunk starting at tile s0 (lane i: tile s0 + i)
+    auto fetch_ids = [&](int s0, int cnt) {
+        int32_t id = 0;
+        if (lane < cnt) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
+        const bool bad_id = lane < cnt && (id < 0 || id >= num_blocks);
+        if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+        ring.my_id = bad_id ? 0 : id;
+    };
+    // unmasked tiles [0, kt_m) through the ring, 64 per sub-chunk
+    for (int s0 = 0; s0 < kt_m; s0 += 64) {
+        const int nblk = min(64, kt_m - s0);
+        fetch_ids(s0, nblk);
+        ring.template prologue<0>(nblk);
+        int i = 0;
+        for (; i + PF + 1 < nblk; i += PF + 1)
+            ring.template steady<0>(i, nblk, qb_op, sl2, col_ok, q4, sm, o);
+        ring.template load<PF>(min(i + PF, nblk - 1));
+        ring.template rest<0>(i, nblk, BS, qb_op, sl2, col_ok, q4, sm, o);
+    }
+    // the diagonal tiles [kt_m, nkt) (one or two), causal limit per column
+    fetch_ids(kt_m, nkt - kt_m);
+    ring.template load<0>(0);
+    if (nkt - kt_m > 1) ring.template load<1>(1);
+    for (int t = 0; t < nkt - kt_m; ++t) {
+        const int base = (kt_m + t) * BS;
+        const int qlim = min(BS, max(0, p_n + 1 - base));
+        const int vrows = min(BS, p_last + 1 - base);
+        if (t == 0)
+            mfma_consume<D, FMT>(ring.kr[0], ring.vr[0], qb_op, sl2, col_ok, q4, qlim, vrows, true, sm, o);
+        else
+            mfma_consume<D, FMT>(ring.kr[1], ring.vr[1], qb_op, sl2, col_ok, q4, qlim, vrows, true, sm, o);
+    }
+
+    float lt = sm.l + __shfl_xor(sm.l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (col_ok) {
+        const float inv = vscale / lt;
+        uint16_t* oh = out + (static_cast<size_t>(row0 + j) * hkv * G + h) * D + NPV * 4 * q4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint32_t wd[NPV / 2];
+#pragma unroll
+            for (int e = 0; e < NPV / 2; ++e)
+                wd[e] = static_cast<uint32_t>(f32_to_bf16_rne(o[2 * e][r] * inv)) |
+                        (static_cast<uint32_t>(f32_to_bf16_rne(o[2 * e + 1][r] * inv)) << 16);
+            if constexpr (NPV == 8)
+                *reinterpret_cast<uint4*>(oh + NPV * r) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            else
+                *reinterpret_cast<uint2*>(oh + NPV * r) = make_uint2(wd[0], wd[1]);
+        }
     }
 }
 
@@ -773,6 +920,42 @@ int dispatch_group(int G, const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t
 #undef MIKV_G
 }
 
+template <int D, int G>
+void launch_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                    const int32_t* table, int32_t mbps, const int32_t* ctx, const int32_t* cu,
+                    int32_t batch, int32_t total, int32_t max_new, float scale_log2, hipStream_t st) {
+    const int hkv = p->num_kv_heads;
+    auto kern = mikv::pool_fp8(p) ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8>
+                                  : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch>;
+    const dim3 grid((max_new + BS - 1) / BS, hkv * G, batch);
+    hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
+                       static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, hkv, p->num_blocks,
+                       total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err);
+}
+
+template <int D>
+int dispatch_prefill(int G, const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                     const int32_t* table, int32_t mbps, const int32_t* ctx, const int32_t* cu,
+                     int32_t batch, int32_t total, int32_t max_new, float scale_log2, hipStream_t st) {
+#define MIKV_G(GG)                                                                             \
+    case GG:                                                                                   \
+        launch_prefill<D, GG>(p, q_rot, out, table, mbps, ctx, cu, batch, total, max_new,     \
+                              scale_log2, st);                                                 \
+        return MI_OK;
+    switch (G) {
+        MIKV_G(1)
+        MIKV_G(2)
+        MIKV_G(3)
+        MIKV_G(4)
+        MIKV_G(5)
+        MIKV_G(6)
+        MIKV_G(7)
+        MIKV_G(8)
+        default: return MI_ERR_UNSUPPORTED;
+    }
+#undef MIKV_G
+}
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
@@ -807,10 +990,30 @@ int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint1
     const dim3 grid(batch, (items + 255) / 256);
     const RopeTable rope = make_rope_table(theta, p->head_dim);
     const bool f8 = pool_fp8(p);
-    auto kern = p->head_dim == 128 ? (f8 ? write_decode_kv_kernel<128, kFmtFp8> : write_decode_kv_kernel<128, kFmtBf16>)
-                                   : (f8 ? write_decode_kv_kernel<64, kFmtFp8> : write_decode_kv_kernel<64, kFmtBf16>);
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, k, v, q_rot, p->k, p->v, table, mbps, ctx, hq,
-                       hkv, p->num_blocks, rope, static_cast<const float*>(p->scales), p->err);
+    auto kern = p->head_dim == 128
+                    ? (f8 ? write_decode_kv_kernel<128, kFmtFp8, false> : write_decode_kv_kernel<128, kFmtBf16, false>)
+                    : (f8 ? write_decode_kv_kernel<64, kFmtFp8, false> : write_decode_kv_kernel<64, kFmtBf16, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, k, v, q_rot, p->k, p->v, table, mbps, ctx,
+                       static_cast<const int32_t*>(nullptr), batch, hq, hkv, p->num_blocks, rope,
+                       static_cast<const float*>(p->scales), p->err);
+    return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+int launch_write_prefill_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, uint16_t* q_rot, const int32_t* table, int32_t mbps,
+                            const int32_t* ctx, const int32_t* cu, int32_t batch, int32_t tokens,
+                            int32_t hq, double theta, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int hkv = p->num_kv_heads;
+    const int items = (hq + hkv) * (p->head_dim / 2) + hkv * (p->head_dim / 8);
+    const dim3 grid(tokens, (items + 255) / 256);
+    const RopeTable rope = make_rope_table(theta, p->head_dim);
+    const bool f8 = pool_fp8(p);
+    auto kern = p->head_dim == 128
+                    ? (f8 ? write_decode_kv_kernel<128, kFmtFp8, true> : write_decode_kv_kernel<128, kFmtBf16, true>)
+                    : (f8 ? write_decode_kv_kernel<64, kFmtFp8, true> : write_decode_kv_kernel<64, kFmtBf16, true>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, k, v, q_rot, p->k, p->v, table, mbps, ctx, cu,
+                       batch, hq, hkv, p->num_blocks, rope, static_cast<const float*>(p->scales), p->err);
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 
@@ -838,6 +1041,22 @@ int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 
+int launch_paged_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                         const int32_t* table, int32_t mbps, const int32_t* ctx, const int32_t* cu,
+                         int32_t batch, int32_t total, int32_t max_new, int32_t hq, float scale,
+                         void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int G = hq / p->num_kv_heads;
+    const float scale_log2 = scale * 1.4426950408889634f;
+    const int rc = p->head_dim == 128
+                       ? dispatch_prefill<128>(G, p, q_rot, out, table, mbps, ctx, cu, batch, total,
+                                               max_new, scale_log2, st)
+                       : dispatch_prefill<64>(G, p, q_rot, out, table, mbps, ctx, cu, batch, total,
+                                              max_new, scale_log2, st);
+    if (rc != MI_OK) return rc;
+    return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
 }  // namespace mikv
 
 // ============================================================== C entry points
@@ -861,6 +1080,36 @@ extern "C" int mi_write_decode_kv(mi_kv_pool_t p, const uint16_t* q, const uint1
     if (batch == 0) return MI_OK;
     if (!q || !k || !v || !q_rot || !table || !ctx || !(theta > 0.0)) return MI_ERR_INVALID_ARG;
     return mikv::launch_write_decode_kv(p, q, k, v, q_rot, table, mbps, ctx, batch, hq, theta, stream);
+}
+
+extern "C" int mi_write_prefill_kv(mi_kv_pool_t p, const uint16_t* q, const uint16_t* k,
+                                   const uint16_t* v, uint16_t* q_rot, const int32_t* table,
+                                   int32_t mbps, const int32_t* ctx, const int32_t* cu, int32_t batch,
+                                   int32_t total_tokens, int32_t hq, double theta, void* stream) {
+    int rc = check_common(p, batch, hq, mbps);
+    if (rc != MI_OK) return rc;
+    if (total_tokens < 0) return MI_ERR_INVALID_ARG;
+    if (mikv::pool_fp8(p)) return MI_ERR_UNSUPPORTED;
+    if (batch == 0 || total_tokens == 0) return MI_OK;
+    if (!q || !k || !v || !q_rot || !table || !ctx || !cu || !(theta > 0.0)) return MI_ERR_INVALID_ARG;
+    return mikv::launch_write_prefill_kv(p, q, k, v, q_rot, table, mbps, ctx, cu, batch, total_tokens,
+                                         hq, theta, stream);
+}
+
+extern "C" int mi_paged_prefill_attention(mi_kv_pool_t p, const uint16_t* q_rot, uint16_t* out,
+                                          const int32_t* table, int32_t mbps, const int32_t* ctx,
+                                          const int32_t* cu, int32_t batch, int32_t total_tokens,
+                                          int32_t max_new_tokens, int32_t hq, float scale,
+                                          void* stream) {
+    int rc = check_common(p, batch, hq, mbps);
+    if (rc != MI_OK) return rc;
+    if (total_tokens < 0 || max_new_tokens < 0 || batch > 65535) return MI_ERR_INVALID_ARG;
+    if (mikv::pool_fp8(p)) return MI_ERR_UNSUPPORTED;
+    if (batch == 0 || total_tokens == 0 || max_new_tokens == 0) return MI_OK;
+    if (!q_rot || !out || !table || !ctx || !cu || q_rot == out) return MI_ERR_INVALID_ARG;
+    if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(p->head_dim));
+    return mikv::launch_paged_prefill(p, q_rot, out, table, mbps, ctx, cu, batch, total_tokens,
+                                      max_new_tokens, hq, scale, stream);
 }
 
 extern "C" size_t mi_paged_gqa_decode_split_workspace_bytes(mi_kv_pool_t p, int32_t batch,

@@ -71,6 +71,14 @@ int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint1
                            const uint16_t* v, uint16_t* q_rot, const int32_t* table,
                            int32_t mbps, const int32_t* ctx, int32_t batch, int32_t hq,
                            double theta, void* stream);
+int launch_write_prefill_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, uint16_t* q_rot, const int32_t* table, int32_t mbps,
+                            const int32_t* ctx, const int32_t* cu, int32_t batch, int32_t tokens,
+                            int32_t hq, double theta, void* stream);
+int launch_paged_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                         const int32_t* table, int32_t mbps, const int32_t* ctx, const int32_t* cu,
+                         int32_t batch, int32_t total, int32_t max_new, int32_t hq, float scale,
+                         void* stream);
 int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                             const int32_t* table, int32_t mbps, const int32_t* ctx,
                             int32_t batch, int32_t hq, float scale, int32_t max_ctx,

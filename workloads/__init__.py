@@ -320,10 +320,11 @@ PREFILL_CONFIGS = {
 }
 
 
-def make_prefill_case(cfg, context_lens, new_lens, pool="poison", seed=None):
+def make_prefill_case(cfg, context_lens, new_lens, pool="poison", seed=None, reserve=0):
     """Draw a prefill chunk. pool = "poison": cached slots [0, ctx) hold N(0,1);
     the slots the chunk will write, the tail and unallocated blocks hold NaN.
-    pool = "bench": every slot of the allocated blocks holds N(0,1)."""
+    pool = "bench": every slot of the allocated blocks holds N(0,1). The block
+    tables cover ctx + n + reserve tokens (reserve: room for decode steps)."""
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
     ctx = np.asarray(context_lens, dtype=np.int32)
     n = np.asarray(new_lens, dtype=np.int32)
@@ -331,7 +332,7 @@ def make_prefill_case(cfg, context_lens, new_lens, pool="poison", seed=None):
     cu = np.zeros(B + 1, dtype=np.int32)
     cu[1:] = np.cumsum(n)
     T = int(cu[-1])
-    total = ctx + n
+    total = ctx + n + int(reserve)
     need = [nblocks(t, bs) for t in total]
     N = cfg.num_blocks
     table = np.full((B, max(max(need), 1)), -1, dtype=np.int32)
