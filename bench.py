@@ -110,6 +110,70 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16"):
     )
 
 
+def run_prefill_bench(args, torch, mk, workloads):
+    """Prefill chunk on a Qwen3-8B-shaped layer: 4 fresh prompts of 2048 tokens
+    (packed, 8192 rows): mi_write_prefill_kv + mi_paged_prefill_attention.
+    The causal attention is a dense contraction: reported against the bf16
+    MFMA peak."""
+    dev = "cuda:0"
+    cfg = workloads.PREFILL_CONFIGS["qwen3_8b_prefill"][0]
+    ctx_l, new_l = (0, 0, 0, 0), (2048, 2048, 2048, 2048)
+    case = workloads.make_prefill_case(cfg, ctx_l, new_l, pool="bench")
+    B, T = len(ctx_l), int(case.cu_seqlens[-1])
+    Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    kp, vp = _dev(case.k_pool, torch, dev), _dev(case.v_pool, torch, dev)
+    q, k, v = _dev(case.q, torch, dev), _dev(case.k, torch, dev), _dev(case.v, torch, dev)
+    q_rot, out = torch.empty_like(q), torch.empty_like(q)
+    table = torch.from_numpy(case.block_table).to(dev)
+    ctx = torch.from_numpy(case.context_lens).to(dev)
+    cu = torch.from_numpy(case.cu_seqlens).to(dev)
+    mbps, max_new = case.block_table.shape[1], int(case.new_lens.max())
+    pool = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp, vp)
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+
+    def step(ev=None):
+        mk.mi_write_prefill_kv(pool, q, k, v, q_rot, table, mbps, ctx, cu, B, T, Hq,
+                               cfg.rope_theta, st)
+        if ev is not None:
+            ev[0].record(stream)
+        mk.mi_paged_prefill_attention(pool, q_rot, out, table, mbps, ctx, cu, B, T, max_new, Hq,
+                                      0.0, st)
+        if ev is not None:
+            ev[1].record(stream)
+
+    steps = max(1, args.steps // 5)
+    for _ in range(max(1, args.warmup // 2)):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    faults = mk.mi_kv_pool_check_errors(pool)
+    mk.mi_kv_pool_destroy(pool)
+    if faults:
+        raise RuntimeError("device fault bits %#x during the prefill benchmark" % faults)
+    flops = workloads.prefill_flops(case.context_lens, case.new_lens, Hq, D)
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    return {
+        "workload": "qwen3-8b-shaped prefill, 4 fresh prompts x 2048 tokens (32/8 heads, D 128)",
+        "steps": steps,
+        "ms_per_step": round(ms, 5),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "attention_avg_launch_ms": round(attn_ms, 5),
+        "attention_flops": int(flops),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
+    }
+
+
 def run_small_workloads(args, torch, mk, workloads):
     """Decode step (write + attention) on the other decode workloads: step time,
     algorithmic GB/s and fraction of the HBM peak (most are launch-latency bound)."""
@@ -263,6 +327,7 @@ def main():
     ap.add_argument("--no-layer", action="store_true", help="skip the full-layer step")
     ap.add_argument("--no-small", action="store_true", help="skip the smaller decode workloads")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache variant of the step")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill chunk")
     ap.add_argument("--layer-only", action="store_true",
                     help="time only the full-layer step (for its kernel profile)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -362,6 +427,8 @@ def main():
             "attention_hbm_frac": round(r8["attn_bytes"] / (attn8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "step_speedup_vs_bf16": round(ms / ms8, 3),
         }
+    if not args.no_prefill:
+        line["prefill"] = run_prefill_bench(args, torch, mk, workloads)
     if not args.no_layer:
         try:
             line["layer_step"] = run_layer_bench(args, torch, mk, workloads)
