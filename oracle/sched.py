@@ -1,0 +1,180 @@
+"""Continuous-batching step planner over the paged KV pool: block lifecycle and
+admission with the KV-protection brakes (test infrastructure only).
+
+Pages followed:
+
+* mini-infer README, "Project overview" and "Architecture": a scheduler keeps
+  waiting and running queues; prefill runs as its own forward and the request
+  then joins the batched decode steps; requests are admitted dynamically at
+  every step (continuous batching); the KV cache manager hands out blocks from
+  a free-block pool and each request owns a BlockTable.
+* nxmr.cn inference-techniques article, section 2.1: a request of n tokens
+  holds ceil(n / page_size) pages, popped from the free list.
+* vLLM-based inference-framework project report, "SLO-aware, KV-cache
+  protecting scheduler": before admitting a new prefill it looks at the free
+  KV-cache space. Hard brake: free space below a critical threshold (10 %) ->
+  no new prefill is admitted. Soft brake: decode work is running and free
+  space is below a safety threshold (30 %) -> no new prefill is admitted.
+  Otherwise new requests proceed.
+
+Readings where the pages are silent (the same in the library):
+
+* Free space = free blocks / pool blocks, measured when the admission is
+  considered (after this step's decode growth and after earlier admissions
+  in the same step); "below" is strict (<).
+* A step: (1) retire running requests that have produced max_new_tokens and
+  return their blocks; (2) give every running request the block its decode
+  write needs (position ctx, i.e. ceil((ctx + 1) / 16) blocks), in arrival
+  order; if the pool is empty, preempt the most recently admitted running
+  request (its blocks return to the pool; it goes back to the head of the
+  waiting queue and will be prefilled again over prompt + generated tokens,
+  vLLM's recompute preemption) and retry; (3) admit waiting requests in FIFO
+  order while a running slot is free, no brake holds and the pool has the
+  ceil(prompt / 16) blocks of the prompt; the first request that cannot be
+  admitted stops admission (no overtaking); (4) emit the plan: the admitted
+  prefills (context 0, n = prompt tokens) and the running decodes (context =
+  tokens cached), then advance: a prefill produces the request's first token,
+  a decode one more.
+* The brake state reported for a step is the one the first admission check
+  saw (0 proceed, 1 soft, 2 hard); with nothing waiting it is evaluated
+  anyway.
+* Blocks come from the pool's LIFO free stack (oracle.paged.FreeBlockStack).
+* A request whose full length (prompt + max_new_tokens) needs more blocks
+  than its table row or the whole pool is refused at submission.
+
+Pinned by tests/test_oracle_sched.py against scenarios whose decisions follow
+from the stated rules by hand, and by invariants (no block in two tables,
+every block returned at the end).
+"""
+from dataclasses import dataclass, field
+
+from . import paged
+
+PROCEED, SOFT, HARD = 0, 1, 2
+
+
+@dataclass
+class Request:
+    rid: int
+    prompt: int
+    max_new: int
+    generated: int = 0
+    ctx: int = 0                  # tokens cached
+    blocks: list = field(default_factory=list)
+
+
+@dataclass
+class Plan:
+    prefill: list                 # (rid, ctx, n, blocks)
+    decode: list                  # (rid, ctx, blocks)
+    preempted: list
+    finished: list
+    brake: int
+
+
+class Scheduler:
+    def __init__(self, num_blocks, block_size=16, max_running=64, hard=0.10, soft=0.30,
+                 max_blocks_per_seq=None):
+        self.pool = paged.FreeBlockStack(num_blocks)
+        self.N = num_blocks
+        self.bs = block_size
+        self.max_running = max_running
+        self.hard = hard
+        self.soft = soft
+        self.mbps = max_blocks_per_seq
+        self.waiting = []
+        self.running = []
+
+    def submit(self, rid, prompt, max_new):
+        """Queue a request; refused (ValueError) if its full length could never
+        fit its block-table row or the pool."""
+        need = paged.blocks_needed(prompt + max_new, self.bs)
+        if prompt < 1 or max_new < 1 or need > self.N or (self.mbps is not None and need > self.mbps):
+            raise ValueError("request can never be scheduled")
+        self.waiting.append(Request(rid, prompt, max_new))
+
+    def _alloc(self, n):
+        try:
+            return self.pool.alloc(n)
+        except MemoryError:
+            return None
+
+    def _free_frac(self):
+        return self.pool.num_free() / self.N
+
+    def _brake(self, decodes_running):
+        f = self._free_frac()
+        if f < self.hard:
+            return HARD
+        if decodes_running and f < self.soft:
+            return SOFT
+        return PROCEED
+
+    def _release(self, r):
+        self.pool.free(r.blocks)
+        r.blocks = []
+
+    def step(self):
+        # (1) retire
+        finished = []
+        keep = []
+        for r in self.running:
+            if r.generated >= r.max_new:
+                self._release(r)
+                finished.append(r.rid)
+            else:
+                keep.append(r)
+        self.running = keep
+        # (2) decode growth, preempting the latest admitted on exhaustion
+        preempted = []
+        i = 0
+        while i < len(self.running):
+            r = self.running[i]
+            need = paged.blocks_needed(r.ctx + 1, self.bs)
+            if len(r.blocks) >= need:
+                i += 1
+                continue
+            ids = self._alloc(1)
+            if ids is not None:
+                r.blocks += ids
+                i += 1
+                continue
+            victim = self.running.pop()          # most recently admitted
+            self._release(victim)
+            victim.prompt = victim.prompt + victim.generated
+            victim.max_new = victim.max_new - victim.generated
+            victim.generated = 0
+            victim.ctx = 0
+            self.waiting.insert(0, victim)
+            preempted.append(victim.rid)
+            # i unchanged: if the victim was r itself, the loop ends
+        # (3) admission
+        decoding = len(self.running) > 0
+        brake = self._brake(decoding)
+        admitted = []
+        while self.waiting and len(self.running) + len(admitted) < self.max_running:
+            if self._brake(decoding) != PROCEED:
+                break
+            r = self.waiting[0]
+            need = paged.blocks_needed(r.prompt, self.bs)
+            ids = self._alloc(need)
+            if ids is None:
+                break
+            self.waiting.pop(0)
+            r.blocks = list(ids)
+            admitted.append(r)
+        # (4) plan, then advance
+        plan = Plan(prefill=[(r.rid, 0, r.prompt, list(r.blocks)) for r in admitted],
+                    decode=[(r.rid, r.ctx, list(r.blocks)) for r in self.running],
+                    preempted=preempted, finished=finished, brake=brake)
+        for r in self.running:
+            r.ctx += 1
+            r.generated += 1
+        for r in admitted:
+            r.ctx = r.prompt
+            r.generated = 1
+        self.running += admitted
+        return plan
+
+    def idle(self):
+        return not self.waiting and not self.running

@@ -1,0 +1,115 @@
+"""Pins for the oracle's step planner (CPU only): brake decisions in scenarios
+worked out by hand from the serving-framework report's rules (hard: free <
+10 %; soft: decodes running and free < 30 %), the block counts of the paged
+cache (ceil(tokens / 16)), recompute preemption order, and lifecycle
+invariants over random request streams."""
+import numpy as np
+import pytest
+
+from oracle import paged, sched
+
+
+def _tables_disjoint_and_complete(s):
+    held = [b for r in s.running for b in r.blocks]
+    assert len(held) == len(set(held))
+    assert len(held) + s.pool.num_free() == s.N
+
+
+def test_fresh_system_admits_until_capacity_ignoring_the_soft_brake():
+    # 100 blocks, prompts of 480 tokens = 30 blocks: no decode is running when
+    # admission starts, so only capacity and the hard brake apply.
+    s = sched.Scheduler(100, max_running=8)
+    for i in range(5):
+        s.submit(i, 480, 4)
+    p = s.step()
+    assert [x[0] for x in p.prefill] == [0, 1, 2]            # 4th needs 30, 10 free
+    assert p.brake == sched.PROCEED and s.pool.num_free() == 10
+    assert all(len(x[3]) == 30 for x in p.prefill)
+    # next step: 3 decodes at ctx 480 need block 31 each -> 7 free (7 %): hard
+    p = s.step()
+    assert p.brake == sched.HARD and p.prefill == []
+    assert [x[1] for x in p.decode] == [480, 480, 480]
+    assert s.pool.num_free() == 7
+
+
+def test_soft_brake_needs_running_decodes_and_is_strict():
+    # 100 blocks. Request A: 70 blocks (1120 tokens) -> 30 free: 30 % is not
+    # below 30 %, so B (1 block) is admitted in the same step.
+    s = sched.Scheduler(100, max_running=8)
+    s.submit(0, 1120, 10)
+    s.submit(1, 16, 10)
+    p = s.step()
+    assert [x[0] for x in p.prefill] == [0, 1]
+    # step 2: A grows to 71 blocks (ctx 1120 -> needs 71), B to 2: 27 free
+    # with decodes running -> soft brake: C waits
+    s.submit(2, 16, 10)
+    p = s.step()
+    assert s.pool.num_free() == 27
+    assert p.brake == sched.SOFT and p.prefill == []
+    assert [x[0] for x in p.decode] == [0, 1]
+
+
+def test_hard_brake_threshold_is_strict():
+    # 10 of 100 free is not below 10 %: admission proceeds when decodes are
+    # idle; at 9 free it is a hard brake.
+    s = sched.Scheduler(100, max_running=8)
+    s.submit(0, 90 * 16, 3)
+    s.submit(1, 16, 3)
+    p = s.step()
+    assert [x[0] for x in p.prefill] == [0, 1] and s.pool.num_free() == 9
+    s.submit(2, 16, 3)
+    p = s.step()                               # growth: ctx 1440 -> 91 blocks, 8 free
+    assert p.brake == sched.HARD and p.prefill == []
+
+
+def test_block_counts_follow_ceil_of_tokens():
+    s = sched.Scheduler(64, max_running=4)
+    s.submit(0, 17, 40)
+    p = s.step()
+    assert len(p.prefill[0][3]) == paged.blocks_needed(17, 16) == 2
+    for step in range(40):
+        p = s.step()
+        if not p.decode:
+            break
+        rid, ctx, blocks = p.decode[0]
+        assert len(blocks) == paged.blocks_needed(ctx + 1, 16)
+
+
+def test_recompute_preemption_takes_the_latest_admitted():
+    # 8 blocks. A (prompt 48 = 3 blocks) and B (prompt 64 = 4 blocks): 1 free.
+    s = sched.Scheduler(8, max_running=4, hard=0.0, soft=0.0)
+    s.submit(0, 48, 40)
+    s.submit(1, 64, 40)
+    p = s.step()
+    assert [x[0] for x in p.prefill] == [0, 1] and s.pool.num_free() == 1
+    # A at ctx 48 needs a 4th block (takes the last free one); B at ctx 64 needs
+    # a 5th: pool empty -> B (latest) is preempted and re-queued
+    p = s.step()
+    assert p.preempted == [1] and [x[0] for x in p.decode] == [0]
+    assert s.waiting[0].rid == 1 and s.waiting[0].prompt == 65 and s.waiting[0].max_new == 39
+    _tables_disjoint_and_complete(s)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_random_streams_keep_invariants_and_finish(seed):
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(40, 200))
+    s = sched.Scheduler(N, max_running=int(rng.integers(2, 9)))
+    produced = {}
+    want = {}
+    rid = 0
+    for t in range(4000):
+        if rid < 60 and rng.random() < 0.3:
+            prompt, new = int(rng.integers(1, 300)), int(rng.integers(1, 60))
+            if paged.blocks_needed(prompt + new, 16) <= N:
+                s.submit(rid, prompt, new)
+                want[rid] = new
+                rid += 1
+        p = s.step()
+        for x in p.prefill + p.decode:
+            produced[x[0]] = produced.get(x[0], 0) + 1
+        _tables_disjoint_and_complete(s)
+        if rid >= 60 and s.idle():
+            break
+    assert s.idle() and s.pool.num_free() == N
+    assert produced == want                       # every request made exactly its tokens
