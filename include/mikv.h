@@ -380,6 +380,80 @@ int mi_decoder_layer_decode(mi_kv_pool_t pool, const mi_layer_config* cfg,
                             int32_t max_context_len,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Continuous-batching step planner (host only): block lifecycle and admission
+ * over a pool's free-block stack, with the KV-protection brakes of the
+ * vLLM-based inference-framework report ("SLO-aware, KV-cache protecting
+ * scheduler": free KV space below a critical threshold stops new prefills
+ * -- hard brake; running decodes with free space below a safety threshold
+ * stop them too -- soft brake; otherwise requests proceed) and the
+ * mini-infer scheduler's waiting/running queues (prefill alone, then batched
+ * decode, admission at every step).
+ *
+ * The planner takes blocks from and returns them to `pool` (mi_kv_alloc_blocks
+ * / mi_kv_free_blocks): while it lives, nothing else may allocate from that
+ * pool. It is not thread-safe.
+ */
+typedef struct mi_sched_s* mi_sched_t;
+
+enum { MI_BRAKE_PROCEED = 0, MI_BRAKE_SOFT = 1, MI_BRAKE_HARD = 2 };
+
+typedef struct {
+    int32_t num_prefill;     /* rows 0 .. num_prefill-1 of the step's outputs */
+    int32_t num_decode;      /* the following num_decode rows */
+    int32_t num_preempted;   /* entries of preempted_ids */
+    int32_t num_finished;    /* entries of finished_ids */
+    int32_t brake;           /* MI_BRAKE_* seen by the step's first admission check */
+    int32_t free_blocks;     /* free blocks after the step's allocations */
+} mi_sched_counts;
+
+/*
+ * max_blocks_per_seq  block-table row length of the plans (and the longest
+ *                     request: ceil((prompt + max_new) / 16) blocks)
+ * max_running         most requests running at once (rows of a plan)
+ * hard_free_frac, soft_free_frac  thresholds on free / pool blocks in [0, 1]
+ *                     (the report's values: 0.10 and 0.30); "below" is strict.
+ */
+int mi_sched_create(mi_sched_t* out, mi_kv_pool_t pool, int32_t max_blocks_per_seq,
+                    int32_t max_running, double hard_free_frac, double soft_free_frac);
+/* Returns every block still held by running requests to the pool. */
+int mi_sched_destroy(mi_sched_t sched);
+
+/*
+ * Queue a request (FIFO). MI_ERR_UNSUPPORTED if prompt_tokens + max_new_tokens
+ * needs more blocks than a table row or the whole pool (it could never run);
+ * MI_ERR_INVALID_ARG for counts < 1.
+ */
+int mi_sched_submit(mi_sched_t sched, int64_t request_id, int32_t prompt_tokens,
+                    int32_t max_new_tokens);
+int32_t mi_sched_num_waiting(mi_sched_t sched);
+int32_t mi_sched_num_running(mi_sched_t sched);
+
+/*
+ * Plan one engine step (host arrays, capacity max_running rows each):
+ *  1. requests that produced max_new_tokens retire (ids in finished_ids) and
+ *     return their blocks;
+ *  2. every running request gets the block its decode write at position
+ *     context_len needs (ceil((context_len + 1) / 16) blocks), in admission
+ *     order; on an empty pool the most recently admitted running request is
+ *     preempted (blocks returned; re-queued first, to be prefilled again over
+ *     its prompt and generated tokens; id in preempted_ids);
+ *  3. waiting requests are admitted in order while a row is free, no brake
+ *     holds (free / pool re-measured before each admission) and the pool
+ *     holds ceil(prompt / 16) blocks; the first that cannot be admitted
+ *     stops admission;
+ *  4. rows: the admitted prefills (context_lens 0, new_tokens = prompt), then
+ *     the decodes (context_lens = tokens cached, new_tokens 1), with their
+ *     block-table rows in block_table [max_running, max_blocks_per_seq]
+ *     (-1 padded) -- the inputs of mi_write_prefill_kv /
+ *     mi_paged_prefill_attention and mi_write_decode_kv / mi_paged_gqa_decode.
+ *     The plan is taken as executed: a prefill yields a request's first
+ *     token, a decode one more.
+ */
+int mi_sched_step(mi_sched_t sched, mi_sched_counts* counts, int64_t* seq_ids,
+                  int32_t* context_lens, int32_t* new_tokens, int32_t* block_table,
+                  int64_t* preempted_ids, int64_t* finished_ids);
+
 #ifdef __cplusplus
 }
 #endif

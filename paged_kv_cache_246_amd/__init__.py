@@ -62,6 +62,12 @@ SIGNATURES = {
                                        _i32, _c.c_double, _vp]),
     "mi_paged_prefill_attention": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                               _i32, _i32, _c.c_float, _vp]),
+    "mi_sched_create": (_c.c_int, [_c.POINTER(_vp), _vp, _i32, _i32, _c.c_double, _c.c_double]),
+    "mi_sched_destroy": (_c.c_int, [_vp]),
+    "mi_sched_submit": (_c.c_int, [_vp, _c.c_int64, _i32, _i32]),
+    "mi_sched_num_waiting": (_i32, [_vp]),
+    "mi_sched_num_running": (_i32, [_vp]),
+    "mi_sched_step": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mi_gather_kv": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp]),
     "mi_decoder_layer_workspace_bytes": (_sz, [_vp, _vp, _i32, _i32]),
     "mi_decoder_layer_decode": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
@@ -295,3 +301,61 @@ def mi_decoder_layer_decode(pool, cfg, weights, x_in, x_out, block_table, max_bl
         pool, ctypes.byref(cfg), ctypes.byref(weights), _ptr(x_in), _ptr(x_out),
         _ptr(block_table), max_blocks_per_seq, _ptr(context_lens), batch, max_context_len,
         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+# --------------------------------------------------------- step planner
+MI_BRAKE_PROCEED, MI_BRAKE_SOFT, MI_BRAKE_HARD = 0, 1, 2
+
+
+class MiSchedCounts(ctypes.Structure):
+    _fields_ = [("num_prefill", ctypes.c_int32), ("num_decode", ctypes.c_int32),
+                ("num_preempted", ctypes.c_int32), ("num_finished", ctypes.c_int32),
+                ("brake", ctypes.c_int32), ("free_blocks", ctypes.c_int32)]
+
+
+class Scheduler:
+    """Host wrapper of mi_sched_*: plans come back as numpy arrays."""
+
+    def __init__(self, pool, max_blocks_per_seq, max_running, hard=0.10, soft=0.30):
+        import numpy as np
+        self._np = np
+        h = _vp()
+        _check("mi_sched_create", lib().mi_sched_create(ctypes.byref(h), pool, max_blocks_per_seq,
+                                                         max_running, hard, soft))
+        self.h = h.value
+        self.mbps, self.max_running = max_blocks_per_seq, max_running
+        R = max_running
+        self.ids = np.zeros(R, np.int64)
+        self.ctx = np.zeros(R, np.int32)
+        self.new = np.zeros(R, np.int32)
+        self.table = np.zeros((R, max_blocks_per_seq), np.int32)
+        self.pre = np.zeros(R, np.int64)
+        self.fin = np.zeros(R, np.int64)
+
+    def submit(self, rid, prompt, max_new):
+        return _check("mi_sched_submit", lib().mi_sched_submit(self.h, rid, prompt, max_new))
+
+    def num_waiting(self):
+        return lib().mi_sched_num_waiting(self.h)
+
+    def num_running(self):
+        return lib().mi_sched_num_running(self.h)
+
+    def step(self):
+        c = MiSchedCounts()
+        ptr = lambda a: a.ctypes.data
+        _check("mi_sched_step", lib().mi_sched_step(self.h, ctypes.byref(c), ptr(self.ids),
+                                                     ptr(self.ctx), ptr(self.new), ptr(self.table),
+                                                     ptr(self.pre), ptr(self.fin)))
+        n = c.num_prefill + c.num_decode
+        return {"num_prefill": c.num_prefill, "num_decode": c.num_decode, "brake": c.brake,
+                "free_blocks": c.free_blocks, "ids": self.ids[:n].copy(),
+                "context_lens": self.ctx[:n].copy(), "new_tokens": self.new[:n].copy(),
+                "block_table": self.table[:n].copy(),
+                "preempted": self.pre[:c.num_preempted].copy(),
+                "finished": self.fin[:c.num_finished].copy()}
+
+    def close(self):
+        if self.h:
+            lib().mi_sched_destroy(self.h)
+            self.h = None
