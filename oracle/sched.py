@@ -42,6 +42,25 @@ Readings where the pages are silent (the same in the library):
 * A request whose full length (prompt + max_new_tokens) needs more blocks
   than its table row or the whole pool is refused at submission.
 
+KV offload (course project, optional task 3 "KV Cache Offloading": move
+inactive KV blocks out to CPU memory and bring them back when needed, with
+an eviction policy). Reading for a paged cache: the inactive blocks are those
+of a preempted request. With a host swap space of S block slots (a LIFO
+stack like the device pool), a preemption victim whose blocks fit the free
+host slots is swapped out instead of recomputed: its device blocks are
+copied to host slots (emitted as (device id, host slot) pairs, to run before
+anything else in the step) and returned to the pool; it keeps its context
+and generated count and joins the swapped queue. The victim is the most
+recently admitted running request (LIFO eviction among running requests).
+Swapped requests come back first, in the order they were swapped out,
+regardless of the brakes (they are not new prefills), and while any request
+remains swapped out no new request is admitted: a swap-in needs the request's blocks plus the block its decode
+write needs; the device blocks are allocated in block order and paired with
+the host slots (emitted as (host slot, device id) pairs, run after the
+swap-outs), the host slots are freed, and the request decodes in this same
+step after the requests already running. Without host space (or when the
+victim's blocks do not fit) preemption recomputes as above.
+
 Pinned by tests/test_oracle_sched.py against scenarios whose decisions follow
 from the stated rules by hand, and by invariants (no block in two tables,
 every block returned at the end).
@@ -61,21 +80,27 @@ class Request:
     generated: int = 0
     ctx: int = 0                  # tokens cached
     blocks: list = field(default_factory=list)
+    host_slots: list = field(default_factory=list)
 
 
 @dataclass
 class Plan:
     prefill: list                 # (rid, ctx, n, blocks)
     decode: list                  # (rid, ctx, blocks)
-    preempted: list
+    preempted: list               # recomputed
     finished: list
     brake: int
+    swapped_out: list = field(default_factory=list)   # rids
+    swap_out: list = field(default_factory=list)      # (device id, host slot)
+    swap_in: list = field(default_factory=list)       # (host slot, device id)
 
 
 class Scheduler:
     def __init__(self, num_blocks, block_size=16, max_running=64, hard=0.10, soft=0.30,
-                 max_blocks_per_seq=None):
+                 max_blocks_per_seq=None, host_slots=0):
         self.pool = paged.FreeBlockStack(num_blocks)
+        self.host = paged.FreeBlockStack(host_slots) if host_slots > 0 else None
+        self.swapped = []
         self.N = num_blocks
         self.bs = block_size
         self.max_running = max_running
@@ -127,6 +152,7 @@ class Scheduler:
         self.running = keep
         # (2) decode growth, preempting the latest admitted on exhaustion
         preempted = []
+        swapped_out, swap_out = [], []
         i = 0
         while i < len(self.running):
             r = self.running[i]
@@ -140,6 +166,14 @@ class Scheduler:
                 i += 1
                 continue
             victim = self.running.pop()          # most recently admitted
+            if self.host is not None and self.host.num_free() >= len(victim.blocks):
+                slots = self.host.alloc(len(victim.blocks))
+                swap_out += list(zip(victim.blocks, slots))
+                self._release(victim)
+                victim.host_slots = slots
+                self.swapped.append(victim)
+                swapped_out.append(victim.rid)
+                continue
             self._release(victim)
             victim.prompt = victim.prompt + victim.generated
             victim.max_new = victim.max_new - victim.generated
@@ -148,11 +182,27 @@ class Scheduler:
             self.waiting.insert(0, victim)
             preempted.append(victim.rid)
             # i unchanged: if the victim was r itself, the loop ends
+        # (3') swap-ins first, oldest swapped first, regardless of the brakes
+        swap_in = []
+        while self.swapped and len(self.running) < self.max_running:
+            r = self.swapped[0]
+            nb = len(r.host_slots)
+            need = max(nb, paged.blocks_needed(r.ctx + 1, self.bs))
+            ids = self._alloc(need)
+            if ids is None:
+                break
+            self.swapped.pop(0)
+            swap_in += list(zip(r.host_slots, ids[:nb]))
+            self.host.free(r.host_slots)
+            r.host_slots = []
+            r.blocks = list(ids)
+            self.running.append(r)
         # (3) admission
         decoding = len(self.running) > 0
         brake = self._brake(decoding)
         admitted = []
-        while self.waiting and len(self.running) + len(admitted) < self.max_running:
+        while (self.waiting and not self.swapped
+               and len(self.running) + len(admitted) < self.max_running):
             if self._brake(decoding) != PROCEED:
                 break
             r = self.waiting[0]
@@ -166,7 +216,8 @@ class Scheduler:
         # (4) plan, then advance
         plan = Plan(prefill=[(r.rid, 0, r.prompt, list(r.blocks)) for r in admitted],
                     decode=[(r.rid, r.ctx, list(r.blocks)) for r in self.running],
-                    preempted=preempted, finished=finished, brake=brake)
+                    preempted=preempted, finished=finished, brake=brake,
+                    swapped_out=swapped_out, swap_out=swap_out, swap_in=swap_in)
         for r in self.running:
             r.ctx += 1
             r.generated += 1
@@ -177,4 +228,4 @@ class Scheduler:
         return plan
 
     def idle(self):
-        return not self.waiting and not self.running
+        return not self.waiting and not self.running and not self.swapped

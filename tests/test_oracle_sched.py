@@ -113,3 +113,78 @@ def test_random_streams_keep_invariants_and_finish(seed):
             break
     assert s.idle() and s.pool.num_free() == N
     assert produced == want                       # every request made exactly its tokens
+
+
+# ------------------------------------------------------------ KV offload
+def test_swap_preemption_keeps_context_and_resumes_first():
+    s = sched.Scheduler(8, max_running=4, hard=0.0, soft=0.0, host_slots=16)
+    s.submit(0, 48, 6)
+    s.submit(1, 64, 40)
+    s.step()
+    p = s.step()
+    # B (latest) swapped out: its 4 blocks to host slots 0..3 in block order
+    assert p.swapped_out == [1] and p.preempted == []
+    assert p.swap_out == [(3, 0), (4, 1), (5, 2), (6, 3)]
+    assert [x[0] for x in p.decode] == [0]
+    s.submit(2, 16, 3)                       # a new request must not overtake B
+    while True:
+        p = s.step()
+        if p.swap_in:
+            break
+        assert p.prefill == []
+    # A finished: B comes back with its 4 blocks + the block for position 64,
+    # decodes at its old context, then C is admitted behind it
+    assert [x[0] for x in p.swap_in] == [0, 1, 2, 3]
+    dec = {x[0]: x for x in p.decode}
+    assert dec[1][1] == 64 and len(dec[1][2]) == 5
+    assert [x[0] for x in p.prefill] == [2]
+
+
+def test_small_host_space_falls_back_to_recompute():
+    s = sched.Scheduler(8, max_running=4, hard=0.0, soft=0.0, host_slots=3)
+    s.submit(0, 48, 40)
+    s.submit(1, 64, 40)
+    s.step()
+    p = s.step()
+    assert p.swapped_out == [] and p.preempted == [1]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_swap_streams_preserve_every_block_content(seed):
+    """Tag every logical block (request, index) as it is written, move tags with
+    the plan's swap-out / swap-in pairs, and check that every running request
+    reads its own tags in order after every step."""
+    rng = np.random.default_rng(50 + seed)
+    N = int(rng.integers(16, 60))
+    s = sched.Scheduler(N, max_running=int(rng.integers(2, 6)), hard=0.0, soft=0.0,
+                        host_slots=int(rng.integers(8, 40)))
+    dev, host = {}, {}
+    want, produced = {}, {}
+    rid = 0
+    for t in range(3000):
+        if rid < 40 and rng.random() < 0.3:
+            prompt, new = int(rng.integers(1, 200)), int(rng.integers(1, 80))
+            if paged.blocks_needed(prompt + new, 16) <= N:
+                s.submit(rid, prompt, new)
+                want[rid] = new
+                rid += 1
+        p = s.step()
+        for d, h in p.swap_out:
+            host[h] = dev.pop(d)
+        for h, d in p.swap_in:
+            dev[d] = host.pop(h)
+        for r_id, ctx, n, blocks in p.prefill:          # prompt writes blocks 0..
+            for j in range(paged.blocks_needed(n, 16)):
+                dev[blocks[j]] = (r_id, j)
+        for r_id, ctx, blocks in p.decode:              # decode writes block ctx // 16
+            j = ctx // 16
+            if ctx % 16 == 0:
+                dev[blocks[j]] = (r_id, j)
+            for i in range(j + 1):
+                assert dev[blocks[i]] == (r_id, i)
+        for x in p.prefill + p.decode:
+            produced[x[0]] = produced.get(x[0], 0) + 1
+        if rid >= 40 and s.idle():
+            break
+    assert s.idle() and s.pool.num_free() == N and s.host.num_free() == s.host.num_blocks
+    assert produced == want
