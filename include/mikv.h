@@ -405,6 +405,9 @@ typedef struct {
     int32_t num_finished;    /* entries of finished_ids */
     int32_t brake;           /* MI_BRAKE_* seen by the step's first admission check */
     int32_t free_blocks;     /* free blocks after the step's allocations */
+    int32_t num_swapped_out; /* entries of swapped_ids */
+    int32_t num_swap_out;    /* (device block, host slot) pairs in swap_out */
+    int32_t num_swap_in;     /* (host slot, device block) pairs in swap_in */
 } mi_sched_counts;
 
 /*
@@ -428,6 +431,19 @@ int mi_sched_submit(mi_sched_t sched, int64_t request_id, int32_t prompt_tokens,
                     int32_t max_new_tokens);
 int32_t mi_sched_num_waiting(mi_sched_t sched);
 int32_t mi_sched_num_running(mi_sched_t sched);
+int32_t mi_sched_num_swapped(mi_sched_t sched);
+
+/*
+ * KV offload (course project, optional task "KV Cache Offloading": inactive
+ * KV blocks go to CPU memory and come back when needed, under an eviction
+ * policy). Gives the planner a host swap space of host_slots blocks (call
+ * before the first step; 0 = none). A preemption victim -- the most recently
+ * admitted running request -- whose blocks fit the free host slots is then
+ * swapped out instead of recomputed: it keeps its context and comes back
+ * before anything new is admitted (swapped requests in swap order, regardless
+ * of the brakes), with its blocks copied back into fresh device blocks.
+ */
+int mi_sched_set_swap_space(mi_sched_t sched, int32_t host_slots);
 
 /*
  * Plan one engine step (host arrays, capacity max_running rows each):
@@ -449,10 +465,34 @@ int32_t mi_sched_num_running(mi_sched_t sched);
  *     mi_paged_prefill_attention and mi_write_decode_kv / mi_paged_gqa_decode.
  *     The plan is taken as executed: a prefill yields a request's first
  *     token, a decode one more.
+ * With swap space (mi_sched_set_swap_space): swapped_ids [max_running] gets
+ * the requests swapped out this step, swap_out [max_running *
+ * max_blocks_per_seq][2] the (device block, host slot) pairs to copy out and
+ * swap_in (same capacity) the (host slot, device block) pairs to copy back
+ * (swapped-in requests decode in this step, after the others). Execute in
+ * order: mi_kv_swap_out, mi_kv_swap_in, then the prefill and decode kernels.
  */
 int mi_sched_step(mi_sched_t sched, mi_sched_counts* counts, int64_t* seq_ids,
                   int32_t* context_lens, int32_t* new_tokens, int32_t* block_table,
-                  int64_t* preempted_ids, int64_t* finished_ids);
+                  int64_t* preempted_ids, int64_t* finished_ids, int64_t* swapped_ids,
+                  int32_t* swap_out, int32_t* swap_in);
+
+/*
+ * Block copies between a pool and a host swap space (KV offload). host_k,
+ * host_v: host arrays [host_slots, num_kv_heads, 16, head_dim] of the pool's
+ * element type (bf16 bits or E4M3 codes), page-locked for asynchronous
+ * copies (e.g. hipHostMalloc); pairs: host array of n (device block, host
+ * slot) pairs for swap_out, n (host slot, device block) pairs for swap_in.
+ * Every id and slot is checked before anything is copied
+ * (MI_ERR_INVALID_ARG). Copies are DMA transfers queued on stream (runs of
+ * consecutive blocks and slots merged into one transfer), asynchronous for
+ * page-locked host memory; the host arrays must stay alive until the stream
+ * reaches them.
+ */
+int mi_kv_swap_out(mi_kv_pool_t pool, void* host_k, void* host_v, int32_t host_slots,
+                   const int32_t* pairs, int32_t n, void* stream);
+int mi_kv_swap_in(mi_kv_pool_t pool, const void* host_k, const void* host_v, int32_t host_slots,
+                  const int32_t* pairs, int32_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -67,7 +67,11 @@ SIGNATURES = {
     "mi_sched_submit": (_c.c_int, [_vp, _c.c_int64, _i32, _i32]),
     "mi_sched_num_waiting": (_i32, [_vp]),
     "mi_sched_num_running": (_i32, [_vp]),
-    "mi_sched_step": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mi_sched_step": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mi_sched_set_swap_space": (_c.c_int, [_vp, _i32]),
+    "mi_sched_num_swapped": (_i32, [_vp]),
+    "mi_kv_swap_out": (_c.c_int, [_vp, _vp, _vp, _i32, _vp, _i32, _vp]),
+    "mi_kv_swap_in": (_c.c_int, [_vp, _vp, _vp, _i32, _vp, _i32, _vp]),
     "mi_gather_kv": (_c.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp]),
     "mi_decoder_layer_workspace_bytes": (_sz, [_vp, _vp, _i32, _i32]),
     "mi_decoder_layer_decode": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
@@ -310,13 +314,16 @@ MI_BRAKE_PROCEED, MI_BRAKE_SOFT, MI_BRAKE_HARD = 0, 1, 2
 class MiSchedCounts(ctypes.Structure):
     _fields_ = [("num_prefill", ctypes.c_int32), ("num_decode", ctypes.c_int32),
                 ("num_preempted", ctypes.c_int32), ("num_finished", ctypes.c_int32),
-                ("brake", ctypes.c_int32), ("free_blocks", ctypes.c_int32)]
+                ("brake", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("num_swapped_out", ctypes.c_int32), ("num_swap_out", ctypes.c_int32),
+                ("num_swap_in", ctypes.c_int32)]
 
 
 class Scheduler:
     """Host wrapper of mi_sched_*: plans come back as numpy arrays."""
 
-    def __init__(self, pool, max_blocks_per_seq, max_running, hard=0.10, soft=0.30):
+    def __init__(self, pool, max_blocks_per_seq, max_running, hard=0.10, soft=0.30,
+                 host_slots=0):
         import numpy as np
         self._np = np
         h = _vp()
@@ -331,6 +338,11 @@ class Scheduler:
         self.table = np.zeros((R, max_blocks_per_seq), np.int32)
         self.pre = np.zeros(R, np.int64)
         self.fin = np.zeros(R, np.int64)
+        self.swp = np.zeros(R, np.int64)
+        self.so = np.zeros((R * max_blocks_per_seq, 2), np.int32)
+        self.si = np.zeros((R * max_blocks_per_seq, 2), np.int32)
+        if host_slots:
+            _check("mi_sched_set_swap_space", lib().mi_sched_set_swap_space(self.h, host_slots))
 
     def submit(self, rid, prompt, max_new):
         return _check("mi_sched_submit", lib().mi_sched_submit(self.h, rid, prompt, max_new))
@@ -341,21 +353,46 @@ class Scheduler:
     def num_running(self):
         return lib().mi_sched_num_running(self.h)
 
+    def num_swapped(self):
+        return lib().mi_sched_num_swapped(self.h)
+
     def step(self):
         c = MiSchedCounts()
         ptr = lambda a: a.ctypes.data
         _check("mi_sched_step", lib().mi_sched_step(self.h, ctypes.byref(c), ptr(self.ids),
                                                      ptr(self.ctx), ptr(self.new), ptr(self.table),
-                                                     ptr(self.pre), ptr(self.fin)))
+                                                     ptr(self.pre), ptr(self.fin), ptr(self.swp),
+                                                     ptr(self.so), ptr(self.si)))
         n = c.num_prefill + c.num_decode
         return {"num_prefill": c.num_prefill, "num_decode": c.num_decode, "brake": c.brake,
                 "free_blocks": c.free_blocks, "ids": self.ids[:n].copy(),
                 "context_lens": self.ctx[:n].copy(), "new_tokens": self.new[:n].copy(),
                 "block_table": self.table[:n].copy(),
                 "preempted": self.pre[:c.num_preempted].copy(),
-                "finished": self.fin[:c.num_finished].copy()}
+                "finished": self.fin[:c.num_finished].copy(),
+                "swapped_out": self.swp[:c.num_swapped_out].copy(),
+                "swap_out": self.so[:c.num_swap_out].copy(),
+                "swap_in": self.si[:c.num_swap_in].copy()}
 
     def close(self):
         if self.h:
             lib().mi_sched_destroy(self.h)
             self.h = None
+
+
+def mi_kv_swap_out(pool, host_k, host_v, host_slots, pairs, stream=None):
+    """pairs: numpy int32 [n, 2] (device block, host slot), host memory."""
+    import numpy as np
+    pr = np.ascontiguousarray(pairs, dtype=np.int32)
+    return _check("mi_kv_swap_out", lib().mi_kv_swap_out(
+        pool, _ptr(host_k), _ptr(host_v), host_slots, pr.ctypes.data if len(pr) else None,
+        len(pr), _stream(stream)))
+
+
+def mi_kv_swap_in(pool, host_k, host_v, host_slots, pairs, stream=None):
+    """pairs: numpy int32 [n, 2] (host slot, device block), host memory."""
+    import numpy as np
+    pr = np.ascontiguousarray(pairs, dtype=np.int32)
+    return _check("mi_kv_swap_in", lib().mi_kv_swap_in(
+        pool, _ptr(host_k), _ptr(host_v), host_slots, pr.ctypes.data if len(pr) else None,
+        len(pr), _stream(stream)))

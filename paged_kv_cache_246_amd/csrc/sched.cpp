@@ -24,6 +24,19 @@
 // "below" is strict) and the pool holds ceil(prompt / 16) blocks, stopping at
 // the first that cannot be admitted; (4) emit prefills then decodes and
 // advance (a prefill yields the first token, a decode one more).
+//
+// KV offload (course project, optional task "KV Cache Offloading": inactive
+// KV blocks move to CPU memory and come back when needed, under an eviction
+// policy). With a host swap space, a preemption victim whose blocks fit the
+// free host slots is swapped out instead of recomputed (its (device block,
+// host slot) pairs are emitted, it keeps its context); the victim is the most
+// recently admitted running request. Swapped requests come back first, in
+// swap order and regardless of the brakes, each with its blocks plus the
+// block its decode needs ((host slot, device block) pairs emitted), and
+// decode in the same step; while any request is swapped out nothing new is
+// admitted. The caller runs the swap-outs, then the swap-ins, before the
+// step's kernels (mi_kv_swap_out / mi_kv_swap_in).
+#include <algorithm>
 #include <deque>
 #include <new>
 #include <vector>
@@ -38,6 +51,7 @@ struct mi_sched_s {
         int32_t generated = 0;
         int32_t ctx = 0;
         std::vector<int32_t> blocks;
+        std::vector<int32_t> host_slots;
     };
     mi_kv_pool_s* pool = nullptr;
     int32_t mbps = 0;
@@ -46,6 +60,10 @@ struct mi_sched_s {
     double soft = 0.0;
     std::deque<Req> waiting;
     std::vector<Req> running;
+    std::deque<Req> swapped;
+    // host swap space: LIFO stack of free slots (first pop returns slot 0)
+    int32_t host_slots = 0;
+    std::vector<int32_t> host_free;
 };
 
 namespace {
@@ -112,6 +130,23 @@ extern "C" int mi_sched_submit(mi_sched_t s, int64_t request_id, int32_t prompt_
     return MI_OK;
 }
 
+extern "C" int mi_sched_set_swap_space(mi_sched_t s, int32_t host_slots) {
+    if (!s || host_slots < 0) return MI_ERR_INVALID_ARG;
+    if (!s->running.empty() || !s->swapped.empty()) return MI_ERR_INVALID_ARG;
+    try {
+        s->host_free.resize(static_cast<size_t>(host_slots));
+    } catch (...) {
+        return MI_ERR_OUT_OF_MEMORY;
+    }
+    for (int32_t i = 0; i < host_slots; ++i) s->host_free[i] = host_slots - 1 - i;
+    s->host_slots = host_slots;
+    return MI_OK;
+}
+
+extern "C" int32_t mi_sched_num_swapped(mi_sched_t s) {
+    return s ? static_cast<int32_t>(s->swapped.size()) : MI_ERR_INVALID_ARG;
+}
+
 extern "C" int32_t mi_sched_num_waiting(mi_sched_t s) {
     return s ? static_cast<int32_t>(s->waiting.size()) : MI_ERR_INVALID_ARG;
 }
@@ -122,12 +157,13 @@ extern "C" int32_t mi_sched_num_running(mi_sched_t s) {
 
 extern "C" int mi_sched_step(mi_sched_t s, mi_sched_counts* counts, int64_t* seq_ids,
                              int32_t* context_lens, int32_t* new_tokens, int32_t* block_table,
-                             int64_t* preempted_ids, int64_t* finished_ids) {
+                             int64_t* preempted_ids, int64_t* finished_ids, int64_t* swapped_ids,
+                             int32_t* swap_out, int32_t* swap_in) {
     if (!s || !counts || !seq_ids || !context_lens || !new_tokens || !block_table ||
-        !preempted_ids || !finished_ids)
+        !preempted_ids || !finished_ids || !swapped_ids || !swap_out || !swap_in)
         return MI_ERR_INVALID_ARG;
     try {
-        int32_t n_fin = 0, n_pre = 0;
+        int32_t n_fin = 0, n_pre = 0, n_swp = 0, n_so = 0, n_si = 0;
         // (1) retire
         std::vector<mi_sched_s::Req> keep;
         keep.reserve(s->running.size());
@@ -157,6 +193,20 @@ extern "C" int mi_sched_step(mi_sched_t s, mi_sched_counts* counts, int64_t* seq
             }
             mi_sched_s::Req victim = std::move(s->running.back());
             s->running.pop_back();
+            if (s->host_free.size() >= victim.blocks.size()) {
+                for (int32_t dev : victim.blocks) {
+                    const int32_t slot = s->host_free.back();
+                    s->host_free.pop_back();
+                    victim.host_slots.push_back(slot);
+                    swap_out[2 * n_so] = dev;
+                    swap_out[2 * n_so + 1] = slot;
+                    ++n_so;
+                }
+                release(s, victim);
+                swapped_ids[n_swp++] = victim.id;
+                s->swapped.push_back(std::move(victim));
+                continue;
+            }
             release(s, victim);
             victim.prompt += victim.generated;
             victim.max_new -= victim.generated;
@@ -165,11 +215,29 @@ extern "C" int mi_sched_step(mi_sched_t s, mi_sched_counts* counts, int64_t* seq
             preempted_ids[n_pre++] = victim.id;
             s->waiting.push_front(std::move(victim));
         }
+        // (3') swap-ins, oldest swapped first, regardless of the brakes
+        while (!s->swapped.empty() && static_cast<int32_t>(s->running.size()) < s->max_running) {
+            auto& r = s->swapped.front();
+            const int32_t nb = static_cast<int32_t>(r.host_slots.size());
+            const int32_t need = std::max(nb, ceil_div(static_cast<int64_t>(r.ctx) + 1, mikv::kBlockSize));
+            std::vector<int32_t> ids(static_cast<size_t>(need));
+            if (mi_kv_alloc_blocks(s->pool, need, ids.data()) != MI_OK) break;
+            for (int32_t j = 0; j < nb; ++j) {
+                swap_in[2 * n_si] = r.host_slots[j];
+                swap_in[2 * n_si + 1] = ids[j];
+                ++n_si;
+            }
+            for (int32_t slot : r.host_slots) s->host_free.push_back(slot);
+            r.host_slots.clear();
+            r.blocks = std::move(ids);
+            s->running.push_back(std::move(r));
+            s->swapped.pop_front();
+        }
         // (3) admission
         const bool decoding = !s->running.empty();
         counts->brake = brake_state(s, decoding);
         std::vector<mi_sched_s::Req> admitted;
-        while (!s->waiting.empty() &&
+        while (!s->waiting.empty() && s->swapped.empty() &&
                static_cast<int32_t>(s->running.size() + admitted.size()) < s->max_running) {
             if (brake_state(s, decoding) != MI_BRAKE_PROCEED) break;
             auto& r = s->waiting.front();
@@ -197,6 +265,9 @@ extern "C" int mi_sched_step(mi_sched_t s, mi_sched_counts* counts, int64_t* seq
         counts->num_decode = static_cast<int32_t>(s->running.size());
         counts->num_preempted = n_pre;
         counts->num_finished = n_fin;
+        counts->num_swapped_out = n_swp;
+        counts->num_swap_out = n_so;
+        counts->num_swap_in = n_si;
         for (auto& r : s->running) {
             r.ctx += 1;
             r.generated += 1;

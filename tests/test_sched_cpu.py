@@ -16,6 +16,9 @@ def _compare(plan, ref, mbps):
     assert plan["brake"] == ref.brake
     assert list(plan["preempted"]) == ref.preempted
     assert list(plan["finished"]) == ref.finished
+    assert list(plan["swapped_out"]) == ref.swapped_out
+    assert [tuple(x) for x in plan["swap_out"]] == ref.swap_out
+    assert [tuple(x) for x in plan["swap_in"]] == ref.swap_in
     for i, (rid, ctx, n, blocks) in enumerate(rows):
         assert plan["ids"][i] == rid and plan["context_lens"][i] == ctx and plan["new_tokens"][i] == n
         want = np.full(mbps, -1, np.int32)
@@ -23,11 +26,12 @@ def _compare(plan, ref, mbps):
         assert np.array_equal(plan["block_table"][i], want)
 
 
-def _run(N, mbps, max_running, requests, hard=0.10, soft=0.30, max_steps=5000):
+def _run(N, mbps, max_running, requests, hard=0.10, soft=0.30, max_steps=5000, host_slots=0):
     """requests: list of (arrival_step, rid, prompt, max_new)."""
     pool = mk.mi_kv_pool_init(N, 16, 2, 64, flags=mk.MI_POOL_HOST_ONLY)
-    s = mk.Scheduler(pool, mbps, max_running, hard, soft)
-    ref = sched.Scheduler(N, max_running=max_running, hard=hard, soft=soft, max_blocks_per_seq=mbps)
+    s = mk.Scheduler(pool, mbps, max_running, hard, soft, host_slots=host_slots)
+    ref = sched.Scheduler(N, max_running=max_running, hard=hard, soft=soft, max_blocks_per_seq=mbps,
+                          host_slots=host_slots)
     try:
         pending = sorted(requests)
         brakes = set()
@@ -44,6 +48,7 @@ def _run(N, mbps, max_running, requests, hard=0.10, soft=0.30, max_steps=5000):
             if not pending and ref.idle():
                 break
         assert ref.idle() and s.num_waiting() == 0 and s.num_running() == 0
+        assert s.num_swapped() == 0
         assert mk.mi_kv_num_free_blocks(pool) == N
         return brakes
     finally:
@@ -91,3 +96,19 @@ def test_submit_refuses_requests_that_can_never_fit():
         s.close()
         assert mk.mi_kv_num_free_blocks(pool) == 10  # destroy returned the blocks
         mk.mi_kv_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_swap_streams_match_the_oracle(seed):
+    rng = np.random.default_rng(200 + seed)
+    N = int(rng.integers(16, 80))
+    mbps = int(rng.integers(6, 30))
+    reqs = []
+    for rid in range(int(rng.integers(20, 60))):
+        prompt = int(rng.integers(1, 16 * mbps // 2))
+        new = int(rng.integers(1, 16 * mbps - prompt + 1))
+        if paged.blocks_needed(prompt + new, 16) > min(N, mbps):
+            continue
+        reqs.append((int(rng.integers(0, 100)), rid, prompt, new))
+    _run(N, mbps, int(rng.integers(2, 8)), reqs, hard=float(rng.choice([0.0, 0.1])),
+         soft=float(rng.choice([0.0, 0.3])), host_slots=int(rng.integers(0, 3 * N)))
