@@ -174,6 +174,51 @@ def run_prefill_bench(args, torch, mk, workloads):
     }
 
 
+def run_offload_bench(args, torch, mk, workloads):
+    """KV offload path: 2048 blocks of a Qwen3-8B-shaped pool (8 KV heads,
+    D 128: 32 KiB per block per cache, 128 MiB in all) swapped out to
+    page-locked host memory and back, once as one run of consecutive blocks
+    and slots and once as scattered pairs (a shuffled block table). PCIe GB/s
+    per direction, K and V bytes."""
+    dev = "cuda:0"
+    N, Hkv, D, n = 4096, 8, 128, 2048
+    kd = torch.zeros((N, Hkv, 16, D), dtype=torch.int16, device=dev)
+    vd = torch.zeros_like(kd)
+    hk = torch.zeros((n, Hkv, 16, D), dtype=torch.int16, pin_memory=True)
+    hv = torch.zeros_like(hk)
+    pool = mk.mi_kv_pool_init(N, 16, Hkv, D, kd, vd)
+    rng = np.random.default_rng(7)
+    res = {}
+    nbytes = 2 * n * Hkv * 16 * D * 2
+    try:
+        for name, ids in (("contiguous", np.arange(n, dtype=np.int32)),
+                          ("scattered", rng.permutation(N)[:n].astype(np.int32))):
+            out_pairs = np.stack([ids, np.arange(n, dtype=np.int32)], 1)
+            in_pairs = np.stack([np.arange(n, dtype=np.int32), ids], 1)
+            for _ in range(2):
+                mk.mi_kv_swap_out(pool, hk, hv, n, out_pairs)
+                mk.mi_kv_swap_in(pool, hk, hv, n, in_pairs)
+            torch.cuda.synchronize()
+            times = {}
+            for label, fn, pairs in (("out", mk.mi_kv_swap_out, out_pairs),
+                                     ("in", mk.mi_kv_swap_in, in_pairs)):
+                t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 5
+                t0.record()
+                for _ in range(reps):
+                    fn(pool, hk, hv, n, pairs)
+                t1.record()
+                torch.cuda.synchronize()
+                times[label] = t0.elapsed_time(t1) / reps
+            res[name] = {"swap_out_ms": round(times["out"], 3), "swap_in_ms": round(times["in"], 3),
+                         "swap_out_GBps": round(nbytes / (times["out"] * 1e-3) / 1e9, 1),
+                         "swap_in_GBps": round(nbytes / (times["in"] * 1e-3) / 1e9, 1)}
+    finally:
+        mk.mi_kv_pool_destroy(pool)
+    res["bytes_per_direction"] = nbytes
+    return res
+
+
 def run_small_workloads(args, torch, mk, workloads):
     """Decode step (write + attention) on the other decode workloads: step time,
     algorithmic GB/s and fraction of the HBM peak (most are launch-latency bound)."""
@@ -328,6 +373,7 @@ def main():
     ap.add_argument("--no-small", action="store_true", help="skip the smaller decode workloads")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache variant of the step")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill chunk")
+    ap.add_argument("--no-offload", action="store_true", help="skip the KV swap measurement")
     ap.add_argument("--layer-only", action="store_true",
                     help="time only the full-layer step (for its kernel profile)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -429,6 +475,8 @@ def main():
         }
     if not args.no_prefill:
         line["prefill"] = run_prefill_bench(args, torch, mk, workloads)
+    if not args.no_offload:
+        line["kv_offload"] = run_offload_bench(args, torch, mk, workloads)
     if not args.no_layer:
         try:
             line["layer_step"] = run_layer_bench(args, torch, mk, workloads)
