@@ -319,35 +319,60 @@ struct MfmaSoftmax {
     float l;      // this lane's sum of 2^(s - m)
 };
 
-// One 16-token tile. Column n (query head in decode, query token in
-// prefill) is live if col_ok. With tail set, key row t of the tile counts for
-// column n only if t < qlim (the lane's column limit: the rows written so far
-// in decode, the causal limit in prefill), and V rows t >= valid_rows are
-// zeroed (their bits may be NaN).
-template <int D, int FMT, int NPV = MfmaTile<D, FMT>::NPV>
-__device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>::NKL],
-                                             uint32_t (&vr)[4][MfmaTile<D, FMT>::VW],
-                                             const uint4 (&qb)[MfmaTile<D, FMT>::NQK], float sl2,
-                                             bool col_ok, int q4, int qlim, int valid_rows,
-                                             bool tail, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
-    using TL = MfmaTile<D, FMT>;
-    // ---- scores of tokens 4q4 .. 4q4+3 for head n
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < TL::NQK; ++j) {
-        uint4 a;
-        if constexpr (FMT == kFmtBf16) {
-            a = kr[j];
-        } else {
-            const uint4 w = kr[j / 2];
-            const uint32_t w0 = (j & 1) ? w.z : w.x;
-            const uint32_t w1 = (j & 1) ? w.w : w.y;
-            a = make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
-                           fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
-        }
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                    __builtin_bit_cast(bf16x8_t, qb[j]), s, 0, 0, 0);
+// Operand builders of one 16-token tile.
+// K operand of 32-dim slice j: the lane's key row, 8 dims (bf16; E4M3 codes
+// widened exactly).
+template <int D, int FMT>
+__device__ __forceinline__ uint4 k_operand(const uint4 (&kr)[MfmaTile<D, FMT>::NKL], int j) {
+    if constexpr (FMT == kFmtBf16) {
+        return kr[j];
+    } else {
+        const uint4 w = kr[j / 2];
+        const uint32_t w0 = (j & 1) ? w.z : w.x;
+        const uint32_t w1 = (j & 1) ? w.w : w.y;
+        return make_uint4(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                          fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1));
     }
+}
+
+// V^T operands (one per output MFMA): dim psi of key rows 4q4 .. 4q4+3, built
+// by 16-bit permutes of the four rows the lane loaded. With tail, rows >=
+// valid_rows are zeroed (their bits may be NaN and 0 * NaN would reach the
+// sum).
+template <int D, int FMT>
+__device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][MfmaTile<D, FMT>::VW], int q4,
+                                           int valid_rows, bool tail,
+                                           s16x4_t (&vt)[MfmaTile<D, FMT>::NPV]) {
+    using TL = MfmaTile<D, FMT>;
+    uint32_t bw[4][TL::BW];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool ok = !tail || 4 * q4 + r < valid_rows;
+#pragma unroll
+        for (int e = 0; e < TL::BW; ++e) {
+            uint32_t x;
+            if constexpr (FMT == kFmtBf16) x = vr[r][e];
+            else x = (e & 1) ? fp8x2_to_bf16x2<true>(vr[r][e / 2]) : fp8x2_to_bf16x2<false>(vr[r][e / 2]);
+            bw[r][e] = ok ? x : 0u;
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < TL::NPV; ++jj) {
+        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+        const int e = jj / 2;
+        const uint32_t lo = __builtin_amdgcn_perm(bw[1][e], bw[0][e], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(bw[3][e], bw[2][e], sel);
+        vt[jj] = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
+    }
+}
+
+// Online-softmax step of one column block: scores of key rows 4q4 .. 4q4+3
+// for column n, masked (column dead, or with tail a key row >= qlim), the
+// running max raised only past the slack (one wave vote), the lane's sum
+// updated; returns the P^T operand (weights rounded to bf16).
+template <int NPV>
+__device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_ok, int q4, int qlim,
+                                                 bool tail, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -372,37 +397,76 @@ __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>:
         p[i] = __builtin_amdgcn_exp2f(sc[i] - sm.m);
         sm.l += p[i];
     }
-    const bf16x4_t pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
-                         static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
-    // ---- V rows 4q4 .. 4q4+3 as bf16 words (masked rows zeroed: their bits
-    // may be NaN and 0 * NaN would reach the sum)
-    uint32_t bw[4][TL::BW];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const bool ok = !tail || 4 * q4 + r < valid_rows;
-#pragma unroll
-        for (int e = 0; e < TL::BW; ++e) {
-            uint32_t x;
-            if constexpr (FMT == kFmtBf16) x = vr[r][e];
-            else x = (e & 1) ? fp8x2_to_bf16x2<true>(vr[r][e / 2]) : fp8x2_to_bf16x2<false>(vr[r][e / 2]);
-            bw[r][e] = ok ? x : 0u;
-        }
-    }
-#pragma unroll
-    for (int jj = 0; jj < NPV; ++jj) {
-        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-        const int e = jj / 2;
-        const uint32_t lo = __builtin_amdgcn_perm(bw[1][e], bw[0][e], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(bw[3][e], bw[2][e], sel);
-        const s16x4_t a = __builtin_bit_cast(s16x4_t, make_uint2(lo, hi));
-        o[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4_t, pb), o[jj], 0, 0, 0);
-    }
+    return bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                    static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
 }
+
+// One 16-token tile for QB column blocks of 16 (query heads in decode, QB = 1;
+// query tokens in prefill). The K operands and the V^T operands are built
+// once and shared by every block. Column n of block c is live if col_ok[c];
+// with tail, key row t counts for it only if t < qlim[c] (the rows written so
+// far in decode, the causal limit in prefill), and V rows >= valid_rows are
+// zeroed.
+template <int D, int FMT, int QB>
+__device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>::NKL],
+                                             const uint32_t (&vr)[4][MfmaTile<D, FMT>::VW],
+                                             const uint4 (&qb)[QB][MfmaTile<D, FMT>::NQK],
+                                             float sl2, const bool (&col_ok)[QB], int q4,
+                                             const int (&qlim)[QB], int valid_rows, bool tail,
+                                             MfmaSoftmax (&sm)[QB],
+                                             f32x4_t (&o)[QB][MfmaTile<D, FMT>::NPV]) {
+    using TL = MfmaTile<D, FMT>;
+    uint4 a[TL::NQK];
+#pragma unroll
+    for (int j = 0; j < TL::NQK; ++j) a[j] = k_operand<D, FMT>(kr, j);
+    bf16x4_t pb[QB];
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < TL::NQK; ++j)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
+                                                        __builtin_bit_cast(bf16x8_t, qb[c][j]), s, 0, 0, 0);
+        pb[c] = softmax_step<TL::NPV>(s, sl2, col_ok[c], q4, qlim[c], tail, sm[c], o[c]);
+    }
+    s16x4_t vt[TL::NPV];
+    v_operands<D, FMT>(vr, q4, valid_rows, tail, vt);
+#pragma unroll
+    for (int c = 0; c < QB; ++c)
+#pragma unroll
+        for (int jj = 0; jj < TL::NPV; ++jj)
+            o[c][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                vt[jj], __builtin_bit_cast(s16x4_t, pb[c]), o[c][jj], 0, 0, 0);
+}
+
+// Per-wave state of the QB column blocks.
+template <int D, int FMT, int QB>
+struct MfmaCols {
+    using TL = MfmaTile<D, FMT>;
+    uint4 qb[QB][TL::NQK];
+    bool col_ok[QB];
+    MfmaSoftmax sm[QB];
+    f32x4_t o[QB][TL::NPV];
+    float sl2;
+    int q4;
+
+    __device__ __forceinline__ void consume(const uint4 (&kr)[TL::NKL], const uint32_t (&vr)[4][TL::VW],
+                                            const int (&qlim)[QB], int valid_rows, bool tail) {
+        mfma_consume<D, FMT, QB>(kr, vr, qb, sl2, col_ok, q4, qlim, valid_rows, tail, sm, o);
+    }
+    // unmasked tile, or a tile whose rows >= valid_rows are masked for every column
+    __device__ __forceinline__ void consume_rows(const uint4 (&kr)[TL::NKL], const uint32_t (&vr)[4][TL::VW],
+                                                 int valid_rows, bool tail) {
+        int lim[QB];
+#pragma unroll
+        for (int c = 0; c < QB; ++c) lim[c] = valid_rows;
+        consume(kr, vr, lim, valid_rows, tail);
+    }
+};
 
 template <int D, int FMT, int PF>
 struct MfmaRing {
     using TL = MfmaTile<D, FMT>;
-    static constexpr int NPV = TL::NPV;
     uint4 kr[PF + 1][TL::NKL];
     uint32_t vr[PF + 1][4][TL::VW];
     const char* kbase;
@@ -429,32 +493,38 @@ struct MfmaRing {
             prologue<S + 1>(nblk);
         }
     }
-    template <int U>
-    __device__ __forceinline__ void steady(int i, int nblk, const uint4 (&qb)[TL::NQK], float sl2,
-                                           bool col_ok, int q4, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
+    // PF + 1 full tiles i .. i+PF; tile i+U prefetches tile i+U+PF
+    template <int U, class Cols>
+    __device__ __forceinline__ void steady(int i, int nblk, Cols& cols) {
         if constexpr (U <= PF) {
             load<(U + PF) % (PF + 1)>(min(i + U + PF, nblk - 1));
-            mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, col_ok, q4, BS, BS, false, sm, o);
-            steady<U + 1>(i, nblk, qb, sl2, col_ok, q4, sm, o);
+            cols.consume_rows(kr[U], vr[U], BS, false);
+            steady<U + 1>(i, nblk, cols);
         }
     }
-    template <int U>
-    __device__ __forceinline__ void rest(int i, int nblk, int valid_rows, const uint4 (&qb)[TL::NQK],
-                                         float sl2, bool col_ok, int q4, MfmaSoftmax& sm,
-                                         f32x4_t (&o)[NPV]) {
+    // the last nblk - i (1 .. PF+1) tiles, all already requested; the final
+    // one may be partial (valid_rows < 16)
+    template <int U, class Cols>
+    __device__ __forceinline__ void rest(int i, int nblk, int valid_rows, Cols& cols) {
         if constexpr (U <= PF) {
             const int tile = i + U;
             if (tile < nblk - 1) {
-                mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, col_ok, q4, BS, BS, false, sm, o);
+                cols.consume_rows(kr[U], vr[U], BS, false);
             } else if (tile == nblk - 1) {
-                if (valid_rows == BS)
-                    mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, col_ok, q4, BS, BS, false, sm, o);
-                else
-                    mfma_consume<D, FMT>(kr[U], vr[U], qb, sl2, col_ok, q4, valid_rows, valid_rows,
-                                         true, sm, o);
+                if (valid_rows == BS) cols.consume_rows(kr[U], vr[U], BS, false);
+                else cols.consume_rows(kr[U], vr[U], valid_rows, true);
             }
-            rest<U + 1>(i, nblk, valid_rows, qb, sl2, col_ok, q4, sm, o);
+            rest<U + 1>(i, nblk, valid_rows, cols);
         }
+    }
+    // every tile of [0, nblk): the unrolled ring loop
+    template <class Cols>
+    __device__ __forceinline__ void run(int nblk, int last_rows, Cols& cols) {
+        prologue<0>(nblk);
+        int i = 0;
+        for (; i + PF + 1 < nblk; i += PF + 1) steady<0>(i, nblk, cols);
+        load<PF>(min(i + PF, nblk - 1));
+        rest<0>(i, nblk, last_rows, cols);
     }
 };
 
@@ -502,23 +572,26 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
 
         // Q^T operand: head n, the lane's 8 dims of each 32-dim slice (the
         // same dims its K row supplies)
-        uint4 qb[TL::NQK];
+        MfmaCols<D, FMT, 1> cols;
         const uint16_t* qh = q_rot + (static_cast<size_t>(b) * hkv * G + g * G + (head_ok ? n : 0)) * D;
 #pragma unroll
         for (int j = 0; j < TL::NQK; ++j) {
             const int d0 = FMT == kFmtBf16 ? 32 * j + 8 * q4 : 64 * (j / 2) + 16 * q4 + 8 * (j & 1);
-            qb[j] = head_ok ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
+            cols.qb[0][j] = head_ok ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
         }
-        float sl2 = scale_log2;
+        cols.sl2 = scale_log2;
         float vscale = 1.f;
         if constexpr (FMT == kFmtFp8) {
-            sl2 *= kv_scales[g];
+            cols.sl2 *= kv_scales[g];
             vscale = kv_scales[hkv + g];
         }
-        MfmaSoftmax sm{head_ok ? kNegInf : 0.f, 0.f};
-        f32x4_t o[NPV];
+        cols.q4 = q4;
+        cols.col_ok[0] = head_ok;
+        cols.sm[0] = MfmaSoftmax{head_ok ? kNegInf : 0.f, 0.f};
 #pragma unroll
-        for (int jj = 0; jj < NPV; ++jj) o[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < NPV; ++jj) cols.o[0][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        MfmaSoftmax& sm = cols.sm[0];
+        f32x4_t (&o)[NPV] = cols.o[0];
 
         MfmaRing<D, FMT, PF> ring;
         ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
@@ -542,12 +615,7 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
             // tile, a cache hit), so the wait before each tile covers exactly
             // the older loads.
             const int last_rows = (s0 + nblk == nt) ? L - (nt - 1) * BS : BS;
-            ring.template prologue<0>(nblk);
-            int i = 0;
-            for (; i + PF + 1 < nblk; i += PF + 1)
-                ring.template steady<0>(i, nblk, qb, sl2, head_ok, q4, sm, o);
-            ring.template load<PF>(min(i + PF, nblk - 1));
-            ring.template rest<0>(i, nblk, last_rows, qb, sl2, head_ok, q4, sm, o);
+            ring.run(nblk, last_rows, cols);
         }
 
         // head totals of the lane sums (same bits in the 4 lanes of a head)
@@ -591,14 +659,15 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
 
 // ======================================================== paged prefill
 // Causal attention of a prefill chunk (packed rows, see the PREFILL write).
-// One wave per (block of 16 new tokens, query head): the MFMA tile of the
-// decode kernel with the 16 columns taken by the block's query tokens
-// instead of the group's heads. The wave streams its sequence's K/V tiles
-// 0 .. last in logical order; tiles whose keys all lie at or before the
-// block's first position are unmasked and go through the register ring, the
-// one or two tiles on the diagonal follow with a per-column causal limit.
-// Blocks are issued longest first (largest key range).
-template <int D, int G, int FMT, int PF>
+// One wave per (block of 16 QB new tokens, query head): the MFMA tile of the
+// decode kernel with QB column blocks taken by the block's query tokens
+// instead of the group's heads, so every K/V tile a wave loads serves 16 QB
+// queries. The wave streams its sequence's K/V tiles 0 .. last in logical
+// order; tiles whose keys all lie at or before the block's first position
+// are unmasked and go through the register ring, the tiles on the diagonal
+// (at most QB + 1) follow with a per-column causal limit. Blocks are issued
+// longest first (largest key range).
+template <int D, int G, int FMT, int PF, int QB>
 __global__ __launch_bounds__(64) void paged_prefill_kernel(
     const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
@@ -607,6 +676,7 @@ __global__ __launch_bounds__(64) void paged_prefill_kernel(
     const float* __restrict__ kv_scales, uint16_t* __restrict__ out, uint32_t* __restrict__ err) {
     using TL = MfmaTile<D, FMT>;
     constexpr int NPV = TL::NPV;
+    constexpr int QT = BS * QB;                  // query tokens per wave
     constexpr size_t TILE = static_cast<size_t>(BS) * TL::ROW;
     const int lane = threadIdx.x;
     const int n = lane & 15;
@@ -623,34 +693,38 @@ __global__ __launch_bounds__(64) void paged_prefill_kernel(
             atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
         return;
     }
-    const int nqb = (nnew + BS - 1) / BS;
+    const int nqb = (nnew + QT - 1) / QT;
     if (static_cast<int>(blockIdx.x) >= nqb) return;
-    const int qb = nqb - 1 - static_cast<int>(blockIdx.x);
-    const int j = qb * BS + n;                   // this lane's query token
-    const bool col_ok = j < nnew;
-    const int p_first = ctx + qb * BS;
-    const int p_last = ctx + min(qb * BS + BS, nnew) - 1;
-    const int p_n = ctx + j;
+    const int j0 = (nqb - 1 - static_cast<int>(blockIdx.x)) * QT;   // first query token
+    const int p_first = ctx + j0;
+    const int p_last = ctx + min(j0 + QT, nnew) - 1;
     const int nkt = p_last / BS + 1;             // tiles holding keys 0 .. p_last
     const int kt_m = (p_first + 1) / BS;         // tiles below are unmasked for every query
 
-    uint4 qb_op[TL::NQK];
-    const uint16_t* qh = q_rot + (static_cast<size_t>(row0 + (col_ok ? j : 0)) * hkv * G + h) * D;
+    MfmaCols<D, FMT, QB> cols;
+    int p_n[QB];
 #pragma unroll
-    for (int jj = 0; jj < TL::NQK; ++jj) {
-        const int d0 = FMT == kFmtBf16 ? 32 * jj + 8 * q4 : 64 * (jj / 2) + 16 * q4 + 8 * (jj & 1);
-        qb_op[jj] = col_ok ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < QB; ++c) {
+        const int j = j0 + BS * c + n;
+        cols.col_ok[c] = j < nnew;
+        p_n[c] = ctx + j;
+        const uint16_t* qh = q_rot + (static_cast<size_t>(row0 + (cols.col_ok[c] ? j : 0)) * hkv * G + h) * D;
+#pragma unroll
+        for (int jj = 0; jj < TL::NQK; ++jj) {
+            const int d0 = FMT == kFmtBf16 ? 32 * jj + 8 * q4 : 64 * (jj / 2) + 16 * q4 + 8 * (jj & 1);
+            cols.qb[c][jj] = cols.col_ok[c] ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
+        }
+        cols.sm[c] = MfmaSoftmax{cols.col_ok[c] ? kNegInf : 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < NPV; ++jj) cols.o[c][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    float sl2 = scale_log2;
+    cols.sl2 = scale_log2;
+    cols.q4 = q4;
     float vscale = 1.f;
     if constexpr (FMT == kFmtFp8) {
-        sl2 *= kv_scales[g];
+        cols.sl2 *= kv_scales[g];
         vscale = kv_scales[hkv + g];
     }
-    MfmaSoftmax sm{col_ok ? kNegInf : 0.f, 0.f};
-    f32x4_t o[NPV];
-#pragma unroll
-    for (int jj = 0; jj < NPV; ++jj) o[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     MfmaRing<D, FMT, PF> ring;
     ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
@@ -673,39 +747,33 @@ __global__ __launch_bounds__(64) void paged_prefill_kernel(
     for (int s0 = 0; s0 < kt_m; s0 += 64) {
         const int nblk = min(64, kt_m - s0);
         fetch_ids(s0, nblk);
-        ring.template prologue<0>(nblk);
-        int i = 0;
-        for (; i + PF + 1 < nblk; i += PF + 1)
-            ring.template steady<0>(i, nblk, qb_op, sl2, col_ok, q4, sm, o);
-        ring.template load<PF>(min(i + PF, nblk - 1));
-        ring.template rest<0>(i, nblk, BS, qb_op, sl2, col_ok, q4, sm, o);
+        ring.run(nblk, BS, cols);
     }
-    // the diagonal tiles [kt_m, nkt) (one or two), causal limit per column
+    // the diagonal tiles [kt_m, nkt), causal limit per column
     fetch_ids(kt_m, nkt - kt_m);
-    ring.template load<0>(0);
-    if (nkt - kt_m > 1) ring.template load<1>(1);
     for (int t = 0; t < nkt - kt_m; ++t) {
         const int base = (kt_m + t) * BS;
-        const int qlim = min(BS, max(0, p_n + 1 - base));
-        const int vrows = min(BS, p_last + 1 - base);
-        if (t == 0)
-            mfma_consume<D, FMT>(ring.kr[0], ring.vr[0], qb_op, sl2, col_ok, q4, qlim, vrows, true, sm, o);
-        else
-            mfma_consume<D, FMT>(ring.kr[1], ring.vr[1], qb_op, sl2, col_ok, q4, qlim, vrows, true, sm, o);
+        int qlim[QB];
+#pragma unroll
+        for (int c = 0; c < QB; ++c) qlim[c] = min(BS, max(0, p_n[c] + 1 - base));
+        ring.template load<0>(t);
+        cols.consume(ring.kr[0], ring.vr[0], qlim, min(BS, p_last + 1 - base), true);
     }
 
-    float lt = sm.l + __shfl_xor(sm.l, 16);
-    lt += __shfl_xor(lt, 32);
-    if (col_ok) {
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
+        float lt = cols.sm[c].l + __shfl_xor(cols.sm[c].l, 16);
+        lt += __shfl_xor(lt, 32);
+        if (!cols.col_ok[c]) continue;
         const float inv = vscale / lt;
-        uint16_t* oh = out + (static_cast<size_t>(row0 + j) * hkv * G + h) * D + NPV * 4 * q4;
+        uint16_t* oh = out + (static_cast<size_t>(row0 + j0 + BS * c + n) * hkv * G + h) * D + NPV * 4 * q4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             uint32_t wd[NPV / 2];
 #pragma unroll
             for (int e = 0; e < NPV / 2; ++e)
-                wd[e] = static_cast<uint32_t>(f32_to_bf16_rne(o[2 * e][r] * inv)) |
-                        (static_cast<uint32_t>(f32_to_bf16_rne(o[2 * e + 1][r] * inv)) << 16);
+                wd[e] = static_cast<uint32_t>(f32_to_bf16_rne(cols.o[c][2 * e][r] * inv)) |
+                        (static_cast<uint32_t>(f32_to_bf16_rne(cols.o[c][2 * e + 1][r] * inv)) << 16);
             if constexpr (NPV == 8)
                 *reinterpret_cast<uint4*>(oh + NPV * r) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
             else
@@ -860,6 +928,12 @@ constexpr int kAttnWavesPerCU = MIKV_TUNE_WAVES_PER_CU;
 #else
 constexpr int kAttnWavesPerCU = 4;
 #endif
+// Query column blocks of 16 per prefill wave.
+#ifdef MIKV_TUNE_PREFILL_QB
+constexpr int kPrefillQB = MIKV_TUNE_PREFILL_QB;
+#else
+constexpr int kPrefillQB = 3;
+#endif
 
 // Grid of the attention kernel on the current device: CUs x min(waves per
 // CU, resident workgroups per CU at the kernel's register budget), cached
@@ -925,9 +999,9 @@ void launch_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                     const int32_t* table, int32_t mbps, const int32_t* ctx, const int32_t* cu,
                     int32_t batch, int32_t total, int32_t max_new, float scale_log2, hipStream_t st) {
     const int hkv = p->num_kv_heads;
-    auto kern = mikv::pool_fp8(p) ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8>
-                                  : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch>;
-    const dim3 grid((max_new + BS - 1) / BS, hkv * G, batch);
+    auto kern = mikv::pool_fp8(p) ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQB>
+                                  : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQB>;
+    const dim3 grid((max_new + BS * kPrefillQB - 1) / (BS * kPrefillQB), hkv * G, batch);
     hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
                        static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, hkv, p->num_blocks,
                        total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err);
