@@ -52,14 +52,6 @@ __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
     return static_cast<double>(__uint_as_float(static_cast<uint32_t>(h) << 16));
 }
 
-// K/V tiles are streamed once per call: non-temporal loads keep them from
-// displacing reusable lines in the caches.
-__device__ __forceinline__ uint4 ld16_stream(const char* base, uint32_t off) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
-    return make_uint4(t.x, t.y, t.z, t.w);
-}
-
 // ============================================================== write_decode_kv
 // One thread per rotated pair (i, i + D/2) of one head, q heads first, then
 // the new k heads, then 16-byte pieces of the V copy; workgroups of 256
@@ -292,18 +284,23 @@ struct MfmaTile {
     static_assert(NKL >= 1 && VW >= 1, "head_dim");
 };
 
-template <int NB>
-__device__ __forceinline__ void ld_stream_words(const char* base, uint32_t off, uint32_t (&w)[NB / 4]) {
+// NB-byte load of words; NT: non-temporal (each tile streamed once, decode),
+// else an ordinary cached load (tiles read again, prefill).
+template <int NB, bool NT>
+__device__ __forceinline__ void ld_words(const char* base, uint32_t off, uint32_t (&w)[NB / 4]) {
     if constexpr (NB == 16) {
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+        const u32x4* p = reinterpret_cast<const u32x4*>(base + off);
+        const u32x4 t = NT ? __builtin_nontemporal_load(p) : *p;
         w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
     } else if constexpr (NB == 8) {
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(base + off));
+        const u32x2* p = reinterpret_cast<const u32x2*>(base + off);
+        const u32x2 t = NT ? __builtin_nontemporal_load(p) : *p;
         w[0] = t.x; w[1] = t.y;
     } else {
-        w[0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned int*>(base + off));
+        const unsigned int* p = reinterpret_cast<const unsigned int*>(base + off);
+        w[0] = NT ? __builtin_nontemporal_load(p) : *p;
     }
 }
 
@@ -464,7 +461,9 @@ struct MfmaCols {
     }
 };
 
-template <int D, int FMT, int PF>
+// NT: non-temporal K/V loads (decode: every tile is read once per call);
+// prefill re-reads tiles across query blocks and heads and keeps them cached.
+template <int D, int FMT, int PF, bool NT = true>
 struct MfmaRing {
     using TL = MfmaTile<D, FMT>;
     uint4 kr[PF + 1][TL::NKL];
@@ -482,9 +481,13 @@ struct MfmaRing {
         const char* kb = kbase + static_cast<size_t>(id) * blk_stride;
         const char* vb = vbase + static_cast<size_t>(id) * blk_stride;
 #pragma unroll
-        for (int j = 0; j < TL::NKL; ++j) kr[S][j] = ld16_stream(kb, koff[j]);
+        for (int j = 0; j < TL::NKL; ++j) {
+            uint32_t w[4];
+            ld_words<16, NT>(kb, koff[j], w);
+            kr[S][j] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ld_stream_words<TL::VB>(vb, voff[r], vr[S][r]);
+        for (int r = 0; r < 4; ++r) ld_words<TL::VB, NT>(vb, voff[r], vr[S][r]);
     }
     template <int S>
     __device__ __forceinline__ void prologue(int nblk) {
@@ -662,7 +665,8 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
 // One wave per (block of 16 QB new tokens, query head): the MFMA tile of the
 // decode kernel with QB column blocks taken by the block's query tokens
 // instead of the group's heads, so every K/V tile a wave loads serves 16 QB
-// queries. The wave streams its sequence's K/V tiles 0 .. last in logical
+// queries; the loads are ordinary cached loads, since the other query blocks
+// and heads of the sequence read the same tiles. The wave streams its sequence's K/V tiles 0 .. last in logical
 // order; tiles whose keys all lie at or before the block's first position
 // are unmasked and go through the register ring, the tiles on the diagonal
 // (at most QB + 1) follow with a per-column causal limit. Blocks are issued
@@ -726,7 +730,7 @@ __global__ __launch_bounds__(64) void paged_prefill_kernel(
         vscale = kv_scales[hkv + g];
     }
 
-    MfmaRing<D, FMT, PF> ring;
+    MfmaRing<D, FMT, PF, false> ring;
     ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
     ring.vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
     ring.blk_stride = static_cast<size_t>(hkv) * TILE;
