@@ -276,3 +276,63 @@ def prefill_step(k_pool, v_pool, q, k, v, block_table, context_lens, cu_seqlens,
     out = paged_prefill_attention(q_rot_bits, k_new, v_new, block_table, context_lens,
                                   cu_seqlens, block_size, scale)
     return out, k_new, v_new, q_rot_bits
+
+
+def write_prefill_kv_fp8(k_pool8, v_pool8, q, k, v, block_table, context_lens, cu_seqlens,
+                         block_size, theta, k_scales, v_scales):
+    """write_prefill_kv into an 8-bit cache: every new token's bf16 K (rotated)
+    and V are quantised with their KV head's scales, as in
+    write_decode_kv_fp8. Returns (k_pool_new, v_pool_new, q_rot_bits)."""
+    k_new = np.array(k_pool8, dtype=np.uint8, copy=True)
+    v_new = np.array(v_pool8, dtype=np.uint8, copy=True)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    q_rot = np.empty((T, Hq, D), dtype=np.float64)
+    for i, b, pos in _prefill_rows(context_lens, cu_seqlens):
+        blk, off = paged.slot(block_table[b], pos, block_size)
+        for g in range(Hkv):
+            k_rot = bf16.decode(bf16.encode(rope.apply(bf16.decode(k[i, g]), pos, theta)))
+            k_new[blk, g, off, :] = fp8.quantize(k_rot, k_scales[g])
+            v_new[blk, g, off, :] = fp8.quantize(bf16.decode(v[i, g]), v_scales[g])
+        for h in range(Hq):
+            q_rot[i, h] = rope.apply(bf16.decode(q[i, h]), pos, theta)
+    return k_new, v_new, bf16.encode(q_rot)
+
+
+def paged_prefill_attention_fp8(q_rot, k_pool8, v_pool8, block_table, context_lens, cu_seqlens,
+                                block_size, k_scales, v_scales, scale=None):
+    """Causal prefill attention over an 8-bit cache: the codes gathered through
+    the block table are dequantised with their head's scales, then the same
+    causal attention as paged_prefill_attention. Returns float64 [T, Hq, D]."""
+    qf = bf16.decode(q_rot)
+    T, Hq, D = qf.shape
+    Hkv = k_pool8.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(np.float64(D))
+    out = np.empty((T, Hq, D), dtype=np.float64)
+    for b in range(len(context_lens)):
+        lo, hi = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        if hi == lo:
+            continue
+        last = int(context_lens[b]) + hi - lo
+        for g in range(Hkv):
+            ks, vs = gather_kv(k_pool8, v_pool8, block_table, block_size, b, g, last)
+            K, V = fp8.dequantize(ks, k_scales[g]), fp8.dequantize(vs, v_scales[g])
+            for i in range(lo, hi):
+                L = int(context_lens[b]) + i - lo + 1
+                for h in range(g * G, (g + 1) * G):
+                    out[i, h] = attend(qf[i, h], K[:L], V[:L], scale)
+    return out
+
+
+def prefill_step_fp8(k_pool8, v_pool8, q, k, v, block_table, context_lens, cu_seqlens,
+                     block_size, theta, k_scales, v_scales, scale=None):
+    """write_prefill_kv_fp8 followed by paged_prefill_attention_fp8.
+    Returns (out_f64, k_pool_new, v_pool_new, q_rot_bits)."""
+    k_new, v_new, q_rot_bits = write_prefill_kv_fp8(k_pool8, v_pool8, q, k, v, block_table,
+                                                    context_lens, cu_seqlens, block_size, theta,
+                                                    k_scales, v_scales)
+    out = paged_prefill_attention_fp8(q_rot_bits, k_new, v_new, block_table, context_lens,
+                                      cu_seqlens, block_size, k_scales, v_scales, scale)
+    return out, k_new, v_new, q_rot_bits

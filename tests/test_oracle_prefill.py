@@ -115,3 +115,30 @@ def test_prefill_flops_closed_form():
     # one sequence, no prefix, n tokens: sum_{p<n} (p+1) = n(n+1)/2 key visits
     assert workloads.prefill_flops([0], [4], 2, 8) == 4 * 8 * 2 * 10
     assert workloads.prefill_flops([3], [2], 1, 1) == 4 * (4 + 5)
+
+
+def test_fp8_prefill_composes_the_pinned_pieces():
+    """8-bit prefill: single-token chunks equal the pinned 8-bit decode step;
+    the attention over codes equals the pinned bf16 prefill attention over
+    their decoded values (scales as exact multipliers)."""
+    from oracle import fp8
+    ks = np.array([0.5, 2.0], np.float32)
+    vs = np.array([4.0, 0.25], np.float32)
+    one = workloads.make_prefill_case(CFG, (0, 17, 40), (1, 1, 1), kv_format="fp8")
+    out, kn, vn, qb = attention.prefill_step_fp8(one.k_pool, one.v_pool, one.q, one.k, one.v,
+                                                 one.block_table, one.context_lens, one.cu_seqlens,
+                                                 16, CFG.rope_theta, ks, vs)
+    ref, kd, vd, qd = attention.decode_step_fp8(one.k_pool, one.v_pool, one.q, one.k, one.v,
+                                                one.block_table, one.context_lens, 16,
+                                                CFG.rope_theta, ks, vs)
+    assert np.array_equal(out, ref) and np.array_equal(kn, kd) and np.array_equal(vn, vd)
+    case = workloads.make_prefill_case(CFG, (3, 16, 40), (20, 9, 30), kv_format="fp8", seed=4)
+    out, kn, vn, qb = attention.prefill_step_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                                 case.block_table, case.context_lens,
+                                                 case.cu_seqlens, 16, CFG.rope_theta, ks, vs)
+    assert np.all(np.isfinite(out))
+    kb = bf16.encode(fp8.decode(kn) * ks[None, :, None, None].astype(np.float64))
+    vb = bf16.encode(fp8.decode(vn) * vs[None, :, None, None].astype(np.float64))
+    ref = attention.paged_prefill_attention(qb, kb, vb, case.block_table, case.context_lens,
+                                            case.cu_seqlens, 16)
+    assert np.array_equal(out, ref)

@@ -320,11 +320,13 @@ PREFILL_CONFIGS = {
 }
 
 
-def make_prefill_case(cfg, context_lens, new_lens, pool="poison", seed=None, reserve=0):
+def make_prefill_case(cfg, context_lens, new_lens, pool="poison", seed=None, reserve=0,
+                      kv_format="bf16"):
     """Draw a prefill chunk. pool = "poison": cached slots [0, ctx) hold N(0,1);
     the slots the chunk will write, the tail and unallocated blocks hold NaN.
     pool = "bench": every slot of the allocated blocks holds N(0,1). The block
-    tables cover ctx + n + reserve tokens (reserve: room for decode steps)."""
+    tables cover ctx + n + reserve tokens (reserve: room for decode steps).
+    kv_format "fp8": pools of E4M3 codes (fp8_normal_like), poison 0x7F."""
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
     ctx = np.asarray(context_lens, dtype=np.int32)
     n = np.asarray(new_lens, dtype=np.int32)
@@ -347,18 +349,24 @@ def make_prefill_case(cfg, context_lens, new_lens, pool="poison", seed=None, res
     k = bf16_normal(rng, (T, Hkv, D))
     v = bf16_normal(rng, (T, Hkv, D))
     shape = (N, Hkv, bs, D)
-    fill = NAN_BF16 if pool == "poison" else np.uint16(0)
-    k_pool = np.full(shape, fill, dtype=np.uint16)
-    v_pool = np.full(shape, fill, dtype=np.uint16)
+    if kv_format == "bf16":
+        draw, nan, dt = bf16_normal, NAN_BF16, np.uint16
+    elif kv_format == "fp8":
+        draw, nan, dt = fp8_normal_like, NAN_FP8, np.uint8
+    else:
+        raise ValueError(kv_format)
+    fill = nan if pool == "poison" else dt(0)
+    k_pool = np.full(shape, fill, dtype=dt)
+    v_pool = np.full(shape, fill, dtype=dt)
     ids = np.concatenate([table[b, :need[b]] for b in range(B)])
-    k_pool[ids] = bf16_normal(rng, (len(ids), Hkv, bs, D))
-    v_pool[ids] = bf16_normal(rng, (len(ids), Hkv, bs, D))
+    k_pool[ids] = draw(rng, (len(ids), Hkv, bs, D))
+    v_pool[ids] = draw(rng, (len(ids), Hkv, bs, D))
     if pool == "poison":
         for b in range(B):
             for p in range(int(ctx[b]), need[b] * bs):
                 blk = table[b, p // bs]
-                k_pool[blk, :, p % bs, :] = NAN_BF16
-                v_pool[blk, :, p % bs, :] = NAN_BF16
+                k_pool[blk, :, p % bs, :] = nan
+                v_pool[blk, :, p % bs, :] = nan
     return PrefillCase(cfg, ctx, n, cu, table, N, q, k, v, k_pool, v_pool)
 
 
