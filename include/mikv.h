@@ -223,8 +223,8 @@ int mi_write_decode_kv(mi_kv_pool_t pool,
  *         i - cu[b] of sequence b.
  *  context_lens  device int32 [batch]: tokens cached before the chunk.
  * Every new token gets the same RoPE, rounding and store as
- * mi_write_decode_kv at its position; the table row must cover
- * context_lens[b] + n_b tokens. 8-bit pools: MI_ERR_UNSUPPORTED.
+ * mi_write_decode_kv at its position (E4M3 codes under the head's scales for
+ * an 8-bit pool); the table row must cover context_lens[b] + n_b tokens.
  */
 int mi_write_prefill_kv(mi_kv_pool_t pool, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, uint16_t* q_rot, const int32_t* block_table,
@@ -243,7 +243,8 @@ int mi_write_prefill_kv(mi_kv_pool_t pool, const uint16_t* q, const uint16_t* k,
  *  max_new_tokens  host-side bound of every n_b (sizes the grid); a larger
  *         n_b, cu beyond total_tokens or a chunk past the table row is a fault
  *         (error word) and that sequence's rows are not written.
- *  batch <= 65535. 8-bit pools: MI_ERR_UNSUPPORTED. No workspace.
+ *  batch <= 65535. No workspace. An 8-bit pool's codes are read back as
+ *  code * scale, as in mi_paged_gqa_decode.
  */
 int mi_paged_prefill_attention(mi_kv_pool_t pool, const uint16_t* q_rot, uint16_t* out,
                                const int32_t* block_table, int32_t max_blocks_per_seq,

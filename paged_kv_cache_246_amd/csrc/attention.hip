@@ -1167,7 +1167,6 @@ extern "C" int mi_write_prefill_kv(mi_kv_pool_t p, const uint16_t* q, const uint
     int rc = check_common(p, batch, hq, mbps);
     if (rc != MI_OK) return rc;
     if (total_tokens < 0) return MI_ERR_INVALID_ARG;
-    if (mikv::pool_fp8(p)) return MI_ERR_UNSUPPORTED;
     if (batch == 0 || total_tokens == 0) return MI_OK;
     if (!q || !k || !v || !q_rot || !table || !ctx || !cu || !(theta > 0.0)) return MI_ERR_INVALID_ARG;
     return mikv::launch_write_prefill_kv(p, q, k, v, q_rot, table, mbps, ctx, cu, batch, total_tokens,
@@ -1182,7 +1181,6 @@ extern "C" int mi_paged_prefill_attention(mi_kv_pool_t p, const uint16_t* q_rot,
     int rc = check_common(p, batch, hq, mbps);
     if (rc != MI_OK) return rc;
     if (total_tokens < 0 || max_new_tokens < 0 || batch > 65535) return MI_ERR_INVALID_ARG;
-    if (mikv::pool_fp8(p)) return MI_ERR_UNSUPPORTED;
     if (batch == 0 || total_tokens == 0 || max_new_tokens == 0) return MI_OK;
     if (!q_rot || !out || !table || !ctx || !cu || q_rot == out) return MI_ERR_INVALID_ARG;
     if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(p->head_dim));

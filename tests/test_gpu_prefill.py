@@ -8,7 +8,8 @@ import paged_kv_cache_246_amd as mk
 import workloads
 from oracle import attention as oatt
 from oracle import bf16 as obf16
-from tests.gpu_harness import (DEV, bits_to_dev, check_tolerance, dev_to_bits, ulp_diff_bf16)
+from tests.gpu_harness import (DEV, bits_to_dev, check_tolerance, codes_to_dev, dev_to_bits,
+                               ulp_diff_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,13 +26,15 @@ def _say(*a):
 
 
 class PrefillOnDevice:
-    def __init__(self, case):
+    def __init__(self, case, k_scales=None, v_scales=None):
         cfg = case.cfg
         self.case = case
+        self.fp8 = case.k_pool.dtype == np.uint8
         self.B = len(case.context_lens)
         self.T = int(case.cu_seqlens[-1])
         self.Hq, self.Hkv, self.D = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
-        self.k_pool, self.v_pool = bits_to_dev(case.k_pool), bits_to_dev(case.v_pool)
+        to_dev = codes_to_dev if self.fp8 else bits_to_dev
+        self.k_pool, self.v_pool = to_dev(case.k_pool), to_dev(case.v_pool)
         self.q, self.k, self.v = bits_to_dev(case.q), bits_to_dev(case.k), bits_to_dev(case.v)
         self.q_rot = torch.empty_like(self.q)
         self.out = torch.empty_like(self.q)
@@ -40,7 +43,10 @@ class PrefillOnDevice:
         self.cu = torch.from_numpy(case.cu_seqlens).to(DEV)
         self.mbps = case.block_table.shape[1]
         self.max_new = int(case.new_lens.max())
-        self.pool = mk.mi_kv_pool_init(case.num_blocks, 16, self.Hkv, self.D, self.k_pool, self.v_pool)
+        self.pool = mk.mi_kv_pool_init(case.num_blocks, 16, self.Hkv, self.D, self.k_pool,
+                                       self.v_pool, flags=mk.MI_POOL_KV_FP8 if self.fp8 else 0)
+        if self.fp8:
+            mk.mi_kv_pool_set_scales(self.pool, k_scales, v_scales)
 
     def run(self):
         mk.mi_write_prefill_kv(self.pool, self.q, self.k, self.v, self.q_rot, self.table, self.mbps,
@@ -189,12 +195,38 @@ def test_prefill_errors_and_faults():
         assert mk.mi_kv_pool_check_errors(dev.pool) & mk.MI_FAULT_CONTEXT_LEN
     finally:
         dev.close()
-    k8 = torch.zeros(64 * 2 * 16 * 64, dtype=torch.uint8, device=DEV)
-    p8 = mk.mi_kv_pool_init(64, 16, 2, 64, k8, k8.clone(), flags=mk.MI_POOL_KV_FP8)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 8, 2), (128, 32, 8), (128, 7, 1)])
+def test_prefill_over_an_8bit_cache(D, Hq, Hkv):
+    """Prefill chunks over an E4M3 pool with per-head scales: written V codes
+    bit-exact, K codes within one code, outputs within tolerance of the
+    oracle's dequantise-then-attend."""
+    from oracle import fp8 as ofp8
+    cfg = workloads.DecodeConfig("pf8", batch=4, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                 block_size=16, num_blocks=128, rope_theta=1e6, ctx_draw="fixed",
+                                 seed=D + Hq)
+    case = workloads.make_prefill_case(cfg, (0, 7, 40, 300), (70, 1, 33, 96), kv_format="fp8")
+    rng = np.random.default_rng(D)
+    ks = rng.uniform(0.3, 3.0, Hkv).astype(np.float32)
+    vs = rng.uniform(0.3, 3.0, Hkv).astype(np.float32)
+    ref, kn, vn, qb = oatt.prefill_step_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                            case.block_table, case.context_lens, case.cu_seqlens,
+                                            16, cfg.rope_theta, ks, vs)
+    dev = PrefillOnDevice(case, ks, vs)
     try:
-        with pytest.raises(mk.MikvError) as e:
-            mk.mi_paged_prefill_attention(p8, dev.q_rot, dev.out, dev.table, dev.mbps, dev.ctx,
-                                          dev.cu, dev.B, dev.T, dev.max_new, dev.Hq)
-        assert e.value.status == mk.MI_ERR_UNSUPPORTED
+        dev.run()
+        assert mk.mi_kv_pool_check_errors(dev.pool) == 0
+        gk, gv = dev.k_pool.cpu().numpy(), dev.v_pool.cpu().numpy()
+        assert np.array_equal(gv, vn)
+        def ordered(x):                 # E4M3 codes in value order
+            x = x.astype(np.int64)
+            return np.where(x & 0x80, -(x & 0x7F), x & 0x7F)
+        changed = gk != kn
+        assert np.abs(ordered(gk[changed]) - ordered(kn[changed])).max(initial=0) <= 1
+        assert not np.isnan(ofp8.decode(gk[changed])).any()
+        assert ulp_diff_bf16(dev_to_bits(dev.q_rot), qb).max() <= 1
+        mx, rel = check_tolerance(dev_to_bits(dev.out), ref, "fp8 prefill D=%d G=%d" % (D, Hq // Hkv))
+        _say("  max|d| %.3g relL2 %.3g, K codes differing: %d" % (mx, rel, int(changed.sum())))
     finally:
-        mk.mi_kv_pool_destroy(p8)
+        dev.close()
