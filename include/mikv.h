@@ -483,12 +483,15 @@ int mi_sched_step(mi_sched_t sched, mi_sched_counts* counts, int64_t* seq_ids,
  * host_v: host arrays [host_slots, num_kv_heads, 16, head_dim] of the pool's
  * element type (bf16 bits or E4M3 codes), page-locked for asynchronous
  * copies (e.g. hipHostMalloc); pairs: host array of n (device block, host
- * slot) pairs for swap_out, n (host slot, device block) pairs for swap_in.
- * Every id and slot is checked before anything is copied
- * (MI_ERR_INVALID_ARG). Copies are DMA transfers queued on stream (runs of
- * consecutive blocks and slots merged into one transfer), asynchronous for
- * page-locked host memory; the host arrays must stay alive until the stream
- * reaches them.
+ * slot) pairs for swap_out, n (host slot, device block) pairs for swap_in;
+ * each destination (slot out, block in) at most once. Every id and slot is
+ * checked before anything is copied (MI_ERR_INVALID_ARG). Pairs are ordered
+ * by host slot and each run of consecutive slots moves in one DMA transfer
+ * queued on stream, asynchronous for page-locked host memory (the host
+ * arrays must stay alive until the stream reaches them); scattered device
+ * blocks of a run are packed / unpacked by a kernel through a device staging
+ * buffer of up to 64 MiB per cache, allocated by the pool's first such swap
+ * and freed with the pool. Swaps on one pool must be ordered on one stream.
  */
 int mi_kv_swap_out(mi_kv_pool_t pool, void* host_k, void* host_v, int32_t host_slots,
                    const int32_t* pairs, int32_t n, void* stream);

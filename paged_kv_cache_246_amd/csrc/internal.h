@@ -18,6 +18,8 @@ struct mi_kv_pool_s {
     void* k = nullptr;               // device [N, Hkv, bs, D]: bf16 bits, or E4M3 codes
     void* v = nullptr;
     float* scales = nullptr;         // device [2 * Hkv] (8-bit pools): K scales, then V scales
+    void* stage = nullptr;           // device staging of scattered swaps (allocated on first use)
+    size_t stage_blocks = 0;         // blocks of K (and again of V) the staging holds
     bool owns_cache = false;
     uint32_t* err = nullptr;         // device error word (MI_FAULT_* bits)
     std::vector<int32_t> stack;      // free-block LIFO; back() is handed out next

@@ -125,6 +125,7 @@ extern "C" int mi_kv_pool_destroy(mi_kv_pool_t p) {
     int st = MI_OK;
     if (p->err && hipFree(p->err) != hipSuccess) st = MI_ERR_HIP;
     if (p->scales && hipFree(p->scales) != hipSuccess) st = MI_ERR_HIP;
+    if (p->stage && hipFree(p->stage) != hipSuccess) st = MI_ERR_HIP;
     if (p->owns_cache) {
         if (hipFree(p->k) != hipSuccess) st = MI_ERR_HIP;
         if (hipFree(p->v) != hipSuccess) st = MI_ERR_HIP;
@@ -220,58 +221,4 @@ extern "C" int mi_kv_pool_check_errors(mi_kv_pool_t p, uint32_t* fault_bits) {
     if (fault_bits) *fault_bits = bits;
     if (st != MI_OK) return st;
     return bits ? MI_ERR_DEVICE_FAULT : MI_OK;
-}
-
-// ------------------------------------------------------------- KV offload
-// Block copies between the pool and a host swap space (same [Hkv, 16, D]
-// tile per block). Runs of pairs with consecutive source and destination
-// indices become one DMA transfer.
-namespace {
-
-int swap_copy(mi_kv_pool_t p, char* dst_k, char* dst_v, const char* src_k, const char* src_v,
-              int32_t host_slots, const int32_t* pairs, int32_t n, bool out, void* stream) {
-    if (!p || !mikv::pool_has_device(p) || host_slots < 0 || n < 0) return MI_ERR_INVALID_ARG;
-    if (n == 0) return MI_OK;
-    if (!pairs || !dst_k || !dst_v || !src_k || !src_v) return MI_ERR_INVALID_ARG;
-    for (int32_t i = 0; i < n; ++i) {
-        const int32_t dev = out ? pairs[2 * i] : pairs[2 * i + 1];
-        const int32_t slot = out ? pairs[2 * i + 1] : pairs[2 * i];
-        if (dev < 0 || dev >= p->num_blocks || slot < 0 || slot >= host_slots) return MI_ERR_INVALID_ARG;
-    }
-    const size_t blk = static_cast<size_t>(p->num_kv_heads) * p->block_size * p->head_dim *
-                       mikv::pool_elem_bytes(p);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipMemcpyKind kind = out ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
-    int32_t i = 0;
-    while (i < n) {
-        int32_t j = i + 1;
-        while (j < n && pairs[2 * j] == pairs[2 * (j - 1)] + 1 && pairs[2 * j + 1] == pairs[2 * (j - 1) + 1] + 1)
-            ++j;
-        const size_t s_off = static_cast<size_t>(pairs[2 * i]) * blk;
-        const size_t d_off = static_cast<size_t>(pairs[2 * i + 1]) * blk;
-        const size_t bytes = static_cast<size_t>(j - i) * blk;
-        if (hipMemcpyAsync(dst_k + d_off, src_k + s_off, bytes, kind, st) != hipSuccess ||
-            hipMemcpyAsync(dst_v + d_off, src_v + s_off, bytes, kind, st) != hipSuccess)
-            return MI_ERR_HIP;
-        i = j;
-    }
-    return MI_OK;
-}
-
-}  // namespace
-
-extern "C" int mi_kv_swap_out(mi_kv_pool_t p, void* host_k, void* host_v, int32_t host_slots,
-                              const int32_t* pairs, int32_t n, void* stream) {
-    if (!p) return MI_ERR_INVALID_ARG;
-    return swap_copy(p, static_cast<char*>(host_k), static_cast<char*>(host_v),
-                     static_cast<const char*>(p->k), static_cast<const char*>(p->v), host_slots,
-                     pairs, n, true, stream);
-}
-
-extern "C" int mi_kv_swap_in(mi_kv_pool_t p, const void* host_k, const void* host_v,
-                             int32_t host_slots, const int32_t* pairs, int32_t n, void* stream) {
-    if (!p) return MI_ERR_INVALID_ARG;
-    return swap_copy(p, static_cast<char*>(p->k), static_cast<char*>(p->v),
-                     static_cast<const char*>(host_k), static_cast<const char*>(host_v), host_slots,
-                     pairs, n, false, stream);
 }

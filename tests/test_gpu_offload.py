@@ -57,6 +57,26 @@ def test_swap_out_then_in_moves_blocks_bit_exactly(fmt):
             assert h == h2
             ek[d2], ev[d2] = kp[d], vp[d]
         assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
+        # consecutive slots holding scattered blocks: packed through the staging buffer
+        before_k = gk.copy()
+        out2 = np.array([[9, 20], [2, 21], [30, 22], [17, 23], [44, 24]], np.int32)
+        mk.mi_kv_swap_out(pool, hk, hv, S, out2)
+        in2 = np.array([[24, 33], [20, 34], [21, 35], [22, 36], [23, 37]], np.int32)
+        mk.mi_kv_swap_in(pool, hk, hv, S, in2)
+        torch.cuda.synchronize()
+        gk2 = dev_to_bits(kd) if fmt == "bf16" else kd.cpu().numpy()
+        gv2 = dev_to_bits(vd) if fmt == "bf16" else vd.cpu().numpy()
+        hkn, hvn = hk.numpy(), hv.numpy()
+        for d, h in out2:
+            assert np.array_equal(as_u(hkn[h]), ek[d]) and np.array_equal(as_u(hvn[h]), ev[d])
+        ek2, ev2 = ek.copy(), ev.copy()
+        src = {h: d for d, h in out2}
+        for h, d in in2:
+            ek2[d], ev2[d] = ek[src[h]], ev[src[h]]
+        assert np.array_equal(gk2, ek2) and np.array_equal(gv2, ev2)
+        assert not np.array_equal(gk2, before_k)
+        with pytest.raises(mk.MikvError):           # one slot named twice
+            mk.mi_kv_swap_out(pool, hk, hv, S, np.array([[1, 2], [3, 2]], np.int32))
         with pytest.raises(mk.MikvError):           # a slot past the swap space: nothing copied
             mk.mi_kv_swap_out(pool, hk, hv, S, np.array([[1, 2], [2, S]], np.int32))
         with pytest.raises(mk.MikvError):           # a block past the pool
