@@ -5,17 +5,24 @@
 // norms; pre-norm order).
 //
 // The projections are skinny (M = batch <= 32 rows) and stream their
-// weights once: bf16 MFMA 16x16x32 tiles, split over K so that enough waves
-// stream in parallel; each split leaves an fp32 partial and the consumer
-// kernel sums the partials in a fixed order (deterministic) and applies the
-// epilogue. RMSNorm is x / rms(x) * w with a per-row scalar 1 / rms(x), so
-// the GEMM runs on x * w and the consumer multiplies by 1 / rms(x). The
-// activations x * w, x2 * w2 and silu(g) * u enter the MFMAs as bf16 hi + lo
-// pairs (fp32-accurate); the attention output o enters as bf16.
+// weights once on bf16 MFMA 16x16x32 tiles. One workgroup owns a few 16-column
+// output tiles over the whole K range: its waves split K, stream their share
+// of the weight rows, and the workgroup sums the per-wave accumulators through
+// LDS in a fixed order (deterministic). Because a workgroup ends with finished
+// output columns, each projection applies its own epilogue and no partial
+// sums leave the chip:
+//   QKV     -- 1 / rms(x) (from the activation stream itself), RoPE, K/V
+//              append into the paged cache, q_rot;
+//   o_proj  -- x2 = x + o W_o^T (fp32);
+//   gate|up -- 1 / rms(x2) (from its activation stream), silu(g) * u;
+//   down    -- out = bf16(x2 + a W_d^T).
+// RMSNorm is x / rms(x) * w with a per-row scalar 1 / rms(x), so the GEMM runs
+// on x * w and the epilogue multiplies by 1 / rms(x). The activations x * w,
+// x2 * w2 and silu(g) * u enter the MFMAs as bf16 hi + lo pairs
+// (fp32-accurate); the attention output o enters as bf16.
 //
-// Launch sequence: gemm(qkv) -> rope_append -> attention (2 kernels) ->
-// gemm(o) -> residual_norm -> gemm(gate|up) -> silu_mul -> gemm(down) ->
-// residual_out.
+// Launch sequence: proj(qkv) -> attention (2 kernels) -> proj(o) ->
+// proj(gate|up) -> proj(down).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -30,11 +37,18 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BS = 16;
-constexpr int kGemmTargetWaves = 3072;   // work items per projection
 constexpr int kKStep = 32;               // K per MFMA
-// MFMA steps per load batch for NW column tiles per wave: NW * KB >= 8
-// weight loads (8 KiB per wave) per batch, at least 2 steps.
-constexpr int batch_steps(int nw) { return nw >= 4 ? 2 : 8 / nw; }
+
+// Tuning of the projection grids (build-time overridable for sweeps):
+// waves per projection (upper bound), LDS bytes per workgroup (upper bound).
+#ifndef MIKV_PROJ_TARGET_WAVES
+#define MIKV_PROJ_TARGET_WAVES 3072
+#endif
+#ifndef MIKV_PROJ_LDS_CAP
+#define MIKV_PROJ_LDS_CAP 65536
+#endif
+constexpr int kProjTargetWaves = MIKV_PROJ_TARGET_WAVES;
+constexpr int kProjLdsCap = MIKV_PROJ_LDS_CAP;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -53,46 +67,47 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
     u += 0x7fffu + ((u >> 16) & 1u);
     return static_cast<uint16_t>(u >> 16);
 }
-__device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(t.x, t.y, t.z, t.w);
-}
-__device__ __forceinline__ uint32_t mul_pack(uint32_t a, uint32_t g) {
-    const float lo = bf16_to_f32(static_cast<uint16_t>(a)) * bf16_to_f32(static_cast<uint16_t>(g));
-    const float hi = bf16_to_f32(static_cast<uint16_t>(a >> 16)) * bf16_to_f32(static_cast<uint16_t>(g >> 16));
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-}
 
 // ------------------------------------------------------------- skinny GEMM
-// P[s][m][n] = sum over k in split s of A[m][k] * W[n][k], m < M. W rows
-// n < n_split come from W0, the rest from W1 (row n - n_split): this fuses
-// gate and up. One wave per (16-column tile, K split). MFMA operand layout
+// Y[m][n] = sum over k of A[m][k] * W[n][k], m < M. MFMA operand layout
 // (16x16x32 bf16): lane l holds A[l % 16][8 (l / 16) .. +8) and
 // B[8 (l / 16) .. +8)[l % 16]; the fp32 result D[4 (l / 16) + i][l % 16],
-// i < 4. A is the activation rows (M padded to 16 per tile with zeros), B the
-// weight rows (W^T), so each lane streams 16 contiguous bytes of one weight
-// row per MFMA step. Lanes of padding rows (m >= M) load a real row again;
-// their output rows are discarded.
+// i < 4. A is the activation rows (M padded to 16 per row tile), B the
+// weight rows (W^T). Lanes of padding rows (m >= M) take an out-of-range
+// offset, so their loads return zeros without touching memory; their output
+// rows are discarded.
 //
 // Activation modes: kActBf16 -- A is bf16; kActGainSplit -- A is bf16 x[m][k]
-// times a bf16 gain[k], formed in fp32; kActF32Split -- A is fp32. In the two
-// split modes the fp32 value a is fed as a_hi = bf16(a) plus a_lo =
-// bf16(a - a_hi), two MFMAs per step, so the activation keeps ~16 significant
-// bits instead of 8 (the weight stream is unchanged).
+// times a bf16 gain[k], formed in fp32; kActF32Split -- A is fp32;
+// kActF32GainSplit -- A is fp32 x[m][k] times a bf16 gain[k]. In the split
+// modes the fp32 value a is fed as a_hi = bf16(a) plus a_lo = bf16(a - a_hi),
+// two MFMAs per step, so the activation keeps ~16 significant bits instead
+// of 8 (the weight stream is unchanged). The gain modes also accumulate the
+// sum of x^2 over the lane's K elements (the RMSNorm statistic of x).
 constexpr int kActBf16 = 0;
 constexpr int kActGainSplit = 1;
 constexpr int kActF32Split = 2;
+constexpr int kActF32GainSplit = 3;
 
+// Epilogues of the fused projection kernel.
+constexpr int kEpiQkv = 0;        // RMSNorm scale, RoPE, K/V append, q_rot
+constexpr int kEpiResidual = 1;   // x2 = x + y (fp32)
+constexpr int kEpiSwiglu = 2;     // a = silu(r g) * (r u), r = 1 / rms(x2) (fp32)
+constexpr int kEpiOut = 3;        // out = bf16(x2 + y)
+
+// hi = bf16(v), lo = bf16(v - hi), both round-to-nearest-even, through the
+// packed hardware conversion (one instruction per pair of values).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo) {
     uint32_t h[4], l[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const uint16_t h0 = f32_to_bf16(v[2 * e]), h1 = f32_to_bf16(v[2 * e + 1]);
-        const uint16_t l0 = f32_to_bf16(v[2 * e] - bf16_to_f32(h0));
-        const uint16_t l1 = f32_to_bf16(v[2 * e + 1] - bf16_to_f32(h1));
-        h[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-        l[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+        const bf16x2_t hp = {static_cast<__bf16>(v[2 * e]), static_cast<__bf16>(v[2 * e + 1])};
+        h[e] = __builtin_bit_cast(uint32_t, hp);
+        const float r0 = v[2 * e] - __uint_as_float(h[e] << 16);
+        const float r1 = v[2 * e + 1] - __uint_as_float(h[e] & 0xffff0000u);
+        const bf16x2_t lp = {static_cast<__bf16>(r0), static_cast<__bf16>(r1)};
+        l[e] = __builtin_bit_cast(uint32_t, lp);
     }
     hi = make_uint4(h[0], h[1], h[2], h[3]);
     lo = make_uint4(l[0], l[1], l[2], l[3]);
@@ -104,6 +119,7 @@ __device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo
 // flight and force full waits). Out-of-range offsets read zeros.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBufferDword3 = 0x00020000;     // raw 32-bit buffer access (gfx9 family)
+constexpr uint32_t kOutOfRange = 0x80000000u;  // lane offset beyond any buffer here: reads 0
 constexpr int kAuxStream = 2;                 // non-temporal: weights are read once
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -117,32 +133,35 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 }
 
 // Loads and MFMAs of one batch of KB K-steps for NW column tiles and MT row
-// tiles. load() only issues memory reads (activations, then weights); the
-// activation's conversion to bf16 (hi, lo) happens in mma(), so prefetching
-// the next batch never waits on its own loads.
+// tiles. load() only issues memory reads (activations, gain, then weights);
+// the activation's conversion to bf16 (hi, lo) happens in mma(), so
+// prefetching the next batch never waits on its own loads.
 //
-// Weight loads come in one of two layouts. Direct (TR = false): each lane
-// loads exactly its MFMA B-operand piece, i.e. 16 rows x 64 bytes per load
-// instruction. Transposed (TR = true): 4 KB lanes share a row, so one
+// Each column tile has its own buffer resource based at its first weight
+// row, so a workgroup's tiles need not be adjacent (RoPE pairs, gate with
+// up). The weights are loaded transposed: 4 KB lanes share a row, so one
 // instruction reads 64 / (4 KB) whole row segments of 64 KB bytes (full
 // 128-byte lines at KB = 2); mma() writes the batch to the wave's LDS tile and
 // reads it back in the MFMA layout (rows padded by 16 bytes).
-template <int MT, int NW, int ACT, int KB, bool TR>
+template <int MT, int NW, int ACT, int KB>
 struct GemmBatch {
-    static constexpr int AE = (ACT == kActF32Split) ? 4 : 2;   // activation element bytes
-    static constexpr int LPR = 4 * KB;                         // transposed: lanes per row
-    static constexpr int RPI = 64 / LPR;                       // transposed: rows per load
+    static constexpr bool GAIN = ACT == kActGainSplit || ACT == kActF32GainSplit;
+    static constexpr bool F32 = ACT == kActF32Split || ACT == kActF32GainSplit;
+    static constexpr int AE = F32 ? 4 : 2;                     // activation element bytes
+    static constexpr int LPR = 4 * KB;                         // lanes per row
+    static constexpr int RPI = 64 / LPR;                       // rows per load
     static constexpr int ROWB = 64 * KB + 16;                  // LDS bytes per row (padded)
-    static constexpr int LDS_BYTES = TR ? 16 * NW * ROWB : 16;
-    uint4 w[KB][NW];       // direct: [step][tile]; transposed: flat [KB * NW] loads
-    uint4 a0[KB][MT];      // bf16 activations, or fp32 elements 0..3
-    uint4 a1[KB][MT];      // gain (kActGainSplit) or fp32 elements 4..7
+    static constexpr int LDS_BYTES = 16 * NW * ROWB;           // per wave
+    uint4 w[KB * NW];                      // load i: tile i / KB, rows (i % KB) RPI ..
+    uint4 a0[KB][MT];                      // bf16 activations, or fp32 elements 0..3
+    uint4 a1[F32 ? KB : 1][F32 ? MT : 1];  // fp32 elements 4..7
+    uint4 gn[GAIN ? KB : 1];               // gain
 
-    // kbyte: byte offset of the batch's first K column in a bf16 row.
-    // Direct: woff[j] = lane's offset in tile j. Transposed: woff[0] = lane's
-    // offset in load 0, wstep = bytes between consecutive loads (RPI rows).
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rw, const uint32_t (&woff)[NW],
-                                         uint32_t wstep, __amdgpu_buffer_rsrc_t ra,
+    // kbyte: byte offset of the batch's first K column in a bf16 row. woff:
+    // the lane's row segment in load 0 of a tile; rowstep: bytes between the
+    // row groups of consecutive loads of a tile (RPI rows).
+    __device__ __forceinline__ void load(const __amdgpu_buffer_rsrc_t (&rw)[NW], uint32_t woff,
+                                         uint32_t rowstep, __amdgpu_buffer_rsrc_t ra,
                                          const uint32_t (&aoff)[MT], __amdgpu_buffer_rsrc_t rg,
                                          uint32_t goff, uint32_t kbyte) {
 #pragma unroll
@@ -151,62 +170,63 @@ struct GemmBatch {
             for (int mt = 0; mt < MT; ++mt) {
                 const uint32_t ak = (kbyte + u * kKStep * 2) / 2 * AE;
                 a0[u][mt] = bload<0>(ra, aoff[mt], ak);
-                if constexpr (ACT == kActF32Split) a1[u][mt] = bload<0>(ra, aoff[mt] + 16, ak);
-                else if constexpr (ACT == kActGainSplit) a1[u][mt] = bload<0>(rg, goff, kbyte + u * kKStep * 2);
-                else a1[u][mt] = make_uint4(0, 0, 0, 0);
+                if constexpr (F32) a1[u][mt] = bload<0>(ra, aoff[mt] + 16, ak);
             }
-        if constexpr (TR) {
+        if constexpr (GAIN) {
 #pragma unroll
-            for (int i = 0; i < KB * NW; ++i)
-                w[i / NW][i % NW] = bload<kAuxStream>(rw, woff[0], kbyte + i * wstep);
-        } else {
-#pragma unroll
-            for (int u = 0; u < KB; ++u)
-#pragma unroll
-                for (int j = 0; j < NW; ++j) w[u][j] = bload<kAuxStream>(rw, woff[j], kbyte + u * kKStep * 2);
+            for (int u = 0; u < KB; ++u) gn[u] = bload<0>(rg, goff, kbyte + u * kKStep * 2);
         }
+#pragma unroll
+        for (int i = 0; i < KB * NW; ++i) w[i] = bload<kAuxStream>(rw[i / KB], woff, kbyte + (i % KB) * rowstep);
     }
 
     // lds: the wave's tile; wr = lane's write offset of load 0 (bytes),
-    // rd = lane's read offset for step 0 of tile 0
-    __device__ __forceinline__ void mma(f32x4_t (&acc)[NW][MT], char* lds, uint32_t wr,
+    // rd = lane's read offset for step 0 of tile 0. ssq[mt] accumulates x^2
+    // of the lane's activation elements (gain modes).
+    __device__ __forceinline__ void mma(f32x4_t (&acc)[NW][MT], float (&ssq)[MT], char* lds, uint32_t wr,
                                         uint32_t rd) const {
-        if constexpr (TR) {
 #pragma unroll
-            for (int i = 0; i < KB * NW; ++i)
-                *reinterpret_cast<uint4*>(lds + wr + i * RPI * ROWB) = w[i / NW][i % NW];
-        }
+        for (int i = 0; i < KB * NW; ++i) *reinterpret_cast<uint4*>(lds + wr + i * RPI * ROWB) = w[i];
 #pragma unroll
         for (int u = 0; u < KB; ++u)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 uint4 hi = a0[u][mt], lo = make_uint4(0, 0, 0, 0);
                 if constexpr (ACT != kActBf16) {
-                    float v[8];
-                    if constexpr (ACT == kActGainSplit) {
+                    float x[8];
+                    if constexpr (F32) {
+                        const uint4 p0 = a0[u][mt], p1 = a1[u][mt];
+                        x[0] = __uint_as_float(p0.x); x[1] = __uint_as_float(p0.y);
+                        x[2] = __uint_as_float(p0.z); x[3] = __uint_as_float(p0.w);
+                        x[4] = __uint_as_float(p1.x); x[5] = __uint_as_float(p1.y);
+                        x[6] = __uint_as_float(p1.z); x[7] = __uint_as_float(p1.w);
+                    } else {
                         const uint32_t aw[4] = {a0[u][mt].x, a0[u][mt].y, a0[u][mt].z, a0[u][mt].w};
-                        const uint32_t gw[4] = {a1[u][mt].x, a1[u][mt].y, a1[u][mt].z, a1[u][mt].w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            v[2 * e] = bf16_to_f32(static_cast<uint16_t>(aw[e])) *
-                                       bf16_to_f32(static_cast<uint16_t>(gw[e]));
-                            v[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(aw[e] >> 16)) *
-                                           bf16_to_f32(static_cast<uint16_t>(gw[e] >> 16));
+                            x[2 * e] = bf16_to_f32(static_cast<uint16_t>(aw[e]));
+                            x[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(aw[e] >> 16));
                         }
+                    }
+                    float v[8];
+                    if constexpr (GAIN) {
+                        const uint32_t gw[4] = {gn[u].x, gn[u].y, gn[u].z, gn[u].w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[2 * e] = x[2 * e] * bf16_to_f32(static_cast<uint16_t>(gw[e]));
+                            v[2 * e + 1] = x[2 * e + 1] * bf16_to_f32(static_cast<uint16_t>(gw[e] >> 16));
+                        }
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ssq[mt] = fmaf(x[e], x[e], ssq[mt]);
                     } else {
-                        const uint4 p0 = a0[u][mt], p1 = a1[u][mt];
-                        v[0] = __uint_as_float(p0.x); v[1] = __uint_as_float(p0.y);
-                        v[2] = __uint_as_float(p0.z); v[3] = __uint_as_float(p0.w);
-                        v[4] = __uint_as_float(p1.x); v[5] = __uint_as_float(p1.y);
-                        v[6] = __uint_as_float(p1.z); v[7] = __uint_as_float(p1.w);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = x[e];
                     }
                     split8(v, hi, lo);
                 }
 #pragma unroll
                 for (int j = 0; j < NW; ++j) {
-                    uint4 wv;
-                    if constexpr (TR) wv = *reinterpret_cast<const uint4*>(lds + rd + j * 16 * ROWB + u * 64);
-                    else wv = w[u][j];
+                    const uint4 wv = *reinterpret_cast<const uint4*>(lds + rd + j * 16 * ROWB + u * 64);
                     acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, hi), __builtin_bit_cast(bf16x8_t, wv), acc[j][mt], 0, 0, 0);
                     if constexpr (ACT != kActBf16)
@@ -218,286 +238,348 @@ struct GemmBatch {
     }
 };
 
-// One wave per (group of NW 16-column tiles, K split). The split's K range is
-// walked in batches of KB MFMA steps through a two-slot register ring: the
-// next batch is in flight while the current one is multiplied (the loop is
-// unrolled by two so the slots are fixed registers). A group never straddles
-// the W0/W1 boundary (n_split is a multiple of 16 NW).
-template <int MT, int NW, int ACT, bool TR>
-__global__ __launch_bounds__(64) void gemm_skinny_kernel(
-    const void* __restrict__ Aptr, const uint16_t* __restrict__ gain, int M, int K,
-    const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int n_split, int N,
-    int k_chunk, float* __restrict__ P) {
-    constexpr int KB = batch_steps(NW);        // MFMA steps per batch
-    using Batch = GemmBatch<MT, NW, ACT, KB, TR>;
-    __shared__ __align__(16) char lds[Batch::LDS_BYTES];
-    const int grp = blockIdx.x;
-    const int s = blockIdx.y;
-    const int lane = threadIdx.x;
+// ------------------------------------------------- fused projection kernel
+
+struct ProjArgs {
+    const void* A;              // activation rows [M][K]: bf16 or fp32 by mode
+    const uint16_t* gain;       // [K] RMSNorm weight (gain modes)
+    const uint16_t* W0;         // weight rows [*][K] bf16
+    const uint16_t* W1;         // up rows (SwiGLU), else unused
+    int M, K, N;                // N: row width of the outputs (hidden or intermediate)
+    float eps;
+    // QKV epilogue
+    int hq, hkv, D;
+    uint16_t* q_rot;
+    void* kc;
+    void* vc;
+    const int32_t* table;
+    int mbps;
+    const int32_t* ctx;
+    int num_blocks;
+    const float* kv_scales;
+    uint32_t* err;
+    int fp8;
+    // residual epilogues
+    const uint16_t* x_in;       // kEpiResidual: bf16 [M][N]
+    const float* x2;            // kEpiOut: fp32 [M][N]
+    float* y_f32;               // kEpiResidual: x2; kEpiSwiglu: a
+    uint16_t* y_bf16;           // kEpiOut
+};
+
+// Waves per workgroup at most: 16 when a wave fits in 128 VGPRs (estimate:
+// two batches of weight, activation and gain registers, the accumulators and
+// about 30 for addresses and temporaries; the QKV epilogue's float64 RoPE
+// needs more), else 8.
+#ifndef MIKV_PROJ_QKV_WAVES
+#define MIKV_PROJ_QKV_WAVES 8
+#endif
+#ifndef MIKV_PROJ_VGPR_EXTRA
+#define MIKV_PROJ_VGPR_EXTRA 30
+#endif
+template <int MT, int NW, int KB, int ACT, int EPI>
+constexpr int proj_max_waves() {
+    using B = GemmBatch<MT, NW, ACT, KB>;
+    constexpr int batch = 4 * (KB * NW + KB * MT * (B::F32 ? 2 : 1) + (B::GAIN ? KB : 0));
+    if (EPI == kEpiQkv) return MIKV_PROJ_QKV_WAVES;
+    return 2 * batch + 4 * NW * MT + MIKV_PROJ_VGPR_EXTRA <= 128 ? 16 : 8;
+}
+
+// LDS bytes per wave: the weight staging tile during the K loop, the
+// accumulators and RMSNorm sums after it.
+template <int MT, int NW, int KB, int ACT>
+constexpr size_t proj_lds_per_wave() {
+    return std::max<size_t>(GemmBatch<MT, NW, ACT, KB>::LDS_BYTES, (NW * MT * 256 + MT * 16) * sizeof(float));
+}
+
+// One workgroup of KS = blockDim / 64 waves per group of NW column tiles.
+// Tiles: QKV -- NP = NW / 2 RoPE pairs (tile j, tile j + D / 32) of one head,
+// so the rotation partners d and d + D / 2 land in one workgroup; SwiGLU --
+// gate tiles g NP .. + NP and the same up tiles; otherwise NW adjacent tiles. Wave w streams the K
+// range [w K / KS, (w + 1) K / KS) through a two-slot register ring (the next
+// batch in flight while the current one is multiplied), then the waves'
+// accumulators (and RMSNorm sums) are summed through LDS in wave order and
+// the epilogue runs on the finished outputs.
+template <int MT, int NW, int KB, int ACT, int EPI>
+__global__ __launch_bounds__((64 * proj_max_waves<MT, NW, KB, ACT, EPI>())) void proj_kernel(
+    ProjArgs a, mikv::RopeTable rope) {
+    using Batch = GemmBatch<MT, NW, ACT, KB>;
+    constexpr int NP = NW / 2;                 // tile pairs (QKV, SwiGLU)
+    static_assert((EPI != kEpiQkv && EPI != kEpiSwiglu) || (NW % 2 == 0), "paired tiles");
+    extern __shared__ __align__(16) char lds[];
+    const int KS = blockDim.x >> 6;
+    // wave index as a scalar: the K offsets of the buffer loads must be
+    // uniform (a per-lane value there turns every load into a loop)
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int col = lane & 15;
     const int kq = lane >> 4;
-    const int n_first = grp * NW * 16;
-    const bool second = n_first >= n_split;
-    const uint16_t* W = second ? W1 : W0;
-    const int row0 = second ? n_first - n_split : n_first;
-    const int rows = second ? N - n_split : n_split;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, static_cast<uint32_t>(static_cast<size_t>(rows) * K * 2));
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Aptr, static_cast<uint32_t>(static_cast<size_t>(M) * K * Batch::AE));
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gain, gain ? static_cast<uint32_t>(K) * 2 : 0u);
-    uint32_t woff[NW];
-    uint32_t wstep = 0, wr = 0, rd = 0;
-    if constexpr (TR) {
-        const int r_in = lane / Batch::LPR, piece = lane % Batch::LPR;
-        woff[0] = (static_cast<uint32_t>(row0 + r_in) * K) * 2 + piece * 16;
+    const int g = blockIdx.x;
+    const int K = a.K;
+    const int M = a.M;
+
+    int tile[NW];
+    const uint16_t* wsrc[NW];
+    int head = 0, j0 = 0;
+    if constexpr (EPI == kEpiQkv) {
+        const int hp = a.D / 32;                // pairs per head
+        const int gph = hp / NP;                // workgroups per head
+        head = g / gph;
+        j0 = (g - head * gph) * NP;
 #pragma unroll
-        for (int j = 1; j < NW; ++j) woff[j] = 0;
-        wstep = static_cast<uint32_t>(Batch::RPI) * K * 2;
-        wr = r_in * Batch::ROWB + piece * 16;
-        rd = col * Batch::ROWB + kq * 16;
+        for (int p = 0; p < NP; ++p) {
+            tile[p] = head * (a.D / 16) + j0 + p;
+            tile[NP + p] = tile[p] + hp;
+            wsrc[p] = wsrc[NP + p] = a.W0;
+        }
+    } else if constexpr (EPI == kEpiSwiglu) {
+        j0 = g * NP;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            tile[p] = tile[NP + p] = j0 + p;
+            wsrc[p] = a.W0;
+            wsrc[NP + p] = a.W1;
+        }
     } else {
 #pragma unroll
-        for (int j = 0; j < NW; ++j) woff[j] = (static_cast<uint32_t>(row0 + j * 16 + col) * K + kq * 8) * 2;
+        for (int j = 0; j < NW; ++j) {
+            tile[j] = g * NW + j;
+            wsrc[j] = a.W0;
+        }
     }
-    // Rows m >= M of the MFMA tile only feed output rows that are never
-    // stored, so those lanes read row M - 1 again.
+    __amdgpu_buffer_rsrc_t rw[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+        rw[j] = make_rsrc(wsrc[j] + static_cast<size_t>(tile[j]) * 16 * K, static_cast<uint32_t>(16 * K * 2));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, static_cast<uint32_t>(static_cast<size_t>(M) * K * Batch::AE));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain, a.gain ? static_cast<uint32_t>(K) * 2 : 0u);
+    const int r_in = lane / Batch::LPR, piece = lane % Batch::LPR;
+    const uint32_t woff = static_cast<uint32_t>(r_in) * K * 2 + piece * 16;
+    const uint32_t rowstep = static_cast<uint32_t>(Batch::RPI) * K * 2;
+    const uint32_t wr = r_in * Batch::ROWB + piece * 16;
+    const uint32_t rd = col * Batch::ROWB + kq * 16;
+    char* stage = lds + wv * Batch::LDS_BYTES;
     uint32_t aoff[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        aoff[mt] = (static_cast<uint32_t>(min(mt * 16 + col, M - 1)) * K + kq * 8) * Batch::AE;
+        aoff[mt] = mt * 16 + col < M ? (static_cast<uint32_t>(mt * 16 + col) * K + kq * 8) * Batch::AE
+                                     : kOutOfRange;
     const uint32_t goff = kq * 8 * 2;
 
     f32x4_t acc[NW][MT];
+    float ssq[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        ssq[mt] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    constexpr uint32_t STEP_BYTES = KB * kKStep * 2;
+    const int k_chunk = K / KS;
+    const int nb = k_chunk / (KB * kKStep);   // batches (>= 1)
+    const uint32_t kb0 = static_cast<uint32_t>(wv) * k_chunk * 2;
+    // The scheduling barriers keep each batch's loads ahead of the previous
+    // batch's MFMAs: left free, the compiler sinks them below the LDS writes
+    // and every batch then waits for all loads (one batch in flight).
+    auto kb = [&](int t) { return kb0 + static_cast<uint32_t>(t) * STEP_BYTES; };
+    Batch b0, b1;
+    b0.load(rw, woff, rowstep, ra, aoff, rg, goff, kb(0));
+    int i = 0;
+    for (; i + 2 < nb; i += 2) {
+        b1.load(rw, woff, rowstep, ra, aoff, rg, goff, kb(i + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        b0.mma(acc, ssq, stage, wr, rd);
+        __builtin_amdgcn_sched_barrier(0);
+        b0.load(rw, woff, rowstep, ra, aoff, rg, goff, kb(i + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        b1.mma(acc, ssq, stage, wr, rd);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i + 1 < nb) {
+        b1.load(rw, woff, rowstep, ra, aoff, rg, goff, kb(i + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        b0.mma(acc, ssq, stage, wr, rd);
+        b1.mma(acc, ssq, stage, wr, rd);
+    } else {
+        b0.mma(acc, ssq, stage, wr, rd);
+    }
+
+    // Per-wave accumulators to LDS (the staging tiles are free once every
+    // wave is past its last MFMA), then sums in wave (K-slice) order.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);
+    float* sred = red + KS * NW * MT * 256;
 #pragma unroll
     for (int j = 0; j < NW; ++j)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    constexpr uint32_t STEP_BYTES = KB * kKStep * 2;
-    const int nb = k_chunk / (KB * kKStep);   // batches (>= 1)
-    const uint32_t kb0 = static_cast<uint32_t>(s) * k_chunk * 2;
-    Batch b0, b1;
-    b0.load(rw, woff, wstep, ra, aoff, rg, goff, kb0);
-    int i = 0;
-    for (; i + 2 < nb; i += 2) {
-        b1.load(rw, woff, wstep, ra, aoff, rg, goff, kb0 + (i + 1) * STEP_BYTES);
-        b0.mma(acc, lds, wr, rd);
-        b0.load(rw, woff, wstep, ra, aoff, rg, goff, kb0 + (i + 2) * STEP_BYTES);
-        b1.mma(acc, lds, wr, rd);
-    }
-    if (i + 1 < nb) {
-        b1.load(rw, woff, wstep, ra, aoff, rg, goff, kb0 + (i + 1) * STEP_BYTES);
-        b0.mma(acc, lds, wr, rd);
-        b1.mma(acc, lds, wr, rd);
-    } else {
-        b0.mma(acc, lds, wr, rd);
-    }
-#pragma unroll
-    for (int j = 0; j < NW; ++j) {
-        const int n = n_first + j * 16 + col;
-#pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mt * 16 + kq * 4 + r;
-                if (m < M) P[(static_cast<size_t>(s) * M + m) * N + n] = acc[j][mt][r];
-            }
-    }
-}
-
-// 1 / sqrt(mean(x^2) + eps) of a bf16 row (H a multiple of 8), by one block.
-__device__ float block_inv_rms(const uint16_t* row, int H, float eps, float* red) {
-    float ss = 0.f;
-    for (int i = threadIdx.x * 8; i < H; i += blockDim.x * 8) {
-        const uint4 w = *reinterpret_cast<const uint4*>(row + i);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            for (int r = 0; r < 4; ++r) red[(((wv * NW + j) * MT + mt) * 4 + r) * 64 + lane] = acc[j][mt][r];
+    if constexpr (Batch::GAIN) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float lo = bf16_to_f32(static_cast<uint16_t>(ws[e]));
-            const float hi = bf16_to_f32(static_cast<uint16_t>(ws[e] >> 16));
-            ss = fmaf(lo, lo, ss);
-            ss = fmaf(hi, hi, ss);
+        for (int mt = 0; mt < MT; ++mt) {
+            float s = ssq[mt];
+            s += __shfl_xor(s, 16);
+            s += __shfl_xor(s, 32);
+            if (kq == 0) sred[(wv * MT + mt) * 16 + col] = s;
         }
     }
-#pragma unroll
-    for (int x = 1; x < 64; x *= 2) ss += __shfl_xor(ss, x);
-    const int wv = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wv] = ss;
     __syncthreads();
-    float tot = 0.f;
-    for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) tot += red[w];
-    return 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
-}
+    // Output (row m, column c of tile j): lane (m % 16 / 4) * 16 + c, element m % 4.
+    auto out = [&](int j, int m, int c) {
+        const int mt = m >> 4, r = m & 15;
+        const int at = ((j * MT + mt) * 4 + (r & 3)) * 64 + (r >> 2) * 16 + c;
+        float v = 0.f;
+        for (int w = 0; w < KS; ++w) v += red[w * NW * MT * 256 + at];
+        return v;
+    };
+    auto inv_rms = [&](int m) {
+        const int mt = m >> 4, r = m & 15;
+        float s = 0.f;
+        for (int w = 0; w < KS; ++w) s += sred[(w * MT + mt) * 16 + r];
+        return 1.0f / sqrtf(s / static_cast<float>(K) + a.eps);
+    };
 
-// Sum of the K-split partials of one output, in split order; the loads are
-// issued eight at a time so the sum costs few memory round trips.
-__device__ __forceinline__ float sum_splits(const float* P, int S, size_t stride, size_t idx) {
-    float v = 0.f;
-    for (int s0 = 0; s0 < S; s0 += 8) {
-        float t[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) t[u] = (s0 + u < S) ? P[(s0 + u) * stride + idx] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (s0 + u < S) v += t[u];
-    }
-    return v;
-}
-
-// ------------------------------------------- RoPE + append from the QKV GEMM
-// qkv[b][c] = inv_rms1(x_b) * sum_s P[s][b][c]. Then, at pos = ctx_b, the
-// same float64 RoPE and single rounding as write_decode_kv: K slot gets
-// bf16(RoPE(k)), V slot bf16(v), q_rot bf16(RoPE(q)); an 8-bit cache (FP8)
-// stores the E4M3 codes of those bf16 K and V under the head's scales.
-template <int D, bool FP8>
-__global__ __launch_bounds__(256) void rope_append_kernel(
-    const float* __restrict__ P, int S, const uint16_t* __restrict__ x, int H, float eps,
-    uint16_t* __restrict__ q_rot, void* __restrict__ kc, void* __restrict__ vc,
-    const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
-    int32_t batch, int32_t hq, int32_t hkv, int32_t num_blocks, mikv::RopeTable rope,
-    const float* __restrict__ kv_scales, uint32_t* __restrict__ err) {
-    constexpr int H2 = D / 2;
-    __shared__ float red[4];
-    const int b = blockIdx.x;
-    const int nqkv = (hq + 2 * hkv) * D;
-    const size_t stride = static_cast<size_t>(batch) * nqkv;
-    const float* Pb = P + static_cast<size_t>(b) * nqkv;
-    const float inv = block_inv_rms(x + static_cast<size_t>(b) * H, H, eps, red);
-    const int pos = ctx_lens[b];
-    const bool pos_ok = pos >= 0 && pos / BS < mbps;
-    const int32_t blk = pos_ok ? table[static_cast<size_t>(b) * mbps + pos / BS] : -1;
-    const bool blk_ok = pos_ok && blk >= 0 && blk < num_blocks;
-    if (blockIdx.y == 0 && threadIdx.x == 0) {
-        if (!pos_ok) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
-        else if (!blk_ok) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
-    }
-    if (!pos_ok) return;
-    const int off = pos % BS;
-    const int n_rot = (hq + hkv) * H2;
-    const int idx = blockIdx.y * blockDim.x + threadIdx.x;
-    if (idx < n_rot) {
-        const int h = idx / H2;
-        const int i = idx - h * H2;
-        if (h >= hq && !blk_ok) return;
-        const double x1 = static_cast<double>(inv * sum_splits(Pb, S, stride, h * D + i));
-        const double x2 = static_cast<double>(inv * sum_splits(Pb, S, stride, h * D + i + H2));
-        const double a = static_cast<double>(pos) * rope.inv_freq[i];
-        double sn, cs;
-        sincos(a, &sn, &cs);
-        const uint16_t r1 = f64_to_bf16(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
-        const uint16_t r2 = f64_to_bf16(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
-        if (h < hq) {
-            uint16_t* dst = q_rot + (static_cast<size_t>(b) * hq + h) * D;
-            dst[i] = r1;
-            dst[i + H2] = r2;
-        } else {
-            const int g = h - hq;
-            const size_t row = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
-            if constexpr (FP8) {
-                uint8_t* dst = static_cast<uint8_t*>(kc) + row;
-                dst[i] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, kv_scales[g]));
-                dst[i + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, kv_scales[g]));
+    if constexpr (EPI == kEpiQkv) {
+        const int D = a.D, H2 = D / 2, hq = a.hq, hkv = a.hkv;
+        for (int it = threadIdx.x; it < M * NP * 16; it += blockDim.x) {
+            const int m = it / (NP * 16);
+            const int p = (it >> 4) % NP, c = it & 15;
+            const int d = (j0 + p) * 16 + c;           // < D / 2
+            const int pos = a.ctx[m];
+            const bool pos_ok = pos >= 0 && pos / BS < a.mbps;
+            const int32_t blk = pos_ok ? a.table[static_cast<size_t>(m) * a.mbps + pos / BS] : -1;
+            const bool blk_ok = pos_ok && blk >= 0 && blk < a.num_blocks;
+            if (g == 0 && p == 0 && c == 0) {
+                if (!pos_ok) atomicOr(a.err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+                else if (!blk_ok) atomicOr(a.err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+            }
+            if (!pos_ok || (head >= hq && !blk_ok)) continue;
+            const float inv = inv_rms(m);
+            const float y0 = inv * out(p, m, c);
+            const float y1 = inv * out(NP + p, m, c);
+            const int off = pos % BS;
+            if (head < hq + hkv) {
+                // the same float64 RoPE and single rounding as write_decode_kv
+                const double x1 = static_cast<double>(y0);
+                const double x2 = static_cast<double>(y1);
+                const double ang = static_cast<double>(pos) * rope.inv_freq[d];
+                double sn, cs;
+                sincos(ang, &sn, &cs);
+                const uint16_t r1 = f64_to_bf16(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
+                const uint16_t r2 = f64_to_bf16(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
+                if (head < hq) {
+                    uint16_t* dst = a.q_rot + (static_cast<size_t>(m) * hq + head) * D;
+                    dst[d] = r1;
+                    dst[d + H2] = r2;
+                } else {
+                    const int gk = head - hq;
+                    const size_t row = ((static_cast<size_t>(blk) * hkv + gk) * BS + off) * D;
+                    if (a.fp8) {
+                        uint8_t* dst = static_cast<uint8_t*>(a.kc) + row;
+                        dst[d] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, a.kv_scales[gk]));
+                        dst[d + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, a.kv_scales[gk]));
+                    } else {
+                        uint16_t* dst = static_cast<uint16_t*>(a.kc) + row;
+                        dst[d] = r1;
+                        dst[d + H2] = r2;
+                    }
+                }
             } else {
-                uint16_t* dst = static_cast<uint16_t*>(kc) + row;
-                dst[i] = r1;
-                dst[i + H2] = r2;
+                const int gv = head - hq - hkv;
+                const size_t row = ((static_cast<size_t>(blk) * hkv + gv) * BS + off) * D;
+                const uint16_t v0 = f32_to_bf16(y0), v1 = f32_to_bf16(y1);
+                if (a.fp8) {
+                    uint8_t* dst = static_cast<uint8_t*>(a.vc) + row;
+                    dst[d] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(v0, a.kv_scales[hkv + gv]));
+                    dst[d + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(v1, a.kv_scales[hkv + gv]));
+                } else {
+                    uint16_t* dst = static_cast<uint16_t*>(a.vc) + row;
+                    dst[d] = v0;
+                    dst[d + H2] = v1;
+                }
             }
         }
-    } else if (blk_ok) {
-        const int e = idx - n_rot;                 // element of the v heads
-        if (e >= hkv * D) return;
-        const int g = e / D;
-        const int d = e - g * D;
-        const float v = inv * sum_splits(Pb, S, stride, (hq + hkv) * D + e);
-        const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D + d;
-        if constexpr (FP8)
-            static_cast<uint8_t*>(vc)[at] =
-                static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(f32_to_bf16(v), kv_scales[hkv + g]));
-        else
-            static_cast<uint16_t*>(vc)[at] = f32_to_bf16(v);
+    } else if constexpr (EPI == kEpiSwiglu) {
+        for (int it = threadIdx.x; it < M * NP * 16; it += blockDim.x) {
+            const int m = it / (NP * 16);
+            const int p = (it >> 4) % NP, c = it & 15;
+            const float inv = inv_rms(m);
+            const float gt = inv * out(p, m, c);
+            const float up = inv * out(NP + p, m, c);
+            const float silu = gt / (1.0f + expf(-gt));
+            a.y_f32[static_cast<size_t>(m) * a.N + (j0 + p) * 16 + c] = silu * up;
+        }
+    } else {
+        for (int it = threadIdx.x; it < M * NW * 16; it += blockDim.x) {
+            const int m = it / (NW * 16);
+            const int j = (it >> 4) % NW, c = it & 15;
+            const size_t at = static_cast<size_t>(m) * a.N + tile[j] * 16 + c;
+            const float y = out(j, m, c);
+            if constexpr (EPI == kEpiResidual) a.y_f32[at] = bf16_to_f32(a.x_in[at]) + y;
+            else a.y_bf16[at] = f32_to_bf16(a.x2[at] + y);
+        }
     }
-}
-
-// x2 = x + sum_s P_o[s]; stores x2 and x2 * w2 (fp32) and, per block of 256
-// columns, the partial sum of x2^2 (the 1 / rms(x2) of silu_mul).
-__global__ __launch_bounds__(256) void residual_norm_kernel(
-    const float* __restrict__ P, int S, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w2,
-    int batch, int H, float* __restrict__ x2, float* __restrict__ xw2, float* __restrict__ ssq) {
-    __shared__ float red[4];
-    const int b = blockIdx.y;
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    float ss = 0.f;
-    if (i < H) {
-        const size_t at = static_cast<size_t>(b) * H + i;
-        const float v = bf16_to_f32(x[at]) + sum_splits(P, S, static_cast<size_t>(batch) * H, at);
-        x2[at] = v;
-        xw2[at] = v * bf16_to_f32(w2[i]);
-        ss = v * v;
-    }
-#pragma unroll
-    for (int k = 1; k < 64; k *= 2) ss += __shfl_xor(ss, k);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    if (threadIdx.x == 0) ssq[static_cast<size_t>(b) * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-// a = silu(r * gate) * (r * up) with r = 1 / rms(x2) from the partial sums
-// of squares, gate/up summed over the K splits (fp32 output).
-__global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ P, int S, int batch,
-                                                       int I, int H, float eps, const float* __restrict__ ssq,
-                                                       int nssq, float* __restrict__ a) {
-    const int b = blockIdx.y;
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= I) return;
-    const float tot = sum_splits(ssq + static_cast<size_t>(b) * nssq, nssq, 1, 0);
-    const float inv = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
-    const size_t stride = static_cast<size_t>(batch) * 2 * I;
-    const size_t row = static_cast<size_t>(b) * 2 * I;
-    const float g = inv * sum_splits(P, S, stride, row + i);
-    const float u = inv * sum_splits(P, S, stride, row + I + i);
-    const float silu = g / (1.0f + expf(-g));
-    a[static_cast<size_t>(b) * I + i] = silu * u;
-}
-
-// out = bf16(x2 + sum_s P_d[s]).
-__global__ __launch_bounds__(256) void residual_out_kernel(const float* __restrict__ P, int S,
-                                                           int batch, int H, const float* __restrict__ x2,
-                                                           uint16_t* __restrict__ out) {
-    const int b = blockIdx.y;
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= H) return;
-    const size_t at = static_cast<size_t>(b) * H + i;
-    out[at] = f32_to_bf16(x2[at] + sum_splits(P, S, static_cast<size_t>(batch) * H, at));
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Shape of a projection's grid: NW column tiles per wave and S K splits.
-// Measured on MI355X (8-row activations, transposed weight loads): 4 tiles
-// (64 weight rows) per wave and about 1536 waves stream best; S is the
-// largest divisor of the K batches that keeps the wave count within that.
-struct GemmShape {
-    int nw, splits;
-};
-GemmShape gemm_shape(int N, int K, int n_split) {
-    const int tiles = N / 16;
-    const int split_tiles = n_split / 16;
-    int nw = 4;
-    while (nw > 1 && (tiles % nw || split_tiles % nw)) nw /= 2;
-    const int target = 1536;
-    const int groups = tiles / nw;
-    const int units = K / (kKStep * batch_steps(nw));
-    int best = 1;
-    for (int d = 1; d <= units; ++d)
-        if (units % d == 0 && static_cast<int64_t>(groups) * d <= target) best = d;
-    return {nw, best};
+// Waves per workgroup of a projection: the largest divisor of the K batches
+// that keeps the workgroup within its wave bound and the LDS cap, and the
+// projection within the target wave count.
+template <int MT, int NW, int KB, int ACT, int EPI>
+int proj_waves(int wgs, int K) {
+    const int units = K / (KB * kKStep);
+    const int max_ks = std::min<int>(proj_max_waves<MT, NW, KB, ACT, EPI>(),
+                                     static_cast<int>(kProjLdsCap / proj_lds_per_wave<MT, NW, KB, ACT>()));
+    int ks = 1;
+    for (int d = 1; d <= std::min(units, max_ks); ++d)
+        if (units % d == 0 && static_cast<int64_t>(wgs) * d <= kProjTargetWaves) ks = d;
+    return ks;
+}
+
+// Tile shapes, measured on MI355X at batch 8: QKV and gate|up pair two tiles
+// per workgroup (KB 2: 4 KiB of weights per wave per batch); o_proj and down
+// take one tile (KB 4), which keeps 256 workgroups at hidden 4096 (groups of
+// two or four tiles were slower: fewer workgroups than CUs).
+#ifndef MIKV_PROJ_NW_QKV
+#define MIKV_PROJ_NW_QKV 2
+#endif
+#ifndef MIKV_PROJ_NW_GU
+#define MIKV_PROJ_NW_GU 2
+#endif
+#ifndef MIKV_PROJ_NW_O
+#define MIKV_PROJ_NW_O 1
+#endif
+#ifndef MIKV_PROJ_NW_D
+#define MIKV_PROJ_NW_D 1
+#endif
+constexpr int kNwQkv = MIKV_PROJ_NW_QKV, kNwGu = MIKV_PROJ_NW_GU;
+static_assert(kNwQkv == 2 || kNwQkv == 4, "QKV pairs per workgroup must divide D / 32 for D = 64 and 128");
+constexpr int kNwO = MIKV_PROJ_NW_O, kNwD = MIKV_PROJ_NW_D;
+// K steps per batch: NW * KB >= 4 loads (4 KiB of weights per wave).
+constexpr int kb_for(int nw) { return nw >= 2 ? 2 : 4; }
+#ifndef MIKV_PROJ_KB_D
+#define MIKV_PROJ_KB_D kb_for(kNwD)
+#endif
+constexpr int kKbD = MIKV_PROJ_KB_D;
+
+template <int MT, int NW, int KB, int ACT, int EPI>
+void launch_proj(const ProjArgs& a, const mikv::RopeTable& rope, int wgs, hipStream_t st) {
+    const int ks = proj_waves<MT, NW, KB, ACT, EPI>(wgs, a.K);
+    const size_t lds = proj_lds_per_wave<MT, NW, KB, ACT>() * ks;
+    hipLaunchKernelGGL((proj_kernel<MT, NW, KB, ACT, EPI>), dim3(wgs), dim3(64 * ks), lds, st, a, rope);
+}
+
+template <int NW, int KB, int ACT, int EPI>
+void launch_proj_m(const ProjArgs& a, const mikv::RopeTable& rope, int wgs, hipStream_t st) {
+    if (a.M <= 16) launch_proj<1, NW, KB, ACT, EPI>(a, rope, wgs, st);
+    else launch_proj<2, NW, KB, ACT, EPI>(a, rope, wgs, st);
 }
 
 struct LayerPlan {
     int H, I, hq, hkv, D, nqkv;
-    GemmShape g_qkv, g_o, g_gu, g_d;
-    int s_qkv, s_o, s_gu, s_d;
-    size_t off_pqkv, off_qrot, off_attn, off_o, off_po, off_x2, off_xw2, off_inv2, off_pgu, off_a,
-        off_pd, total;
+    size_t off_qrot, off_attn, off_o, off_x2, off_a, total;
     size_t attn_bytes;
 };
 
@@ -508,14 +590,6 @@ bool plan_layer(const mi_layer_config* c, int batch, int max_ctx, LayerPlan* pl)
     pl->hkv = c->num_kv_heads;
     pl->D = c->head_dim;
     pl->nqkv = (pl->hq + 2 * pl->hkv) * pl->D;
-    pl->g_qkv = gemm_shape(pl->nqkv, pl->H, pl->nqkv);
-    pl->g_o = gemm_shape(pl->H, pl->hq * pl->D, pl->H);
-    pl->g_gu = gemm_shape(2 * pl->I, pl->H, pl->I);
-    pl->g_d = gemm_shape(pl->H, pl->I, pl->H);
-    pl->s_qkv = pl->g_qkv.splits;
-    pl->s_o = pl->g_o.splits;
-    pl->s_gu = pl->g_gu.splits;
-    pl->s_d = pl->g_d.splits;
     const size_t B = static_cast<size_t>(batch);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -523,19 +597,13 @@ bool plan_layer(const mi_layer_config* c, int batch, int max_ctx, LayerPlan* pl)
         off = align_up(off + bytes, 256);
         return at;
     };
-    pl->off_pqkv = take(pl->s_qkv * B * pl->nqkv * sizeof(float));
     pl->off_qrot = take(B * pl->hq * pl->D * 2);
     pl->attn_bytes = mikv::attention_workspace_bytes(batch, pl->hq, pl->hkv, pl->D, max_ctx,
                                                      mikv::kDefaultSplitTokens);
     pl->off_attn = take(pl->attn_bytes);
     pl->off_o = take(B * pl->hq * pl->D * 2);
-    pl->off_po = take(pl->s_o * B * pl->H * sizeof(float));
     pl->off_x2 = take(B * pl->H * sizeof(float));
-    pl->off_xw2 = take(B * pl->H * sizeof(float));
-    pl->off_inv2 = take(B * ((pl->H + 255) / 256) * sizeof(float));
-    pl->off_pgu = take(pl->s_gu * B * 2 * pl->I * sizeof(float));
     pl->off_a = take(B * pl->I * sizeof(float));
-    pl->off_pd = take(pl->s_d * B * pl->H * sizeof(float));
     pl->total = off;
     return true;
 }
@@ -551,37 +619,6 @@ int check_layer(const mi_layer_config* c, const mi_kv_pool_s* p, int batch, int 
         return MI_ERR_UNSUPPORTED;
     if (batch > mikv::kMaxLayerBatch) return MI_ERR_UNSUPPORTED;
     return MI_OK;
-}
-
-#ifndef MIKV_GEMM_TRANSPOSED
-#define MIKV_GEMM_TRANSPOSED true
-#endif
-
-template <int MT, int ACT>
-void launch_gemm_mt(const void* A, const uint16_t* gain, int M, int K, const uint16_t* W0,
-                    const uint16_t* W1, int n_split, int N, GemmShape g, float* P, hipStream_t st) {
-    constexpr bool TR = MIKV_GEMM_TRANSPOSED;
-    const dim3 grid(N / 16 / g.nw, g.splits);
-    const int k_chunk = K / g.splits;
-    if (g.nw == 8)
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 8, ACT, TR>), grid, dim3(64), 0, st, A, gain, M, K, W0,
-                           W1, n_split, N, k_chunk, P);
-    else if (g.nw == 4)
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 4, ACT, TR>), grid, dim3(64), 0, st, A, gain, M, K, W0,
-                           W1, n_split, N, k_chunk, P);
-    else if (g.nw == 2)
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 2, ACT, TR>), grid, dim3(64), 0, st, A, gain, M, K, W0,
-                           W1, n_split, N, k_chunk, P);
-    else
-        hipLaunchKernelGGL((gemm_skinny_kernel<MT, 1, ACT, TR>), grid, dim3(64), 0, st, A, gain, M, K, W0,
-                           W1, n_split, N, k_chunk, P);
-}
-
-template <int ACT>
-void launch_gemm_act(const void* A, const uint16_t* gain, int M, int K, const uint16_t* W0,
-                     const uint16_t* W1, int n_split, int N, GemmShape g, float* P, hipStream_t st) {
-    if (M <= 16) launch_gemm_mt<1, ACT>(A, gain, M, K, W0, W1, n_split, N, g, P, st);
-    else launch_gemm_mt<2, ACT>(A, gain, M, K, W0, W1, n_split, N, g, P, st);
 }
 
 }  // namespace
@@ -611,51 +648,80 @@ extern "C" int mi_decoder_layer_decode(mi_kv_pool_t p, const mi_layer_config* cf
     if (ws_bytes < pl.total) return MI_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(ws);
-    float* p_qkv = reinterpret_cast<float*>(base + pl.off_pqkv);
     uint16_t* q_rot = reinterpret_cast<uint16_t*>(base + pl.off_qrot);
     uint16_t* o = reinterpret_cast<uint16_t*>(base + pl.off_o);
-    float* p_o = reinterpret_cast<float*>(base + pl.off_po);
     float* x2 = reinterpret_cast<float*>(base + pl.off_x2);
-    float* xw2 = reinterpret_cast<float*>(base + pl.off_xw2);
-    float* inv2 = reinterpret_cast<float*>(base + pl.off_inv2);
-    float* p_gu = reinterpret_cast<float*>(base + pl.off_pgu);
-    float* a = reinterpret_cast<float*>(base + pl.off_a);
-    float* p_d = reinterpret_cast<float*>(base + pl.off_pd);
+    float* act = reinterpret_cast<float*>(base + pl.off_a);
     const int H = pl.H, I = pl.I, D = pl.D, hq = pl.hq, hkv = pl.hkv;
+    const mikv::RopeTable rope = mikv::make_rope_table(cfg->rope_theta, D);
 
-    // 1. [q|k|v] partials of bf16(x * ln1_w) W_qkv^T
-    launch_gemm_act<kActGainSplit>(x_in, w->ln1_w, batch, H, w->w_qkv, w->w_qkv, pl.nqkv, pl.nqkv,
-                                   pl.g_qkv, p_qkv, st);
-    // 2. 1/rms(x), RoPE, append K/V, q_rot
+    // 1. [q|k|v] = (x * ln1_w) W_qkv^T / rms(x); RoPE, K/V append, q_rot
     {
-        const int items = (hq + hkv) * (D / 2) + hkv * D;
-        const dim3 grid(batch, (items + 255) / 256);
-        const mikv::RopeTable rope = mikv::make_rope_table(cfg->rope_theta, D);
-        const bool f8 = mikv::pool_fp8(p);
-        auto kern = D == 128 ? (f8 ? rope_append_kernel<128, true> : rope_append_kernel<128, false>)
-                             : (f8 ? rope_append_kernel<64, true> : rope_append_kernel<64, false>);
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, p_qkv, pl.s_qkv, x_in, H, cfg->rms_eps, q_rot,
-                           p->k, p->v, table, mbps, ctx, batch, hq, hkv, p->num_blocks, rope,
-                           static_cast<const float*>(p->scales), p->err);
+        ProjArgs a{};
+        a.A = x_in;
+        a.gain = w->ln1_w;
+        a.W0 = a.W1 = w->w_qkv;
+        a.M = batch;
+        a.K = H;
+        a.N = pl.nqkv;
+        a.eps = cfg->rms_eps;
+        a.hq = hq;
+        a.hkv = hkv;
+        a.D = D;
+        a.q_rot = q_rot;
+        a.kc = p->k;
+        a.vc = p->v;
+        a.table = table;
+        a.mbps = mbps;
+        a.ctx = ctx;
+        a.num_blocks = p->num_blocks;
+        a.kv_scales = static_cast<const float*>(p->scales);
+        a.err = p->err;
+        a.fp8 = mikv::pool_fp8(p) ? 1 : 0;
+        launch_proj_m<kNwQkv, kb_for(kNwQkv), kActGainSplit, kEpiQkv>(a, rope, pl.nqkv / 16 / kNwQkv, st);
     }
-    // 3. paged GQA decode attention
+    // 2. paged GQA decode attention
     rc = mikv::launch_paged_gqa_decode(p, q_rot, o, table, mbps, ctx, batch, hq,
                                        1.0f / sqrtf(static_cast<float>(D)), max_ctx,
                                        mikv::kDefaultSplitTokens, base + pl.off_attn, stream);
     if (rc != MI_OK) return rc;
-    // 4. o_proj partials, 5. x2 = x + o W_o^T, bf16(x2 * ln2_w), 1/rms(x2)
-    launch_gemm_act<kActBf16>(o, nullptr, batch, hq * D, w->w_o, w->w_o, H, H, pl.g_o, p_o, st);
-    const int nssq = (H + 255) / 256;
-    hipLaunchKernelGGL(residual_norm_kernel, dim3(nssq, batch), dim3(256), 0, st, p_o, pl.s_o, x_in,
-                       w->ln2_w, batch, H, x2, xw2, inv2);
-    // 6. gate|up partials, 7. a = silu(g) * u
-    launch_gemm_act<kActF32Split>(xw2, nullptr, batch, H, w->w_gate, w->w_up, I, 2 * I, pl.g_gu, p_gu,
-                                  st);
-    hipLaunchKernelGGL(silu_mul_kernel, dim3((I + 255) / 256, batch), dim3(256), 0, st, p_gu, pl.s_gu,
-                       batch, I, H, cfg->rms_eps, inv2, nssq, a);
-    // 8. down partials, 9. out = x2 + a W_d^T
-    launch_gemm_act<kActF32Split>(a, nullptr, batch, I, w->w_down, w->w_down, H, H, pl.g_d, p_d, st);
-    hipLaunchKernelGGL(residual_out_kernel, dim3((H + 255) / 256, batch), dim3(256), 0, st, p_d, pl.s_d,
-                       batch, H, x2, x_out);
+    // 3. x2 = x + o W_o^T
+    {
+        ProjArgs a{};
+        a.A = o;
+        a.W0 = a.W1 = w->w_o;
+        a.M = batch;
+        a.K = hq * D;
+        a.N = H;
+        a.x_in = x_in;
+        a.y_f32 = x2;
+        launch_proj_m<kNwO, kb_for(kNwO), kActBf16, kEpiResidual>(a, rope, H / 16 / kNwO, st);
+    }
+    // 4. a = silu(r2 W_gate^T) * (r2 W_up^T), r2 = x2 * ln2_w / rms(x2)
+    {
+        ProjArgs a{};
+        a.A = x2;
+        a.gain = w->ln2_w;
+        a.W0 = w->w_gate;
+        a.W1 = w->w_up;
+        a.M = batch;
+        a.K = H;
+        a.N = I;
+        a.eps = cfg->rms_eps;
+        a.y_f32 = act;
+        launch_proj_m<kNwGu, kb_for(kNwGu), kActF32GainSplit, kEpiSwiglu>(a, rope, 2 * I / 16 / kNwGu, st);
+    }
+    // 5. out = bf16(x2 + a W_down^T)
+    {
+        ProjArgs a{};
+        a.A = act;
+        a.W0 = a.W1 = w->w_down;
+        a.M = batch;
+        a.K = I;
+        a.N = H;
+        a.x2 = x2;
+        a.y_bf16 = x_out;
+        launch_proj_m<kNwD, kKbD, kActF32Split, kEpiOut>(a, rope, H / 16 / kNwD, st);
+    }
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
