@@ -25,6 +25,10 @@ namespace {
 constexpr int BS = 16;                // tokens per KV block
 constexpr float kNegInf = -INFINITY;
 constexpr float kRescaleSlack = 8.0f; // log2 units: running max may lag by 2^8
+#ifndef MIKV_TUNE_PREFILL_RAW
+#define MIKV_TUNE_PREFILL_RAW 1
+#endif
+constexpr bool kPrefillRawSoftmax = MIKV_TUNE_PREFILL_RAW != 0;   // prefill softmax form (see softmax_step)
 
 // ---------------------------------------------------------------- bf16 helpers
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -367,17 +371,24 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][MfmaTile<D, F
 // for column n, masked (column dead, or with tail a key row >= qlim), the
 // running max raised only past the slack (one wave vote), the lane's sum
 // updated; returns the P^T operand (weights rounded to bf16).
-template <int NPV>
+//
+// RAW (prefill): the max is taken on the raw scores and scaled once (the
+// scale is positive) and the scale folds into the exponent's FMA; without
+// tail nothing is masked -- a dead column there has a zero query, finite
+// scores and an output that is never stored.
+template <int NPV, bool RAW = false>
 __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_ok, int q4, int qlim,
                                                  bool tail, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        sc[i] = s[i] * sl2;
-        const bool ok = col_ok && (!tail || 4 * q4 + i < qlim);
-        sc[i] = ok ? sc[i] : kNegInf;
+        sc[i] = RAW ? s[i] : s[i] * sl2;
+        if (!RAW || tail) {
+            const bool ok = col_ok && (!tail || 4 * q4 + i < qlim);
+            sc[i] = ok ? sc[i] : kNegInf;
+        }
     }
-    const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * (RAW ? sl2 : 1.0f);
     if (__ballot(mx > sm.m + kRescaleSlack) != 0) {
         float hm = fmaxf(mx, __shfl_xor(mx, 16));
         hm = fmaxf(hm, __shfl_xor(hm, 32));
@@ -391,7 +402,7 @@ __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(sc[i] - sm.m);
+        p[i] = __builtin_amdgcn_exp2f(RAW ? fmaf(sc[i], sl2, -sm.m) : sc[i] - sm.m);
         sm.l += p[i];
     }
     return bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
@@ -404,7 +415,7 @@ __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_
 // with tail, key row t counts for it only if t < qlim[c] (the rows written so
 // far in decode, the causal limit in prefill), and V rows >= valid_rows are
 // zeroed.
-template <int D, int FMT, int QB>
+template <int D, int FMT, int QB, bool RAW = false>
 __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>::NKL],
                                              const uint32_t (&vr)[4][MfmaTile<D, FMT>::VW],
                                              const uint4 (&qb)[QB][MfmaTile<D, FMT>::NQK],
@@ -424,7 +435,7 @@ __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>:
         for (int j = 0; j < TL::NQK; ++j)
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
                                                         __builtin_bit_cast(bf16x8_t, qb[c][j]), s, 0, 0, 0);
-        pb[c] = softmax_step<TL::NPV>(s, sl2, col_ok[c], q4, qlim[c], tail, sm[c], o[c]);
+        pb[c] = softmax_step<TL::NPV, RAW>(s, sl2, col_ok[c], q4, qlim[c], tail, sm[c], o[c]);
     }
     s16x4_t vt[TL::NPV];
     v_operands<D, FMT>(vr, q4, valid_rows, tail, vt);
@@ -436,8 +447,8 @@ __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>:
                 vt[jj], __builtin_bit_cast(s16x4_t, pb[c]), o[c][jj], 0, 0, 0);
 }
 
-// Per-wave state of the QB column blocks.
-template <int D, int FMT, int QB>
+// Per-wave state of the QB column blocks (RAW: the prefill softmax form).
+template <int D, int FMT, int QB, bool RAW = false>
 struct MfmaCols {
     using TL = MfmaTile<D, FMT>;
     uint4 qb[QB][TL::NQK];
@@ -449,7 +460,7 @@ struct MfmaCols {
 
     __device__ __forceinline__ void consume(const uint4 (&kr)[TL::NKL], const uint32_t (&vr)[4][TL::VW],
                                             const int (&qlim)[QB], int valid_rows, bool tail) {
-        mfma_consume<D, FMT, QB>(kr, vr, qb, sl2, col_ok, q4, qlim, valid_rows, tail, sm, o);
+        mfma_consume<D, FMT, QB, RAW>(kr, vr, qb, sl2, col_ok, q4, qlim, valid_rows, tail, sm, o);
     }
     // unmasked tile, or a tile whose rows >= valid_rows are masked for every column
     __device__ __forceinline__ void consume_rows(const uint4 (&kr)[TL::NKL], const uint32_t (&vr)[4][TL::VW],
@@ -705,7 +716,7 @@ __global__ __launch_bounds__(64) void paged_prefill_kernel(
     const int nkt = p_last / BS + 1;             // tiles holding keys 0 .. p_last
     const int kt_m = (p_first + 1) / BS;         // tiles below are unmasked for every query
 
-    MfmaCols<D, FMT, QB> cols;
+    MfmaCols<D, FMT, QB, kPrefillRawSoftmax> cols;
     int p_n[QB];
 #pragma unroll
     for (int c = 0; c < QB; ++c) {
@@ -930,7 +941,7 @@ constexpr int kAttnPrefetchFp8 = 2;
 #ifdef MIKV_TUNE_WAVES_PER_CU
 constexpr int kAttnWavesPerCU = MIKV_TUNE_WAVES_PER_CU;
 #else
-constexpr int kAttnWavesPerCU = 4;
+constexpr int kAttnWavesPerCU = 3;
 #endif
 // Query column blocks of 16 per prefill wave.
 #ifdef MIKV_TUNE_PREFILL_QB

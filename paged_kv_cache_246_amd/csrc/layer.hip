@@ -527,14 +527,18 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Waves per workgroup of a projection: the largest divisor of the K batches
 // that keeps the workgroup within its wave bound and the LDS cap, and the
 // projection within the target wave count.
+#ifndef MIKV_PROJ_TARGET_D
+#define MIKV_PROJ_TARGET_D MIKV_PROJ_TARGET_WAVES
+#endif
 template <int MT, int NW, int KB, int ACT, int EPI>
 int proj_waves(int wgs, int K) {
+    const int target = EPI == kEpiOut ? MIKV_PROJ_TARGET_D : kProjTargetWaves;
     const int units = K / (KB * kKStep);
     const int max_ks = std::min<int>(proj_max_waves<MT, NW, KB, ACT, EPI>(),
                                      static_cast<int>(kProjLdsCap / proj_lds_per_wave<MT, NW, KB, ACT>()));
     int ks = 1;
     for (int d = 1; d <= std::min(units, max_ks); ++d)
-        if (units % d == 0 && static_cast<int64_t>(wgs) * d <= kProjTargetWaves) ks = d;
+        if (units % d == 0 && static_cast<int64_t>(wgs) * d <= target) ks = d;
     return ks;
 }
 
