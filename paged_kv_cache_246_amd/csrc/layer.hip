@@ -374,6 +374,37 @@ __global__ __launch_bounds__((64 * proj_max_waves<MT, NW, KB, ACT, EPI>())) void
         for (int j = 0; j < NW; ++j) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
+    // QKV: the thread's first epilogue item's position, block and rotation
+    // (float64 sincos) are computed here, while the first weight batches are
+    // in flight, rather than after the K loop.
+    int pre_pos = -1;
+    int32_t pre_blk = -1;
+    double pre_sn = 0.0, pre_cs = 1.0;
+    if constexpr (EPI == kEpiQkv) {
+        const int it = threadIdx.x;
+        if (it < M * NP * 16) {
+            const int m = it / (NP * 16);
+            const int d = (j0 + (it >> 4) % NP) * 16 + (it & 15);
+            pre_pos = a.ctx[m];
+            if (pre_pos >= 0 && pre_pos / BS < a.mbps) {
+                pre_blk = a.table[static_cast<size_t>(m) * a.mbps + pre_pos / BS];
+                if (head < a.hq + a.hkv) sincos(static_cast<double>(pre_pos) * rope.inv_freq[d], &pre_sn, &pre_cs);
+            }
+        }
+    }
+
+    // Residual epilogues: the thread's first output's residual input is
+    // loaded here for the same reason.
+    float pre_res = 0.f;
+    if constexpr (EPI == kEpiResidual || EPI == kEpiOut) {
+        const int it = threadIdx.x;
+        if (it < M * NW * 16) {
+            const size_t at = static_cast<size_t>(it / (NW * 16)) * a.N + tile[(it >> 4) % NW] * 16 + (it & 15);
+            if constexpr (EPI == kEpiResidual) pre_res = bf16_to_f32(a.x_in[at]);
+            else pre_res = a.x2[at];
+        }
+    }
+
     constexpr uint32_t STEP_BYTES = KB * kKStep * 2;
     const int k_chunk = K / KS;
     const int nb = k_chunk / (KB * kKStep);   // batches (>= 1)
@@ -446,9 +477,10 @@ __global__ __launch_bounds__((64 * proj_max_waves<MT, NW, KB, ACT, EPI>())) void
             const int m = it / (NP * 16);
             const int p = (it >> 4) % NP, c = it & 15;
             const int d = (j0 + p) * 16 + c;           // < D / 2
-            const int pos = a.ctx[m];
+            const bool first = it == static_cast<int>(threadIdx.x);
+            const int pos = first ? pre_pos : a.ctx[m];
             const bool pos_ok = pos >= 0 && pos / BS < a.mbps;
-            const int32_t blk = pos_ok ? a.table[static_cast<size_t>(m) * a.mbps + pos / BS] : -1;
+            const int32_t blk = !pos_ok ? -1 : first ? pre_blk : a.table[static_cast<size_t>(m) * a.mbps + pos / BS];
             const bool blk_ok = pos_ok && blk >= 0 && blk < a.num_blocks;
             if (g == 0 && p == 0 && c == 0) {
                 if (!pos_ok) atomicOr(a.err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
@@ -463,9 +495,8 @@ __global__ __launch_bounds__((64 * proj_max_waves<MT, NW, KB, ACT, EPI>())) void
                 // the same float64 RoPE and single rounding as write_decode_kv
                 const double x1 = static_cast<double>(y0);
                 const double x2 = static_cast<double>(y1);
-                const double ang = static_cast<double>(pos) * rope.inv_freq[d];
-                double sn, cs;
-                sincos(ang, &sn, &cs);
+                double sn = pre_sn, cs = pre_cs;
+                if (!first) sincos(static_cast<double>(pos) * rope.inv_freq[d], &sn, &cs);
                 const uint16_t r1 = f64_to_bf16(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
                 const uint16_t r2 = f64_to_bf16(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
                 if (head < hq) {
@@ -516,8 +547,9 @@ __global__ __launch_bounds__((64 * proj_max_waves<MT, NW, KB, ACT, EPI>())) void
             const int j = (it >> 4) % NW, c = it & 15;
             const size_t at = static_cast<size_t>(m) * a.N + tile[j] * 16 + c;
             const float y = out(j, m, c);
-            if constexpr (EPI == kEpiResidual) a.y_f32[at] = bf16_to_f32(a.x_in[at]) + y;
-            else a.y_bf16[at] = f32_to_bf16(a.x2[at] + y);
+            const bool first = it == static_cast<int>(threadIdx.x);
+            if constexpr (EPI == kEpiResidual) a.y_f32[at] = (first ? pre_res : bf16_to_f32(a.x_in[at])) + y;
+            else a.y_bf16[at] = f32_to_bf16((first ? pre_res : a.x2[at]) + y);
         }
     }
 }
