@@ -219,6 +219,116 @@ def run_offload_bench(args, torch, mk, workloads):
     return res
 
 
+def run_serving_offload_bench(args, torch, mk):
+    """KV offload as a second workload: the library's step planner serving 16
+    requests with 4K-8K-token prompts (seed 9, 128-256 new tokens each) on a
+    Qwen3-8B-shaped cache (32/8 heads, D 128) of 2048 blocks, 8 running at
+    most, tight KV brakes (2 % / 5 %) and a 4096-slot page-locked host swap
+    space, so decode growth forces swap-outs and later swap-ins. Every step
+    runs the plan through the C ABI: swaps, then prefill rows (write +
+    causal attention), then decode rows (write + attention); q, k, v are
+    fresh N(0, 1) draws on the device. GPU time per phase from HIP events,
+    planner host time per step."""
+    import time
+    dev = "cuda:0"
+    N, Hq, Hkv, D, theta, R, S = 2048, 32, 8, 128, 1e6, 8, 4096
+    mbps = (8192 + 256 + 15) // 16 + 1
+    rng = np.random.default_rng(9)
+    reqs = [(i, int(rng.integers(4096, 8193)), int(rng.integers(128, 257))) for i in range(16)]
+    kd = torch.zeros((N, Hkv, 16, D), dtype=torch.int16, device=dev)
+    vd = torch.zeros_like(kd)
+    hk = torch.zeros((S, Hkv, 16, D), dtype=torch.int16, pin_memory=True)
+    hv = torch.zeros_like(hk)
+    pool = mk.mi_kv_pool_init(N, 16, Hkv, D, kd, vd)
+    sch = mk.Scheduler(pool, mbps, R, hard=0.02, soft=0.05, host_slots=S)
+    ws_bytes = mk.mi_paged_gqa_decode_workspace_bytes(pool, R, Hq, mbps * 16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    rnd = lambda *shape: torch.randn(shape, dtype=torch.bfloat16, device=dev, generator=gen).view(torch.int16)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    phases = {"swap": [], "prefill": [], "decode": []}
+    plan_s, steps = 0.0, 0
+    tok = {"prefill": 0, "decode": 0, "swap_blocks_out": 0, "swap_blocks_in": 0}
+    try:
+        for rid, prompt, new in reqs:
+            sch.submit(rid, prompt, new)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        while sch.num_waiting() or sch.num_running() or sch.num_swapped():
+            t0 = time.perf_counter()
+            plan = sch.step()
+            plan_s += time.perf_counter() - t0
+            steps += 1
+            so, si = plan["swap_out"], plan["swap_in"]
+            if len(so) or len(si):
+                a, b = ev(), ev()
+                a.record()
+                if len(so):
+                    mk.mi_kv_swap_out(pool, hk, hv, S, so)
+                if len(si):
+                    mk.mi_kv_swap_in(pool, hk, hv, S, si)
+                b.record()
+                phases["swap"].append((a, b))
+                tok["swap_blocks_out"] += len(so)
+                tok["swap_blocks_in"] += len(si)
+            npf, ndc = plan["num_prefill"], plan["num_decode"]
+            if npf:
+                ctx = plan["context_lens"][:npf]
+                n = plan["new_tokens"][:npf]
+                cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+                T = int(cu[-1])
+                q, k, v = rnd(T, Hq, D), rnd(T, Hkv, D), rnd(T, Hkv, D)
+                qr, out = torch.empty_like(q), torch.empty_like(q)
+                td = torch.from_numpy(np.ascontiguousarray(plan["block_table"][:npf])).to(dev)
+                cd, cud = torch.from_numpy(ctx).to(dev), torch.from_numpy(cu).to(dev)
+                a, b = ev(), ev()
+                a.record()
+                mk.mi_write_prefill_kv(pool, q, k, v, qr, td, mbps, cd, cud, npf, T, Hq, theta)
+                mk.mi_paged_prefill_attention(pool, qr, out, td, mbps, cd, cud, npf, T, int(n.max()), Hq)
+                b.record()
+                phases["prefill"].append((a, b))
+                tok["prefill"] += T
+            if ndc:
+                ctx = np.ascontiguousarray(plan["context_lens"][npf:npf + ndc])
+                q, k, v = rnd(ndc, Hq, D), rnd(ndc, Hkv, D), rnd(ndc, Hkv, D)
+                qr, out = torch.empty_like(q), torch.empty_like(q)
+                td = torch.from_numpy(np.ascontiguousarray(plan["block_table"][npf:npf + ndc])).to(dev)
+                cd = torch.from_numpy(ctx).to(dev)
+                a, b = ev(), ev()
+                a.record()
+                mk.mi_write_decode_kv(pool, q, k, v, qr, td, mbps, cd, ndc, Hq, theta)
+                mk.mi_paged_gqa_decode(pool, qr, out, td, mbps, cd, ndc, Hq, 0.0, int(ctx.max()), ws,
+                                       ws_bytes)
+                b.record()
+                phases["decode"].append((a, b))
+                tok["decode"] += ndc
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        faults = mk.mi_kv_pool_check_errors(pool)
+    finally:
+        sch.close()
+        mk.mi_kv_pool_destroy(pool)
+    if faults:
+        raise RuntimeError("device fault bits %#x during the serving benchmark" % faults)
+    ms = {k: sum(a.elapsed_time(b) for a, b in v) for k, v in phases.items()}
+    block_bytes = 2 * Hkv * 16 * D * 2
+    swapped = (tok["swap_blocks_out"] + tok["swap_blocks_in"]) * block_bytes
+    return {
+        "workload": "step planner over 16 Qwen3-8B-shaped requests, prompts U[4096, 8192], "
+                    "128-256 new tokens, 2048-block pool, 8 running, brakes 2 %/5 %, 4096 host slots",
+        "steps": steps,
+        "prefill_tokens": tok["prefill"], "decode_tokens": tok["decode"],
+        "swap_blocks_out": tok["swap_blocks_out"], "swap_blocks_in": tok["swap_blocks_in"],
+        "gpu_ms": {k: round(v, 3) for k, v in ms.items()},
+        "prefill_tokens_per_s_gpu": round(tok["prefill"] / (ms["prefill"] * 1e-3), 1) if ms["prefill"] else None,
+        "decode_tokens_per_s_gpu": round(tok["decode"] / (ms["decode"] * 1e-3), 1) if ms["decode"] else None,
+        "swap_GBps": round(swapped / (ms["swap"] * 1e-3) / 1e9, 2) if ms["swap"] else None,
+        "planner_us_per_step": round(plan_s / steps * 1e6, 2),
+        "wall_s": round(wall, 3),
+    }
+
+
 def run_small_workloads(args, torch, mk, workloads):
     """Decode step (write + attention) on the other decode workloads: step time,
     algorithmic GB/s and fraction of the HBM peak (most are launch-latency bound)."""
@@ -374,6 +484,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit cache variant of the step")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill chunk")
     ap.add_argument("--no-offload", action="store_true", help="skip the KV swap measurement")
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the planner-driven serving run with KV offload")
     ap.add_argument("--layer-only", action="store_true",
                     help="time only the full-layer step (for its kernel profile)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -477,6 +589,8 @@ def main():
         line["prefill"] = run_prefill_bench(args, torch, mk, workloads)
     if not args.no_offload:
         line["kv_offload"] = run_offload_bench(args, torch, mk, workloads)
+    if not args.no_serving:
+        line["serving_offload"] = run_serving_offload_bench(args, torch, mk)
     if not args.no_layer:
         try:
             line["layer_step"] = run_layer_bench(args, torch, mk, workloads)
