@@ -32,8 +32,10 @@ Modules:
   paged      block counts, slot mapping, free-block stack, size formula
   rope       rotary position embedding, half-split pairing
   attention  write_decode_kv, gather, paged GQA decode attention (bf16 and
-             8-bit caches)
+             8-bit caches), the split-K partial statistics and their merge,
+             prefill (packed prompt write, causal attention)
   layer      RMSNorm, SiLU, SwiGLU, full decoder-layer decode step
+  sched      continuous-batching step planner with the KV brakes and swap
 
 Every function is pinned by the ``-m "not gpu"`` tests against closed forms,
 invariants, brute force or independent library routines. Any function without

@@ -86,6 +86,39 @@ def attend(q_vec, K, V, scale):
     return (p @ V) / np.sum(p)
 
 
+def partial_attend(q_vec, K, V, scale):
+    """The softmax statistics of one piece of the key range (the split-K step
+    of the decode path; nxmr.cn section 5.1's stable form kept unnormalised):
+    m = max of the scores, l = sum of exp(s - m), acc = sum of exp(s - m) V.
+    An empty piece returns (-inf, 0, 0).
+    """
+    s = (K @ q_vec) * scale
+    if s.size == 0:
+        return -np.inf, 0.0, np.zeros(V.shape[1])
+    m = np.max(s)
+    p = np.exp(s - m)
+    return m, np.sum(p), p @ V
+
+
+def combine_partials(parts):
+    """Merge the (m, l, acc) of the pieces of one key range: with M = max m_i,
+    out = sum_i exp(m_i - M) acc_i / sum_i exp(m_i - M) l_i. Pieces are taken
+    in the order given (the result is the same for any order in exact
+    arithmetic). Pinned by tests/test_oracle_combine.py: equal to attend()
+    over the whole range for any split, empty pieces included.
+    """
+    M = max(m for m, _, _ in parts)
+    l = 0.0
+    acc = 0.0
+    for m, li, ai in parts:
+        if m == -np.inf:
+            continue
+        w = np.exp(m - M)
+        l = l + w * li
+        acc = acc + w * ai
+    return acc / l
+
+
 def paged_gqa_decode(q_rot, k_pool, v_pool, block_table, context_lens, block_size,
                      scale=None, q_is_bits=True):
     """Paged GQA decode attention: every query head of every sequence attends
