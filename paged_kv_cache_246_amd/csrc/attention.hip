@@ -31,9 +31,6 @@ constexpr float kRescaleSlack = 8.0f; // log2 units: running max may lag by 2^8
 constexpr bool kPrefillRawSoftmax = MIKV_TUNE_PREFILL_RAW != 0;   // prefill softmax form (see softmax_step)
 
 // ---------------------------------------------------------------- bf16 helpers
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
