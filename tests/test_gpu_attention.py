@@ -137,6 +137,30 @@ def test_split_sizes_all_within_tolerance_and_permutation_invariant(split):
         dc.close()
 
 
+def test_repeated_calls_with_other_splits_in_between_are_bit_identical():
+    """A call with many cut segments (16-token shares), one with few, then the
+    first again on the same pool: the repeats are bit-identical, so no state
+    of one call (partials, merge bookkeeping) leaks into the next."""
+    cfg = workloads.CONFIGS["qwen3_1p7b"]
+    case = workloads.make_decode_case(cfg, pool="poison")
+    ref, _, _, _ = oatt.decode_step(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                    case.block_table, case.context_lens, 16, cfg.rope_theta)
+    dc = DeviceCase(case)
+    try:
+        dc.write()
+        outs = []
+        for split in (16, 1024, 16, 1024):
+            dc.attend(split_tokens=split)
+            torch.cuda.synchronize()
+            outs.append(dev_to_bits(dc.out))
+            check_tolerance(outs[-1], ref, "split %d" % split)
+        assert np.array_equal(outs[0], outs[2])
+        assert np.array_equal(outs[1], outs[3])
+        assert dc.faults() == 0
+    finally:
+        dc.close()
+
+
 @pytest.mark.parametrize("name,len_extra", [("tiny", 1), ("qwen3_1p7b", 0), ("qwen3_1p7b", 1)])
 def test_gather_bit_exact(name, len_extra):
     cfg = workloads.CONFIGS[name]
