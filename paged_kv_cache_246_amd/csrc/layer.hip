@@ -143,10 +143,18 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 // instruction reads 64 / (4 KB) whole row segments of 64 KB bytes (full
 // 128-byte lines at KB = 2); mma() writes the batch to the wave's LDS tile and
 // reads it back in the MFMA layout (rows padded by 16 bytes).
-template <int MT, int NW, int ACT, int KB>
+template <int MT, int NW, int ACT, int KB, bool HALF = false>
 struct GemmBatch {
     static constexpr bool GAIN = ACT == kActGainSplit || ACT == kActF32GainSplit;
     static constexpr bool F32 = ACT == kActF32Split || ACT == kActF32GainSplit;
+    // HALF (fp32 modes, at most 8 rows): one load per K step fills all 64
+    // lanes -- lane 16 q + c loads elements 4 (c / 8) .. + 4 of the lane's
+    // 8-element segment of row c % 8 -- and the two halves of a segment are
+    // joined by a lane rotation by 8 within each row of 16 lanes. Lanes c >= 8
+    // then feed copies of rows 0..7 as MFMA rows 8..15, whose outputs are
+    // never read.
+    static constexpr bool F32H = F32 && HALF;
+    static_assert(!HALF || (F32 && MT == 1), "HALF: fp32 activations, one row tile");
     static constexpr int AE = F32 ? 4 : 2;                     // activation element bytes
     static constexpr int LPR = 4 * KB;                         // lanes per row
     static constexpr int RPI = 64 / LPR;                       // rows per load
@@ -154,7 +162,7 @@ struct GemmBatch {
     static constexpr int LDS_BYTES = 16 * NW * ROWB;           // per wave
     uint4 w[KB * NW];                      // load i: tile i / KB, rows (i % KB) RPI ..
     uint4 a0[KB][MT];                      // bf16 activations, or fp32 elements 0..3
-    uint4 a1[F32 ? KB : 1][F32 ? MT : 1];  // fp32 elements 4..7
+    uint4 a1[F32 && !HALF ? KB : 1][F32 && !HALF ? MT : 1];  // fp32 elements 4..7
     uint4 gn[GAIN ? KB : 1];               // gain
 
     // kbyte: byte offset of the batch's first K column in a bf16 row. woff:
@@ -170,7 +178,7 @@ struct GemmBatch {
             for (int mt = 0; mt < MT; ++mt) {
                 const uint32_t ak = (kbyte + u * kKStep * 2) / 2 * AE;
                 a0[u][mt] = bload<0>(ra, aoff[mt], ak);
-                if constexpr (F32) a1[u][mt] = bload<0>(ra, aoff[mt] + 16, ak);
+                if constexpr (F32 && !HALF) a1[u][mt] = bload<0>(ra, aoff[mt] + 16, ak);
             }
         if constexpr (GAIN) {
 #pragma unroll
@@ -194,7 +202,19 @@ struct GemmBatch {
                 uint4 hi = a0[u][mt], lo = make_uint4(0, 0, 0, 0);
                 if constexpr (ACT != kActBf16) {
                     float x[8];
-                    if constexpr (F32) {
+                    if constexpr (F32H) {
+                        // own 4 elements, then the partner lane's (c xor 8) 4
+                        const uint4 p0 = a0[u][mt];
+                        constexpr int kRowRor8 = 0x128;      // DPP: rotate right by 8 within 16 lanes
+                        const uint32_t q0 = __builtin_amdgcn_mov_dpp(static_cast<int>(p0.x), kRowRor8, 0xf, 0xf, false);
+                        const uint32_t q1 = __builtin_amdgcn_mov_dpp(static_cast<int>(p0.y), kRowRor8, 0xf, 0xf, false);
+                        const uint32_t q2 = __builtin_amdgcn_mov_dpp(static_cast<int>(p0.z), kRowRor8, 0xf, 0xf, false);
+                        const uint32_t q3 = __builtin_amdgcn_mov_dpp(static_cast<int>(p0.w), kRowRor8, 0xf, 0xf, false);
+                        x[0] = __uint_as_float(p0.x); x[1] = __uint_as_float(p0.y);
+                        x[2] = __uint_as_float(p0.z); x[3] = __uint_as_float(p0.w);
+                        x[4] = __uint_as_float(q0); x[5] = __uint_as_float(q1);
+                        x[6] = __uint_as_float(q2); x[7] = __uint_as_float(q3);
+                    } else if constexpr (F32) {
                         const uint4 p0 = a0[u][mt], p1 = a1[u][mt];
                         x[0] = __uint_as_float(p0.x); x[1] = __uint_as_float(p0.y);
                         x[2] = __uint_as_float(p0.z); x[3] = __uint_as_float(p0.w);
@@ -276,10 +296,10 @@ struct ProjArgs {
 #ifndef MIKV_PROJ_VGPR_EXTRA
 #define MIKV_PROJ_VGPR_EXTRA 30
 #endif
-template <int MT, int NW, int KB, int ACT, int EPI>
+template <int MT, int NW, int KB, int ACT, int EPI, bool HALF>
 constexpr int proj_max_waves() {
-    using B = GemmBatch<MT, NW, ACT, KB>;
-    constexpr int batch = 4 * (KB * NW + KB * MT * (B::F32 ? 2 : 1) + (B::GAIN ? KB : 0));
+    using B = GemmBatch<MT, NW, ACT, KB, HALF>;
+    constexpr int batch = 4 * (KB * NW + KB * MT * (B::F32 && !HALF ? 2 : 1) + (B::GAIN ? KB : 0));
     if (EPI == kEpiQkv) return MIKV_PROJ_QKV_WAVES;
     return 2 * batch + 4 * NW * MT + MIKV_PROJ_VGPR_EXTRA <= 128 ? 16 : 8;
 }
@@ -299,10 +319,10 @@ constexpr size_t proj_lds_per_wave() {
 // batch in flight while the current one is multiplied), then the waves'
 // accumulators (and RMSNorm sums) are summed through LDS in wave order and
 // the epilogue runs on the finished outputs.
-template <int MT, int NW, int KB, int ACT, int EPI>
-__global__ __launch_bounds__((64 * proj_max_waves<MT, NW, KB, ACT, EPI>())) void proj_kernel(
+template <int MT, int NW, int KB, int ACT, int EPI, bool HALF>
+__global__ __launch_bounds__((64 * proj_max_waves<MT, NW, KB, ACT, EPI, HALF>())) void proj_kernel(
     ProjArgs a, mikv::RopeTable rope) {
-    using Batch = GemmBatch<MT, NW, ACT, KB>;
+    using Batch = GemmBatch<MT, NW, ACT, KB, HALF>;
     constexpr int NP = NW / 2;                 // tile pairs (QKV, SwiGLU)
     static_assert((EPI != kEpiQkv && EPI != kEpiSwiglu) || (NW % 2 == 0), "paired tiles");
     extern __shared__ __align__(16) char lds[];
@@ -360,9 +380,14 @@ __global__ __launch_bounds__((64 * proj_max_waves<MT, NW, KB, ACT, EPI>())) void
     char* stage = lds + wv * Batch::LDS_BYTES;
     uint32_t aoff[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-        aoff[mt] = mt * 16 + col < M ? (static_cast<uint32_t>(mt * 16 + col) * K + kq * 8) * Batch::AE
+    for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (Batch::F32H)
+            aoff[mt] = (col & 7) < M ? (static_cast<uint32_t>(col & 7) * K + kq * 8 + 4 * (col >> 3)) * Batch::AE
                                      : kOutOfRange;
+        else
+            aoff[mt] = mt * 16 + col < M ? (static_cast<uint32_t>(mt * 16 + col) * K + kq * 8) * Batch::AE
+                                         : kOutOfRange;
+    }
     const uint32_t goff = kq * 8 * 2;
 
     f32x4_t acc[NW][MT];
@@ -559,14 +584,17 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Waves per workgroup of a projection: the largest divisor of the K batches
 // that keeps the workgroup within its wave bound and the LDS cap, and the
 // projection within the target wave count.
+// down (256 workgroups at hidden 4096) takes up to 16 waves each: with the
+// one-load fp32 activations a wave fits in 76 registers, and 16 waves per
+// workgroup measured faster than 8 or 12 on MI355X.
 #ifndef MIKV_PROJ_TARGET_D
-#define MIKV_PROJ_TARGET_D MIKV_PROJ_TARGET_WAVES
+#define MIKV_PROJ_TARGET_D 4096
 #endif
-template <int MT, int NW, int KB, int ACT, int EPI>
+template <int MT, int NW, int KB, int ACT, int EPI, bool HALF>
 int proj_waves(int wgs, int K) {
     const int target = EPI == kEpiOut ? MIKV_PROJ_TARGET_D : kProjTargetWaves;
     const int units = K / (KB * kKStep);
-    const int max_ks = std::min<int>(proj_max_waves<MT, NW, KB, ACT, EPI>(),
+    const int max_ks = std::min<int>(proj_max_waves<MT, NW, KB, ACT, EPI, HALF>(),
                                      static_cast<int>(kProjLdsCap / proj_lds_per_wave<MT, NW, KB, ACT>()));
     int ks = 1;
     for (int d = 1; d <= std::min(units, max_ks); ++d)
@@ -600,16 +628,20 @@ constexpr int kb_for(int nw) { return nw >= 2 ? 2 : 4; }
 #endif
 constexpr int kKbD = MIKV_PROJ_KB_D;
 
-template <int MT, int NW, int KB, int ACT, int EPI>
+template <int MT, int NW, int KB, int ACT, int EPI, bool HALF = false>
 void launch_proj(const ProjArgs& a, const mikv::RopeTable& rope, int wgs, hipStream_t st) {
-    const int ks = proj_waves<MT, NW, KB, ACT, EPI>(wgs, a.K);
+    const int ks = proj_waves<MT, NW, KB, ACT, EPI, HALF>(wgs, a.K);
     const size_t lds = proj_lds_per_wave<MT, NW, KB, ACT>() * ks;
-    hipLaunchKernelGGL((proj_kernel<MT, NW, KB, ACT, EPI>), dim3(wgs), dim3(64 * ks), lds, st, a, rope);
+    hipLaunchKernelGGL((proj_kernel<MT, NW, KB, ACT, EPI, HALF>), dim3(wgs), dim3(64 * ks), lds, st, a, rope);
 }
 
+// Row tiles by batch; fp32 activations of at most 8 rows take the one-load
+// form (GemmBatch HALF).
 template <int NW, int KB, int ACT, int EPI>
 void launch_proj_m(const ProjArgs& a, const mikv::RopeTable& rope, int wgs, hipStream_t st) {
-    if (a.M <= 16) launch_proj<1, NW, KB, ACT, EPI>(a, rope, wgs, st);
+    constexpr bool kF32 = ACT == kActF32Split || ACT == kActF32GainSplit;
+    if (kF32 && a.M <= 8) launch_proj<1, NW, KB, ACT, EPI, kF32>(a, rope, wgs, st);
+    else if (a.M <= 16) launch_proj<1, NW, KB, ACT, EPI>(a, rope, wgs, st);
     else launch_proj<2, NW, KB, ACT, EPI>(a, rope, wgs, st);
 }
 
