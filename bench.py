@@ -432,6 +432,33 @@ def run_layer_bench(args, torch, mk, workloads):
     }
 
 
+def run_stream_read(torch, mk):
+    """Streaming-read bandwidth of the part (mi_hbm_stream_read): 1 GiB read
+    by 512 workgroups of 256 threads, one contiguous chunk each, non-temporal
+    16-byte loads; a 512 MiB fill between timed reads evicts the caches.
+    Median of 10 reads."""
+    dev = "cuda:0"
+    n, wgs = 1 << 30, 512
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(3)
+    sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        mk.mi_hbm_stream_read(src, n, sink, wgs, stream.cuda_stream)
+    ms = []
+    for i in range(10):
+        flush.fill_(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        mk.mi_hbm_stream_read(src, n, sink, wgs, stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    med = float(np.median(ms))
+    return {"bytes": n, "workgroups": wgs, "median_ms": round(med, 5),
+            "GBps": round(n / (med * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(case, cfg, workloads, budget_s):
     """The fp64 oracle as it stands, timed on whole sequences of the same
     workload (write then attention), pass after pass over the batch until
@@ -490,6 +517,8 @@ def main():
     ap.add_argument("--layer-only", action="store_true",
                     help="time only the full-layer step (for its kernel profile)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-stream-read", action="store_true",
+                    help="skip the streaming-read bandwidth measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -570,7 +599,16 @@ def main():
             "algorithmic_bytes": int(r["attn_bytes"]),
             "traffic": recorded_traffic(),
         },
+        "attention_launch_ms": {
+            "p10": round(float(np.percentile(r["attn_ms"], 10)), 5),
+            "p50": round(float(np.percentile(r["attn_ms"], 50)), 5),
+            "p90": round(float(np.percentile(r["attn_ms"], 90)), 5),
+        },
     }
+    if not args.no_stream_read:
+        sr = run_stream_read(torch, mk)
+        line["hbm_stream_read"] = sr
+        line["roofline"]["frac_of_stream_read"] = round(achieved / sr["GBps"], 4)
     if not args.no_fp8:
         r8 = run_attention_bench(args, torch, mk, workloads, kv_format="fp8")
         ms8 = r8["ms_step"]

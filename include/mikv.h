@@ -498,6 +498,20 @@ int mi_kv_swap_out(mi_kv_pool_t pool, void* host_k, void* host_v, int32_t host_s
 int mi_kv_swap_in(mi_kv_pool_t pool, const void* host_k, const void* host_v, int32_t host_slots,
                   const int32_t* pairs, int32_t n, void* stream);
 
+/*
+ * Measurement utility (not a step of the method): reads `bytes` of device
+ * memory at `src` (16-byte aligned, bytes a multiple of 16) with 16-byte
+ * non-temporal loads, each of `workgroups` workgroups of 256 threads one
+ * contiguous chunk (a tail of fewer than `workgroups` 16-byte units is not
+ * read), and stores one folded word per thread into `sink` (device,
+ * workgroups * 256 uint32, caller-owned). Timing it gives the streaming-read
+ * bandwidth the part delivers, the practical ceiling next to the published
+ * HBM peak. Asynchronous on `stream`; MI_ERR_INVALID_ARG for null pointers,
+ * misalignment or workgroups outside 1..65536 or above bytes / 16.
+ */
+int mi_hbm_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,7 @@ SIGNATURES = {
     "mi_paged_gqa_decode_split": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                              _c.c_float, _i32, _i32, _vp, _sz, _vp]),
     "mi_paged_gqa_decode_split_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32]),
+    "mi_hbm_stream_read": (_c.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "mi_write_prefill_kv": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                        _i32, _c.c_double, _vp]),
     "mi_paged_prefill_attention": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
@@ -396,3 +397,9 @@ def mi_kv_swap_in(pool, host_k, host_v, host_slots, pairs, stream=None):
     return _check("mi_kv_swap_in", lib().mi_kv_swap_in(
         pool, _ptr(host_k), _ptr(host_v), host_slots, pr.ctypes.data if len(pr) else None,
         len(pr), _stream(stream)))
+
+
+# ------------------------------------------------------------ measurement
+def mi_hbm_stream_read(src, nbytes, sink, workgroups, stream=None):
+    return _check("mi_hbm_stream_read", lib().mi_hbm_stream_read(
+        _ptr(src), nbytes, _ptr(sink), workgroups, _stream(stream)))

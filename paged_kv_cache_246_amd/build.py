@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libmikv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["pool.cpp", "sched.cpp", "swap.hip", "attention.hip", "layer.hip"]
+SOURCES = ["pool.cpp", "sched.cpp", "swap.hip", "attention.hip", "layer.hip", "calib.hip"]
 
 # Packed fp32 instructions are kept out of every device build.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
