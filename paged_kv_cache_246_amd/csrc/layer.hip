@@ -627,6 +627,13 @@ constexpr int kb_for(int nw) { return nw >= 2 ? 2 : 4; }
 #define MIKV_PROJ_KB_D kb_for(kNwD)
 #endif
 constexpr int kKbD = MIKV_PROJ_KB_D;
+// o_proj (bf16 activations, one tile): 8 K steps per batch (8 KiB of
+// weights per wave in flight per slot) measured 0.5 us faster than 4 on the
+// Qwen3-8B-shaped layer.
+#ifndef MIKV_PROJ_KB_O
+#define MIKV_PROJ_KB_O 8
+#endif
+constexpr int kKbO = MIKV_PROJ_KB_O;
 
 template <int MT, int NW, int KB, int ACT, int EPI, bool HALF = false>
 void launch_proj(const ProjArgs& a, const mikv::RopeTable& rope, int wgs, hipStream_t st) {
@@ -763,7 +770,7 @@ extern "C" int mi_decoder_layer_decode(mi_kv_pool_t p, const mi_layer_config* cf
         a.N = H;
         a.x_in = x_in;
         a.y_f32 = x2;
-        launch_proj_m<kNwO, kb_for(kNwO), kActBf16, kEpiResidual>(a, rope, H / 16 / kNwO, st);
+        launch_proj_m<kNwO, kKbO, kActBf16, kEpiResidual>(a, rope, H / 16 / kNwO, st);
     }
     // 4. a = silu(r2 W_gate^T) * (r2 W_up^T), r2 = x2 * ln2_w / rms(x2)
     {
