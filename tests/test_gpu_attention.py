@@ -220,6 +220,32 @@ def test_group_sizes_head_dims_and_block_boundaries(D, Hq, Hkv):
         dc.close()
 
 
+@pytest.mark.parametrize("B,ctx_hi", [(65, 40), (130, 200), (1024, 300)])
+def test_batches_past_one_prefix_chunk_and_at_the_maximum(B, ctx_hi):
+    """The kernels build the tile prefix over the batch 64 sequences at a time
+    with a carry: batches of 65 and 130 cross one and two chunk boundaries,
+    1024 is the largest batch a call accepts. Write and attention against the
+    oracle, two split sizes."""
+    cfg = workloads.DecodeConfig("big_batch", batch=B, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                 block_size=16, num_blocks=0, rope_theta=1e4, ctx_draw="uniform",
+                                 ctx_lo=0, ctx_hi=ctx_hi, seed=B)
+    case = workloads.make_decode_case(cfg, pool="poison")
+    _say("batch", B, "tokens", int(case.context_lens.sum()) + B)
+    ref, _, _, _ = oatt.decode_step(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                    case.block_table, case.context_lens, 16, cfg.rope_theta)
+    dc = DeviceCase(case)
+    try:
+        dc.write()
+        _check_write(case, dc)
+        for split in (0, 64):
+            dc.attend(split_tokens=split)
+            torch.cuda.synchronize()
+            check_tolerance(dev_to_bits(dc.out), ref, "B=%d split=%d" % (B, split))
+        assert dc.faults() == 0
+    finally:
+        dc.close()
+
+
 def test_long_context_config_full_size_sampled():
     """Qwen3-8B-shaped long-context workload at full size in the benchmark's
     launch configuration; the oracle computes sampled (sequence, kv head)

@@ -41,6 +41,11 @@ MID = workloads.DecodeConfig(
     "mid_batch_layer", batch=12, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
     num_blocks=256, rope_theta=1e6, ctx_draw="uniform", ctx_lo=0, ctx_hi=150, seed=14,
     hidden=768, intermediate=1536, rms_eps=1e-6)
+# Batch 17: the second 16-row tile holds one row.
+B17 = workloads.DecodeConfig(
+    "b17_layer", batch=17, num_q_heads=8, num_kv_heads=4, head_dim=64, block_size=16,
+    num_blocks=256, rope_theta=1e4, ctx_draw="uniform", ctx_lo=0, ctx_hi=120, seed=16,
+    hidden=512, intermediate=768, rms_eps=1e-6)
 ONE = workloads.DecodeConfig(
     "one_row_layer", batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, block_size=16,
     num_blocks=32, rope_theta=1e4, ctx_draw="fixed", ctx_fixed=(33,), seed=15,
@@ -99,8 +104,8 @@ def _check_cache(case, cfg, gk, gv, kn, vn):
 
 
 @pytest.mark.parametrize("cfg,std", [(SMALL, 0.05), (WIDE, 0.05), (MAXB, 0.02), (MID, 0.03),
-                                     (ONE, 0.05)],
-                         ids=["small", "wide_b20", "max_b32_g8", "mid_b12", "one_b1"])
+                                     (ONE, 0.05), (B17, 0.05)],
+                         ids=["small", "wide_b20", "max_b32_g8", "mid_b12", "one_b1", "b17"])
 def test_layer_small_shapes(cfg, std):
     print("layer", cfg.name, flush=True)
     case = workloads.make_decode_case(cfg, pool="poison")
