@@ -315,7 +315,15 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 struct MfmaSoftmax {
     float m;      // running max of head n (log2 units), shared by its 4 lanes
     float l;      // this lane's sum of 2^(s - m)
+    float top = kNegInf;   // FIXED form: largest exponent argument s - m seen by this lane
 };
+
+// FIXED softmax form (prefill): a column's reference m is the largest score
+// of the first key tile it reads and is never raised, so no tile rescales the
+// accumulators. The weights 2^(s - m) stay finite while every later score
+// exceeds m by at most kFixedHeadroom (log2 units); a wave in which one did
+// not repeats its work with the online rescaling form.
+constexpr float kFixedHeadroom = 64.0f;
 
 // Operand builders of one 16-token tile.
 // K operand of 32-dim slice j: the lane's key row, 8 dims (bf16; E4M3 codes
@@ -373,9 +381,10 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][MfmaTile<D, F
 // scale is positive) and the scale folds into the exponent's FMA; without
 // tail nothing is masked -- a dead column there has a zero query, finite
 // scores and an output that is never stored.
-template <int NPV, bool RAW = false>
+template <int NPV, bool RAW = false, bool FIXED = false>
 __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_ok, int q4, int qlim,
                                                  bool tail, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
+    static_assert(!FIXED || RAW, "the fixed-reference form works on raw scores");
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -384,6 +393,28 @@ __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_
             const bool ok = col_ok && (!tail || 4 * q4 + i < qlim);
             sc[i] = ok ? sc[i] : kNegInf;
         }
+    }
+    if constexpr (FIXED) {
+        // first tile of the live columns (reference still -inf): the column's
+        // largest score, shared by its 4 lanes; never raised afterwards
+        if (__ballot(sm.m == kNegInf) != 0) {
+            const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * sl2;
+            float hm = fmaxf(mx, __shfl_xor(mx, 16));
+            hm = fmaxf(hm, __shfl_xor(hm, 32));
+            if (sm.m == kNegInf) sm.m = hm;
+        }
+        float p[4];
+        float top = sm.top;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = fmaf(sc[i], sl2, -sm.m);
+            top = fmaxf(top, a);
+            p[i] = __builtin_amdgcn_exp2f(a);
+            sm.l += p[i];
+        }
+        sm.top = top;
+        return bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                        static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
     }
     const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * (RAW ? sl2 : 1.0f);
     if (__ballot(mx > sm.m + kRescaleSlack) != 0) {
@@ -412,7 +443,7 @@ __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_
 // with tail, key row t counts for it only if t < qlim[c] (the rows written so
 // far in decode, the causal limit in prefill), and V rows >= valid_rows are
 // zeroed.
-template <int D, int FMT, int QB, bool RAW = false>
+template <int D, int FMT, int QB, bool RAW = false, bool FIXED = false>
 __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>::NKL],
                                              const uint32_t (&vr)[4][MfmaTile<D, FMT>::VW],
                                              const uint4 (&qb)[QB][MfmaTile<D, FMT>::NQK],
@@ -432,7 +463,7 @@ __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>:
         for (int j = 0; j < TL::NQK; ++j)
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
                                                         __builtin_bit_cast(bf16x8_t, qb[c][j]), s, 0, 0, 0);
-        pb[c] = softmax_step<TL::NPV, RAW>(s, sl2, col_ok[c], q4, qlim[c], tail, sm[c], o[c]);
+        pb[c] = softmax_step<TL::NPV, RAW, FIXED>(s, sl2, col_ok[c], q4, qlim[c], tail, sm[c], o[c]);
     }
     s16x4_t vt[TL::NPV];
     v_operands<D, FMT>(vr, q4, valid_rows, tail, vt);
@@ -444,8 +475,9 @@ __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>:
                 vt[jj], __builtin_bit_cast(s16x4_t, pb[c]), o[c][jj], 0, 0, 0);
 }
 
-// Per-wave state of the QB column blocks (RAW: the prefill softmax form).
-template <int D, int FMT, int QB, bool RAW = false>
+// Per-wave state of the QB column blocks (RAW: the prefill softmax form;
+// FIXED: its fixed-reference variant).
+template <int D, int FMT, int QB, bool RAW = false, bool FIXED = false>
 struct MfmaCols {
     using TL = MfmaTile<D, FMT>;
     uint4 qb[QB][TL::NQK];
@@ -457,7 +489,7 @@ struct MfmaCols {
 
     __device__ __forceinline__ void consume(const uint4 (&kr)[TL::NKL], const uint32_t (&vr)[4][TL::VW],
                                             const int (&qlim)[QB], int valid_rows, bool tail) {
-        mfma_consume<D, FMT, QB, RAW>(kr, vr, qb, sl2, col_ok, q4, qlim, valid_rows, tail, sm, o);
+        mfma_consume<D, FMT, QB, RAW, FIXED>(kr, vr, qb, sl2, col_ok, q4, qlim, valid_rows, tail, sm, o);
     }
     // unmasked tile, or a tile whose rows >= valid_rows are masked for every column
     __device__ __forceinline__ void consume_rows(const uint4 (&kr)[TL::NKL], const uint32_t (&vr)[4][TL::VW],
@@ -713,85 +745,117 @@ __global__ __launch_bounds__(64) void paged_prefill_kernel(
     const int nkt = p_last / BS + 1;             // tiles holding keys 0 .. p_last
     const int kt_m = (p_first + 1) / BS;         // tiles below are unmasked for every query
 
-    MfmaCols<D, FMT, QB, kPrefillRawSoftmax> cols;
     int p_n[QB];
 #pragma unroll
-    for (int c = 0; c < QB; ++c) {
-        const int j = j0 + BS * c + n;
-        cols.col_ok[c] = j < nnew;
-        p_n[c] = ctx + j;
-        const uint16_t* qh = q_rot + (static_cast<size_t>(row0 + (cols.col_ok[c] ? j : 0)) * hkv * G + h) * D;
-#pragma unroll
-        for (int jj = 0; jj < TL::NQK; ++jj) {
-            const int d0 = FMT == kFmtBf16 ? 32 * jj + 8 * q4 : 64 * (jj / 2) + 16 * q4 + 8 * (jj & 1);
-            cols.qb[c][jj] = cols.col_ok[c] ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
-        }
-        cols.sm[c] = MfmaSoftmax{cols.col_ok[c] ? kNegInf : 0.f, 0.f};
-#pragma unroll
-        for (int jj = 0; jj < NPV; ++jj) cols.o[c][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    cols.sl2 = scale_log2;
-    cols.q4 = q4;
-    float vscale = 1.f;
+    for (int c = 0; c < QB; ++c) p_n[c] = ctx + j0 + BS * c + n;
+    float sl2 = scale_log2, vscale = 1.f;
     if constexpr (FMT == kFmtFp8) {
-        cols.sl2 *= kv_scales[g];
+        sl2 *= kv_scales[g];
         vscale = kv_scales[hkv + g];
     }
 
-    MfmaRing<D, FMT, PF, false> ring;
-    ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
-    ring.vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
-    ring.blk_stride = static_cast<size_t>(hkv) * TILE;
+    // query operands and fresh softmax state of the wave's QB column blocks
+    auto init_cols = [&](auto& cl) {
 #pragma unroll
-    for (int jj = 0; jj < TL::NKL; ++jj) ring.koff[jj] = n * TL::ROW + 64 * jj + 16 * q4;
+        for (int c = 0; c < QB; ++c) {
+            const int j = j0 + BS * c + n;
+            cl.col_ok[c] = j < nnew;
+            const uint16_t* qh = q_rot + (static_cast<size_t>(row0 + (cl.col_ok[c] ? j : 0)) * hkv * G + h) * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ring.voff[r] = (4 * q4 + r) * TL::ROW + TL::VB * n;
-
-    // block ids of the sub-chunk starting at tile s0 (lane i: tile s0 + i)
-    auto fetch_ids = [&](int s0, int cnt) {
-        int32_t id = 0;
-        if (lane < cnt) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
-        const bool bad_id = lane < cnt && (id < 0 || id >= num_blocks);
-        if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
-        ring.my_id = bad_id ? 0 : id;
-    };
-    // unmasked tiles [0, kt_m) through the ring, 64 per sub-chunk
-    for (int s0 = 0; s0 < kt_m; s0 += 64) {
-        const int nblk = min(64, kt_m - s0);
-        fetch_ids(s0, nblk);
-        ring.run(nblk, BS, cols);
-    }
-    // the diagonal tiles [kt_m, nkt), causal limit per column
-    fetch_ids(kt_m, nkt - kt_m);
-    for (int t = 0; t < nkt - kt_m; ++t) {
-        const int base = (kt_m + t) * BS;
-        int qlim[QB];
+            for (int jj = 0; jj < TL::NQK; ++jj) {
+                const int d0 = FMT == kFmtBf16 ? 32 * jj + 8 * q4 : 64 * (jj / 2) + 16 * q4 + 8 * (jj & 1);
+                cl.qb[c][jj] = cl.col_ok[c] ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
+            }
+            cl.sm[c] = MfmaSoftmax{cl.col_ok[c] ? kNegInf : 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < QB; ++c) qlim[c] = min(BS, max(0, p_n[c] + 1 - base));
-        ring.template load<0>(t);
-        cols.consume(ring.kr[0], ring.vr[0], qlim, min(BS, p_last + 1 - base), true);
-    }
-
-#pragma unroll
-    for (int c = 0; c < QB; ++c) {
-        float lt = cols.sm[c].l + __shfl_xor(cols.sm[c].l, 16);
-        lt += __shfl_xor(lt, 32);
-        if (!cols.col_ok[c]) continue;
-        const float inv = vscale / lt;
-        uint16_t* oh = out + (static_cast<size_t>(row0 + j0 + BS * c + n) * hkv * G + h) * D + NPV * 4 * q4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            uint32_t wd[NPV / 2];
-#pragma unroll
-            for (int e = 0; e < NPV / 2; ++e)
-                wd[e] = static_cast<uint32_t>(f32_to_bf16_rne(cols.o[c][2 * e][r] * inv)) |
-                        (static_cast<uint32_t>(f32_to_bf16_rne(cols.o[c][2 * e + 1][r] * inv)) << 16);
-            if constexpr (NPV == 8)
-                *reinterpret_cast<uint4*>(oh + NPV * r) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-            else
-                *reinterpret_cast<uint2*>(oh + NPV * r) = make_uint2(wd[0], wd[1]);
+            for (int jj = 0; jj < NPV; ++jj) cl.o[c][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+        cl.sl2 = sl2;
+        cl.q4 = q4;
+    };
+
+    // every key tile of the block: [0, kt_m) unmasked through the register
+    // ring, 64 per sub-chunk, then the diagonal tiles [kt_m, nkt) with a causal
+    // limit per column
+    auto run_pass = [&](auto& cl) {
+        MfmaRing<D, FMT, PF, false> ring;
+        ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
+        ring.vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
+        ring.blk_stride = static_cast<size_t>(hkv) * TILE;
+#pragma unroll
+        for (int jj = 0; jj < TL::NKL; ++jj) ring.koff[jj] = n * TL::ROW + 64 * jj + 16 * q4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ring.voff[r] = (4 * q4 + r) * TL::ROW + TL::VB * n;
+
+        // block ids of the sub-chunk starting at tile s0 (lane i: tile s0 + i)
+        auto fetch_ids = [&](int s0, int cnt) {
+            int32_t id = 0;
+            if (lane < cnt) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
+            const bool bad_id = lane < cnt && (id < 0 || id >= num_blocks);
+            if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+            ring.my_id = bad_id ? 0 : id;
+        };
+        for (int s0 = 0; s0 < kt_m; s0 += 64) {
+            const int nblk = min(64, kt_m - s0);
+            fetch_ids(s0, nblk);
+            ring.run(nblk, BS, cl);
+        }
+        fetch_ids(kt_m, nkt - kt_m);
+        for (int t = 0; t < nkt - kt_m; ++t) {
+            const int base = (kt_m + t) * BS;
+            int qlim[QB];
+#pragma unroll
+            for (int c = 0; c < QB; ++c) qlim[c] = min(BS, max(0, p_n[c] + 1 - base));
+            ring.template load<0>(t);
+            cl.consume(ring.kr[0], ring.vr[0], qlim, min(BS, p_last + 1 - base), true);
+        }
+    };
+
+    auto store = [&](auto& cl) {
+#pragma unroll
+        for (int c = 0; c < QB; ++c) {
+            float lt = cl.sm[c].l + __shfl_xor(cl.sm[c].l, 16);
+            lt += __shfl_xor(lt, 32);
+            if (!cl.col_ok[c]) continue;
+            const float inv = vscale / lt;
+            uint16_t* oh = out + (static_cast<size_t>(row0 + j0 + BS * c + n) * hkv * G + h) * D + NPV * 4 * q4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t wd[NPV / 2];
+#pragma unroll
+                for (int e = 0; e < NPV / 2; ++e)
+                    wd[e] = static_cast<uint32_t>(f32_to_bf16_rne(cl.o[c][2 * e][r] * inv)) |
+                            (static_cast<uint32_t>(f32_to_bf16_rne(cl.o[c][2 * e + 1][r] * inv)) << 16);
+                if constexpr (NPV == 8)
+                    *reinterpret_cast<uint4*>(oh + NPV * r) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                else
+                    *reinterpret_cast<uint2*>(oh + NPV * r) = make_uint2(wd[0], wd[1]);
+            }
+        }
+    };
+
+    // Fixed-reference pass (no rescaling in the tile loop); a wave in which a
+    // score outgrew its column's reference by more than the headroom repeats
+    // the pass with the online rescaling form.
+    MfmaCols<D, FMT, QB, kPrefillRawSoftmax, kPrefillRawSoftmax> cols;
+    init_cols(cols);
+    run_pass(cols);
+    bool redo = false;
+    if constexpr (kPrefillRawSoftmax) {
+        float top = kNegInf;
+#pragma unroll
+        for (int c = 0; c < QB; ++c)
+            if (cols.col_ok[c]) top = fmaxf(top, cols.sm[c].top);
+        redo = __ballot(!(top <= kFixedHeadroom)) != 0;
     }
+    if (!redo) {
+        store(cols);
+        return;
+    }
+    MfmaCols<D, FMT, QB, kPrefillRawSoftmax, false> safe;
+    init_cols(safe);
+    run_pass(safe);
+    store(safe);
 }
 
 // Combine kernel: one workgroup per (query head, sequence). It rebuilds the

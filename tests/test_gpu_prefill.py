@@ -108,6 +108,27 @@ def test_prefill_groups_head_dims_and_diagonals(D, Hq, Hkv):
     _full_check(case, "G=%d D=%d" % (Hq // Hkv, D))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_score_far_above_the_first_tile_takes_the_rescaling_pass(D):
+    """The prefill kernel's first pass fixes each query's softmax reference at
+    the largest score of the first key tile; every query here is the same
+    vector u and token 40's key is 30 u, so for the queries at and after
+    position 40 one score lies hundreds of log2 units above that reference
+    (its weight would overflow float32). Those waves must repeat the chunk
+    with the online rescaling form and still match the oracle; the other
+    waves keep their first-pass results."""
+    cfg = workloads.DecodeConfig("pf_far", batch=2, num_q_heads=4, num_kv_heads=2, head_dim=D,
+                                 block_size=16, num_blocks=32, rope_theta=1e4, ctx_draw="fixed",
+                                 seed=40 + D)
+    case = workloads.make_prefill_case(cfg, (0, 20), (100, 60))
+    u = case.q[0, 0].copy()
+    case.q[:] = u
+    big = obf16.encode(30.0 * obf16.decode(u))
+    case.k[40] = big                       # sequence 0, position 40
+    case.k[case.cu_seqlens[1] + 30] = big  # sequence 1, position 50 (after 20 cached)
+    _full_check(case, "far scores D=%d" % D)
+
+
 def test_prefill_qwen3_8b_shape_sampled_rows():
     """Qwen3-8B-shaped chunk (32/8 heads, D 128): a 1000-token prompt, a 700-token
     chunk after 600 cached tokens and a 64-token chunk after 3000; sampled
