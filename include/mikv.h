@@ -238,7 +238,12 @@ int mi_write_prefill_kv(mi_kv_pool_t pool, const uint16_t* q, const uint16_t* k,
  * that sequence through its block table (cached prefix and the chunk),
  *     out[i,h] = sum_{t <= p} softmax(scale * <q_rot[i,h], K[slot(b,t), g]>)_t V[slot(b,t), g]
  * with g = h / (num_q_heads / num_kv_heads). fp32 accumulation on MFMA, one
- * rounding to bf16 (same arithmetic as mi_paged_gqa_decode, no split).
+ * rounding to bf16 (no split). Each query's softmax is first taken relative
+ * to the largest score of its first key tile, which is never raised; if any
+ * later score exceeds it by more than 2^64 (in weight), the call repeats the
+ * chunk with the running-maximum form (nxmr.cn article, section 5.1) in a
+ * second launch, gated by a generation-numbered word in the pool, so prefill
+ * calls on one pool must run one after another on one stream.
  *  q_rot, out  device bf16 [total_tokens, num_q_heads, head_dim], no aliasing
  *  max_new_tokens  host-side bound of every n_b (sizes the grid); a larger
  *         n_b, cu beyond total_tokens or a chunk past the table row is a fault

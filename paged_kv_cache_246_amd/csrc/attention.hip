@@ -711,13 +711,32 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
 // are unmasked and go through the register ring, the tiles on the diagonal
 // (at most QB + 1) follow with a per-column causal limit. Blocks are issued
 // longest first (largest key range).
-template <int D, int G, int FMT, int PF, int QB>
-__global__ __launch_bounds__(64) void paged_prefill_kernel(
+// Two launches per prefill call. kPrefillFixed: the fixed-reference form;
+// a wave whose scores outgrew a column's reference by more than the headroom
+// writes the call's generation number into the pool's redo word.
+// kPrefillRescale: the online rescaling form, over every query block, only if
+// the redo word holds this call's generation (every wave exits at once
+// otherwise). Generations count the calls on a pool, so the word needs no
+// clearing between calls.
+constexpr int kPrefillFixed = 0;
+constexpr int kPrefillRescale = 1;
+#ifndef MIKV_TUNE_PREFILL_FIXED_WAVES
+#define MIKV_TUNE_PREFILL_FIXED_WAVES 1
+#endif
+constexpr int kPrefillFixedWaves = MIKV_TUNE_PREFILL_FIXED_WAVES;   // waves per SIMD the fixed form is built for
+
+template <int D, int G, int FMT, int PF, int QB, int MODE>
+__global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1) void paged_prefill_kernel(
     const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu, int32_t hkv,
     int32_t num_blocks, int32_t total, int32_t max_new, float scale_log2,
-    const float* __restrict__ kv_scales, uint16_t* __restrict__ out, uint32_t* __restrict__ err) {
+    const float* __restrict__ kv_scales, uint16_t* __restrict__ out, uint32_t* __restrict__ err,
+    uint32_t* __restrict__ redo_word, uint32_t gen) {
+    static_assert(MODE == kPrefillRescale || kPrefillRawSoftmax, "the fixed form works on raw scores");
+    if constexpr (MODE == kPrefillRescale) {
+        if (__builtin_amdgcn_readfirstlane(*redo_word) != gen) return;
+    }
     using TL = MfmaTile<D, FMT>;
     constexpr int NPV = TL::NPV;
     constexpr int QT = BS * QB;                  // query tokens per wave
@@ -834,28 +853,17 @@ __global__ __launch_bounds__(64) void paged_prefill_kernel(
         }
     };
 
-    // Fixed-reference pass (no rescaling in the tile loop); a wave in which a
-    // score outgrew its column's reference by more than the headroom repeats
-    // the pass with the online rescaling form.
-    MfmaCols<D, FMT, QB, kPrefillRawSoftmax, kPrefillRawSoftmax> cols;
+    MfmaCols<D, FMT, QB, kPrefillRawSoftmax, MODE == kPrefillFixed> cols;
     init_cols(cols);
     run_pass(cols);
-    bool redo = false;
-    if constexpr (kPrefillRawSoftmax) {
+    store(cols);
+    if constexpr (MODE == kPrefillFixed) {
         float top = kNegInf;
 #pragma unroll
         for (int c = 0; c < QB; ++c)
             if (cols.col_ok[c]) top = fmaxf(top, cols.sm[c].top);
-        redo = __ballot(!(top <= kFixedHeadroom)) != 0;
+        if (__ballot(!(top <= kFixedHeadroom)) != 0 && lane == 0) atomicExch(redo_word, gen);
     }
-    if (!redo) {
-        store(cols);
-        return;
-    }
-    MfmaCols<D, FMT, QB, kPrefillRawSoftmax, false> safe;
-    init_cols(safe);
-    run_pass(safe);
-    store(safe);
 }
 
 // Combine kernel: one workgroup per (query head, sequence). It rebuilds the
@@ -1004,12 +1012,17 @@ constexpr int kAttnWavesPerCU = MIKV_TUNE_WAVES_PER_CU;
 #else
 constexpr int kAttnWavesPerCU = 3;
 #endif
-// Query column blocks of 16 per prefill wave.
+// Query column blocks of 16 per prefill wave (the fixed-reference launch and
+// the rescaling one).
 #ifdef MIKV_TUNE_PREFILL_QB
 constexpr int kPrefillQB = MIKV_TUNE_PREFILL_QB;
 #else
 constexpr int kPrefillQB = 3;
 #endif
+#ifndef MIKV_TUNE_PREFILL_QB_FIXED
+#define MIKV_TUNE_PREFILL_QB_FIXED 3
+#endif
+constexpr int kPrefillQBFixed = MIKV_TUNE_PREFILL_QB_FIXED;
 
 // Grid of the attention kernel on the current device: CUs x min(waves per
 // CU, resident workgroups per CU at the kernel's register budget), cached
@@ -1075,12 +1088,24 @@ void launch_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                     const int32_t* table, int32_t mbps, const int32_t* ctx, const int32_t* cu,
                     int32_t batch, int32_t total, int32_t max_new, float scale_log2, hipStream_t st) {
     const int hkv = p->num_kv_heads;
-    auto kern = mikv::pool_fp8(p) ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQB>
-                                  : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQB>;
-    const dim3 grid((max_new + BS * kPrefillQB - 1) / (BS * kPrefillQB), hkv * G, batch);
-    hipLaunchKernelGGL(kern, grid, dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
+    const bool f8 = mikv::pool_fp8(p);
+    uint32_t gen = ++p->prefill_gen;
+    if (gen == 0) gen = ++p->prefill_gen;           // 0 is the word's initial value
+    uint32_t* redo = p->err + mikv::kPrefillRedoWord;
+    auto fixed = f8 ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQBFixed, kPrefillFixed>
+                    : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQBFixed, kPrefillFixed>;
+    auto rescale = f8 ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQB, kPrefillRescale>
+                      : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQB, kPrefillRescale>;
+    const dim3 grid_f((max_new + BS * kPrefillQBFixed - 1) / (BS * kPrefillQBFixed), hkv * G, batch);
+    const dim3 grid_r((max_new + BS * kPrefillQB - 1) / (BS * kPrefillQB), hkv * G, batch);
+    hipLaunchKernelGGL(fixed, grid_f, dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
                        static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, hkv, p->num_blocks,
-                       total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err);
+                       total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err,
+                       redo, gen);
+    hipLaunchKernelGGL(rescale, grid_r, dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
+                       static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, hkv, p->num_blocks,
+                       total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err,
+                       redo, gen);
 }
 
 template <int D>

@@ -21,7 +21,8 @@ struct mi_kv_pool_s {
     void* stage = nullptr;           // device staging of scattered swaps (allocated on first use)
     size_t stage_blocks = 0;         // blocks of K (and again of V) the staging holds
     bool owns_cache = false;
-    uint32_t* err = nullptr;         // device error word (MI_FAULT_* bits)
+    uint32_t* err = nullptr;         // device words: [0] error (MI_FAULT_* bits), [1] prefill redo
+    mutable uint32_t prefill_gen = 0;  // generation number of the last prefill call on the pool
     std::vector<int32_t> stack;      // free-block LIFO; back() is handed out next
     std::vector<uint8_t> allocated;  // 1 if the id is currently handed out
 };
@@ -29,6 +30,7 @@ struct mi_kv_pool_s {
 namespace mikv {
 
 constexpr int kBlockSize = 16;
+constexpr int kPrefillRedoWord = 1;        // index of the prefill redo word in the pool's device words
 
 // RoPE inverse frequencies theta^(-2i/D), i < D/2, computed on the host in
 // float64 and passed to the kernels by value.

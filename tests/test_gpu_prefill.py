@@ -126,7 +126,21 @@ def test_prefill_score_far_above_the_first_tile_takes_the_rescaling_pass(D):
     big = obf16.encode(30.0 * obf16.decode(u))
     case.k[40] = big                       # sequence 0, position 40
     case.k[case.cu_seqlens[1] + 30] = big  # sequence 1, position 50 (after 20 cached)
-    _full_check(case, "far scores D=%d" % D)
+    ref, kn, vn, qb = oatt.prefill_step(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                        case.block_table, case.context_lens, case.cu_seqlens, 16,
+                                        case.cfg.rope_theta)
+    dev = PrefillOnDevice(case)
+    try:
+        # three calls on one pool: each call has its own generation number in
+        # the pool's redo word, so every call repeats and none reads a stale one
+        for call in range(3):
+            dev.out.fill_(0)
+            dev.run()
+            _check_write(case, dev, kn, vn, qb)
+            check_tolerance(dev_to_bits(dev.out), ref, "far scores D=%d call %d" % (D, call))
+        assert mk.mi_kv_pool_check_errors(dev.pool) == 0
+    finally:
+        dev.close()
 
 
 def test_prefill_qwen3_8b_shape_sampled_rows():
