@@ -54,15 +54,17 @@ __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
 }
 
 // ============================================================== write_decode_kv
-// One thread per rotated pair (i, i + D/2) of one head, q heads first, then
-// the new k heads, then 16-byte pieces of the V copy; workgroups of 256
-// threads tile that index space (grid.y) for each sequence (grid.x). The
-// angle pos * theta^(-2i/D) (inverse frequencies from the host table), its
-// sine and cosine and the rotation are float64 with separately rounded
-// products, rounded once to bf16. An 8-bit cache (FMT = kFmtFp8) stores the
-// E4M3 codes of that bf16 K and of v under the head's scales.
+// Per row (grid.x): rotation threads, each owning pair (i, i + D/2) of one
+// head (decode) or of every (kRotThreads / (D/2))-th head (prefill), q heads
+// first, then the new k heads; then 16-byte pieces of the V copy; workgroups
+// of 256 threads tile that index space (grid.y). The angle pos * theta^(-2i/D) (inverse
+// frequencies from the host table), its sine and cosine and the rotation are
+// float64 with separately rounded products, rounded once to bf16. An 8-bit
+// cache (FMT = kFmtFp8) stores the E4M3 codes of that bf16 K and of v under
+// the head's scales.
 constexpr int kFmtBf16 = 0;
 constexpr int kFmtFp8 = 1;
+constexpr int kRotThreads = 512;     // rotation threads per prefill row of write_decode_kv
 
 // With PREFILL the rows of q, k, v are the packed new tokens of a prefill
 // chunk (grid.x = total tokens): row i belongs to the sequence b with
@@ -99,39 +101,62 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     }
     if (!pos_ok) return;
     const int off = pos % BS;
-    const int n_rot = (hq + hkv) * H2;
+    // Rotation threads: thread (grp, i) owns pair i of the heads grp, grp + NG,
+    // grp + 2 NG, ... (q heads, then the new k heads) and computes their
+    // angle's float64 sine and cosine once; its heads go in batches of 8 whose
+    // loads are issued before any store. A decode row (few rows, latency
+    // bound) takes one head per thread (NG = all heads); a prefill row (many
+    // rows, bound by the sines and cosines) shares each angle over
+    // (Hq + Hkv) / NG heads, NG = kRotThreads / (D/2).
+    const int nh = hq + hkv;
+    const int NG = PREFILL ? kRotThreads / H2 : nh;
+    const int n_rot = NG * H2;
     const int idx = blockIdx.y * blockDim.x + threadIdx.x;
     if (idx < n_rot) {
-        const int h = idx / H2;
-        const int i = idx - h * H2;
-        if (h >= hq && !blk_ok) return;
-        const int g = h - hq;
-        const uint16_t* src = h < hq ? q + (static_cast<size_t>(row) * hq + h) * D
-                                     : k + (static_cast<size_t>(row) * hkv + g) * D;
-        const double x1 = bf16_to_f64(src[i]);
-        const double x2 = bf16_to_f64(src[i + H2]);
-        const double a = static_cast<double>(pos) * rope.inv_freq[i];
+        const int grp = idx / H2;
+        const int i = idx - grp * H2;
+        if (grp >= nh) return;
         double sn, cs;
-        sincos(a, &sn, &cs);
-        const double y1 = __dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn));
-        const double y2 = __dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn));
-        const uint16_t r1 = f64_to_bf16_rne(y1);
-        const uint16_t r2 = f64_to_bf16_rne(y2);
-        if (h < hq) {
-            uint16_t* dst = q_rot + (static_cast<size_t>(row) * hq + h) * D;
-            dst[i] = r1;
-            dst[i + H2] = r2;
-        } else {
-            const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
-            if constexpr (FMT == kFmtBf16) {
-                uint16_t* dst = static_cast<uint16_t*>(kc) + at;
-                dst[i] = r1;
-                dst[i + H2] = r2;
-            } else {
-                uint8_t* dst = static_cast<uint8_t*>(kc) + at;
-                const float s = kv_scales[g];
-                dst[i] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, s));
-                dst[i + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, s));
+        sincos(static_cast<double>(pos) * rope.inv_freq[i], &sn, &cs);
+        for (int h0 = grp; h0 < nh; h0 += 8 * NG) {
+            uint16_t in1[8], in2[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int h = h0 + NG * t;
+                in1[t] = in2[t] = 0;
+                if (h < nh) {
+                    const uint16_t* src = h < hq ? q + (static_cast<size_t>(row) * hq + h) * D
+                                                 : k + (static_cast<size_t>(row) * hkv + (h - hq)) * D;
+                    in1[t] = src[i];
+                    in2[t] = src[i + H2];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int h = h0 + NG * t;
+                if (h >= nh || (h >= hq && !blk_ok)) continue;
+                const double x1 = bf16_to_f64(in1[t]);
+                const double x2 = bf16_to_f64(in2[t]);
+                const uint16_t r1 = f64_to_bf16_rne(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
+                const uint16_t r2 = f64_to_bf16_rne(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
+                if (h < hq) {
+                    uint16_t* dst = q_rot + (static_cast<size_t>(row) * hq + h) * D;
+                    dst[i] = r1;
+                    dst[i + H2] = r2;
+                } else {
+                    const int g = h - hq;
+                    const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
+                    if constexpr (FMT == kFmtBf16) {
+                        uint16_t* dst = static_cast<uint16_t*>(kc) + at;
+                        dst[i] = r1;
+                        dst[i + H2] = r2;
+                    } else {
+                        uint8_t* dst = static_cast<uint8_t*>(kc) + at;
+                        const float sc = kv_scales[g];
+                        dst[i] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, sc));
+                        dst[i + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, sc));
+                    }
+                }
             }
         }
     } else if (blk_ok) {
@@ -1180,7 +1205,7 @@ int launch_write_prefill_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint
                             int32_t hq, double theta, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int hkv = p->num_kv_heads;
-    const int items = (hq + hkv) * (p->head_dim / 2) + hkv * (p->head_dim / 8);
+    const int items = kRotThreads + hkv * (p->head_dim / 8);
     const dim3 grid(tokens, (items + 255) / 256);
     const RopeTable rope = make_rope_table(theta, p->head_dim);
     const bool f8 = pool_fp8(p);
