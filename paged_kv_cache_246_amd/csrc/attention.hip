@@ -64,7 +64,13 @@ __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
 // the head's scales.
 constexpr int kFmtBf16 = 0;
 constexpr int kFmtFp8 = 1;
-constexpr int kRotThreads = 512;     // rotation threads per prefill row of write_decode_kv
+#ifndef MIKV_TUNE_ROT_THREADS
+#define MIKV_TUNE_ROT_THREADS 256
+#endif
+// Rotation threads per prefill row of write_decode_kv: 256 (each angle shared
+// by a quarter of the heads at D = 128) measured fastest on MI355X (512: +1 %,
+// 1024: +4 % on a 4 x 2048-token prefill step).
+constexpr int kRotThreads = MIKV_TUNE_ROT_THREADS;
 
 // With PREFILL the rows of q, k, v are the packed new tokens of a prefill
 // chunk (grid.x = total tokens): row i belongs to the sequence b with
