@@ -243,7 +243,9 @@ int mi_write_prefill_kv(mi_kv_pool_t pool, const uint16_t* q, const uint16_t* k,
  * later score exceeds it by more than 2^64 (in weight), the call repeats the
  * chunk with the running-maximum form (nxmr.cn article, section 5.1) in a
  * second launch, gated by a generation-numbered word in the pool, so prefill
- * calls on one pool must run one after another on one stream.
+ * calls on one pool must run one after another on one stream. (A captured
+ * call replays with its generation number: once a replay has needed the
+ * repeat, later replays repeat too -- same results, more time.)
  *  q_rot, out  device bf16 [total_tokens, num_q_heads, head_dim], no aliasing
  *  max_new_tokens  host-side bound of every n_b (sizes the grid); a larger
  *         n_b, cu beyond total_tokens or a chunk past the table row is a fault
