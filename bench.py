@@ -94,6 +94,26 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16"):
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in evs]
+
+    # The same step as one launch (mi_paged_gqa_decode_step), timed alike.
+    ms_one = None
+    if not args.split:
+        ws1_bytes = mk.mi_paged_gqa_decode_workspace_bytes(pool, B, Hq, max_ctx)
+        ws1 = torch.empty(ws1_bytes, dtype=torch.uint8, device=dev)
+
+        def one():
+            mk.mi_paged_gqa_decode_step(pool, q, k, v, q_rot, out, table, mbps, ctx, B, Hq,
+                                        cfg.rope_theta, 0.0, max_ctx, ws1, ws1_bytes, st)
+
+        for _ in range(args.warmup):
+            one()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            one()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_one = t0.elapsed_time(t1) / args.steps
     faults = mk.mi_kv_pool_check_errors(pool)
     mk.mi_kv_pool_destroy(pool)
     if faults:
@@ -103,7 +123,7 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16"):
     attn_bytes = workloads.attention_bytes(ctx_np, Hq, Hkv, D, 16, kv_elem_bytes=kv_elem)
     write_bytes = workloads.write_bytes(B, Hq, Hkv, D, kv_elem_bytes=kv_elem)
     return dict(
-        case=case, cfg=cfg, ms_step=ms_step, wall=wall, attn_ms=attn_ms,
+        case=case, cfg=cfg, ms_step=ms_step, ms_one=ms_one, wall=wall, attn_ms=attn_ms,
         attn_bytes=attn_bytes, step_bytes=attn_bytes + write_bytes,
         tokens=int(ctx_np.sum()) + B,
         split=args.split or None,
@@ -615,6 +635,11 @@ def main():
             "algorithmic_bytes": int(r["attn_bytes"]),
             "traffic": recorded_traffic(),
         },
+        "decode_step_one_launch": None if r["ms_one"] is None else {
+            "entry_point": "mi_paged_gqa_decode_step",
+            "ms_per_step": round(r["ms_one"], 5),
+            "GBps": round(r["step_bytes"] / (r["ms_one"] * 1e-3) / 1e9, 1),
+        },
         "attention_launch_ms": {
             "p10": round(float(np.percentile(r["attn_ms"], 10)), 5),
             "p50": round(float(np.percentile(r["attn_ms"], 50)), 5),
@@ -639,6 +664,7 @@ def main():
             "attention_GBps": round(r8["attn_bytes"] / (attn8 * 1e-3) / 1e9, 1),
             "attention_hbm_frac": round(r8["attn_bytes"] / (attn8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "step_speedup_vs_bf16": round(ms / ms8, 3),
+            "one_launch_ms_per_step": None if r8["ms_one"] is None else round(r8["ms_one"], 5),
         }
     if not args.no_prefill:
         line["prefill"] = run_prefill_bench(args, torch, mk, workloads)

@@ -506,6 +506,36 @@ int mi_kv_swap_in(mi_kv_pool_t pool, const void* host_k, const void* host_v, int
                   const int32_t* pairs, int32_t n, void* stream);
 
 /*
+ * One decode step in one attention launch (mini-infer "decode_batch":
+ * write_decode_kv of the new token, then attention over the gathered cache;
+ * course project 2.1: RoPE, KV-cache append, GQA): the effect of
+ * mi_write_decode_kv followed by mi_paged_gqa_decode with the same
+ * arguments, without the separate write launch. The wave that reads a
+ * sequence's last tile for a kv head first writes that head's new k (RoPE)
+ * and v into the slot, so the cache after the call and q_rot are
+ * bit-identical to mi_write_decode_kv's. The query operand of the attention
+ * is rotated by each wave itself in float32 (within one bf16 rounding of the
+ * float64 rotation), so out can differ from the two-call path in the last
+ * bits, within the same tolerance of the exact result.
+ *  q, k, v  device bf16 as for mi_write_decode_kv (not modified)
+ *  q_rot    device bf16 [batch, num_q_heads, head_dim] receiving RoPE(q), or
+ *           NULL; must not alias q or out
+ *  out      device bf16 [batch, num_q_heads, head_dim]; must not alias q
+ *  rope_theta, softmax_scale, max_context_len, workspace: as for
+ *           mi_write_decode_kv and mi_paged_gqa_decode (workspace query:
+ *           mi_paged_gqa_decode_workspace_bytes)
+ * A sequence whose length is out of range (a recorded fault) gets no cache
+ * write and NaN outputs. batch == 0 is a no-op.
+ */
+int mi_paged_gqa_decode_step(mi_kv_pool_t pool, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, uint16_t* q_rot, uint16_t* out,
+                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t batch,
+                             int32_t num_q_heads, double rope_theta, float softmax_scale,
+                             int32_t max_context_len, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * Measurement utility (not a step of the method): reads `bytes` of device
  * memory at `src` (16-byte aligned, bytes a multiple of 16) with 16-byte
  * non-temporal loads, each of `workgroups` workgroups of 256 threads one

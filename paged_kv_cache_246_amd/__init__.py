@@ -59,6 +59,8 @@ SIGNATURES = {
                                              _c.c_float, _i32, _i32, _vp, _sz, _vp]),
     "mi_paged_gqa_decode_split_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32]),
     "mi_hbm_stream_read": (_c.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "mi_paged_gqa_decode_step": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                            _i32, _c.c_double, _c.c_float, _i32, _vp, _sz, _vp]),
     "mi_write_prefill_kv": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
                                        _i32, _c.c_double, _vp]),
     "mi_paged_prefill_attention": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
@@ -259,6 +261,15 @@ def mi_paged_gqa_decode_split(pool, q_rot, out, block_table, max_blocks_per_seq,
         pool, _ptr(q_rot), _ptr(out), _ptr(block_table), max_blocks_per_seq,
         _ptr(context_lens), batch, num_q_heads, float(softmax_scale), max_context_len,
         split_tokens, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mi_paged_gqa_decode_step(pool, q, k, v, q_rot, out, block_table, max_blocks_per_seq,
+                             context_lens, batch, num_q_heads, rope_theta, softmax_scale,
+                             max_context_len, workspace, workspace_bytes, stream=None):
+    return _check("mi_paged_gqa_decode_step", lib().mi_paged_gqa_decode_step(
+        pool, _ptr(q), _ptr(k), _ptr(v), _ptr(q_rot), _ptr(out), _ptr(block_table),
+        max_blocks_per_seq, _ptr(context_lens), batch, num_q_heads, float(rope_theta),
+        float(softmax_scale), max_context_len, _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def mi_write_prefill_kv(pool, q, k, v, q_rot, block_table, max_blocks_per_seq, context_lens,

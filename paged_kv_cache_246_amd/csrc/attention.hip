@@ -602,18 +602,120 @@ struct MfmaRing {
     }
 };
 
-template <int D, int G, int FMT, int PF>
+// The new token of a one-launch decode step (STEP kernels): q, k and v (bf16
+// [B, Hq, D], [B, Hkv, D], [B, Hkv, D]), the RoPE inverse frequencies and an
+// optional q_rot output.
+struct StepToken {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* q_rot;
+    mikv::RopeTable rope;
+};
+
+// STEP: write_decode_kv happens inside the attention launch. The wave whose
+// piece holds a segment's last tile owns the segment's write: before loading
+// any tile it rotates the new k (and, if asked for, the G query heads for
+// q_rot) with the float64 rotation and single rounding of write_decode_kv,
+// stores k and v into the slot and waits for its stores, so the new token is
+// then read back from the cache like every other. Each segment's last tile
+// belongs to exactly one piece: every slot is written once, and read only by
+// its writer. Every piece also needs the rotated query heads as its MFMA
+// operand; those it rotates itself in float32 (angle reduced to a fraction
+// of a turn in float64, hardware sine and cosine), which differs from the
+// float64 rotation by at most one bf16 rounding.
+template <int D, int G, int FMT>
+__device__ __forceinline__ void step_owner_write(const StepToken& tok, int b, int g, int hkv, int pos,
+                                                 int32_t blk, const float* kv_scales, uint8_t* kc,
+                                                 uint8_t* vc, int lane) {
+    constexpr int H2 = D / 2;
+    const int i = lane % H2;
+    double sn, cs;
+    sincos(static_cast<double>(pos) * tok.rope.inv_freq[i], &sn, &cs);
+    auto rot = [&](uint16_t a, uint16_t c, uint16_t& r1, uint16_t& r2) {
+        const double x1 = bf16_to_f64(a), x2 = bf16_to_f64(c);
+        r1 = f64_to_bf16_rne(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
+        r2 = f64_to_bf16_rne(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
+    };
+    if (tok.q_rot) {
+        const size_t qrow = (static_cast<size_t>(b) * hkv + g) * G * D;
+#pragma unroll
+        for (int p = lane; p < G * H2; p += 64) {
+            const int h = p / H2;
+            uint16_t r1, r2;
+            rot(tok.q[qrow + h * D + i], tok.q[qrow + h * D + i + H2], r1, r2);
+            tok.q_rot[qrow + h * D + i] = r1;
+            tok.q_rot[qrow + h * D + i + H2] = r2;
+        }
+    }
+    if (blk >= 0) {
+        const size_t krow = (static_cast<size_t>(b) * hkv + g) * D;
+        const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + pos % BS) * D;
+        if (lane < H2) {
+            uint16_t r1, r2;
+            rot(tok.k[krow + i], tok.k[krow + i + H2], r1, r2);
+            if constexpr (FMT == kFmtBf16) {
+                uint16_t* dst = reinterpret_cast<uint16_t*>(kc) + at;
+                dst[i] = r1;
+                dst[i + H2] = r2;
+            } else {
+                const float ks = kv_scales[g];
+                kc[at + i] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, ks));
+                kc[at + i + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, ks));
+            }
+        }
+        if (lane < D / 8) {
+            const uint4 val = *reinterpret_cast<const uint4*>(tok.v + krow + 8 * lane);
+            if constexpr (FMT == kFmtBf16)
+                *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(vc) + at + 8 * lane) = val;
+            else
+                *reinterpret_cast<uint2*>(vc + at + 8 * lane) =
+                    mikv_dev::e4m3_quantize_bf16x8(val, kv_scales[hkv + g]);
+        }
+    }
+    // every store of the wave complete before its first tile load
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// The G query heads of segment (b, g) rotated at pos in float32, into LDS.
+template <int D, int G>
+__device__ __forceinline__ void step_query_operand(const StepToken& tok, int b, int g, int hkv, int pos,
+                                                   uint16_t* QR, int lane) {
+    constexpr int H2 = D / 2;
+    const int i = lane % H2;
+    const double turns = static_cast<double>(pos) * tok.rope.inv_freq[i] * 0.15915494309189535;
+    const float frac = static_cast<float>(turns - floor(turns));
+    const float sn = __builtin_amdgcn_sinf(frac);
+    const float cs = __builtin_amdgcn_cosf(frac);
+    const size_t qrow = (static_cast<size_t>(b) * hkv + g) * G * D;
+#pragma unroll
+    for (int p = lane; p < G * H2; p += 64) {
+        const int h = p / H2;
+        const float x1 = __uint_as_float(static_cast<uint32_t>(tok.q[qrow + h * D + i]) << 16);
+        const float x2 = __uint_as_float(static_cast<uint32_t>(tok.q[qrow + h * D + i + H2]) << 16);
+        QR[h * D + i] = f32_to_bf16_rne(fmaf(x1, cs, -x2 * sn));
+        QR[h * D + i + H2] = f32_to_bf16_rne(fmaf(x2, cs, x1 * sn));
+    }
+}
+
+// The cache pointers are read-only (and restrict) except in STEP kernels,
+// which write the new token's slot.
+template <bool STEP> struct CachePtr { typedef const uint8_t* __restrict__ type; };
+template <> struct CachePtr<true> { typedef uint8_t* type; };
+
+template <int D, int G, int FMT, int PF, bool STEP>
 __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
-    const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
-    const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
+    const uint16_t* __restrict__ q_rot, typename CachePtr<STEP>::type kc,
+    typename CachePtr<STEP>::type vc, const int32_t* __restrict__ table, int32_t mbps,
     const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t hkv, int32_t num_blocks,
     int32_t max_ctx, int32_t min_tiles, float scale_log2, const float* __restrict__ kv_scales,
     float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
-    uint32_t* __restrict__ err) {
+    uint32_t* __restrict__ err, StepToken tok) {
     using TL = MfmaTile<D, FMT>;
     constexpr int NPV = TL::NPV;
     constexpr size_t TILE = static_cast<size_t>(BS) * TL::ROW;   // bytes per (block, head) tile
     __shared__ int TP[kMaxBatch + 1];
+    __shared__ __align__(16) uint16_t QR[STEP ? G * D : 8];     // rotated q of the segment (STEP)
     const int w = blockIdx.x;
     const int lane = threadIdx.x;
     const int n = lane & 15;
@@ -647,11 +749,28 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
         // Q^T operand: head n, the lane's 8 dims of each 32-dim slice (the
         // same dims its K row supplies)
         MfmaCols<D, FMT, 1> cols;
-        const uint16_t* qh = q_rot + (static_cast<size_t>(b) * hkv * G + g * G + (head_ok ? n : 0)) * D;
+        auto load_q = [&](const uint16_t* qh) {
 #pragma unroll
-        for (int j = 0; j < TL::NQK; ++j) {
-            const int d0 = FMT == kFmtBf16 ? 32 * j + 8 * q4 : 64 * (j / 2) + 16 * q4 + 8 * (j & 1);
-            cols.qb[0][j] = head_ok ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < TL::NQK; ++j) {
+                const int d0 = FMT == kFmtBf16 ? 32 * j + 8 * q4 : 64 * (j / 2) + 16 * q4 + 8 * (j & 1);
+                cols.qb[0][j] = head_ok ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
+            }
+        };
+        // block ids of the piece's first chunk (lane i: its i-th tile)
+        int32_t id0 = 0;
+        if (lane < min(64, t1 - t0)) id0 = table[static_cast<size_t>(b) * mbps + t0 + lane];
+        if constexpr (STEP) {
+            const int pos = L - 1;
+            if (t1 == nt) {                   // this piece holds the segment's last tile
+                int32_t blk = table[static_cast<size_t>(b) * mbps + pos / BS];
+                if (blk < 0 || blk >= num_blocks) blk = -1;     // recorded by the tile loop
+                step_owner_write<D, G, FMT>(tok, b, g, hkv, pos, blk, kv_scales, kc, vc, lane);
+            }
+            step_query_operand<D, G>(tok, b, g, hkv, pos, QR, lane);
+            __syncthreads();
+            load_q(QR + (head_ok ? n : 0) * D);
+        } else {
+            load_q(q_rot + (static_cast<size_t>(b) * hkv * G + g * G + (head_ok ? n : 0)) * D);
         }
         cols.sl2 = scale_log2;
         float vscale = 1.f;
@@ -678,8 +797,8 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
 
         for (int s0 = t0; s0 < t1; s0 += 64) {
             const int nblk = min(64, t1 - s0);
-            int32_t id = 0;
-            if (lane < nblk) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
+            int32_t id = id0;
+            if (s0 != t0 && lane < nblk) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
             const bool bad_id = lane < nblk && (id < 0 || id >= num_blocks);
             if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
             ring.my_id = bad_id ? 0 : id;
@@ -1073,32 +1192,47 @@ int attention_waves(K kernel) {
     return cached[dev];
 }
 
+template <int D, int G, bool STEP>
+void launch_attn_kernel(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                        const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
+                        float scale_log2, int32_t max_ctx, int32_t min_tiles, float* part_acc,
+                        float2* part_ml, const StepToken& tok, hipStream_t st) {
+    typedef typename CachePtr<STEP>::type CP;
+    const int hkv = p->num_kv_heads;
+    auto kern = mikv::pool_fp8(p) ? paged_attn_mfma_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, STEP>
+                                  : paged_attn_mfma_kernel<D, G, kFmtBf16, kAttnPrefetch, STEP>;
+    const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, attention_waves(kern));
+    hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot, static_cast<CP>(p->k),
+                       static_cast<CP>(p->v), table, mbps, ctx, batch, hkv, p->num_blocks, max_ctx,
+                       min_tiles, scale_log2, static_cast<const float*>(p->scales), part_acc, part_ml,
+                       out, p->err, tok);
+    hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), dim3(hkv * G, batch), dim3(256), 0, st,
+                       part_acc, part_ml, ctx, batch, mbps, hkv, max_ctx, waves, min_tiles, out);
+}
+
+// tok: NULL for the attention call, else the decode step's new token.
 template <int D, int G>
 void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                  const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                  float scale_log2, int32_t max_ctx, int32_t min_tiles, float* part_acc,
-                 float2* part_ml, hipStream_t st) {
-    const int hkv = p->num_kv_heads;
-    auto kern = mikv::pool_fp8(p) ? paged_attn_mfma_kernel<D, G, kFmtFp8, kAttnPrefetchFp8>
-                                  : paged_attn_mfma_kernel<D, G, kFmtBf16, kAttnPrefetch>;
-    const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, attention_waves(kern));
-    hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
-                       static_cast<const uint8_t*>(p->v), table, mbps, ctx, batch, hkv,
-                       p->num_blocks, max_ctx, min_tiles, scale_log2,
-                       static_cast<const float*>(p->scales), part_acc, part_ml, out, p->err);
-    hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), dim3(hkv * G, batch), dim3(256), 0, st,
-                       part_acc, part_ml, ctx, batch, mbps, hkv, max_ctx, waves, min_tiles, out);
+                 float2* part_ml, const StepToken* tok, hipStream_t st) {
+    if (tok)
+        launch_attn_kernel<D, G, true>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
+                                       min_tiles, part_acc, part_ml, *tok, st);
+    else
+        launch_attn_kernel<D, G, false>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
+                                        min_tiles, part_acc, part_ml, StepToken{}, st);
 }
 
 template <int D>
 int dispatch_group(int G, const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                    const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                    float scale_log2, int32_t max_ctx, int32_t min_tiles, float* pa, float2* pm,
-                   hipStream_t st) {
+                   const StepToken* tok, hipStream_t st) {
 #define MIKV_G(GG)                                                                             \
     case GG:                                                                                   \
         launch_attn<D, GG>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,        \
-                           min_tiles, pa, pm, st);                                             \
+                           min_tiles, pa, pm, tok, st);                                        \
         return MI_OK;
     switch (G) {
         MIKV_G(1)
@@ -1223,10 +1357,12 @@ int launch_write_prefill_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 
-int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
-                            const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
-                            int32_t hq, float scale, int32_t max_ctx, int32_t split_tokens,
-                            void* ws, void* stream) {
+namespace {
+
+int launch_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, const int32_t* table,
+                  int32_t mbps, const int32_t* ctx, int32_t batch, int32_t hq, float scale,
+                  int32_t max_ctx, int32_t split_tokens, void* ws, const StepToken* tok,
+                  void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int G = hq / p->num_kv_heads;
     const int min_tiles = split_tokens / BS;
@@ -1239,12 +1375,36 @@ int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16
     int rc;
     if (p->head_dim == 128)
         rc = dispatch_group<128>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                 min_tiles, pa, pm, st);
+                                 min_tiles, pa, pm, tok, st);
     else
         rc = dispatch_group<64>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                min_tiles, pa, pm, st);
+                                min_tiles, pa, pm, tok, st);
     if (rc != MI_OK) return rc;
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                            const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
+                            int32_t hq, float scale, int32_t max_ctx, int32_t split_tokens,
+                            void* ws, void* stream) {
+    return launch_decode(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx, split_tokens,
+                         ws, nullptr, stream);
+}
+
+int launch_decode_step(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, uint16_t* q_rot, uint16_t* out, const int32_t* table,
+                       int32_t mbps, const int32_t* ctx, int32_t batch, int32_t hq, double theta,
+                       float scale, int32_t max_ctx, void* ws, void* stream) {
+    StepToken tok;
+    tok.q = q;
+    tok.k = k;
+    tok.v = v;
+    tok.q_rot = q_rot;
+    tok.rope = make_rope_table(theta, p->head_dim);
+    return launch_decode(p, nullptr, out, table, mbps, ctx, batch, hq, scale, max_ctx,
+                         kDefaultSplitTokens, ws, &tok, stream);
 }
 
 int launch_paged_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
@@ -1392,4 +1552,24 @@ extern "C" int mi_kv_pool_quantize(mi_kv_pool_t p, const uint16_t* k_src, const 
                        static_cast<uint8_t*>(p->k), static_cast<uint8_t*>(p->v), pieces,
                        p->num_kv_heads, static_cast<const float*>(p->scales));
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
+}
+
+extern "C" int mi_paged_gqa_decode_step(mi_kv_pool_t p, const uint16_t* q, const uint16_t* k,
+                                        const uint16_t* v, uint16_t* q_rot, uint16_t* out,
+                                        const int32_t* table, int32_t mbps, const int32_t* ctx,
+                                        int32_t batch, int32_t hq, double theta, float scale,
+                                        int32_t max_ctx, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_common(p, batch, hq, mbps);
+    if (rc != MI_OK) return rc;
+    if (max_ctx < 0) return MI_ERR_INVALID_ARG;
+    if (batch > mikv::kMaxBatch) return MI_ERR_UNSUPPORTED;
+    if (batch == 0) return MI_OK;
+    if (!q || !k || !v || !out || !table || !ctx || !ws || !(theta > 0.0)) return MI_ERR_INVALID_ARG;
+    if (out == q || (q_rot && (q_rot == q || q_rot == out))) return MI_ERR_INVALID_ARG;
+    if (ws_bytes < mikv::attention_workspace_bytes(batch, hq, p->num_kv_heads, p->head_dim, max_ctx,
+                                                   mikv::kDefaultSplitTokens))
+        return MI_ERR_WORKSPACE_TOO_SMALL;
+    if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(p->head_dim));
+    return mikv::launch_decode_step(p, q, k, v, q_rot, out, table, mbps, ctx, batch, hq, theta, scale,
+                                    max_ctx, ws, stream);
 }

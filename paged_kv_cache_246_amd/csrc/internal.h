@@ -87,5 +87,10 @@ int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16
                             const int32_t* table, int32_t mbps, const int32_t* ctx,
                             int32_t batch, int32_t hq, float scale, int32_t max_ctx,
                             int32_t split_tokens, void* ws, void* stream);
+// write_decode_kv and the attention in one launch (plus the combine).
+int launch_decode_step(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, uint16_t* q_rot, uint16_t* out, const int32_t* table,
+                       int32_t mbps, const int32_t* ctx, int32_t batch, int32_t hq, double theta,
+                       float scale, int32_t max_ctx, void* ws, void* stream);
 
 }  // namespace mikv
