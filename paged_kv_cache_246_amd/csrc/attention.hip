@@ -617,10 +617,10 @@ struct StepToken {
 // piece holds a segment's last tile owns the segment's write: before loading
 // any tile it rotates the new k (and, if asked for, the G query heads for
 // q_rot) with the float64 rotation and single rounding of write_decode_kv,
-// stores k and v into the slot and waits for its stores, so the new token is
-// then read back from the cache like every other. Each segment's last tile
-// belongs to exactly one piece: every slot is written once, and read only by
-// its writer. Every piece also needs the rotated query heads as its MFMA
+// stores k and v into the slot, and the piece waits for those stores before
+// its first tile load, so the new token is read back from the cache like
+// every other. Each segment's last tile belongs to exactly one piece: every
+// slot is written once, and read only by its writer. Every piece also needs the rotated query heads as its MFMA
 // operand; those it rotates itself in float32 (angle reduced to a fraction
 // of a turn in float64, hardware sine and cosine), which differs from the
 // float64 rotation by at most one bf16 rounding.
@@ -673,8 +673,6 @@ __device__ __forceinline__ void step_owner_write(const StepToken& tok, int b, in
                     mikv_dev::e4m3_quantize_bf16x8(val, kv_scales[hkv + g]);
         }
     }
-    // every store of the wave complete before its first tile load
-    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // The G query heads of segment (b, g) rotated at pos in float32, into LDS.
@@ -767,6 +765,9 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
                 step_owner_write<D, G, FMT>(tok, b, g, hkv, pos, blk, kv_scales, kc, vc, lane);
             }
             step_query_operand<D, G>(tok, b, g, hkv, pos, QR, lane);
+            // the owner's stores complete before the piece's first tile load
+            // (their latency overlaps the query loads)
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             load_q(QR + (head_ok ? n : 0) * D);
         } else {

@@ -179,3 +179,47 @@ def test_step_argument_errors():
         assert dc.faults() == 0
     finally:
         dc.close()
+
+
+def test_step_faults_are_recorded_not_fatal():
+    """A bad block id planted from the host: recorded, and the cache ends as
+    after the two calls with the same table. A length beyond max_context_len:
+    recorded, that sequence gets NaN outputs and no cache write."""
+    case = workloads.make_decode_case(workloads.CONFIGS["tiny"], pool="poison")
+    ctx = case.context_lens
+    bad = case.block_table.copy()
+    bad[1, int(ctx[1]) // 16] = case.num_blocks + 5          # the slot's own block
+    bad[0, 0] = -3                                           # a block read, not written
+    two, one = DeviceCase(case), DeviceCase(case)
+    try:
+        for dc in (two, one):
+            dc.table.copy_(torch.from_numpy(bad.astype(np.int32)))
+        two.write()
+        two.attend()
+        _step(one)
+        torch.cuda.synchronize()
+        assert two.faults() & mk.MI_FAULT_BLOCK_ID
+        assert one.faults() & mk.MI_FAULT_BLOCK_ID
+        assert torch.equal(one.k_pool, two.k_pool) and torch.equal(one.v_pool, two.v_pool)
+        assert one.faults() == 0                             # the read clears the word
+    finally:
+        one.close()
+        two.close()
+
+    dc = DeviceCase(case)
+    try:
+        k0, v0 = dc.k_pool.clone(), dc.v_pool.clone()
+        b_long = int(np.argmax(ctx))
+        dc.max_ctx = int(ctx.min())
+        _step(dc)
+        torch.cuda.synchronize()
+        assert dc.faults() & mk.MI_FAULT_CONTEXT_LEN
+        out = bf16_bits_to_f64(dev_to_bits(dc.out))
+        assert np.all(np.isnan(out[b_long]))
+        blk, off = int(case.block_table[b_long, int(ctx[b_long]) // 16]), int(ctx[b_long]) % 16
+        assert torch.equal(dc.k_pool[blk, :, off], k0[blk, :, off])
+        assert torch.equal(dc.v_pool[blk, :, off], v0[blk, :, off])
+        b_short = int(np.argmin(ctx))
+        assert np.all(np.isfinite(out[b_short]))
+    finally:
+        dc.close()
