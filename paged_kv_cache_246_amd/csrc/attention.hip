@@ -591,14 +591,21 @@ struct MfmaRing {
             rest<U + 1>(i, nblk, valid_rows, cols);
         }
     }
-    // every tile of [0, nblk): the unrolled ring loop
-    template <class Cols>
-    __device__ __forceinline__ void run(int nblk, int last_rows, Cols& cols) {
+    // every tile of [0, nblk): the unrolled ring loop. prep() runs once the
+    // first tiles are requested, before any is consumed (work whose loads
+    // may then overlap the tiles' own).
+    template <class Cols, class Prep>
+    __device__ __forceinline__ void run(int nblk, int last_rows, Cols& cols, Prep&& prep) {
         prologue<0>(nblk);
+        prep();
         int i = 0;
         for (; i + PF + 1 < nblk; i += PF + 1) steady<0>(i, nblk, cols);
         load<PF>(min(i + PF, nblk - 1));
         rest<0>(i, nblk, last_rows, cols);
+    }
+    template <class Cols>
+    __device__ __forceinline__ void run(int nblk, int last_rows, Cols& cols) {
+        run(nblk, last_rows, cols, [] {});
     }
 };
 
@@ -620,10 +627,13 @@ struct StepToken {
 // stores k and v into the slot, and the piece waits for those stores before
 // its first tile load, so the new token is read back from the cache like
 // every other. Each segment's last tile belongs to exactly one piece: every
-// slot is written once, and read only by its writer. Every piece also needs the rotated query heads as its MFMA
-// operand; those it rotates itself in float32 (angle reduced to a fraction
-// of a turn in float64, hardware sine and cosine), which differs from the
-// float64 rotation by at most one bf16 rounding.
+// slot is written once, and read only by its writer. Every piece also needs
+// the rotated query heads as its MFMA operand; those it rotates itself in
+// float32 (angle reduced to a fraction of a turn in float64, hardware sine
+// and cosine), which differs from the float64 rotation by at most one bf16
+// rounding. The wave loads its q elements and their rotation partners
+// before its first tile load and rotates them once that load is issued, so
+// the two memory round trips overlap.
 template <int D, int G, int FMT>
 __device__ __forceinline__ void step_owner_write(const StepToken& tok, int b, int g, int hkv, int pos,
                                                  int32_t blk, const float* kv_scales, uint8_t* kc,
@@ -675,24 +685,46 @@ __device__ __forceinline__ void step_owner_write(const StepToken& tok, int b, in
     }
 }
 
-// The G query heads of segment (b, g) rotated at pos in float32, into LDS.
-template <int D, int G>
-__device__ __forceinline__ void step_query_operand(const StepToken& tok, int b, int g, int hkv, int pos,
-                                                   uint16_t* QR, int lane) {
+// cos and sin of the H2 RoPE angles at pos, float32, into LDS (lane i < H2:
+// angle i, reduced to a fraction of a turn in float64 first).
+template <int D>
+__device__ __forceinline__ void step_angles(const StepToken& tok, int pos, float2* CS, int lane) {
     constexpr int H2 = D / 2;
-    const int i = lane % H2;
-    const double turns = static_cast<double>(pos) * tok.rope.inv_freq[i] * 0.15915494309189535;
-    const float frac = static_cast<float>(turns - floor(turns));
-    const float sn = __builtin_amdgcn_sinf(frac);
-    const float cs = __builtin_amdgcn_cosf(frac);
-    const size_t qrow = (static_cast<size_t>(b) * hkv + g) * G * D;
+    if (lane < H2) {
+        const double turns = static_cast<double>(pos) * tok.rope.inv_freq[lane] * 0.15915494309189535;
+        const float frac = static_cast<float>(turns - floor(turns));
+        CS[lane] = make_float2(__builtin_amdgcn_cosf(frac), __builtin_amdgcn_sinf(frac));
+    }
+}
+
+// Rotates the lane's 8-dim slices of its query head (raw bf16 in x, the
+// partner dims d +- D/2 in px; slice j starts at dim dim0[j]) with the LDS
+// angle table, into bf16 operand words.
+template <int D, int NQ>
+__device__ __forceinline__ void step_rotate_q(const uint4 (&x)[NQ], const uint4 (&px)[NQ],
+                                              const int (&dim0)[NQ], const float2* CS,
+                                              uint4 (&qb)[NQ]) {
+    constexpr int H2 = D / 2;
+    auto el = [](const uint4& u, int e) {
+        const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    };
 #pragma unroll
-    for (int p = lane; p < G * H2; p += 64) {
-        const int h = p / H2;
-        const float x1 = __uint_as_float(static_cast<uint32_t>(tok.q[qrow + h * D + i]) << 16);
-        const float x2 = __uint_as_float(static_cast<uint32_t>(tok.q[qrow + h * D + i + H2]) << 16);
-        QR[h * D + i] = f32_to_bf16_rne(fmaf(x1, cs, -x2 * sn));
-        QR[h * D + i + H2] = f32_to_bf16_rne(fmaf(x2, cs, x1 * sn));
+    for (int j = 0; j < NQ; ++j) {
+        const bool lo = dim0[j] < H2;
+        const float2* cs = CS + (lo ? dim0[j] : dim0[j] - H2);
+        uint32_t wd[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float2 a = cs[e], c = cs[e + 1];
+            const float x0 = el(x[j], e), x1 = el(x[j], e + 1);
+            const float p0 = el(px[j], e), p1 = el(px[j], e + 1);
+            const float r0 = lo ? fmaf(x0, a.x, -p0 * a.y) : fmaf(x0, a.x, p0 * a.y);
+            const float r1 = lo ? fmaf(x1, c.x, -p1 * c.y) : fmaf(x1, c.x, p1 * c.y);
+            wd[e / 2] = static_cast<uint32_t>(f32_to_bf16_rne(r0)) |
+                        (static_cast<uint32_t>(f32_to_bf16_rne(r1)) << 16);
+        }
+        qb[j] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
 }
 
@@ -713,7 +745,7 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
     constexpr int NPV = TL::NPV;
     constexpr size_t TILE = static_cast<size_t>(BS) * TL::ROW;   // bytes per (block, head) tile
     __shared__ int TP[kMaxBatch + 1];
-    __shared__ __align__(16) uint16_t QR[STEP ? G * D : 8];     // rotated q of the segment (STEP)
+    __shared__ __align__(16) float2 CS[STEP ? D / 2 : 1];       // RoPE cos, sin at pos (STEP)
     const int w = blockIdx.x;
     const int lane = threadIdx.x;
     const int n = lane & 15;
@@ -757,6 +789,9 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
         // block ids of the piece's first chunk (lane i: its i-th tile)
         int32_t id0 = 0;
         if (lane < min(64, t1 - t0)) id0 = table[static_cast<size_t>(b) * mbps + t0 + lane];
+        // STEP: the raw query slices and their rotation partners
+        uint4 qraw[TL::NQK], qpart[TL::NQK];
+        int qdim[TL::NQK];
         if constexpr (STEP) {
             const int pos = L - 1;
             if (t1 == nt) {                   // this piece holds the segment's last tile
@@ -764,12 +799,18 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
                 if (blk < 0 || blk >= num_blocks) blk = -1;     // recorded by the tile loop
                 step_owner_write<D, G, FMT>(tok, b, g, hkv, pos, blk, kv_scales, kc, vc, lane);
             }
-            step_query_operand<D, G>(tok, b, g, hkv, pos, QR, lane);
+            const uint16_t* qh = tok.q + (static_cast<size_t>(b) * hkv * G + g * G + (head_ok ? n : 0)) * D;
+#pragma unroll
+            for (int j = 0; j < TL::NQK; ++j) {
+                qdim[j] = FMT == kFmtBf16 ? 32 * j + 8 * q4 : 64 * (j / 2) + 16 * q4 + 8 * (j & 1);
+                qraw[j] = *reinterpret_cast<const uint4*>(qh + qdim[j]);
+                qpart[j] = *reinterpret_cast<const uint4*>(qh + (qdim[j] + D / 2) % D);
+            }
+            step_angles<D>(tok, pos, CS, lane);
             // the owner's stores complete before the piece's first tile load
-            // (their latency overlaps the query loads)
-            __builtin_amdgcn_s_waitcnt(0);
+            // (the barrier's fence keeps the tile loads below this point)
+            if (t1 == nt) __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            load_q(QR + (head_ok ? n : 0) * D);
         } else {
             load_q(q_rot + (static_cast<size_t>(b) * hkv * G + g * G + (head_ok ? n : 0)) * D);
         }
@@ -809,7 +850,16 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
             // tile, a cache hit), so the wait before each tile covers exactly
             // the older loads.
             const int last_rows = (s0 + nblk == nt) ? L - (nt - 1) * BS : BS;
-            ring.run(nblk, last_rows, cols);
+            ring.run(nblk, last_rows, cols, [&] {
+                if constexpr (STEP) {
+                    if (s0 == t0) {
+                        step_rotate_q<D>(qraw, qpart, qdim, CS, cols.qb[0]);
+#pragma unroll
+                        for (int j = 0; j < TL::NQK; ++j)
+                            if (!head_ok) cols.qb[0][j] = make_uint4(0, 0, 0, 0);
+                    }
+                }
+            });
         }
 
         // head totals of the lane sums (same bits in the 4 lanes of a head)
