@@ -223,3 +223,21 @@ def test_step_faults_are_recorded_not_fatal():
         assert np.all(np.isfinite(out[b_short]))
     finally:
         dc.close()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (3, 1), (8, 1), (10, 2)])
+def test_step_8bit_group_sizes_head_dims(D, Hq, Hkv):
+    """The 8-bit cache's query-slice layout at both head dims and several
+    group sizes, contexts on and around block boundaries, per-head scales."""
+    cfg = _custom_cfg(Hq, Hkv, D, seed=7 * D + Hq)
+    ctx = [0, 15, 16, 17, 33, 64, 100]
+    case = workloads.make_decode_case(cfg, pool="poison", context_lens=ctx, num_blocks=96,
+                                      kv_format="fp8")
+    ks = np.linspace(0.5, 1.5, Hkv).astype(np.float32)
+    vs = np.linspace(2.0, 0.75, Hkv).astype(np.float32)
+    ref, _, _, _ = oatt.decode_step_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                        case.block_table, case.context_lens, 16, cfg.rope_theta,
+                                        ks, vs)
+    _say("step fp8 groups", Hq, Hkv, "D", D)
+    _against_two_calls(case, ref, "fp8 G=%d D=%d" % (Hq // Hkv, D), ks, vs)
