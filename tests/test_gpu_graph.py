@@ -1,4 +1,4 @@
-"""The decode step captured in a HIP graph (torch.cuda.CUDAGraph) and replayed:
+"""The decode step and the decoder layer captured in HIP graphs (torch.cuda.CUDAGraph) and replayed:
 as two calls (mi_write_decode_kv + mi_paged_gqa_decode) and as one launch
 (mi_paged_gqa_decode_step). Each replay runs on new query values written
 into the captured buffers, with eager steps and synchronisations between
@@ -74,6 +74,87 @@ def test_decode_step_graph_replays(name, one_launch):
             assert torch.equal(graphed.k_pool, eager.k_pool), "replay %d: K cache differs" % i
             assert torch.equal(graphed.v_pool, eager.v_pool), "replay %d: V cache differs" % i
         assert eager.faults() == 0 and graphed.faults() == 0
+        del g
+    finally:
+        eager.close()
+        graphed.close()
+
+
+LAYER = workloads.DecodeConfig(
+    "graph_layer", batch=12, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+    num_blocks=256, rope_theta=1e6, ctx_draw="uniform", ctx_lo=0, ctx_hi=150, seed=21,
+    hidden=768, intermediate=1536, rms_eps=1e-6)
+
+
+class _LayerSetup:
+    """One decoder layer over its own pool copy, callable on a given stream."""
+
+    def __init__(self, cfg, case, w):
+        self.B = len(case.context_lens)
+        self.kp, self.vp = bits_to_dev(case.k_pool), bits_to_dev(case.v_pool)
+        self.wd = {n: bits_to_dev(a) for n, a in w.items()}
+        self.x = torch.empty((self.B, cfg.hidden), dtype=torch.int16, device=DEV)
+        self.xo = torch.empty_like(self.x)
+        self.table = torch.from_numpy(case.block_table).to(DEV)
+        self.ctx = torch.from_numpy(case.context_lens).to(DEV)
+        self.mbps, self.max_ctx = case.block_table.shape[1], int(case.context_lens.max())
+        self.pool = mk.mi_kv_pool_init(case.num_blocks, 16, cfg.num_kv_heads, cfg.head_dim,
+                                       self.kp, self.vp)
+        self.lc = mk.layer_config(cfg.hidden, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                                  cfg.intermediate, cfg.rms_eps, cfg.rope_theta)
+        self.lw = mk.layer_weights(**self.wd)
+        self.need = mk.mi_decoder_layer_workspace_bytes(self.lc, self.pool, self.B, self.max_ctx)
+        self.ws = torch.empty(self.need, dtype=torch.uint8, device=DEV)
+
+    def __call__(self, stream):
+        mk.mi_decoder_layer_decode(self.pool, self.lc, self.lw, self.x, self.xo, self.table,
+                                   self.mbps, self.ctx, self.B, self.max_ctx, self.ws, self.need,
+                                   stream.cuda_stream)
+
+    def close(self):
+        if self.pool:
+            mk.mi_kv_pool_destroy(self.pool)
+            self.pool = None
+
+
+def test_decoder_layer_graph_replays():
+    """The full decoder-layer decode step captured once and replayed on four
+    new hidden-state batches equals the eager layer bit for bit."""
+    print("graph layer", flush=True)
+    cfg = LAYER
+    case = workloads.make_decode_case(cfg, pool="poison")
+    w = workloads.make_layer_weights(cfg, std=0.03)
+    xs = [workloads.make_layer_input(workloads.DecodeConfig(**{**cfg.__dict__, "seed": 30 + i}))
+          for i in range(4)]
+    eager, graphed = _LayerSetup(cfg, case, w), _LayerSetup(cfg, case, w)
+    try:
+        side = torch.cuda.Stream()
+        graphed.x.copy_(bits_to_dev(xs[0]))
+        with torch.cuda.stream(side):
+            graphed(side)                               # first call outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            graphed(side)
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        eager.x.copy_(bits_to_dev(xs[0]))
+        eager(cur)                                      # the same first call, eagerly
+        torch.cuda.synchronize()
+        for i, xi in enumerate(xs):
+            xdev = bits_to_dev(xi)
+            eager.x.copy_(xdev)
+            graphed.x.copy_(xdev)
+            torch.cuda.synchronize()
+            eager(cur)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(graphed.xo, eager.xo), "replay %d: outputs differ" % i
+            assert torch.equal(graphed.kp, eager.kp), "replay %d: K cache differs" % i
+            assert torch.equal(graphed.vp, eager.vp), "replay %d: V cache differs" % i
+        assert mk.mi_kv_pool_check_errors(eager.pool) == 0
+        assert mk.mi_kv_pool_check_errors(graphed.pool) == 0
         del g
     finally:
         eager.close()
