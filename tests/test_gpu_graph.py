@@ -1,9 +1,10 @@
-"""The decode step and the decoder layer captured in HIP graphs (torch.cuda.CUDAGraph) and replayed:
-as two calls (mi_write_decode_kv + mi_paged_gqa_decode) and as one launch
-(mi_paged_gqa_decode_step). Each replay runs on new query values written
-into the captured buffers, with eager steps and synchronisations between
-replays, and must equal, bit for bit, the same step run eagerly on a second
-copy of the inputs (needs an MI355X)."""
+"""HIP graph capture (torch.cuda.CUDAGraph) of the decode step, as two calls
+(mi_write_decode_kv + mi_paged_gqa_decode) and as one launch
+(mi_paged_gqa_decode_step), and of the full decoder layer. Each graph is
+captured once and replayed on new inputs written into the captured buffers,
+with eager work and synchronisations between replays; every replay must
+equal, bit for bit, the same call run eagerly on a second copy of the inputs
+(needs an MI355X)."""
 import numpy as np
 import pytest
 import torch
