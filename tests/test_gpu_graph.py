@@ -1,6 +1,7 @@
 """HIP graph capture (torch.cuda.CUDAGraph) of the decode step, as two calls
 (mi_write_decode_kv + mi_paged_gqa_decode) and as one launch
-(mi_paged_gqa_decode_step), and of the full decoder layer. Each graph is
+(mi_paged_gqa_decode_step), of the full decoder layer and of a prefill
+chunk (with and without the rescaling repeat). Each graph is
 captured once and replayed on new inputs written into the captured buffers,
 with eager work and synchronisations between replays; every replay must
 equal, bit for bit, the same call run eagerly on a second copy of the inputs
@@ -11,6 +12,7 @@ import torch
 
 import paged_kv_cache_246_amd as mk
 import workloads
+from oracle import bf16 as obf16
 from tests.gpu_harness import DEV, DeviceCase, bits_to_dev
 
 pytestmark = pytest.mark.gpu
@@ -154,6 +156,74 @@ def test_decoder_layer_graph_replays():
             assert torch.equal(graphed.xo, eager.xo), "replay %d: outputs differ" % i
             assert torch.equal(graphed.kp, eager.kp), "replay %d: K cache differs" % i
             assert torch.equal(graphed.vp, eager.vp), "replay %d: V cache differs" % i
+        assert mk.mi_kv_pool_check_errors(eager.pool) == 0
+        assert mk.mi_kv_pool_check_errors(graphed.pool) == 0
+        del g
+    finally:
+        eager.close()
+        graphed.close()
+
+
+def _prefill_call(dev, stream):
+    st = stream.cuda_stream
+    mk.mi_write_prefill_kv(dev.pool, dev.q, dev.k, dev.v, dev.q_rot, dev.table, dev.mbps, dev.ctx,
+                           dev.cu, dev.B, dev.T, dev.Hq, dev.case.cfg.rope_theta, st)
+    mk.mi_paged_prefill_attention(dev.pool, dev.q_rot, dev.out, dev.table, dev.mbps, dev.ctx,
+                                  dev.cu, dev.B, dev.T, dev.max_new, dev.Hq, 0.0, st)
+
+
+def _far_case(D):
+    """Every query the same vector u, one key 30 u: later queries score far
+    above their first key tile, so the attention repeats the chunk with the
+    rescaling launch."""
+    cfg = workloads.DecodeConfig("pf_far_graph", batch=2, num_q_heads=4, num_kv_heads=2,
+                                 head_dim=D, block_size=16, num_blocks=32, rope_theta=1e4,
+                                 ctx_draw="fixed", seed=50 + D)
+    case = workloads.make_prefill_case(cfg, (0, 20), (100, 60))
+    u = case.q[0, 0].copy()
+    case.q[:] = u
+    case.k[40] = obf16.encode(30.0 * obf16.decode(u))        # sequence 0, position 40
+    return case
+
+
+@pytest.mark.parametrize("kind", ["mixed", "far"])
+def test_prefill_graph_replays(kind):
+    """Prefill (KV write + causal attention) captured once and replayed three
+    times, eager prefill calls between replays: every replay equals the eager
+    call bit for bit, also when the chunk needs the rescaling repeat (then the
+    captured call repeats on every replay)."""
+    from tests.test_gpu_prefill import PrefillOnDevice
+    print("graph prefill", kind, flush=True)
+    if kind == "mixed":
+        cfg = workloads.DecodeConfig("pf_graph", batch=3, num_q_heads=8, num_kv_heads=2,
+                                     head_dim=128, block_size=16, num_blocks=64, rope_theta=1e6,
+                                     ctx_draw="fixed", seed=60)
+        case = workloads.make_prefill_case(cfg, (0, 37, 16), (50, 9, 33))
+    else:
+        case = _far_case(128)
+    eager, graphed = PrefillOnDevice(case), PrefillOnDevice(case)
+    try:
+        side = torch.cuda.Stream()
+        cur = torch.cuda.current_stream()
+        _prefill_call(graphed, side)                    # first call outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            _prefill_call(graphed, side)
+        torch.cuda.synchronize()
+        for i in range(3):
+            eager.out.fill_(0)
+            graphed.out.fill_(0)
+            torch.cuda.synchronize()
+            _prefill_call(eager, cur)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(graphed.out, eager.out), "replay %d: outputs differ" % i
+            assert torch.equal(graphed.q_rot, eager.q_rot), "replay %d: q_rot differs" % i
+            assert torch.equal(graphed.k_pool, eager.k_pool), "replay %d: K cache differs" % i
+            assert torch.equal(graphed.v_pool, eager.v_pool), "replay %d: V cache differs" % i
+            assert bool(torch.isfinite(graphed.out.view(torch.bfloat16).float()).all())
         assert mk.mi_kv_pool_check_errors(eager.pool) == 0
         assert mk.mi_kv_pool_check_errors(graphed.pool) == 0
         del g
