@@ -1,11 +1,11 @@
 """HIP graph capture (torch.cuda.CUDAGraph) of the decode step, as two calls
 (mi_write_decode_kv + mi_paged_gqa_decode) and as one launch
 (mi_paged_gqa_decode_step), of the full decoder layer and of a prefill
-chunk (with and without the rescaling repeat). Each graph is
-captured once and replayed on new inputs written into the captured buffers,
-with eager work and synchronisations between replays; every replay must
-equal, bit for bit, the same call run eagerly on a second copy of the inputs
-(needs an MI355X)."""
+chunk (with and without the rescaling repeat). Each graph is captured
+once and replayed several times (the decode step and the layer on new
+inputs written into the captured buffers), with eager work and
+synchronisations between replays; every replay must equal, bit for bit, the
+same call run eagerly on a second copy of the inputs (needs an MI355X)."""
 import numpy as np
 import pytest
 import torch
