@@ -45,10 +45,11 @@ def _make_step(dc, one_launch, stream):
 
 
 @pytest.mark.parametrize("one_launch", [False, True])
-@pytest.mark.parametrize("name", ["qwen3_1p7b", "qwen2p5_7b_b8"])
-def test_decode_step_graph_replays(name, one_launch):
-    print("graph", name, "one launch" if one_launch else "two calls", flush=True)
-    case = workloads.make_decode_case(workloads.CONFIGS[name], pool="poison")
+@pytest.mark.parametrize("name,fmt", [("qwen3_1p7b", "bf16"), ("qwen2p5_7b_b8", "bf16"),
+                                      ("qwen3_1p7b", "fp8")])
+def test_decode_step_graph_replays(name, fmt, one_launch):
+    print("graph", name, fmt, "one launch" if one_launch else "two calls", flush=True)
+    case = workloads.make_decode_case(workloads.CONFIGS[name], pool="poison", kv_format=fmt)
     rng = np.random.default_rng(11)
     qs = [rng.standard_normal(case.q.shape).astype(np.float32) for _ in range(4)]
     qs = [(torch.from_numpy(x).to(torch.bfloat16).view(torch.int16)).to(DEV) for x in qs]
