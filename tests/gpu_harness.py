@@ -103,3 +103,47 @@ def ulp_diff_bf16(a_bits, b_bits):
         mag = x & 0x7FFF
         return np.where(x & 0x8000, -mag, mag)
     return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def check_decode_write(case, gk, gv, gq, kn, vn, qrot_bits):
+    """Pools after a GPU decode write (gk, gv: bf16 bits) and its q_rot (gq)
+    vs the oracle's write (kn, vn, qrot_bits): V bit-exact and nothing else
+    moved; K at the written slots and q_rot within one bf16 ulp, every other K
+    element bit-identical. Returns the number of elements one ulp off."""
+    assert np.array_equal(gv, vn)
+    slots = np.zeros(case.k_pool.shape[:3], dtype=bool)
+    for b, ctx in enumerate(case.context_lens):
+        slots[case.block_table[b, ctx // 16], :, ctx % 16] = True
+    assert np.array_equal(gk[~slots], kn[~slots])
+    u = ulp_diff_bf16(gk[slots], kn[slots])
+    assert u.max() <= 1, "K write off by %d ulp" % u.max()
+    uq = ulp_diff_bf16(gq, qrot_bits)
+    assert uq.max() <= 1
+    return int((u > 0).sum() + (uq > 0).sum())
+
+
+_ORACLE_CACHE = {}
+
+
+def oracle_decode_step(case, key, k_scales=None, v_scales=None):
+    """The oracle's write + attention of a decode case, (out_f64, k_new, v_new,
+    q_rot_bits), computed once per key and kept for the rest of the session (the
+    full-size long-context workload takes seconds; several test files check
+    against it). An 8-bit case takes the oracle's 8-bit step with the given
+    scales."""
+    from oracle import attention as oatt
+    if key not in _ORACLE_CACHE:
+        cfg = case.cfg
+        if case.k_pool.dtype == np.uint8:
+            _ORACLE_CACHE[key] = oatt.decode_step_fp8(
+                case.k_pool, case.v_pool, case.q, case.k, case.v, case.block_table,
+                case.context_lens, cfg.block_size, cfg.rope_theta, k_scales, v_scales)
+        else:
+            _ORACLE_CACHE[key] = oatt.decode_step(
+                case.k_pool, case.v_pool, case.q, case.k, case.v, case.block_table,
+                case.context_lens, cfg.block_size, cfg.rope_theta)
+    return _ORACLE_CACHE[key]
+
+
+def drop_oracle(key):
+    _ORACLE_CACHE.pop(key, None)

@@ -11,8 +11,9 @@ from oracle import attention as oatt
 from oracle import bf16 as obf16
 from oracle import fp8 as ofp8
 from oracle import layer as olayer
-from tests.gpu_harness import (DEV, DeviceCase, bf16_bits_to_f64, bits_to_dev, check_tolerance,
-                               codes_to_dev, dev_to_bits, ulp_diff_bf16)
+from tests.gpu_harness import (DEV, DeviceCase, bits_to_dev, check_tolerance,
+                               codes_to_dev, dev_to_bits, drop_oracle, oracle_decode_step,
+                               ulp_diff_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -82,14 +83,18 @@ def test_quantize_every_bf16_pattern_bit_exact():
         assert nk == 0 and nv == 0
 
 
-def _check_write_fp8(case, dc, ks, vs):
+def _check_write_fp8(case, dc, ks, vs, oracle_write=None):
     """Codes after the GPU write vs the oracle's: V codes bit-exact; K codes
     equal except where the bf16 RoPE value itself may differ by one ulp
-    (then within one code); q_rot within one bf16 ulp; nothing else moved."""
+    (then within one code); q_rot within one bf16 ulp; nothing else moved.
+    oracle_write: the oracle's (k_new, v_new, q_rot_bits) if already computed."""
     cfg = case.cfg
-    kn, vn, qb, _ = oatt.write_decode_kv_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
-                                             case.block_table, case.context_lens, 16,
-                                             cfg.rope_theta, ks, vs)
+    if oracle_write is None:
+        kn, vn, qb, _ = oatt.write_decode_kv_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                                 case.block_table, case.context_lens, 16,
+                                                 cfg.rope_theta, ks, vs)
+    else:
+        kn, vn, qb = oracle_write
     gk, gv = _codes(dc.k_pool), _codes(dc.v_pool)
     assert np.array_equal(gv, vn)
     slots = np.zeros(case.k_pool.shape[:3], dtype=bool)
@@ -210,40 +215,30 @@ def test_fp8_gather_bit_exact():
         dc.close()
 
 
-def test_fp8_long_context_full_size_sampled():
-    """The long-context workload over an 8-bit cache at full size in the
-    benchmark's launch configuration; sampled (sequence, kv head) pairs from
-    the oracle, which dequantises the codes the GPU wrote."""
+def test_fp8_long_context_full_size():
+    """The long-context workload over an 8-bit cache with per-head scales, at
+    full size in the benchmark's launch configuration, every output against
+    the oracle: the whole K and V code pools and q_rot after the write, then
+    all B x Hq x D attention outputs (the oracle dequantises the codes)."""
     cfg = workloads.CONFIGS["qwen3_8b_long"]
     case = workloads.make_decode_case(cfg, pool="poison", kv_format="fp8")
-    _say("fp8 qwen3_8b_long")
-    dc = DeviceCase(case)
+    ks, vs = _scales(cfg.num_kv_heads, 45)
+    _say("fp8 qwen3_8b_long, scales", ks, vs)
+    dc = DeviceCase(case, ks, vs)
     try:
         dc.write()
         dc.attend()
         torch.cuda.synchronize()
         out = dev_to_bits(dc.out)
         assert dc.faults() == 0
-        ctx = case.context_lens
-        ones = np.ones(cfg.num_kv_heads, np.float32)
-        kn, vn, qb, _ = oatt.write_decode_kv_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v,
-                                                 case.block_table, ctx, 16, cfg.rope_theta,
-                                                 ones, ones)
-        G = cfg.group
-        rng = np.random.default_rng(45)
-        picks = {int(np.argmax(ctx)), int(np.argmin(ctx))} | set(rng.choice(len(ctx), 4, replace=False).tolist())
-        scale = 1.0 / np.sqrt(cfg.head_dim)
-        for b in sorted(picks):
-            g = int(rng.integers(cfg.num_kv_heads))
-            L = int(ctx[b]) + 1
-            ksq, vsq = oatt.gather_kv(kn, vn, case.block_table, 16, b, g, L)
-            K, V = ofp8.dequantize(ksq, 1.0), ofp8.dequantize(vsq, 1.0)
-            ref = np.stack([oatt.attend(obf16.decode(qb[b, h]), K, V, scale)
-                            for h in range(g * G, (g + 1) * G)])
-            check_tolerance(out[b, g * G:(g + 1) * G], ref, "fp8 b=%d g=%d L=%d" % (b, g, L))
-        assert np.all(np.isfinite(bf16_bits_to_f64(out)))
+        ref, kn, vn, qb = oracle_decode_step(case, "qwen3_8b_long_fp8", ks, vs)
+        off = _check_write_fp8(case, dc, ks, vs, (kn, vn, qb))
     finally:
         dc.close()
+    drop_oracle("qwen3_8b_long_fp8")
+    mx, rel = check_tolerance(out, ref, "fp8 qwen3_8b_long")
+    _say("  K codes one step apart: %d; max|d| %.3g relL2 %.3g over %d outputs"
+         % (off, mx, rel, out.size))
 
 
 LAYER_SMALL = workloads.DecodeConfig(

@@ -84,6 +84,83 @@ def test_decode_step_graph_replays(name, fmt, one_launch):
         graphed.close()
 
 
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_decode_step_graph_replays_with_growing_contexts(one_launch):
+    """The serving use of a captured step: the graph is captured once with a
+    max_context_len that leaves room for 20 more tokens, and before each
+    replay every sequence's length grows by one on the device (a new block
+    id entered in its table row whenever the new token starts a block), with
+    new q, k and v. Every replay equals the eager step on a second copy bit
+    for bit, and the oracle's step from the pools as they were before it:
+    the write (V bit-exact, K and q_rot within one ulp, nothing else moved)
+    and the outputs (within tolerance)."""
+    from oracle import attention as oatt
+    from tests.gpu_harness import check_decode_write, check_tolerance, dev_to_bits
+    steps = 20
+    cfg = workloads.CONFIGS["qwen3_1p7b"]
+    case = workloads.make_decode_case(cfg, pool="poison")
+    B = len(case.context_lens)
+    old = case.block_table
+    used = set(old[old >= 0].tolist())
+    free = [i for i in range(case.num_blocks) if i not in used]
+    mb = max(old.shape[1], max(workloads.nblocks(c + 1 + steps, 16) for c in case.context_lens))
+    case.block_table = np.full((B, mb), -1, np.int32)
+    case.block_table[:, :old.shape[1]] = old
+    print("graph growing contexts", "one launch" if one_launch else "two calls", flush=True)
+    eager, graphed = DeviceCase(case), DeviceCase(case)
+    try:
+        for dc in (eager, graphed):
+            dc.max_ctx = int(case.context_lens.max()) + steps
+        side = torch.cuda.Stream()
+        step_e, _ = _make_step(eager, one_launch, torch.cuda.current_stream())
+        step_g, _ = _make_step(graphed, one_launch, side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step_g()
+        torch.cuda.synchronize()
+        ctx = case.context_lens.copy()
+        table = case.block_table.copy()
+        rng = np.random.default_rng(12)
+        crossed = 0
+        for i in range(steps):
+            if i:
+                ctx += 1                                # the previous step's token is cached
+            for b in range(B):
+                if ctx[b] % 16 == 0 and table[b, ctx[b] // 16] < 0:
+                    table[b, ctx[b] // 16] = free.pop()
+                    crossed += 1
+            q = workloads.bf16_normal(rng, case.q.shape)
+            k = workloads.bf16_normal(rng, case.k.shape)
+            v = workloads.bf16_normal(rng, case.v.shape)
+            kp0, vp0 = dev_to_bits(eager.k_pool), dev_to_bits(eager.v_pool)
+            for dc in (eager, graphed):
+                dc.ctx.copy_(torch.from_numpy(ctx))
+                dc.table.copy_(torch.from_numpy(table))
+                dc.q.copy_(bits_to_dev(q))
+                dc.k.copy_(bits_to_dev(k))
+                dc.v.copy_(bits_to_dev(v))
+            torch.cuda.synchronize()
+            step_e()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(graphed.out, eager.out), "replay %d: outputs differ" % i
+            assert torch.equal(graphed.q_rot, eager.q_rot), "replay %d: q_rot differs" % i
+            assert torch.equal(graphed.k_pool, eager.k_pool), "replay %d: K cache differs" % i
+            assert torch.equal(graphed.v_pool, eager.v_pool), "replay %d: V cache differs" % i
+            ref, kn, vn, qb = oatt.decode_step(kp0, vp0, q, k, v, table, ctx, 16, cfg.rope_theta)
+            check_decode_write(workloads.DecodeCase(cfg, ctx, table, case.num_blocks, q, k, v, kp0, vp0),
+                               dev_to_bits(graphed.k_pool), dev_to_bits(graphed.v_pool),
+                               dev_to_bits(graphed.q_rot), kn, vn, qb)
+            check_tolerance(dev_to_bits(graphed.out), ref, "replay %d" % i)
+        assert crossed >= B, crossed                    # every sequence entered a new block
+        assert eager.faults() == 0 and graphed.faults() == 0
+        del g
+    finally:
+        eager.close()
+        graphed.close()
+
+
 LAYER = workloads.DecodeConfig(
     "graph_layer", batch=12, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
     num_blocks=256, rope_theta=1e6, ctx_draw="uniform", ctx_lo=0, ctx_hi=150, seed=21,

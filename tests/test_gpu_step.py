@@ -11,7 +11,8 @@ import torch
 import paged_kv_cache_246_amd as mk
 import workloads
 from oracle import attention as oatt
-from tests.gpu_harness import (DEV, DeviceCase, bf16_bits_to_f64, check_tolerance, dev_to_bits)
+from tests.gpu_harness import (DEV, DeviceCase, bf16_bits_to_f64, check_decode_write,
+                               check_tolerance, dev_to_bits, oracle_decode_step)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,10 +122,11 @@ def test_step_without_q_rot_output():
     _against_two_calls(case, _ref(case), "no q_rot", with_q_rot=False)
 
 
-def test_step_long_context_full_size_sampled():
+def test_step_long_context_full_size():
     """The Qwen3-8B-shaped long-context workload at full size: the whole cache
-    and q_rot equal the two-call path's; sampled (sequence, kv head) outputs
-    against the oracle, every output close to the two-call path's."""
+    and q_rot equal the two-call path's bit for bit (and so the oracle's write,
+    checked with the two-call path), and every output is within tolerance of
+    the oracle and close to the two-call path's."""
     cfg = workloads.CONFIGS["qwen3_8b_long"]
     case = workloads.make_decode_case(cfg, pool="poison")
     _say("step qwen3_8b_long")
@@ -137,25 +139,17 @@ def test_step_long_context_full_size_sampled():
         assert torch.equal(one.k_pool, two.k_pool) and torch.equal(one.v_pool, two.v_pool)
         assert torch.equal(one.q_rot, two.q_rot)
         out1, out2 = dev_to_bits(one.out), dev_to_bits(two.out)
-        assert one.faults() == 0
+        gk, gv, gq = dev_to_bits(one.k_pool), dev_to_bits(one.v_pool), dev_to_bits(one.q_rot)
+        assert one.faults() == 0 and two.faults() == 0
     finally:
         one.close()
         two.close()
+    ref, kn, vn, qb = oracle_decode_step(case, "qwen3_8b_long")
+    check_decode_write(case, gk, gv, gq, kn, vn, qb)
+    mx, rel = check_tolerance(out1, ref, "step qwen3_8b_long")
     d = np.abs(bf16_bits_to_f64(out1) - bf16_bits_to_f64(out2))
-    assert np.all(np.isfinite(bf16_bits_to_f64(out1))) and d.max() <= 1e-2, d.max()
-    ctx = case.context_lens
-    kn, vn, qb, _ = oatt.write_decode_kv(case.k_pool, case.v_pool, case.q, case.k, case.v,
-                                         case.block_table, ctx, 16, cfg.rope_theta)
-    from oracle import bf16 as obf16
-    G = cfg.group
-    rng = np.random.default_rng(45)
-    scale = 1.0 / np.sqrt(cfg.head_dim)
-    for b in sorted({int(np.argmax(ctx)), int(np.argmin(ctx))} | set(rng.choice(len(ctx), 3, replace=False).tolist())):
-        g = int(rng.integers(cfg.num_kv_heads))
-        ks, vs = oatt.gather_kv(kn, vn, case.block_table, 16, b, g, int(ctx[b]) + 1)
-        K, V = obf16.decode(ks), obf16.decode(vs)
-        ref = np.stack([oatt.attend(obf16.decode(qb[b, h]), K, V, scale) for h in range(g * G, (g + 1) * G)])
-        check_tolerance(out1[b, g * G:(g + 1) * G], ref, "b=%d g=%d" % (b, g))
+    assert d.max() <= 1e-2, d.max()
+    _say("  max|d| %.3g relL2 %.3g over %d outputs, vs two calls %.3g" % (mx, rel, out1.size, d.max()))
 
 
 def test_step_argument_errors():
