@@ -74,7 +74,8 @@ enum {
     MI_ERR_HIP = -4,                  /* a HIP runtime call or kernel launch failed */
     MI_ERR_UNSUPPORTED = -5,          /* valid but unsupported shape */
     MI_ERR_WORKSPACE_TOO_SMALL = -6,  /* workspace_bytes below the size query */
-    MI_ERR_DEVICE_FAULT = -7          /* mi_kv_pool_check_errors found a recorded fault */
+    MI_ERR_DEVICE_FAULT = -7,         /* mi_kv_pool_check_errors found a recorded fault */
+    MI_ERR_SCRATCH_TOO_SMALL = -8     /* the call needs more than MI_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Device error-word bits (mi_kv_pool_check_errors). */
@@ -534,6 +535,29 @@ int mi_paged_gqa_decode_step(mi_kv_pool_t pool, const uint16_t* q, const uint16_
                              int32_t num_q_heads, double rope_theta, float softmax_scale,
                              int32_t max_context_len, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * mi_paged_gqa_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, results and default split as mi_paged_gqa_decode
+ * (the same kernels, bit-identical outputs), but no workspace: the split-K
+ * partials go to a fixed device array of MI_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends (its address on a device
+ * is taken when the first pool is created there). The call allocates nothing.
+ * The partials need 2 * W * G * (4 * head_dim + 8) bytes for a grid of W
+ * waves (three per compute unit, fewer for small workloads): 6.4 MB at
+ * G = 8, head_dim = 128 on 256 compute units. A call that would need more
+ * returns MI_ERR_SCRATCH_TOO_SMALL and launches nothing. Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller; every slot a
+ * call reads it has written itself, so nothing needs clearing between calls.
+ */
+#define MI_NOALLOC_SCRATCH_BYTES (8u << 20)
+int mi_paged_gqa_decode_noalloc(mi_kv_pool_t pool, const uint16_t* q_rot, uint16_t* out,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t batch,
+                                int32_t num_q_heads, float softmax_scale,
+                                int32_t max_context_len, void* stream);
 
 /*
  * Measurement utility (not a step of the method): reads `bytes` of device

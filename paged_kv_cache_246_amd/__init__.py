@@ -21,6 +21,8 @@ MI_ERR_HIP = -4
 MI_ERR_UNSUPPORTED = -5
 MI_ERR_WORKSPACE_TOO_SMALL = -6
 MI_ERR_DEVICE_FAULT = -7
+MI_ERR_SCRATCH_TOO_SMALL = -8
+MI_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 MI_FAULT_BLOCK_ID = 1
 MI_FAULT_CONTEXT_LEN = 2
@@ -58,6 +60,8 @@ SIGNATURES = {
     "mi_paged_gqa_decode_split": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                              _c.c_float, _i32, _i32, _vp, _sz, _vp]),
     "mi_paged_gqa_decode_split_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32, _i32]),
+    "mi_paged_gqa_decode_noalloc": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                               _c.c_float, _i32, _vp]),
     "mi_hbm_stream_read": (_c.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "mi_paged_gqa_decode_step": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                             _i32, _c.c_double, _c.c_float, _i32, _vp, _sz, _vp]),
@@ -252,6 +256,14 @@ def mi_paged_gqa_decode(pool, q_rot, out, block_table, max_blocks_per_seq, conte
         pool, _ptr(q_rot), _ptr(out), _ptr(block_table), max_blocks_per_seq,
         _ptr(context_lens), batch, num_q_heads, float(softmax_scale), max_context_len,
         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mi_paged_gqa_decode_noalloc(pool, q_rot, out, block_table, max_blocks_per_seq, context_lens,
+                                batch, num_q_heads, softmax_scale, max_context_len, stream=None):
+    return _check("mi_paged_gqa_decode_noalloc", lib().mi_paged_gqa_decode_noalloc(
+        pool, _ptr(q_rot), _ptr(out), _ptr(block_table), max_blocks_per_seq,
+        _ptr(context_lens), batch, num_q_heads, float(softmax_scale), max_context_len,
+        _stream(stream)))
 
 
 def mi_paged_gqa_decode_split(pool, q_rot, out, block_table, max_blocks_per_seq, context_lens,

@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "e4m3.h"
 #include "internal.h"
@@ -1243,6 +1244,20 @@ int attention_waves(K kernel) {
     return cached[dev];
 }
 
+// Upper bound of attention_waves() on the current device without naming a
+// kernel: kAttnWavesPerCU waves on every CU (cached per device).
+int resident_wave_bound() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return mikv::kMaxAttnWaves;
+    if (cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return mikv::kMaxAttnWaves;
+    cached[dev] = std::min(mikv::kMaxAttnWaves, kAttnWavesPerCU * cus);
+    return cached[dev];
+}
+
 template <int D, int G, bool STEP>
 void launch_attn_kernel(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                         const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
@@ -1408,16 +1423,57 @@ int launch_write_prefill_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 
+// ----------------------------------------------- allocation-free decode
+// Callers that cannot allocate device memory (code under HIP graph capture,
+// tight serving loops, harnesses that forbid hipMalloc) get the split-K
+// partials of the decode attention in this fixed device array instead of a
+// workspace. Every device the library runs on holds its own copy until the
+// process ends. Host code never uses the array's name as an address: the
+// address of the current device's copy comes from hipGetSymbolAddress, taken
+// once per device at pool creation (setup_noalloc_scratch) and kept in
+// g_scratch_addr.
 namespace {
 
+static __device__ __align__(256) uint8_t scratch[MI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+}  // namespace
+
+int setup_noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MI_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev]) return MI_OK;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MI_ERR_HIP;
+    g_scratch_addr[dev] = ptr;
+    return MI_OK;
+}
+
+void* noalloc_scratch(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_addr[dev];
+}
+
+namespace {
+
+// ws_waves: the wave count the workspace's partial slots are laid out for
+// (at least the grid the launch takes); 0 selects the bound the workspace
+// queries use.
 int launch_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, const int32_t* table,
                   int32_t mbps, const int32_t* ctx, int32_t batch, int32_t hq, float scale,
                   int32_t max_ctx, int32_t split_tokens, void* ws, const StepToken* tok,
-                  void* stream) {
+                  void* stream, int ws_waves = 0) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int G = hq / p->num_kv_heads;
     const int min_tiles = split_tokens / BS;
-    const int waves_bound = attention_grid_waves(batch, p->num_kv_heads, max_ctx, min_tiles, kMaxAttnWaves);
+    const int waves_bound = ws_waves > 0 ? ws_waves
+                                         : attention_grid_waves(batch, p->num_kv_heads, max_ctx,
+                                                                min_tiles, kMaxAttnWaves);
     const size_t slots = 2 * static_cast<size_t>(waves_bound) * G;
     float* pa = static_cast<float*>(ws);
     float2* pm = reinterpret_cast<float2*>(static_cast<char*>(ws) +
@@ -1442,6 +1498,23 @@ int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16
                             void* ws, void* stream) {
     return launch_decode(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx, split_tokens,
                          ws, nullptr, stream);
+}
+
+int launch_paged_gqa_decode_noalloc(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                                    const int32_t* table, int32_t mbps, const int32_t* ctx,
+                                    int32_t batch, int32_t hq, float scale, int32_t max_ctx,
+                                    void* stream) {
+    void* ws = noalloc_scratch(p->device);
+    if (!ws) return MI_ERR_HIP;
+    // the partial slots are laid out for the grid the launch takes (at most
+    // kAttnWavesPerCU waves per CU), not for the workspace queries' bound
+    const int min_tiles = kDefaultSplitTokens / BS;
+    const int waves = attention_grid_waves(batch, p->num_kv_heads, max_ctx, min_tiles, resident_wave_bound());
+    const size_t slots = 2 * static_cast<size_t>(waves) * (hq / p->num_kv_heads);
+    const size_t need = align_up(slots * p->head_dim * sizeof(float), 256) + align_up(slots * sizeof(float2), 256);
+    if (need > MI_NOALLOC_SCRATCH_BYTES) return MI_ERR_SCRATCH_TOO_SMALL;
+    return launch_decode(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx,
+                         kDefaultSplitTokens, ws, nullptr, stream, waves);
 }
 
 int launch_decode_step(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
@@ -1623,4 +1696,19 @@ extern "C" int mi_paged_gqa_decode_step(mi_kv_pool_t p, const uint16_t* q, const
     if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(p->head_dim));
     return mikv::launch_decode_step(p, q, k, v, q_rot, out, table, mbps, ctx, batch, hq, theta, scale,
                                     max_ctx, ws, stream);
+}
+
+extern "C" int mi_paged_gqa_decode_noalloc(mi_kv_pool_t p, const uint16_t* q_rot, uint16_t* out,
+                                           const int32_t* table, int32_t mbps, const int32_t* ctx,
+                                           int32_t batch, int32_t hq, float scale, int32_t max_ctx,
+                                           void* stream) {
+    int rc = check_common(p, batch, hq, mbps);
+    if (rc != MI_OK) return rc;
+    if (max_ctx < 0) return MI_ERR_INVALID_ARG;
+    if (batch > mikv::kMaxBatch) return MI_ERR_UNSUPPORTED;
+    if (batch == 0) return MI_OK;
+    if (!q_rot || !out || !table || !ctx || q_rot == out) return MI_ERR_INVALID_ARG;
+    if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(p->head_dim));
+    return mikv::launch_paged_gqa_decode_noalloc(p, q_rot, out, table, mbps, ctx, batch, hq, scale,
+                                                 max_ctx, stream);
 }

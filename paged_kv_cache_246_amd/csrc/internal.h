@@ -87,6 +87,17 @@ int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16
                             const int32_t* table, int32_t mbps, const int32_t* ctx,
                             int32_t batch, int32_t hq, float scale, int32_t max_ctx,
                             int32_t split_tokens, void* ws, void* stream);
+// mi_paged_gqa_decode with its partials in the library's fixed device
+// scratch array instead of a workspace (no allocation).
+int launch_paged_gqa_decode_noalloc(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
+                                    const int32_t* table, int32_t mbps, const int32_t* ctx,
+                                    int32_t batch, int32_t hq, float scale, int32_t max_ctx,
+                                    void* stream);
+// Takes the current device's address of the scratch array (once per device;
+// called at pool creation with the pool's device current).
+int setup_noalloc_scratch();
+void* noalloc_scratch(int device);
+
 // write_decode_kv and the attention in one launch (plus the combine).
 int launch_decode_step(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
                        const uint16_t* v, uint16_t* q_rot, uint16_t* out, const int32_t* table,

@@ -25,6 +25,7 @@ extern "C" const char* mi_status_string(int status) {
         case MI_ERR_UNSUPPORTED: return "unsupported shape";
         case MI_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case MI_ERR_DEVICE_FAULT: return "device-side fault recorded";
+        case MI_ERR_SCRATCH_TOO_SMALL: return "call needs more than the fixed scratch array";
         default: return "unknown status";
     }
 }
@@ -81,7 +82,8 @@ extern "C" int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t bl
             p->owns_cache = true;
         }
         bool ok = hipMalloc(reinterpret_cast<void**>(&p->err), 256) == hipSuccess &&
-                  hipMemset(p->err, 0, 256) == hipSuccess;
+                  hipMemset(p->err, 0, 256) == hipSuccess &&
+                  mikv::setup_noalloc_scratch() == MI_OK;
         if (ok && mikv::pool_fp8(p)) {
             const std::vector<float> one(2 * static_cast<size_t>(num_kv_heads), 1.0f);
             ok = hipMalloc(reinterpret_cast<void**>(&p->scales), one.size() * sizeof(float)) == hipSuccess &&

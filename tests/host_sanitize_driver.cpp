@@ -11,6 +11,13 @@
 
 #include "mikv.h"
 
+// Device pools take the address of the library's scratch array (attention.hip,
+// device code) at creation; host-only pools never do, so the host build links
+// this stand-in, which a host-only pool never calls.
+namespace mikv {
+int setup_noalloc_scratch() { std::abort(); }
+}
+
 static int g_checks = 0;
 #define CHECK(cond)                                                              \
     do {                                                                         \
