@@ -87,7 +87,8 @@ enum {
 /* Pool flags. */
 enum {
     MI_POOL_HOST_ONLY = 1u,           /* block bookkeeping only: no device memory, no kernels */
-    MI_POOL_KV_FP8 = 2u               /* 8-bit cache: E4M3 codes with per-KV-head scales */
+    MI_POOL_KV_FP8 = 2u,              /* 8-bit cache: E4M3 codes with per-KV-head scales */
+    MI_POOL_SWAP_STAGING = 4u         /* device staging for scattered KV swaps (mi_kv_swap_out/in) */
 };
 
 /* Static description of a status code. Never NULL. */
@@ -118,7 +119,11 @@ typedef struct mi_kv_pool_s* mi_kv_pool_t;
  *                 value / scale, with one K scale and one V scale per KV head
  *                 (all 1.0 until mi_kv_pool_set_scales). vLLM-based
  *                 inference-framework report, "FP8 KV Cache quantisation": the
- *                 cache is held in FP8 to cut the bytes the attention moves.
+ *                 cache is held in FP8 to cut the bytes the attention moves;
+ *               MI_POOL_SWAP_STAGING: also allocate a device staging buffer
+ *                 for KV swaps (two halves of min(64 MiB, pool bytes), freed
+ *                 on destroy), with which mi_kv_swap_out/in move a run of
+ *                 scattered device blocks in one transfer.
  * The free-block stack starts full; the first allocation returns ids 0, 1, ...
  * The current HIP device at this call is the pool's device.
  */
@@ -446,8 +451,8 @@ int32_t mi_sched_num_swapped(mi_sched_t sched);
  * KV offload (course project, optional task "KV Cache Offloading": inactive
  * KV blocks go to CPU memory and come back when needed, under an eviction
  * policy). Gives the planner a host swap space of host_slots blocks (call
- * before the first step; 0 = none). A preemption victim -- the most recently
- * admitted running request -- whose blocks fit the free host slots is then
+ * before the first step; 0 = none). A preemption victim (picked by the
+ * eviction policy, mi_sched_set_eviction) whose blocks fit the free host slots is then
  * swapped out instead of recomputed: it keeps its context and comes back
  * before anything new is admitted (swapped requests in swap order, regardless
  * of the brakes), with its blocks copied back into fresh device blocks.
@@ -455,13 +460,30 @@ int32_t mi_sched_num_swapped(mi_sched_t sched);
 int mi_sched_set_swap_space(mi_sched_t sched, int32_t host_slots);
 
 /*
+ * Eviction policy of the planner (the same optional task: "design an eviction
+ * policy -- LRU / FIFO / by layer / by token segment"). It picks the running
+ * request that makes room when the pool runs dry, for swap-out and for
+ * recompute preemption alike:
+ *  MI_EVICT_LIFO  the most recently admitted running request (the default;
+ *                 vLLM's preemption order);
+ *  MI_EVICT_FIFO  the running request that entered the running set first
+ *                 (admitted, or swapped back in, earliest);
+ *  MI_EVICT_LRU   the least recently used running request: every step reads
+ *                 the KV of every running request, so this is the FIFO
+ *                 victim (identical plans).
+ * May be changed between steps. MI_ERR_INVALID_ARG for another value.
+ */
+enum { MI_EVICT_LIFO = 0, MI_EVICT_FIFO = 1, MI_EVICT_LRU = 2 };
+int mi_sched_set_eviction(mi_sched_t sched, int32_t policy);
+
+/*
  * Plan one engine step (host arrays, capacity max_running rows each):
  *  1. requests that produced max_new_tokens retire (ids in finished_ids) and
  *     return their blocks;
  *  2. every running request gets the block its decode write at position
  *     context_len needs (ceil((context_len + 1) / 16) blocks), in admission
- *     order; on an empty pool the most recently admitted running request is
- *     preempted (blocks returned; re-queued first, to be prefilled again over
+ *     order; on an empty pool the running request the eviction policy picks
+ *     is preempted (blocks returned; re-queued first, to be prefilled again over
  *     its prompt and generated tokens; id in preempted_ids);
  *  3. waiting requests are admitted in order while a row is free, no brake
  *     holds (free / pool re-measured before each admission) and the pool
@@ -497,9 +519,10 @@ int mi_sched_step(mi_sched_t sched, mi_sched_counts* counts, int64_t* seq_ids,
  * by host slot and each run of consecutive slots moves in one DMA transfer
  * queued on stream, asynchronous for page-locked host memory (the host
  * arrays must stay alive until the stream reaches them); scattered device
- * blocks of a run are packed / unpacked by a kernel through a device staging
- * buffer of up to 64 MiB per cache, allocated by the pool's first such swap
- * and freed with the pool. Swaps on one pool must be ordered on one stream.
+ * blocks of a run are packed / unpacked by a kernel through the pool's
+ * staging buffer (pools created with MI_POOL_SWAP_STAGING, in chunks of its
+ * size), else moved one block per transfer. No device memory is allocated.
+ * Swaps on one pool must be ordered on one stream.
  */
 int mi_kv_swap_out(mi_kv_pool_t pool, void* host_k, void* host_v, int32_t host_slots,
                    const int32_t* pairs, int32_t n, void* stream);

@@ -25,10 +25,11 @@ Readings where the pages are silent (the same in the library):
 * A step: (1) retire running requests that have produced max_new_tokens and
   return their blocks; (2) give every running request the block its decode
   write needs (position ctx, i.e. ceil((ctx + 1) / 16) blocks), in arrival
-  order; if the pool is empty, preempt the most recently admitted running
-  request (its blocks return to the pool; it goes back to the head of the
-  waiting queue and will be prefilled again over prompt + generated tokens,
-  vLLM's recompute preemption) and retry; (3) admit waiting requests in FIFO
+  order; if the pool is empty, preempt the running request the eviction
+  policy picks (below; by default the most recently admitted one): its
+  blocks return to the pool; it goes back to the head of the waiting queue
+  and will be prefilled again over prompt + generated tokens (vLLM's
+  recompute preemption); then retry; (3) admit waiting requests in FIFO
   order while a running slot is free, no brake holds and the pool has the
   ceil(prompt / 16) blocks of the prompt; the first request that cannot be
   admitted stops admission (no overtaking); (4) emit the plan: the admitted
@@ -50,8 +51,8 @@ stack like the device pool), a preemption victim whose blocks fit the free
 host slots is swapped out instead of recomputed: its device blocks are
 copied to host slots (emitted as (device id, host slot) pairs, to run before
 anything else in the step) and returned to the pool; it keeps its context
-and generated count and joins the swapped queue. The victim is the most
-recently admitted running request (LIFO eviction among running requests).
+and generated count and joins the swapped queue. The victim is the one the
+eviction policy below picks.
 Swapped requests come back first, in the order they were swapped out,
 regardless of the brakes (they are not new prefills), and while any request
 remains swapped out no new request is admitted: a swap-in needs the request's blocks plus the block its decode
@@ -60,6 +61,21 @@ the host slots (emitted as (host slot, device id) pairs, run after the
 swap-outs), the host slots are freed, and the request decodes in this same
 step after the requests already running. Without host space (or when the
 victim's blocks do not fit) preemption recomputes as above.
+
+Eviction policy (the same page: "design an eviction policy -- LRU / FIFO /
+by layer / by token segment"). It picks the victim among the running
+requests, for swap-out and for recompute preemption alike:
+
+* LIFO (the default): the most recently admitted running request (vLLM's
+  preemption order);
+* FIFO: the running request that entered the running set first (admitted,
+  or swapped back in, earliest) -- first in, first out;
+* LRU: the least recently used running request. Every step reads the KV of
+  every running request (each one decodes), so the last use of all of them
+  is the previous step and recency cannot separate them; ties go to the one
+  that has held its blocks longest, which makes LRU pick the FIFO victim.
+  LRU is accepted as a name for that policy (the tests check that the two
+  give identical plans).
 
 Pinned by tests/test_oracle_sched.py against scenarios whose decisions follow
 from the stated rules by hand, and by invariants (no block in two tables,
@@ -70,6 +86,7 @@ from dataclasses import dataclass, field
 from . import paged
 
 PROCEED, SOFT, HARD = 0, 1, 2
+EVICT_LIFO, EVICT_FIFO, EVICT_LRU = 0, 1, 2
 
 
 @dataclass
@@ -97,7 +114,7 @@ class Plan:
 
 class Scheduler:
     def __init__(self, num_blocks, block_size=16, max_running=64, hard=0.10, soft=0.30,
-                 max_blocks_per_seq=None, host_slots=0):
+                 max_blocks_per_seq=None, host_slots=0, evict=EVICT_LIFO):
         self.pool = paged.FreeBlockStack(num_blocks)
         self.host = paged.FreeBlockStack(host_slots) if host_slots > 0 else None
         self.swapped = []
@@ -108,7 +125,10 @@ class Scheduler:
         self.soft = soft
         self.mbps = max_blocks_per_seq
         self.waiting = []
-        self.running = []
+        self.running = []               # in the order they entered the running set
+        if evict not in (EVICT_LIFO, EVICT_FIFO, EVICT_LRU):
+            raise ValueError("unknown eviction policy")
+        self.evict = evict
 
     def submit(self, rid, prompt, max_new):
         """Queue a request; refused (ValueError) if its full length could never
@@ -135,6 +155,10 @@ class Scheduler:
             return SOFT
         return PROCEED
 
+    def _victim_index(self):
+        """Index in self.running (entry order) of the request to evict."""
+        return len(self.running) - 1 if self.evict == EVICT_LIFO else 0
+
     def _release(self, r):
         self.pool.free(r.blocks)
         r.blocks = []
@@ -150,7 +174,7 @@ class Scheduler:
             else:
                 keep.append(r)
         self.running = keep
-        # (2) decode growth, preempting the latest admitted on exhaustion
+        # (2) decode growth, evicting a running request on exhaustion
         preempted = []
         swapped_out, swap_out = [], []
         i = 0
@@ -165,7 +189,8 @@ class Scheduler:
                 r.blocks += ids
                 i += 1
                 continue
-            victim = self.running.pop()          # most recently admitted
+            vi = self._victim_index()
+            victim = self.running.pop(vi)
             if self.host is not None and self.host.num_free() >= len(victim.blocks):
                 slots = self.host.alloc(len(victim.blocks))
                 swap_out += list(zip(victim.blocks, slots))
@@ -173,6 +198,8 @@ class Scheduler:
                 victim.host_slots = slots
                 self.swapped.append(victim)
                 swapped_out.append(victim.rid)
+                if vi < i:
+                    i -= 1
                 continue
             self._release(victim)
             victim.prompt = victim.prompt + victim.generated
@@ -181,7 +208,10 @@ class Scheduler:
             victim.ctx = 0
             self.waiting.insert(0, victim)
             preempted.append(victim.rid)
-            # i unchanged: if the victim was r itself, the loop ends
+            # i unchanged: if the victim was r itself the loop ends; if it
+            # stood before r, r moved down one place
+            if vi < i:
+                i -= 1
         # (3') swap-ins first, oldest swapped first, regardless of the brakes
         swap_in = []
         while self.swapped and len(self.running) < self.max_running:

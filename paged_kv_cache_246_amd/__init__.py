@@ -28,6 +28,10 @@ MI_FAULT_BLOCK_ID = 1
 MI_FAULT_CONTEXT_LEN = 2
 MI_POOL_HOST_ONLY = 1
 MI_POOL_KV_FP8 = 2
+MI_POOL_SWAP_STAGING = 4
+MI_EVICT_LIFO = 0
+MI_EVICT_FIFO = 1
+MI_EVICT_LRU = 2
 
 _c = ctypes
 _vp = _c.c_void_p
@@ -76,6 +80,7 @@ SIGNATURES = {
     "mi_sched_num_running": (_i32, [_vp]),
     "mi_sched_step": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mi_sched_set_swap_space": (_c.c_int, [_vp, _i32]),
+    "mi_sched_set_eviction": (_c.c_int, [_vp, _i32]),
     "mi_sched_num_swapped": (_i32, [_vp]),
     "mi_kv_swap_out": (_c.c_int, [_vp, _vp, _vp, _i32, _vp, _i32, _vp]),
     "mi_kv_swap_in": (_c.c_int, [_vp, _vp, _vp, _i32, _vp, _i32, _vp]),
@@ -347,7 +352,7 @@ class Scheduler:
     """Host wrapper of mi_sched_*: plans come back as numpy arrays."""
 
     def __init__(self, pool, max_blocks_per_seq, max_running, hard=0.10, soft=0.30,
-                 host_slots=0):
+                 host_slots=0, evict=MI_EVICT_LIFO):
         import numpy as np
         self._np = np
         h = _vp()
@@ -367,6 +372,8 @@ class Scheduler:
         self.si = np.zeros((R * max_blocks_per_seq, 2), np.int32)
         if host_slots:
             _check("mi_sched_set_swap_space", lib().mi_sched_set_swap_space(self.h, host_slots))
+        if evict != MI_EVICT_LIFO:
+            _check("mi_sched_set_eviction", lib().mi_sched_set_eviction(self.h, evict))
 
     def submit(self, rid, prompt, max_new):
         return _check("mi_sched_submit", lib().mi_sched_submit(self.h, rid, prompt, max_new))

@@ -18,7 +18,7 @@ struct mi_kv_pool_s {
     void* k = nullptr;               // device [N, Hkv, bs, D]: bf16 bits, or E4M3 codes
     void* v = nullptr;
     float* scales = nullptr;         // device [2 * Hkv] (8-bit pools): K scales, then V scales
-    void* stage = nullptr;           // device staging of scattered swaps (allocated on first use)
+    void* stage = nullptr;           // device staging of scattered swaps (MI_POOL_SWAP_STAGING)
     size_t stage_blocks = 0;         // blocks of K (and again of V) the staging holds
     bool owns_cache = false;
     uint32_t* err = nullptr;         // device words: [0] error (MI_FAULT_* bits), [1] prefill redo
@@ -30,6 +30,7 @@ struct mi_kv_pool_s {
 namespace mikv {
 
 constexpr int kBlockSize = 16;
+constexpr size_t kSwapStageBytes = size_t{64} << 20;   // swap staging per cache (K, and again V)
 constexpr int kPrefillRedoWord = 1;        // index of the prefill redo word in the pool's device words
 
 // RoPE inverse frequencies theta^(-2i/D), i < D/2, computed on the host in

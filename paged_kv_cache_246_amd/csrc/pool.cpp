@@ -9,6 +9,7 @@
 // MI_ERR_NO_FREE_BLOCKS instead.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <new>
 #include <vector>
@@ -37,7 +38,8 @@ extern "C" int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t bl
     *out = nullptr;
     if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
         return MI_ERR_INVALID_ARG;
-    if (flags & ~static_cast<uint32_t>(MI_POOL_HOST_ONLY | MI_POOL_KV_FP8)) return MI_ERR_INVALID_ARG;
+    if (flags & ~static_cast<uint32_t>(MI_POOL_HOST_ONLY | MI_POOL_KV_FP8 | MI_POOL_SWAP_STAGING))
+        return MI_ERR_INVALID_ARG;
     if ((k_cache == nullptr) != (v_cache == nullptr)) return MI_ERR_INVALID_ARG;
     if ((flags & MI_POOL_HOST_ONLY) && k_cache) return MI_ERR_INVALID_ARG;
     if (block_size != mikv::kBlockSize) return MI_ERR_UNSUPPORTED;
@@ -84,6 +86,12 @@ extern "C" int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t bl
         bool ok = hipMalloc(reinterpret_cast<void**>(&p->err), 256) == hipSuccess &&
                   hipMemset(p->err, 0, 256) == hipSuccess &&
                   mikv::setup_noalloc_scratch() == MI_OK;
+        if (ok && (flags & MI_POOL_SWAP_STAGING)) {
+            const size_t blk = bytes / static_cast<size_t>(num_blocks);
+            p->stage_blocks = std::min(mikv::kSwapStageBytes / blk, static_cast<size_t>(num_blocks));
+            ok = hipMalloc(&p->stage, 2 * p->stage_blocks * blk) == hipSuccess;
+            if (!ok) p->stage = nullptr;
+        }
         if (ok && mikv::pool_fp8(p)) {
             const std::vector<float> one(2 * static_cast<size_t>(num_kv_heads), 1.0f);
             ok = hipMalloc(reinterpret_cast<void**>(&p->scales), one.size() * sizeof(float)) == hipSuccess &&
@@ -93,6 +101,7 @@ extern "C" int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t bl
         if (!ok || hipDeviceSynchronize() != hipSuccess) {
             if (p->err) (void)hipFree(p->err);
             if (p->scales) (void)hipFree(p->scales);
+            if (p->stage) (void)hipFree(p->stage);
             if (p->owns_cache) {
                 (void)hipFree(p->k);
                 (void)hipFree(p->v);

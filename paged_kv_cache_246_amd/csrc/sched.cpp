@@ -29,14 +29,20 @@
 // KV blocks move to CPU memory and come back when needed, under an eviction
 // policy). With a host swap space, a preemption victim whose blocks fit the
 // free host slots is swapped out instead of recomputed (its (device block,
-// host slot) pairs are emitted, it keeps its context); the victim is the most
-// recently admitted running request. Swapped requests come back first, in
+// host slot) pairs are emitted, it keeps its context). The victim, for
+// swap-out and recompute alike, is picked by the eviction policy: LIFO (the
+// default) the most recently admitted running request, FIFO the one that
+// entered the running set first (admitted or swapped back in earliest); LRU
+// picks the FIFO victim, since every running request's KV is read at every
+// step and the longest-held one is the least recently used in a tie. The
+// running list is kept in entry order. Swapped requests come back first, in
 // swap order and regardless of the brakes, each with its blocks plus the
 // block its decode needs ((host slot, device block) pairs emitted), and
 // decode in the same step; while any request is swapped out nothing new is
 // admitted. The caller runs the swap-outs, then the swap-ins, before the
 // step's kernels (mi_kv_swap_out / mi_kv_swap_in).
 #include <algorithm>
+#include <cstddef>
 #include <deque>
 #include <new>
 #include <vector>
@@ -64,6 +70,7 @@ struct mi_sched_s {
     // host swap space: LIFO stack of free slots (first pop returns slot 0)
     int32_t host_slots = 0;
     std::vector<int32_t> host_free;
+    int32_t evict = MI_EVICT_LIFO;
 };
 
 namespace {
@@ -143,6 +150,13 @@ extern "C" int mi_sched_set_swap_space(mi_sched_t s, int32_t host_slots) {
     return MI_OK;
 }
 
+extern "C" int mi_sched_set_eviction(mi_sched_t s, int32_t policy) {
+    if (!s || (policy != MI_EVICT_LIFO && policy != MI_EVICT_FIFO && policy != MI_EVICT_LRU))
+        return MI_ERR_INVALID_ARG;
+    s->evict = policy;
+    return MI_OK;
+}
+
 extern "C" int32_t mi_sched_num_swapped(mi_sched_t s) {
     return s ? static_cast<int32_t>(s->swapped.size()) : MI_ERR_INVALID_ARG;
 }
@@ -176,7 +190,7 @@ extern "C" int mi_sched_step(mi_sched_t s, mi_sched_counts* counts, int64_t* seq
             }
         }
         s->running.swap(keep);
-        // (2) decode growth with recompute preemption of the latest admitted
+        // (2) decode growth, evicting a running request when the pool is empty
         size_t i = 0;
         while (i < s->running.size()) {
             auto& r = s->running[i];
@@ -191,8 +205,10 @@ extern "C" int mi_sched_step(mi_sched_t s, mi_sched_counts* counts, int64_t* seq
                 ++i;
                 continue;
             }
-            mi_sched_s::Req victim = std::move(s->running.back());
-            s->running.pop_back();
+            const size_t vi = s->evict == MI_EVICT_LIFO ? s->running.size() - 1 : 0;
+            mi_sched_s::Req victim = std::move(s->running[vi]);
+            s->running.erase(s->running.begin() + static_cast<std::ptrdiff_t>(vi));
+            if (vi < i) --i;          // the request that needs a block moved down one place
             if (s->host_free.size() >= victim.blocks.size()) {
                 for (int32_t dev : victim.blocks) {
                     const int32_t slot = s->host_free.back();

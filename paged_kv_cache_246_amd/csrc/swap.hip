@@ -8,9 +8,11 @@
 // 32-64 KiB take on the link, so pairs are ordered by host slot and runs of
 // consecutive slots move in one transfer. When the device side of a run is
 // not consecutive too, the blocks are first packed (swap-out) or last
-// unpacked (swap-in) by a kernel through a device staging buffer, so every
-// run is a single transfer whatever the device ids. Ids and slots are
-// validated on the host before anything is queued.
+// unpacked (swap-in) by a kernel through the pool's device staging buffer
+// (allocated with the pool, MI_POOL_SWAP_STAGING), so every run is a single
+// transfer whatever the device ids; a pool without staging moves such a run
+// one block per transfer. Nothing here allocates device memory. Ids and
+// slots are validated on the host before anything is queued.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -22,7 +24,6 @@
 namespace {
 
 constexpr int kIdsPerLaunch = 256;
-constexpr size_t kStageBytes = size_t{64} << 20;   // per cache (K, and again V)
 
 struct IdBatch {
     int32_t ids[kIdsPerLaunch];
@@ -82,29 +83,17 @@ int swap_blocks(mi_kv_pool_t p, char* host_k, char* host_v, int32_t host_slots,
 
     // runs of consecutive host slots; a run whose device ids are consecutive
     // too goes straight between pool and host
-    size_t staged = 0;
     std::vector<std::pair<int32_t, int32_t>> runs;          // [begin, end) in `order`
     for (int32_t i = 0; i < n;) {
         int32_t j = i + 1;
         while (j < n && slot[order[j]] == slot[order[j - 1]] + 1) ++j;
         runs.emplace_back(i, j);
-        bool direct = true;
-        for (int32_t k = i + 1; k < j; ++k) direct &= dev[order[k]] == dev[order[k - 1]] + 1;
-        if (!direct) staged += static_cast<size_t>(j - i);
         i = j;
     }
     auto copy = [&](char* dk, char* dv, const char* sk, const char* sv, size_t bytes) {
         return hipMemcpyAsync(dk, sk, bytes, kind, st) == hipSuccess &&
                hipMemcpyAsync(dv, sv, bytes, kind, st) == hipSuccess;
     };
-    if (staged > 0 && !p->stage) {
-        const size_t want = std::min(kStageBytes / blk, static_cast<size_t>(p->num_blocks));
-        if (hipMalloc(&p->stage, 2 * want * blk) != hipSuccess) {
-            p->stage = nullptr;
-            return MI_ERR_OUT_OF_MEMORY;
-        }
-        p->stage_blocks = want;
-    }
     char* stage = static_cast<char*>(p->stage);
     const size_t half = p->stage_blocks * blk;
     for (const auto& run : runs) {
@@ -118,6 +107,16 @@ int swap_blocks(mi_kv_pool_t p, char* host_k, char* host_v, int32_t host_slots,
             const bool ok = out ? copy(host_k + h0, host_v + h0, pk + d0, pv + d0, bytes)
                                 : copy(pk + d0, pv + d0, host_k + h0, host_v + h0, bytes);
             if (!ok) return MI_ERR_HIP;
+            continue;
+        }
+        if (!stage) {        // no staging buffer: one transfer per block
+            for (int32_t k = run.first; k < run.second; ++k) {
+                const size_t d0 = static_cast<size_t>(dev[order[k]]) * blk;
+                const size_t hk = static_cast<size_t>(slot[order[k]]) * blk;
+                const bool ok = out ? copy(host_k + hk, host_v + hk, pk + d0, pv + d0, blk)
+                                    : copy(pk + d0, pv + d0, host_k + hk, host_v + hk, blk);
+                if (!ok) return MI_ERR_HIP;
+            }
             continue;
         }
         // through the staging buffer, a chunk at a time

@@ -20,8 +20,12 @@ def _need_gpu():
     mk.lib()
 
 
+@pytest.mark.parametrize("staging", [True, False], ids=["staged", "per_block"])
 @pytest.mark.parametrize("fmt", ["bf16", "fp8"])
-def test_swap_out_then_in_moves_blocks_bit_exactly(fmt):
+def test_swap_out_then_in_moves_blocks_bit_exactly(fmt, staging):
+    """Pairs in runs of consecutive slots over consecutive and over scattered
+    device blocks, on a pool with a staging buffer (scattered runs packed into
+    one transfer) and on one without (one transfer per block)."""
     N, Hkv, D, S = 48, 4, 128, 40
     rng = np.random.default_rng(5)
     if fmt == "bf16":
@@ -37,6 +41,8 @@ def test_swap_out_then_in_moves_blocks_bit_exactly(fmt):
         hk = torch.zeros((S, Hkv, 16, D), dtype=torch.uint8, pin_memory=True)
         flags = mk.MI_POOL_KV_FP8
     hv = torch.zeros_like(hk)
+    if staging:
+        flags |= mk.MI_POOL_SWAP_STAGING
     pool = mk.mi_kv_pool_init(N, 16, Hkv, D, kd, vd, flags=flags)
     try:
         # a run of consecutive pairs (merged into one transfer) and scattered ones
@@ -57,7 +63,8 @@ def test_swap_out_then_in_moves_blocks_bit_exactly(fmt):
             assert h == h2
             ek[d2], ev[d2] = kp[d], vp[d]
         assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
-        # consecutive slots holding scattered blocks: packed through the staging buffer
+        # consecutive slots holding scattered blocks (packed through the staging
+        # buffer when the pool has one)
         before_k = gk.copy()
         out2 = np.array([[9, 20], [2, 21], [30, 22], [17, 23], [44, 24]], np.int32)
         mk.mi_kv_swap_out(pool, hk, hv, S, out2)
@@ -85,10 +92,12 @@ def test_swap_out_then_in_moves_blocks_bit_exactly(fmt):
         mk.mi_kv_pool_destroy(pool)
 
 
-def test_planner_loop_with_kv_offload():
-    """Tight pool with a host swap space: requests are swapped out and back
-    while decoding; every step's outputs and the final cache match the oracle
-    executing the same plans (copies included)."""
+@pytest.mark.parametrize("evict", [mk.MI_EVICT_LIFO, mk.MI_EVICT_FIFO, mk.MI_EVICT_LRU],
+                         ids=["lifo", "fifo", "lru"])
+def test_planner_loop_with_kv_offload(evict):
+    """Tight pool with a host swap space, under each eviction policy: requests
+    are swapped out and back while decoding; every step's outputs and the
+    final cache match the oracle executing the same plans (copies included)."""
     Hq, Hkv, D, theta = 8, 2, 64, 1e4
     N, mbps, R, S = 14, 12, 4, 24
     rng = np.random.default_rng(78)
@@ -99,8 +108,8 @@ def test_planner_loop_with_kv_offload():
     kd, vd = bits_to_dev(kp), bits_to_dev(vp)
     hk = torch.zeros((S, Hkv, 16, D), dtype=torch.int16, pin_memory=True)
     hv = torch.zeros_like(hk)
-    pool = mk.mi_kv_pool_init(N, 16, Hkv, D, kd, vd)
-    s = mk.Scheduler(pool, mbps, R, host_slots=S)
+    pool = mk.mi_kv_pool_init(N, 16, Hkv, D, kd, vd, flags=mk.MI_POOL_SWAP_STAGING)
+    s = mk.Scheduler(pool, mbps, R, host_slots=S, evict=evict)
     reqs = [(0, 0, 40, 30), (0, 1, 70, 24), (1, 2, 17, 40), (2, 3, 100, 8), (3, 4, 5, 35),
             (6, 5, 33, 9)]
     pending = sorted(reqs)

@@ -90,11 +90,84 @@ def test_recompute_preemption_takes_the_latest_admitted():
     _tables_disjoint_and_complete(s)
 
 
+def test_fifo_recompute_preemption_takes_the_earliest_admitted():
+    # The same pool as above under FIFO eviction. Step 2: A (entered first)
+    # takes the last free block for position 48; B at ctx 64 needs a 5th: the
+    # pool is empty, so A is preempted (its 4 blocks return), and B retries
+    # and gets one of them.
+    s = sched.Scheduler(8, max_running=4, hard=0.0, soft=0.0, evict=sched.EVICT_FIFO)
+    s.submit(0, 48, 40)
+    s.submit(1, 64, 40)
+    s.step()
+    p = s.step()
+    assert p.preempted == [0] and [x[0] for x in p.decode] == [1]
+    assert p.decode[0][1] == 64 and len(p.decode[0][2]) == 5
+    assert s.waiting[0].rid == 0 and s.waiting[0].prompt == 49 and s.waiting[0].max_new == 39
+    assert s.pool.num_free() == 3
+    _tables_disjoint_and_complete(s)
+
+
+def test_fifo_swap_out_moves_the_earliest_admitted():
+    # Blocks come off the LIFO free stack 0, 1, 2, ...: A holds 0-2, B 3-6; at
+    # step 2 A takes 7 for position 48, B needs a 5th block: A (first in) goes
+    # to host slots 0-3 in block order; its blocks return in that order, so
+    # B's 5th block is 7 (the last one pushed).
+    s = sched.Scheduler(8, max_running=4, hard=0.0, soft=0.0, host_slots=16,
+                        evict=sched.EVICT_FIFO)
+    s.submit(0, 48, 6)
+    s.submit(1, 64, 40)
+    s.step()
+    p = s.step()
+    assert p.swapped_out == [0] and p.preempted == []
+    assert p.swap_out == [(0, 0), (1, 1), (2, 2), (7, 3)]
+    assert [(x[0], x[1], x[2]) for x in p.decode] == [(1, 64, [3, 4, 5, 6, 7])]
+    # A (ctx 48, 4 host blocks) needs 4 device blocks to come back: with 3
+    # free it waits while B decodes; B retires after 39 decodes at 7 blocks
+    # (positions up to 103), then A returns in the same step with its old context
+    while True:
+        p = s.step()
+        if p.swap_in:
+            break
+        assert [x[0] for x in p.decode] == [1]
+    assert p.finished == [1] and [x[0] for x in p.swap_in] == [0, 1, 2, 3]
+    assert [(x[0], x[1]) for x in p.decode] == [(0, 48)]
+
+
+def test_lru_gives_the_fifo_plans():
+    """Every running request is read at every step, so the least recently used
+    one is the one holding its blocks longest: the FIFO victim. Same random
+    streams (with host swap space) under both names, plan for plan."""
+    for seed in range(4):
+        plans = []
+        for evict in (sched.EVICT_FIFO, sched.EVICT_LRU):
+            rng = np.random.default_rng(90 + seed)
+            N = int(rng.integers(16, 60))
+            s = sched.Scheduler(N, max_running=int(rng.integers(2, 6)), hard=0.02, soft=0.05,
+                                host_slots=int(rng.integers(0, 40)), evict=evict)
+            out = []
+            rid = 0
+            for t in range(1500):
+                if rid < 30 and rng.random() < 0.3:
+                    prompt, new = int(rng.integers(1, 200)), int(rng.integers(1, 80))
+                    if paged.blocks_needed(prompt + new, 16) <= N:
+                        s.submit(rid, prompt, new)
+                        rid += 1
+                out.append(s.step())
+            plans.append(out)
+        assert plans[0] == plans[1]
+
+
+def test_unknown_eviction_policy_is_refused():
+    with pytest.raises(ValueError):
+        sched.Scheduler(8, evict=3)
+
+
+@pytest.mark.parametrize("evict", [sched.EVICT_LIFO, sched.EVICT_FIFO])
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
-def test_random_streams_keep_invariants_and_finish(seed):
+def test_random_streams_keep_invariants_and_finish(seed, evict):
     rng = np.random.default_rng(seed)
     N = int(rng.integers(40, 200))
-    s = sched.Scheduler(N, max_running=int(rng.integers(2, 9)))
+    s = sched.Scheduler(N, max_running=int(rng.integers(2, 9)), evict=evict)
     produced = {}
     want = {}
     rid = 0
@@ -149,15 +222,16 @@ def test_small_host_space_falls_back_to_recompute():
     assert p.swapped_out == [] and p.preempted == [1]
 
 
+@pytest.mark.parametrize("evict", [sched.EVICT_LIFO, sched.EVICT_FIFO])
 @pytest.mark.parametrize("seed", [0, 1, 2])
-def test_swap_streams_preserve_every_block_content(seed):
+def test_swap_streams_preserve_every_block_content(seed, evict):
     """Tag every logical block (request, index) as it is written, move tags with
     the plan's swap-out / swap-in pairs, and check that every running request
     reads its own tags in order after every step."""
     rng = np.random.default_rng(50 + seed)
     N = int(rng.integers(16, 60))
     s = sched.Scheduler(N, max_running=int(rng.integers(2, 6)), hard=0.0, soft=0.0,
-                        host_slots=int(rng.integers(8, 40)))
+                        host_slots=int(rng.integers(8, 40)), evict=evict)
     dev, host = {}, {}
     want, produced = {}, {}
     rid = 0

@@ -26,12 +26,13 @@ def _compare(plan, ref, mbps):
         assert np.array_equal(plan["block_table"][i], want)
 
 
-def _run(N, mbps, max_running, requests, hard=0.10, soft=0.30, max_steps=5000, host_slots=0):
+def _run(N, mbps, max_running, requests, hard=0.10, soft=0.30, max_steps=5000, host_slots=0,
+         evict=sched.EVICT_LIFO):
     """requests: list of (arrival_step, rid, prompt, max_new)."""
     pool = mk.mi_kv_pool_init(N, 16, 2, 64, flags=mk.MI_POOL_HOST_ONLY)
-    s = mk.Scheduler(pool, mbps, max_running, hard, soft, host_slots=host_slots)
+    s = mk.Scheduler(pool, mbps, max_running, hard, soft, host_slots=host_slots, evict=evict)
     ref = sched.Scheduler(N, max_running=max_running, hard=hard, soft=soft, max_blocks_per_seq=mbps,
-                          host_slots=host_slots)
+                          host_slots=host_slots, evict=evict)
     try:
         pending = sorted(requests)
         brakes = set()
@@ -63,8 +64,9 @@ def test_hand_made_stream_hits_every_brake():
     assert mk.MI_BRAKE_SOFT in brakes
 
 
+@pytest.mark.parametrize("evict", [mk.MI_EVICT_LIFO, mk.MI_EVICT_FIFO])
 @pytest.mark.parametrize("seed", range(6))
-def test_random_streams_match_the_oracle(seed):
+def test_random_streams_match_the_oracle(seed, evict):
     rng = np.random.default_rng(100 + seed)
     N = int(rng.integers(30, 300))
     mbps = int(rng.integers(8, 40))
@@ -76,7 +78,7 @@ def test_random_streams_match_the_oracle(seed):
             continue
         reqs.append((int(rng.integers(0, 200)), rid, prompt, new))
     _run(N, mbps, int(rng.integers(1, 12)), reqs, hard=float(rng.choice([0.0, 0.1, 0.2])),
-         soft=float(rng.choice([0.0, 0.3, 0.5])))
+         soft=float(rng.choice([0.0, 0.3, 0.5])), evict=evict)
 
 
 def test_submit_refuses_requests_that_can_never_fit():
@@ -98,8 +100,9 @@ def test_submit_refuses_requests_that_can_never_fit():
         mk.mi_kv_pool_destroy(pool)
 
 
+@pytest.mark.parametrize("evict", [mk.MI_EVICT_LIFO, mk.MI_EVICT_FIFO, mk.MI_EVICT_LRU])
 @pytest.mark.parametrize("seed", range(6))
-def test_random_swap_streams_match_the_oracle(seed):
+def test_random_swap_streams_match_the_oracle(seed, evict):
     rng = np.random.default_rng(200 + seed)
     N = int(rng.integers(16, 80))
     mbps = int(rng.integers(6, 30))
@@ -111,4 +114,15 @@ def test_random_swap_streams_match_the_oracle(seed):
             continue
         reqs.append((int(rng.integers(0, 100)), rid, prompt, new))
     _run(N, mbps, int(rng.integers(2, 8)), reqs, hard=float(rng.choice([0.0, 0.1])),
-         soft=float(rng.choice([0.0, 0.3])), host_slots=int(rng.integers(0, 3 * N)))
+         soft=float(rng.choice([0.0, 0.3])), host_slots=int(rng.integers(0, 3 * N)), evict=evict)
+
+
+def test_eviction_policy_argument():
+    pool = mk.mi_kv_pool_init(10, 16, 2, 64, flags=mk.MI_POOL_HOST_ONLY)
+    s = mk.Scheduler(pool, 8, 4)
+    try:
+        assert mk.lib().mi_sched_set_eviction(s.h, 3) == mk.MI_ERR_INVALID_ARG
+        assert mk.lib().mi_sched_set_eviction(s.h, mk.MI_EVICT_FIFO) == mk.MI_OK
+    finally:
+        s.close()
+        mk.mi_kv_pool_destroy(pool)
