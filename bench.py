@@ -756,6 +756,8 @@ def main():
                     help="skip the planner-driven serving run with KV offload")
     ap.add_argument("--layer-only", action="store_true",
                     help="time only the full-layer step (for its kernel profile)")
+    ap.add_argument("--small-only", action="store_true",
+                    help="time only the smaller decode workloads (for their kernel profile)")
     ap.add_argument("--cpu-budget", type=float, default=8.0,
                     help="seconds of oracle time on the long-context workload per thread count")
     ap.add_argument("--no-flushed", action="store_true",
@@ -796,6 +798,13 @@ def main():
         print(json.dumps({"metric": "layer-step tokens/s", "value": lay["tokens_per_s"],
                           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
                           "warmup": args.warmup, "layer_step": lay}), flush=True)
+        return
+
+    if args.small_only:
+        print(json.dumps({"metric": "decode step time, smaller workloads", "steps": args.steps,
+                          "warmup": args.warmup,
+                          "other_workloads": run_small_workloads(args, torch, mk, workloads)}),
+              flush=True)
         return
 
     r = run_attention_bench(args, torch, mk, workloads)

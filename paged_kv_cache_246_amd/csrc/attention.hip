@@ -413,9 +413,12 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][MfmaTile<D, F
 // scale is positive) and the scale folds into the exponent's FMA; without
 // tail nothing is masked -- a dead column there has a zero query, finite
 // scores and an output that is never stored.
-template <int NPV, bool RAW = false, bool FIXED = false>
+// With PLO the rounding remainders of the weights, bf16(p - bf16(p)), go to
+// *plo (the weighted V sum then takes p at about 16 significant bits).
+template <int NPV, bool RAW = false, bool FIXED = false, bool PLO = false>
 __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_ok, int q4, int qlim,
-                                                 bool tail, MfmaSoftmax& sm, f32x4_t (&o)[NPV]) {
+                                                 bool tail, MfmaSoftmax& sm, f32x4_t (&o)[NPV],
+                                                 bf16x4_t* plo = nullptr) {
     static_assert(!FIXED || RAW, "the fixed-reference form works on raw scores");
     float sc[4];
 #pragma unroll
@@ -465,8 +468,14 @@ __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_
         p[i] = __builtin_amdgcn_exp2f(RAW ? fmaf(sc[i], sl2, -sm.m) : sc[i] - sm.m);
         sm.l += p[i];
     }
-    return bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
-                    static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+    const bf16x4_t hi = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                         static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+    if constexpr (PLO)
+        *plo = bf16x4_t{static_cast<__bf16>(p[0] - static_cast<float>(hi[0])),
+                        static_cast<__bf16>(p[1] - static_cast<float>(hi[1])),
+                        static_cast<__bf16>(p[2] - static_cast<float>(hi[2])),
+                        static_cast<__bf16>(p[3] - static_cast<float>(hi[3]))};
+    return hi;
 }
 
 // One 16-token tile for QB column blocks of 16 (query heads in decode, QB = 1;
@@ -475,10 +484,14 @@ __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_
 // with tail, key row t counts for it only if t < qlim[c] (the rows written so
 // far in decode, the causal limit in prefill), and V rows >= valid_rows are
 // zeroed.
-template <int D, int FMT, int QB, bool RAW = false, bool FIXED = false>
+// PAIR: the query operand is a bf16 pair, qb the rounded value and ql the
+// rounding remainder, and so are the softmax weights (about 16 significant
+// bits each); both contractions take one MFMA per half.
+template <int D, int FMT, int QB, bool RAW = false, bool FIXED = false, bool PAIR = false>
 __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>::NKL],
                                              const uint32_t (&vr)[4][MfmaTile<D, FMT>::VW],
                                              const uint4 (&qb)[QB][MfmaTile<D, FMT>::NQK],
+                                             const uint4 (&ql)[PAIR ? QB : 1][MfmaTile<D, FMT>::NQK],
                                              float sl2, const bool (&col_ok)[QB], int q4,
                                              const int (&qlim)[QB], int valid_rows, bool tail,
                                              MfmaSoftmax (&sm)[QB],
@@ -488,31 +501,42 @@ __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>:
 #pragma unroll
     for (int j = 0; j < TL::NQK; ++j) a[j] = k_operand<D, FMT>(kr, j);
     bf16x4_t pb[QB];
+    bf16x4_t pl[PAIR ? QB : 1];
 #pragma unroll
     for (int c = 0; c < QB; ++c) {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < TL::NQK; ++j)
+        for (int j = 0; j < TL::NQK; ++j) {
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
                                                         __builtin_bit_cast(bf16x8_t, qb[c][j]), s, 0, 0, 0);
-        pb[c] = softmax_step<TL::NPV, RAW, FIXED>(s, sl2, col_ok[c], q4, qlim[c], tail, sm[c], o[c]);
+            if constexpr (PAIR)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
+                                                            __builtin_bit_cast(bf16x8_t, ql[c][j]), s, 0, 0, 0);
+        }
+        pb[c] = softmax_step<TL::NPV, RAW, FIXED, PAIR>(s, sl2, col_ok[c], q4, qlim[c], tail, sm[c], o[c],
+                                                        PAIR ? &pl[c] : nullptr);
     }
     s16x4_t vt[TL::NPV];
     v_operands<D, FMT>(vr, q4, valid_rows, tail, vt);
 #pragma unroll
     for (int c = 0; c < QB; ++c)
 #pragma unroll
-        for (int jj = 0; jj < TL::NPV; ++jj)
+        for (int jj = 0; jj < TL::NPV; ++jj) {
             o[c][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
                 vt[jj], __builtin_bit_cast(s16x4_t, pb[c]), o[c][jj], 0, 0, 0);
+            if constexpr (PAIR)
+                o[c][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    vt[jj], __builtin_bit_cast(s16x4_t, pl[c]), o[c][jj], 0, 0, 0);
+        }
 }
 
 // Per-wave state of the QB column blocks (RAW: the prefill softmax form;
-// FIXED: its fixed-reference variant).
-template <int D, int FMT, int QB, bool RAW = false, bool FIXED = false>
+// FIXED: its fixed-reference variant; PAIR: query and weights as bf16 pairs).
+template <int D, int FMT, int QB, bool RAW = false, bool FIXED = false, bool PAIR = false>
 struct MfmaCols {
     using TL = MfmaTile<D, FMT>;
     uint4 qb[QB][TL::NQK];
+    uint4 ql[PAIR ? QB : 1][TL::NQK];
     bool col_ok[QB];
     MfmaSoftmax sm[QB];
     f32x4_t o[QB][TL::NPV];
@@ -521,7 +545,8 @@ struct MfmaCols {
 
     __device__ __forceinline__ void consume(const uint4 (&kr)[TL::NKL], const uint32_t (&vr)[4][TL::VW],
                                             const int (&qlim)[QB], int valid_rows, bool tail) {
-        mfma_consume<D, FMT, QB, RAW, FIXED>(kr, vr, qb, sl2, col_ok, q4, qlim, valid_rows, tail, sm, o);
+        mfma_consume<D, FMT, QB, RAW, FIXED, PAIR>(kr, vr, qb, ql, sl2, col_ok, q4, qlim, valid_rows, tail,
+                                                   sm, o);
     }
     // unmasked tile, or a tile whose rows >= valid_rows are masked for every column
     __device__ __forceinline__ void consume_rows(const uint4 (&kr)[TL::NKL], const uint32_t (&vr)[4][TL::VW],
@@ -729,19 +754,30 @@ __device__ __forceinline__ void step_rotate_q(const uint4 (&x)[NQ], const uint4 
     }
 }
 
+// Inputs and outputs of the attention inside the decoder layer (LAYER
+// kernels): the query arrives as a bf16 pair (q_rot, the rounded value, and
+// q_lo, the remainder), the softmax weights enter the V product as bf16
+// pairs too, and the output is stored in float32 for the o projection, which
+// takes it as a bf16 pair.
+struct LayerIO {
+    const uint16_t* q_lo;      // [B, Hq, D] bf16
+    float* out;                // [B, Hq, D] float32
+};
+
 // The cache pointers are read-only (and restrict) except in STEP kernels,
 // which write the new token's slot.
 template <bool STEP> struct CachePtr { typedef const uint8_t* __restrict__ type; };
 template <> struct CachePtr<true> { typedef uint8_t* type; };
 
-template <int D, int G, int FMT, int PF, bool STEP>
+template <int D, int G, int FMT, int PF, bool STEP, bool LAYER = false>
 __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
     const uint16_t* __restrict__ q_rot, typename CachePtr<STEP>::type kc,
     typename CachePtr<STEP>::type vc, const int32_t* __restrict__ table, int32_t mbps,
     const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t hkv, int32_t num_blocks,
     int32_t max_ctx, int32_t min_tiles, float scale_log2, const float* __restrict__ kv_scales,
     float* __restrict__ part_acc, float2* __restrict__ part_ml, uint16_t* __restrict__ out,
-    uint32_t* __restrict__ err, StepToken tok) {
+    uint32_t* __restrict__ err, StepToken tok, LayerIO lio) {
+    static_assert(!(STEP && LAYER), "the layer path runs the two-call form");
     using TL = MfmaTile<D, FMT>;
     constexpr int NPV = TL::NPV;
     constexpr size_t TILE = static_cast<size_t>(BS) * TL::ROW;   // bytes per (block, head) tile
@@ -779,12 +815,15 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
 
         // Q^T operand: head n, the lane's 8 dims of each 32-dim slice (the
         // same dims its K row supplies)
-        MfmaCols<D, FMT, 1> cols;
-        auto load_q = [&](const uint16_t* qh) {
+        MfmaCols<D, FMT, 1, false, false, LAYER> cols;
+        auto load_q = [&](size_t qoff) {
 #pragma unroll
             for (int j = 0; j < TL::NQK; ++j) {
                 const int d0 = FMT == kFmtBf16 ? 32 * j + 8 * q4 : 64 * (j / 2) + 16 * q4 + 8 * (j & 1);
-                cols.qb[0][j] = head_ok ? *reinterpret_cast<const uint4*>(qh + d0) : make_uint4(0, 0, 0, 0);
+                cols.qb[0][j] = head_ok ? *reinterpret_cast<const uint4*>(q_rot + qoff + d0) : make_uint4(0, 0, 0, 0);
+                if constexpr (LAYER)
+                    cols.ql[0][j] = head_ok ? *reinterpret_cast<const uint4*>(lio.q_lo + qoff + d0)
+                                            : make_uint4(0, 0, 0, 0);
             }
         };
         // block ids of the piece's first chunk (lane i: its i-th tile)
@@ -813,7 +852,7 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
             if (t1 == nt) __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         } else {
-            load_q(q_rot + (static_cast<size_t>(b) * hkv * G + g * G + (head_ok ? n : 0)) * D);
+            load_q((static_cast<size_t>(b) * hkv * G + g * G + (head_ok ? n : 0)) * D);
         }
         cols.sl2 = scale_log2;
         float vscale = 1.f;
@@ -870,7 +909,17 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
         const size_t slot = 2 * static_cast<size_t>(w) + (first_piece ? 0 : 1);
         if (head_ok) {
             const int dbase = NPV * 4 * q4;     // first of the lane's D/4 dims
-            if (whole) {
+            if (whole && LAYER) {
+                const float inv = vscale / lt;
+                float* of = lio.out + (static_cast<size_t>(b) * hkv * G + g * G + n) * D + dbase;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int e = 0; e < NPV / 4; ++e)
+                        reinterpret_cast<float4*>(of + NPV * r)[e] =
+                            make_float4(o[4 * e][r] * inv, o[4 * e + 1][r] * inv,
+                                        o[4 * e + 2][r] * inv, o[4 * e + 3][r] * inv);
+            } else if (whole) {
                 const float inv = vscale / lt;
                 uint16_t* oh = out + (static_cast<size_t>(b) * hkv * G + g * G + n) * D + dbase;
 #pragma unroll
@@ -1075,11 +1124,14 @@ __global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1)
 // rescaling; the NCG groups are then merged in order. One memory round trip
 // for the partition, one per four pieces; a single rounding to bf16.
 // Sequences with an out-of-range length (no tiles) get NaN outputs.
-template <int D, int G>
+// F32OUT (the decoder layer): the merged output is stored in float32 to
+// out_f32 instead of bf16.
+template <int D, int G, bool F32OUT = false>
 __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
     const float* __restrict__ part_acc, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ ctx_lens, int32_t batch, int32_t mbps, int32_t hkv,
-    int32_t max_ctx, int32_t grid_waves, int32_t min_tiles, uint16_t* __restrict__ out) {
+    int32_t max_ctx, int32_t grid_waves, int32_t min_tiles, uint16_t* __restrict__ out,
+    float* __restrict__ out_f32) {
     constexpr int NCG = 256 / D;        // piece groups
     __shared__ int TP[kMaxBatch + 1];
     __shared__ float sm[NCG][D], sl[NCG][D], sa[NCG][D];
@@ -1088,7 +1140,8 @@ __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
     const int g = hq_idx / G;
     const int h = hq_idx - g * G;
     const int t = threadIdx.x;
-    uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + hq_idx) * D;
+    const size_t orow = (static_cast<size_t>(b) * hkv * G + hq_idx) * D;
+    uint16_t* o = F32OUT ? nullptr : out + orow;
 
     if (t < 64) {
         bool bad;
@@ -1098,7 +1151,10 @@ __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
     const int T = TP[batch];
     const int nt = (TP[b + 1] - TP[b]) / hkv;
     if (nt == 0) {                                  // length out of range
-        if (t < D) o[t] = 0x7fc0;
+        if (t < D) {
+            if constexpr (F32OUT) out_f32[orow + t] = __builtin_nanf("");
+            else o[t] = 0x7fc0;
+        }
         return;
     }
     const int W = active_waves(T, grid_waves, min_tiles);
@@ -1153,7 +1209,8 @@ __global__ __launch_bounds__(256) void paged_attn_combine_kernel(
             lt = fmaf(sl[c2][t], f, lt);
             at = fmaf(sa[c2][t], f, at);
         }
-        o[t] = f32_to_bf16_rne(at / lt);
+        if constexpr (F32OUT) out_f32[orow + t] = at / lt;
+        else o[t] = f32_to_bf16_rne(at / lt);
     }
 }
 
@@ -1258,47 +1315,51 @@ int resident_wave_bound() {
     return cached[dev];
 }
 
-template <int D, int G, bool STEP>
+template <int D, int G, bool STEP, bool LAYER>
 void launch_attn_kernel(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                         const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                         float scale_log2, int32_t max_ctx, int32_t min_tiles, float* part_acc,
-                        float2* part_ml, const StepToken& tok, hipStream_t st) {
+                        float2* part_ml, const StepToken& tok, const LayerIO& lio, hipStream_t st) {
     typedef typename CachePtr<STEP>::type CP;
     const int hkv = p->num_kv_heads;
-    auto kern = mikv::pool_fp8(p) ? paged_attn_mfma_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, STEP>
-                                  : paged_attn_mfma_kernel<D, G, kFmtBf16, kAttnPrefetch, STEP>;
+    auto kern = mikv::pool_fp8(p) ? paged_attn_mfma_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, STEP, LAYER>
+                                  : paged_attn_mfma_kernel<D, G, kFmtBf16, kAttnPrefetch, STEP, LAYER>;
     const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, attention_waves(kern));
     hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot, static_cast<CP>(p->k),
                        static_cast<CP>(p->v), table, mbps, ctx, batch, hkv, p->num_blocks, max_ctx,
                        min_tiles, scale_log2, static_cast<const float*>(p->scales), part_acc, part_ml,
-                       out, p->err, tok);
-    hipLaunchKernelGGL((paged_attn_combine_kernel<D, G>), dim3(hkv * G, batch), dim3(256), 0, st,
-                       part_acc, part_ml, ctx, batch, mbps, hkv, max_ctx, waves, min_tiles, out);
+                       out, p->err, tok, lio);
+    hipLaunchKernelGGL((paged_attn_combine_kernel<D, G, LAYER>), dim3(hkv * G, batch), dim3(256), 0, st,
+                       part_acc, part_ml, ctx, batch, mbps, hkv, max_ctx, waves, min_tiles, out, lio.out);
 }
 
-// tok: NULL for the attention call, else the decode step's new token.
+// tok: NULL for the attention call, else the decode step's new token; lio:
+// non-NULL for the decoder layer's attention.
 template <int D, int G>
 void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                  const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                  float scale_log2, int32_t max_ctx, int32_t min_tiles, float* part_acc,
-                 float2* part_ml, const StepToken* tok, hipStream_t st) {
+                 float2* part_ml, const StepToken* tok, const LayerIO* lio, hipStream_t st) {
     if (tok)
-        launch_attn_kernel<D, G, true>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                       min_tiles, part_acc, part_ml, *tok, st);
+        launch_attn_kernel<D, G, true, false>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
+                                              min_tiles, part_acc, part_ml, *tok, LayerIO{}, st);
+    else if (lio)
+        launch_attn_kernel<D, G, false, true>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
+                                              min_tiles, part_acc, part_ml, StepToken{}, *lio, st);
     else
-        launch_attn_kernel<D, G, false>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                        min_tiles, part_acc, part_ml, StepToken{}, st);
+        launch_attn_kernel<D, G, false, false>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
+                                               min_tiles, part_acc, part_ml, StepToken{}, LayerIO{}, st);
 }
 
 template <int D>
 int dispatch_group(int G, const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                    const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                    float scale_log2, int32_t max_ctx, int32_t min_tiles, float* pa, float2* pm,
-                   const StepToken* tok, hipStream_t st) {
+                   const StepToken* tok, const LayerIO* lio, hipStream_t st) {
 #define MIKV_G(GG)                                                                             \
     case GG:                                                                                   \
         launch_attn<D, GG>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,        \
-                           min_tiles, pa, pm, tok, st);                                        \
+                           min_tiles, pa, pm, tok, lio, st);                                   \
         return MI_OK;
     switch (G) {
         MIKV_G(1)
@@ -1467,7 +1528,7 @@ namespace {
 int launch_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, const int32_t* table,
                   int32_t mbps, const int32_t* ctx, int32_t batch, int32_t hq, float scale,
                   int32_t max_ctx, int32_t split_tokens, void* ws, const StepToken* tok,
-                  void* stream, int ws_waves = 0) {
+                  void* stream, int ws_waves = 0, const LayerIO* lio = nullptr) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int G = hq / p->num_kv_heads;
     const int min_tiles = split_tokens / BS;
@@ -1482,10 +1543,10 @@ int launch_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, c
     int rc;
     if (p->head_dim == 128)
         rc = dispatch_group<128>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                 min_tiles, pa, pm, tok, st);
+                                 min_tiles, pa, pm, tok, lio, st);
     else
         rc = dispatch_group<64>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                min_tiles, pa, pm, tok, st);
+                                min_tiles, pa, pm, tok, lio, st);
     if (rc != MI_OK) return rc;
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
@@ -1498,6 +1559,17 @@ int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16
                             void* ws, void* stream) {
     return launch_decode(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx, split_tokens,
                          ws, nullptr, stream);
+}
+
+int launch_layer_attention(const mi_kv_pool_s* p, const uint16_t* q_hi, const uint16_t* q_lo,
+                           float* out, const int32_t* table, int32_t mbps, const int32_t* ctx,
+                           int32_t batch, int32_t hq, float scale, int32_t max_ctx, void* ws,
+                           void* stream) {
+    LayerIO lio;
+    lio.q_lo = q_lo;
+    lio.out = out;
+    return launch_decode(p, q_hi, nullptr, table, mbps, ctx, batch, hq, scale, max_ctx,
+                         kDefaultSplitTokens, ws, nullptr, stream, 0, &lio);
 }
 
 int launch_paged_gqa_decode_noalloc(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,

@@ -88,6 +88,13 @@ int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16
                             const int32_t* table, int32_t mbps, const int32_t* ctx,
                             int32_t batch, int32_t hq, float scale, int32_t max_ctx,
                             int32_t split_tokens, void* ws, void* stream);
+// The decoder layer's attention (the default split): the query as a bf16
+// pair (q_hi + q_lo, [B, Hq, D] each), the output in float32 [B, Hq, D];
+// workspace as for launch_paged_gqa_decode.
+int launch_layer_attention(const mi_kv_pool_s* p, const uint16_t* q_hi, const uint16_t* q_lo,
+                           float* out, const int32_t* table, int32_t mbps, const int32_t* ctx,
+                           int32_t batch, int32_t hq, float scale, int32_t max_ctx, void* ws,
+                           void* stream);
 // mi_paged_gqa_decode with its partials in the library's fixed device
 // scratch array instead of a workspace (no allocation).
 int launch_paged_gqa_decode_noalloc(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,

@@ -18,8 +18,10 @@
 //   down    -- out = bf16(x2 + a W_d^T).
 // RMSNorm is x / rms(x) * w with a per-row scalar 1 / rms(x), so the GEMM runs
 // on x * w and the epilogue multiplies by 1 / rms(x). The activations x * w,
-// x2 * w2 and silu(g) * u enter the MFMAs as bf16 hi + lo pairs
-// (fp32-accurate); the attention output o enters as bf16.
+// o, x2 * w2 and silu(g) * u enter the MFMAs as bf16 hi + lo pairs (about 16
+// significant bits); inside the layer the rotated query also reaches the
+// attention's score MFMAs as a bf16 pair (q_rot and its remainder q_lo) and
+// the attention output o is kept in float32.
 //
 // Launch sequence: proj(qkv) -> attention (2 kernels) -> proj(o) ->
 // proj(gate|up) -> proj(down).
@@ -269,7 +271,8 @@ struct ProjArgs {
     float eps;
     // QKV epilogue
     int hq, hkv, D;
-    uint16_t* q_rot;
+    uint16_t* q_rot;            // bf16 of the rotated query
+    uint16_t* q_lo;             // bf16 of its remainder (q_rot + q_lo: ~16 significant bits)
     void* kc;
     void* vc;
     const int32_t* table;
@@ -525,9 +528,13 @@ __global__ __launch_bounds__((64 * proj_max_waves<MT, NW, KB, ACT, EPI, HALF>())
                 const uint16_t r1 = f64_to_bf16(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
                 const uint16_t r2 = f64_to_bf16(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
                 if (head < hq) {
-                    uint16_t* dst = a.q_rot + (static_cast<size_t>(m) * hq + head) * D;
-                    dst[d] = r1;
-                    dst[d + H2] = r2;
+                    const size_t at = (static_cast<size_t>(m) * hq + head) * D;
+                    const double y1 = __dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn));
+                    const double y2 = __dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn));
+                    a.q_rot[at + d] = r1;
+                    a.q_rot[at + d + H2] = r2;
+                    a.q_lo[at + d] = f64_to_bf16(y1 - static_cast<double>(bf16_to_f32(r1)));
+                    a.q_lo[at + d + H2] = f64_to_bf16(y2 - static_cast<double>(bf16_to_f32(r2)));
                 } else {
                     const int gk = head - hq;
                     const size_t row = ((static_cast<size_t>(blk) * hkv + gk) * BS + off) * D;
@@ -627,11 +634,10 @@ constexpr int kb_for(int nw) { return nw >= 2 ? 2 : 4; }
 #define MIKV_PROJ_KB_D kb_for(kNwD)
 #endif
 constexpr int kKbD = MIKV_PROJ_KB_D;
-// o_proj (bf16 activations, one tile): 8 K steps per batch (8 KiB of
-// weights per wave in flight per slot) measured 0.5 us faster than 4 on the
-// Qwen3-8B-shaped layer.
+// o_proj (float32 activations as bf16 pairs, one tile): 4 K steps per batch,
+// as down.
 #ifndef MIKV_PROJ_KB_O
-#define MIKV_PROJ_KB_O 8
+#define MIKV_PROJ_KB_O 4
 #endif
 constexpr int kKbO = MIKV_PROJ_KB_O;
 
@@ -654,7 +660,7 @@ void launch_proj_m(const ProjArgs& a, const mikv::RopeTable& rope, int wgs, hipS
 
 struct LayerPlan {
     int H, I, hq, hkv, D, nqkv;
-    size_t off_qrot, off_attn, off_o, off_x2, off_a, total;
+    size_t off_qrot, off_qlo, off_attn, off_o, off_x2, off_a, total;
     size_t attn_bytes;
 };
 
@@ -673,10 +679,11 @@ bool plan_layer(const mi_layer_config* c, int batch, int max_ctx, LayerPlan* pl)
         return at;
     };
     pl->off_qrot = take(B * pl->hq * pl->D * 2);
+    pl->off_qlo = take(B * pl->hq * pl->D * 2);
     pl->attn_bytes = mikv::attention_workspace_bytes(batch, pl->hq, pl->hkv, pl->D, max_ctx,
                                                      mikv::kDefaultSplitTokens);
     pl->off_attn = take(pl->attn_bytes);
-    pl->off_o = take(B * pl->hq * pl->D * 2);
+    pl->off_o = take(B * pl->hq * pl->D * sizeof(float));
     pl->off_x2 = take(B * pl->H * sizeof(float));
     pl->off_a = take(B * pl->I * sizeof(float));
     pl->total = off;
@@ -724,7 +731,8 @@ extern "C" int mi_decoder_layer_decode(mi_kv_pool_t p, const mi_layer_config* cf
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(ws);
     uint16_t* q_rot = reinterpret_cast<uint16_t*>(base + pl.off_qrot);
-    uint16_t* o = reinterpret_cast<uint16_t*>(base + pl.off_o);
+    uint16_t* q_lo = reinterpret_cast<uint16_t*>(base + pl.off_qlo);
+    float* o = reinterpret_cast<float*>(base + pl.off_o);
     float* x2 = reinterpret_cast<float*>(base + pl.off_x2);
     float* act = reinterpret_cast<float*>(base + pl.off_a);
     const int H = pl.H, I = pl.I, D = pl.D, hq = pl.hq, hkv = pl.hkv;
@@ -744,6 +752,7 @@ extern "C" int mi_decoder_layer_decode(mi_kv_pool_t p, const mi_layer_config* cf
         a.hkv = hkv;
         a.D = D;
         a.q_rot = q_rot;
+        a.q_lo = q_lo;
         a.kc = p->k;
         a.vc = p->v;
         a.table = table;
@@ -755,10 +764,10 @@ extern "C" int mi_decoder_layer_decode(mi_kv_pool_t p, const mi_layer_config* cf
         a.fp8 = mikv::pool_fp8(p) ? 1 : 0;
         launch_proj_m<kNwQkv, kb_for(kNwQkv), kActGainSplit, kEpiQkv>(a, rope, pl.nqkv / 16 / kNwQkv, st);
     }
-    // 2. paged GQA decode attention
-    rc = mikv::launch_paged_gqa_decode(p, q_rot, o, table, mbps, ctx, batch, hq,
-                                       1.0f / sqrtf(static_cast<float>(D)), max_ctx,
-                                       mikv::kDefaultSplitTokens, base + pl.off_attn, stream);
+    // 2. paged GQA decode attention (query as a bf16 pair, float32 output)
+    rc = mikv::launch_layer_attention(p, q_rot, q_lo, o, table, mbps, ctx, batch, hq,
+                                      1.0f / sqrtf(static_cast<float>(D)), max_ctx,
+                                      base + pl.off_attn, stream);
     if (rc != MI_OK) return rc;
     // 3. x2 = x + o W_o^T
     {
@@ -770,7 +779,7 @@ extern "C" int mi_decoder_layer_decode(mi_kv_pool_t p, const mi_layer_config* cf
         a.N = H;
         a.x_in = x_in;
         a.y_f32 = x2;
-        launch_proj_m<kNwO, kKbO, kActBf16, kEpiResidual>(a, rope, H / 16 / kNwO, st);
+        launch_proj_m<kNwO, kKbO, kActF32Split, kEpiResidual>(a, rope, H / 16 / kNwO, st);
     }
     // 4. a = silu(r2 W_gate^T) * (r2 W_up^T), r2 = x2 * ln2_w / rms(x2)
     {

@@ -26,10 +26,11 @@ WIDE = workloads.DecodeConfig(
 
 # The largest batch (32: two 16-row MFMA tiles), an 8-head query group and a
 # 3x hidden intermediate: every projection's workgroup runs more epilogue
-# items than it has threads. Weights N(0, 0.02) as in the Qwen3-8B-shaped
-# workload: with 0.05 at this width the outputs reach |20| and the bf16
-# roundings the device path makes by design (q_rot, o) alone move the exact
-# result past the elementwise bound (checked against the oracle on the CPU).
+# items than it has threads. Tested with weights N(0, 0.02), as in the
+# Qwen3-8B-shaped workload, and N(0, 0.05), where the outputs reach |20|:
+# there a bf16 rounding of the rotated query or of the attention output would
+# alone move the result past the elementwise bound, so the layer keeps both
+# at about 16 significant bits (bf16 pairs, float32).
 MAXB = workloads.DecodeConfig(
     "max_batch_layer", batch=32, num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=16,
     num_blocks=1024, rope_theta=1e6, ctx_draw="uniform", ctx_lo=0, ctx_hi=300, seed=13,
@@ -141,9 +142,10 @@ def _check_cache(case, cfg, gk, gv, inter, w):
           flush=True)
 
 
-@pytest.mark.parametrize("cfg,std", [(SMALL, 0.05), (WIDE, 0.05), (MAXB, 0.02), (MID, 0.03),
-                                     (ONE, 0.05), (B17, 0.05)],
-                         ids=["small", "wide_b20", "max_b32_g8", "mid_b12", "one_b1", "b17"])
+@pytest.mark.parametrize("cfg,std", [(SMALL, 0.05), (WIDE, 0.05), (MAXB, 0.02), (MAXB, 0.05),
+                                     (MID, 0.03), (ONE, 0.05), (B17, 0.05)],
+                         ids=["small", "wide_b20", "max_b32_g8", "max_b32_g8_std05", "mid_b12",
+                              "one_b1", "b17"])
 def test_layer_small_shapes(cfg, std):
     print("layer", cfg.name, flush=True)
     case = workloads.make_decode_case(cfg, pool="poison")
