@@ -26,10 +26,7 @@ namespace {
 constexpr int BS = 16;                // tokens per KV block
 constexpr float kNegInf = -INFINITY;
 constexpr float kRescaleSlack = 8.0f; // log2 units: running max may lag by 2^8
-#ifndef MIKV_TUNE_PREFILL_RAW
-#define MIKV_TUNE_PREFILL_RAW 1
-#endif
-constexpr bool kPrefillRawSoftmax = MIKV_TUNE_PREFILL_RAW != 0;   // prefill softmax form (see softmax_step)
+constexpr bool kPrefillRawSoftmax = true;   // prefill softmax form (see softmax_step)
 
 // ---------------------------------------------------------------- bf16 helpers
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -65,13 +62,10 @@ __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
 // the head's scales.
 constexpr int kFmtBf16 = 0;
 constexpr int kFmtFp8 = 1;
-#ifndef MIKV_TUNE_ROT_THREADS
-#define MIKV_TUNE_ROT_THREADS 256
-#endif
 // Rotation threads per prefill row of write_decode_kv: 256 (each angle shared
 // by a quarter of the heads at D = 128) measured fastest on MI355X (512: +1 %,
 // 1024: +4 % on a 4 x 2048-token prefill step).
-constexpr int kRotThreads = MIKV_TUNE_ROT_THREADS;
+constexpr int kRotThreads = 256;
 
 // With PREFILL the rows of q, k, v are the packed new tokens of a prefill
 // chunk (grid.x = total tokens): row i belongs to the sequence b with
@@ -971,10 +965,7 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
 // clearing between calls.
 constexpr int kPrefillFixed = 0;
 constexpr int kPrefillRescale = 1;
-#ifndef MIKV_TUNE_PREFILL_FIXED_WAVES
-#define MIKV_TUNE_PREFILL_FIXED_WAVES 1
-#endif
-constexpr int kPrefillFixedWaves = MIKV_TUNE_PREFILL_FIXED_WAVES;   // waves per SIMD the fixed form is built for
+constexpr int kPrefillFixedWaves = 1;   // waves per SIMD the fixed form is built for
 
 template <int D, int G, int FMT, int PF, int QB, int MODE>
 __global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1) void paged_prefill_kernel(
@@ -1256,32 +1247,13 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
 // consumed measured fastest on MI355X (long contexts and short batches
 // alike): more or deeper streams only add pieces to combine. 8-bit tiles are
 // half the bytes, so that cache keeps more of them in flight.
-#ifdef MIKV_TUNE_MFMA_PF
-constexpr int kAttnPrefetch = MIKV_TUNE_MFMA_PF;
-#else
 constexpr int kAttnPrefetch = 1;
-#endif
-#ifdef MIKV_TUNE_FP8_PF
-constexpr int kAttnPrefetchFp8 = MIKV_TUNE_FP8_PF;
-#else
 constexpr int kAttnPrefetchFp8 = 2;
-#endif
-#ifdef MIKV_TUNE_WAVES_PER_CU
-constexpr int kAttnWavesPerCU = MIKV_TUNE_WAVES_PER_CU;
-#else
 constexpr int kAttnWavesPerCU = 3;
-#endif
 // Query column blocks of 16 per prefill wave (the fixed-reference launch and
 // the rescaling one).
-#ifdef MIKV_TUNE_PREFILL_QB
-constexpr int kPrefillQB = MIKV_TUNE_PREFILL_QB;
-#else
 constexpr int kPrefillQB = 3;
-#endif
-#ifndef MIKV_TUNE_PREFILL_QB_FIXED
-#define MIKV_TUNE_PREFILL_QB_FIXED 3
-#endif
-constexpr int kPrefillQBFixed = MIKV_TUNE_PREFILL_QB_FIXED;
+constexpr int kPrefillQBFixed = 3;
 
 // Grid of the attention kernel on the current device: CUs x min(waves per
 // CU, resident workgroups per CU at the kernel's register budget), cached

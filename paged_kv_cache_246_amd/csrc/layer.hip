@@ -41,16 +41,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int BS = 16;
 constexpr int kKStep = 32;               // K per MFMA
 
-// Tuning of the projection grids (build-time overridable for sweeps):
-// waves per projection (upper bound), LDS bytes per workgroup (upper bound).
-#ifndef MIKV_PROJ_TARGET_WAVES
-#define MIKV_PROJ_TARGET_WAVES 3072
-#endif
-#ifndef MIKV_PROJ_LDS_CAP
-#define MIKV_PROJ_LDS_CAP 65536
-#endif
-constexpr int kProjTargetWaves = MIKV_PROJ_TARGET_WAVES;
-constexpr int kProjLdsCap = MIKV_PROJ_LDS_CAP;
+// Projection grids: waves per projection (upper bound), LDS bytes per
+// workgroup (upper bound).
+constexpr int kProjTargetWaves = 3072;
+constexpr int kProjLdsCap = 65536;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
@@ -293,18 +287,14 @@ struct ProjArgs {
 // two batches of weight, activation and gain registers, the accumulators and
 // about 30 for addresses and temporaries; the QKV epilogue's float64 RoPE
 // needs more), else 8.
-#ifndef MIKV_PROJ_QKV_WAVES
-#define MIKV_PROJ_QKV_WAVES 8
-#endif
-#ifndef MIKV_PROJ_VGPR_EXTRA
-#define MIKV_PROJ_VGPR_EXTRA 30
-#endif
+constexpr int kProjQkvWaves = 8;
+constexpr int kProjVgprExtra = 30;
 template <int MT, int NW, int KB, int ACT, int EPI, bool HALF>
 constexpr int proj_max_waves() {
     using B = GemmBatch<MT, NW, ACT, KB, HALF>;
     constexpr int batch = 4 * (KB * NW + KB * MT * (B::F32 && !HALF ? 2 : 1) + (B::GAIN ? KB : 0));
-    if (EPI == kEpiQkv) return MIKV_PROJ_QKV_WAVES;
-    return 2 * batch + 4 * NW * MT + MIKV_PROJ_VGPR_EXTRA <= 128 ? 16 : 8;
+    if (EPI == kEpiQkv) return kProjQkvWaves;
+    return 2 * batch + 4 * NW * MT + kProjVgprExtra <= 128 ? 16 : 8;
 }
 
 // LDS bytes per wave: the weight staging tile during the K loop, the
@@ -594,12 +584,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // down (256 workgroups at hidden 4096) takes up to 16 waves each: with the
 // one-load fp32 activations a wave fits in 76 registers, and 16 waves per
 // workgroup measured faster than 8 or 12 on MI355X.
-#ifndef MIKV_PROJ_TARGET_D
-#define MIKV_PROJ_TARGET_D 4096
-#endif
+constexpr int kProjTargetWavesDown = 4096;
 template <int MT, int NW, int KB, int ACT, int EPI, bool HALF>
 int proj_waves(int wgs, int K) {
-    const int target = EPI == kEpiOut ? MIKV_PROJ_TARGET_D : kProjTargetWaves;
+    const int target = EPI == kEpiOut ? kProjTargetWavesDown : kProjTargetWaves;
     const int units = K / (KB * kKStep);
     const int max_ks = std::min<int>(proj_max_waves<MT, NW, KB, ACT, EPI, HALF>(),
                                      static_cast<int>(kProjLdsCap / proj_lds_per_wave<MT, NW, KB, ACT>()));
@@ -613,33 +601,15 @@ int proj_waves(int wgs, int K) {
 // per workgroup (KB 2: 4 KiB of weights per wave per batch); o_proj and down
 // take one tile (KB 4), which keeps 256 workgroups at hidden 4096 (groups of
 // two or four tiles were slower: fewer workgroups than CUs).
-#ifndef MIKV_PROJ_NW_QKV
-#define MIKV_PROJ_NW_QKV 2
-#endif
-#ifndef MIKV_PROJ_NW_GU
-#define MIKV_PROJ_NW_GU 2
-#endif
-#ifndef MIKV_PROJ_NW_O
-#define MIKV_PROJ_NW_O 1
-#endif
-#ifndef MIKV_PROJ_NW_D
-#define MIKV_PROJ_NW_D 1
-#endif
-constexpr int kNwQkv = MIKV_PROJ_NW_QKV, kNwGu = MIKV_PROJ_NW_GU;
+constexpr int kNwQkv = 2, kNwGu = 2;
 static_assert(kNwQkv == 2 || kNwQkv == 4, "QKV pairs per workgroup must divide D / 32 for D = 64 and 128");
-constexpr int kNwO = MIKV_PROJ_NW_O, kNwD = MIKV_PROJ_NW_D;
+constexpr int kNwO = 1, kNwD = 1;
 // K steps per batch: NW * KB >= 4 loads (4 KiB of weights per wave).
 constexpr int kb_for(int nw) { return nw >= 2 ? 2 : 4; }
-#ifndef MIKV_PROJ_KB_D
-#define MIKV_PROJ_KB_D kb_for(kNwD)
-#endif
-constexpr int kKbD = MIKV_PROJ_KB_D;
+constexpr int kKbD = kb_for(kNwD);
 // o_proj (float32 activations as bf16 pairs, one tile): 4 K steps per batch,
 // as down.
-#ifndef MIKV_PROJ_KB_O
-#define MIKV_PROJ_KB_O 4
-#endif
-constexpr int kKbO = MIKV_PROJ_KB_O;
+constexpr int kKbO = 4;
 
 template <int MT, int NW, int KB, int ACT, int EPI, bool HALF = false>
 void launch_proj(const ProjArgs& a, const mikv::RopeTable& rope, int wgs, hipStream_t st) {
