@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "e4m3.h"
 #include "internal.h"
@@ -1108,6 +1109,317 @@ __global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1)
     }
 }
 
+// ============================================== prefill, shared-tile form
+// Causal attention of a prefill chunk with the K/V tiles shared by the query
+// heads of a KV group. One workgroup per (32-token query block, KV head g,
+// sequence), one wave per query head of the group (G waves). The key range
+// 0 .. p_last of the block goes by in steps of 64 keys (four 16-token cache
+// blocks): the workgroup copies a step's K and V from the paged cache into
+// LDS once (double buffered, one barrier per step; the copy of step s + 1 is
+// in flight while step s is computed) and every wave contracts its own
+// head's 32 queries against them on 32x32x16 bf16 MFMAs:
+//  - S^T = K Q^T per 32-key half t: 32 keys x 32 queries, D / 16 MFMAs (the
+//    two halves are independent chains); lane l holds query l % 32 (its B
+//    operand column, Q^T loaded once) and receives the scores of keys
+//    32 t + 8 (i / 4) + 4 (l / 32) + i % 4, i < 16;
+//  - O^T += V^T P^T: D / 32 dim tiles x 4 MFMAs of 16 keys. P^T is the score
+//    layout itself (registers 8 (a % 2) .. + 7 of half a / 2 are the B
+//    operand of key group a), so V is stored transposed in LDS with the keys
+//    of each group in the matching order: key 16a + r sits at column 16a +
+//    8 ((r / 4) % 2) + (r % 4) + 4 (r / 8), and the A operand of a lane is one
+//    16-byte read.
+// Rows of K and of V^T are padded (16 bytes) so the operand reads of 8
+// consecutive lanes fall on distinct banks. The softmax uses the fixed
+// reference of the register form (the largest score of the first step, never
+// raised); a wave whose scores climb past it by more than kFixedHeadroom
+// writes the call's generation into the redo word, and the rescaling launch
+// repeats the chunk. Keys after the block's last position are not used
+// (zero rows, so NaN bits in the cache tail never reach an MFMA); keys after
+// a query's own position are masked by selection on the diagonal steps.
+constexpr int kFaRows = 32;         // query tokens per wave
+constexpr int kFaKeys = 64;         // keys per step
+constexpr int kFaIdWindow = 512;    // block ids held in LDS at a time
+
+template <int D>
+struct FaLayout {
+    static constexpr int KROW = D * 2 + 16;             // bytes per K row
+    static constexpr int VROW = kFaKeys * 2 + 16;       // bytes per V^T row
+    static constexpr int KBYTES = kFaKeys * KROW;
+    static constexpr int BUF = KBYTES + D * VROW;        // one stage: K, then V^T
+};
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Column of key r (0 .. kFaKeys - 1) of a step in the V^T rows.
+__device__ __forceinline__ int fa_vcol(int r) {
+    const int q = r & 15;
+    return (r & ~15) + 8 * ((q >> 2) & 1) + (q & 3) + 4 * (q >> 3);
+}
+
+template <int D, int G, int FMT>
+__global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
+    const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
+    const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu, int32_t hkv,
+    int32_t num_blocks, int32_t total, int32_t max_new, float scale_log2,
+    const float* __restrict__ kv_scales, uint16_t* __restrict__ out, uint32_t* __restrict__ err,
+    uint32_t* __restrict__ redo_word, uint32_t gen) {
+    using L = FaLayout<D>;
+    constexpr int NT = 64 * G;              // threads
+    constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1;
+    constexpr int CPR = D / 8;              // 8-element pieces per key row
+    constexpr int KITEMS = kFaKeys * CPR;   // K pieces per step
+    constexpr int VITEMS = kFaKeys / 2 * CPR;   // V items: 8 dims of two keys
+    constexpr int KPER = (KITEMS + NT - 1) / NT;
+    constexpr int VPER = (VITEMS + NT - 1) / NT;
+    constexpr int NKK = D / 16;             // score MFMAs per 32-key half
+    constexpr int NDT = D / 32;             // output dim tiles
+    constexpr int NH = kFaKeys / 32;        // 32-key halves per step
+    constexpr int BPS = kFaKeys / BS;       // cache blocks per step
+    __shared__ __align__(16) char lds[2 * L::BUF];
+    __shared__ int32_t ids_lds[kFaIdWindow];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int g = blockIdx.y;
+    const int b = blockIdx.z;
+    const int h = g * G + w;
+    const int hq = hkv * G;
+    const int row0 = cu[b];
+    const int nnew = cu[b + 1] - row0;
+    const int ctx = ctx_lens[b];
+    if (row0 < 0 || nnew < 0 || row0 + nnew > total || nnew > max_new || ctx < 0 ||
+        ctx + nnew > mbps * BS) {
+        if (blockIdx.x == 0 && g == 0 && tid == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+        return;
+    }
+    const int nqb = (nnew + kFaRows - 1) / kFaRows;
+    if (static_cast<int>(blockIdx.x) >= nqb) return;
+    const int j0 = (nqb - 1 - static_cast<int>(blockIdx.x)) * kFaRows;   // longest blocks first
+    const int p_first = ctx + j0;
+    const int p_last = ctx + min(j0 + kFaRows, nnew) - 1;
+    const int nks = p_last / kFaKeys + 1;       // steps holding keys 0 .. p_last
+    const int ks_m = (p_first + 1) / kFaKeys;   // steps before this are unmasked for every query
+    const int jq = j0 + col;                    // this lane's query token
+    const bool q_ok = jq < nnew;
+    const int pq = ctx + jq;
+
+    float sl2 = scale_log2, vscale = 1.f;
+    if constexpr (FMT == kFmtFp8) {
+        sl2 *= kv_scales[g];
+        vscale = kv_scales[hkv + g];
+    }
+
+    // Q^T operand of the score MFMAs: dims 16 kk + 8 half .. + 8 of the query
+    uint4 qop[NKK];
+    {
+        const uint16_t* qh = q_rot + (static_cast<size_t>(row0 + (q_ok ? jq : 0)) * hq + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            qop[kk] = q_ok ? *reinterpret_cast<const uint4*>(qh + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0);
+    }
+
+    // Block ids of the sequence in an LDS window of kFaIdWindow entries,
+    // refilled between barriers (range-checked when filled: a bad id is
+    // recorded and replaced by 0).
+    const int nblk_seq = p_last / BS + 1;
+    int ids_base = 0;
+    auto fill_ids = [&](int base) {
+        ids_base = base;
+        for (int i = tid; i < kFaIdWindow; i += NT) {
+            int32_t id = 0;
+            if (base + i < nblk_seq) {
+                id = table[static_cast<size_t>(b) * mbps + base + i];
+                if (id < 0 || id >= num_blocks) {
+                    atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+                    id = 0;
+                }
+            }
+            ids_lds[i] = id;
+        }
+    };
+
+    // Copy of one step (keys 64 s .. 64 s + 63) through registers into LDS:
+    // K in 8-element pieces, V in pairs of keys (8 dims each) for the
+    // transposed store. Every load is issued (positions past p_last read
+    // p_last's row and are zeroed when stored), so the waits before the
+    // stores count exactly the loads of the older stage.
+    typedef typename std::conditional<FMT == kFmtBf16, uint4, uint2>::type Piece;
+    struct Stage {
+        Piece k[KPER];
+        Piece v[VPER][2];
+    };
+    const size_t head_off = static_cast<size_t>(g) * BS * D;
+    auto addr = [&](int pos, int piece) {     // pos <= p_last
+        const int32_t id = ids_lds[pos / BS - ids_base];
+        return (static_cast<size_t>(id) * hkv * BS * D + head_off + static_cast<size_t>(pos % BS) * D + 8 * piece) * ESZ;
+    };
+    auto fetch = [&](int s, Stage& st) {
+#pragma unroll
+        for (int u = 0; u < KPER; ++u) {
+            const int it = min(tid + u * NT, KITEMS - 1);
+            const int pos = min(kFaKeys * s + it / CPR, p_last);
+            st.k[u] = *reinterpret_cast<const Piece*>(kc + addr(pos, it % CPR));
+        }
+#pragma unroll
+        for (int u = 0; u < VPER; ++u) {
+            const int it = min(tid + u * NT, VITEMS - 1);
+            const int pos = kFaKeys * s + 2 * (it % (kFaKeys / 2));
+            const int piece = it / (kFaKeys / 2);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                st.v[u][e] = *reinterpret_cast<const Piece*>(vc + addr(min(pos + e, p_last), piece));
+        }
+    };
+    auto widen = [&](const Piece& x) -> uint4 {       // 8 elements as bf16 (E4M3 codes widened exactly)
+        if constexpr (FMT == kFmtBf16) {
+            return x;
+        } else {
+            return make_uint4(fp8x2_to_bf16x2<false>(x.x), fp8x2_to_bf16x2<true>(x.x),
+                              fp8x2_to_bf16x2<false>(x.y), fp8x2_to_bf16x2<true>(x.y));
+        }
+    };
+    auto stash = [&](int s, const Stage& st) {
+        char* kb = lds + (s & 1) * L::BUF;
+        char* vb = kb + L::KBYTES;
+        const int rows = p_last + 1 - kFaKeys * s;     // valid key rows of the step (1 .. 64)
+#pragma unroll
+        for (int u = 0; u < KPER; ++u) {
+            const int it = tid + u * NT;
+            if (it < KITEMS) {
+                const uint4 x = (it / CPR) < rows ? widen(st.k[u]) : make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4*>(kb + (it / CPR) * L::KROW + (it % CPR) * 16) = x;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < VPER; ++u) {
+            const int it = tid + u * NT;
+            if (it < VITEMS) {
+                const int r = 2 * (it % (kFaKeys / 2));       // keys r, r + 1: adjacent columns
+                const int piece = it / (kFaKeys / 2);
+                const uint4 a = r < rows ? widen(st.v[u][0]) : make_uint4(0, 0, 0, 0);
+                const uint4 c = r + 1 < rows ? widen(st.v[u][1]) : make_uint4(0, 0, 0, 0);
+                const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
+                char* dst = vb + (8 * piece) * L::VROW + fa_vcol(r) * 2;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                    *reinterpret_cast<uint32_t*>(dst + e * L::VROW) =
+                        __builtin_amdgcn_perm(cw[e / 2], aw[e / 2], sel);
+                }
+            }
+        }
+    };
+
+    f32x16_t oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16_t{};
+    float m = kNegInf, l = 0.f, top = kNegInf;
+
+    // One step: scores, softmax, weighted V sum from LDS buffer s % 2.
+    auto compute = [&](int s) {
+        const char* kb = lds + (s & 1) * L::BUF;
+        const char* vb = kb + L::KBYTES;
+        f32x16_t sacc[NH];
+#pragma unroll
+        for (int t = 0; t < NH; ++t) sacc[t] = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int t = 0; t < NH; ++t) {
+                const uint4 a = *reinterpret_cast<const uint4*>(kb + (32 * t + col) * L::KROW + (16 * kk + 8 * half) * 2);
+                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                  __builtin_bit_cast(bf16x8_t, qop[kk]), sacc[t], 0, 0, 0);
+            }
+        float sc[NH][16];
+        if (s >= ks_m) {            // diagonal step: key position <= the query's own
+#pragma unroll
+            for (int t = 0; t < NH; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kp = kFaKeys * s + 32 * t + 8 * (i / 4) + 4 * half + (i % 4);
+                    sc[t][i] = kp <= pq ? sacc[t][i] : kNegInf;
+                }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NH; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[t][i] = sacc[t][i];
+        }
+        if (s == 0) {               // the fixed reference: largest score of the first step
+            float mx = sc[0][0];
+#pragma unroll
+            for (int t = 0; t < NH; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[t][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+            m = q_ok ? mx : 0.f;
+        }
+        bf16x8_t pb[2 * NH];
+#pragma unroll
+        for (int t = 0; t < NH; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float a = fmaf(sc[t][i], sl2, -m);
+                top = fmaxf(top, a);
+                const float p = __builtin_amdgcn_exp2f(a);
+                l += p;
+                pb[2 * t + i / 8][i % 8] = static_cast<__bf16>(p);
+            }
+#pragma unroll
+        for (int a = 0; a < 2 * NH; ++a)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const uint4 v = *reinterpret_cast<const uint4*>(vb + (32 * dt + col) * L::VROW + (16 * a + 8 * half) * 2);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v), pb[a],
+                                                                   oacc[dt], 0, 0, 0);
+            }
+    };
+
+    // Step s + 1 is fetched into registers while step s is computed from
+    // LDS, then stored to the other LDS buffer; one barrier per step. The
+    // fetch is issued unconditionally (past the last step it reads the last
+    // step again and is dropped), so every path keeps the same loads in
+    // flight.
+    Stage st;
+    fill_ids(0);
+    __syncthreads();
+    fetch(0, st);
+    stash(0, st);
+    __syncthreads();
+    for (int s = 0; s < nks; ++s) {
+        if (BPS * (min(s + 1, nks - 1) + 1) - ids_base > kFaIdWindow) {   // uniform: next id window
+            fill_ids(BPS * min(s + 1, nks - 1));
+            __syncthreads();
+        }
+        fetch(min(s + 1, nks - 1), st);
+        compute(s);
+        if (s + 1 < nks) stash(s + 1, st);
+        __syncthreads();
+    }
+
+    const float lt = l + __shfl_xor(l, 32);
+    if (q_ok) {
+        const float inv = vscale / lt;
+        uint16_t* oh = out + (static_cast<size_t>(row0 + jq) * hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * dt + 8 * r4 + 4 * half;
+                const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * r4] * inv)) |
+                                    (static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * r4 + 1] * inv)) << 16);
+                const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * r4 + 2] * inv)) |
+                                    (static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * r4 + 3] * inv)) << 16);
+                *reinterpret_cast<uint2*>(oh + d0) = make_uint2(w0, w1);
+            }
+    }
+    if (__ballot(q_ok && !(top <= kFixedHeadroom)) != 0 && lane == 0) atomicExch(redo_word, gen);
+}
+
 // Combine kernel: one workgroup per (query head, sequence). It rebuilds the
 // same partition, and if the segment was cut into pieces, merges their
 // partials in range order. Thread (d, cg) folds the pieces cg, cg + NCG, ...
@@ -1356,13 +1668,12 @@ void launch_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
     uint32_t gen = ++p->prefill_gen;
     if (gen == 0) gen = ++p->prefill_gen;           // 0 is the word's initial value
     uint32_t* redo = p->err + mikv::kPrefillRedoWord;
-    auto fixed = f8 ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQBFixed, kPrefillFixed>
-                    : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQBFixed, kPrefillFixed>;
+    auto fixed = f8 ? paged_prefill_fa_kernel<D, G, kFmtFp8> : paged_prefill_fa_kernel<D, G, kFmtBf16>;
     auto rescale = f8 ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQB, kPrefillRescale>
                       : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQB, kPrefillRescale>;
-    const dim3 grid_f((max_new + BS * kPrefillQBFixed - 1) / (BS * kPrefillQBFixed), hkv * G, batch);
+    const dim3 grid_f((max_new + kFaRows - 1) / kFaRows, hkv, batch);
     const dim3 grid_r((max_new + BS * kPrefillQB - 1) / (BS * kPrefillQB), hkv * G, batch);
-    hipLaunchKernelGGL(fixed, grid_f, dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
+    hipLaunchKernelGGL(fixed, grid_f, dim3(64 * G), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
                        static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, hkv, p->num_blocks,
                        total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err,
                        redo, gen);
