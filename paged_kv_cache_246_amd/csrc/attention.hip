@@ -351,6 +351,7 @@ struct MfmaSoftmax {
 // exceeds m by at most kFixedHeadroom (log2 units); a wave in which one did
 // not repeats its work with the online rescaling form.
 constexpr float kFixedHeadroom = 64.0f;
+constexpr float kFixedHeadroomSum = 18446744073709551616.0f;   // 2^64
 
 // Operand builders of one 16-token tile.
 // K operand of 32-dim slice j: the lane's key row, 8 dims (bf16; E4M3 codes
@@ -1111,8 +1112,11 @@ __global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1)
 
 // ============================================== prefill, shared-tile form
 // Causal attention of a prefill chunk with the K/V tiles shared by the query
-// heads of a KV group. One workgroup per (32-token query block, KV head g,
-// sequence), one wave per query head of the group (G waves). The key range
+// heads of a KV group. One workgroup per (KV head g, sequence, 32-token query
+// block), one wave per query head of the group (G waves); the blocks with the
+// longest key ranges are dispatched first across the whole chunk
+// (fa_block_of_rank). A sequence with a bad length or chunk is recorded as a
+// fault by the first workgroup and gets no blocks. The key range
 // 0 .. p_last of the block goes by in steps of 64 keys (four 16-token cache
 // blocks): the workgroup copies a step's K and V from the paged cache into
 // LDS once (double buffered, one barrier per step; the copy of step s + 1 is
@@ -1131,9 +1135,9 @@ __global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1)
 // Rows of K and of V^T are padded (16 bytes) so the operand reads of 8
 // consecutive lanes fall on distinct banks. The softmax uses the fixed
 // reference of the register form (the largest score of the first step, never
-// raised); a wave whose scores climb past it by more than kFixedHeadroom
-// writes the call's generation into the redo word, and the rescaling launch
-// repeats the chunk. Keys after the block's last position are not used
+// raised). A query whose row sum ends above 2^kFixedHeadroom (which any
+// single weight above that bound forces) makes the wave write the call's
+// generation into the redo word, and the rescaling launch repeats the chunk. Keys after the block's last position are not used
 // (zero rows, so NaN bits in the cache tail never reach an MFMA); keys after
 // a query's own position are masked by selection on the diagonal steps.
 constexpr int kFaRows = 32;         // query tokens per wave
@@ -1156,11 +1160,97 @@ __device__ __forceinline__ int fa_vcol(int r) {
     return (r & ~15) + 8 * ((q >> 2) & 1) + (q & 3) + 4 * (q >> 3);
 }
 
+// Longest-first order of the query blocks of a chunk. Block y of sequence b
+// (y = 0 holds the chunk's last tokens) is ranked by A_b - kFaRows y, with
+// A_b = ctx_b + kFaRows nqb_b (its key count, rounded up to the block grid
+// for y = 0), descending, ties in sequence order. The block of rank r is found
+// without a sort: the largest key count T with more than r blocks at or above
+// it, then the (r - count above T)-th sequence, in order, that has a block
+// exactly at T. The search for T is 64-way: each lane counts the blocks at or
+// above its own candidate, over all sequences (lane b holds sequence b's A_b
+// and nqb_b), and the range shrinks 64 times per round.
+// Wave-uniform; every lane returns the same (b, y), or b = -1 past the last
+// block. When every sequence has the same key count, and beyond kFaRankBatch
+// sequences (where the search would cost more than it saves), the order is
+// plain block-index major instead, which for one key count is the same order.
+// Sequences with a bad length (recorded by the kernel) have no blocks.
+struct FaBlock {
+    int b, y;
+};
+constexpr int kFaRankBatch = 64;
+__device__ __forceinline__ FaBlock fa_block_of_rank(int r, const int32_t* __restrict__ ctx_lens,
+                                                    const int32_t* __restrict__ cu, int batch, int total,
+                                                    int max_new, int mbps, int lane) {
+    auto seq = [&](int bb, int& A, int& nq) {       // A_b and nqb_b of sequence bb (0 blocks if bad)
+        A = 0;
+        nq = 0;
+        if (bb < batch) {
+            const int row0 = cu[bb], n = cu[bb + 1] - row0, c = ctx_lens[bb];
+            if (!(row0 < 0 || n < 0 || row0 + n > total || n > max_new || c < 0 || c + n > mbps * BS)) {
+                nq = (n + kFaRows - 1) / kFaRows;
+                A = c + kFaRows * nq;
+            }
+        }
+    };
+    auto plain = [&]() {                            // block index major
+        const int y = r / batch, bb = r % batch;
+        int A, nq;
+        seq(bb, A, nq);
+        return FaBlock{y < nq ? bb : -1, y};
+    };
+    if (batch > kFaRankBatch) return plain();
+    int A, nq;
+    seq(lane, A, nq);
+    int amax = 0, amin = INT_MAX, tmin = INT_MAX;   // tmin: key count of the shortest last block
+    for (int bb = 0; bb < batch; ++bb) {            // scalar: lane bb's values are uniform
+        const int Ab = __builtin_amdgcn_readlane(A, bb), nb = __builtin_amdgcn_readlane(nq, bb);
+        if (nb > 0) {
+            amax = max(amax, Ab);
+            amin = min(amin, Ab);
+            tmin = min(tmin, Ab - kFaRows * (nb - 1));
+        }
+    }
+    if (amax == amin) return plain();               // one key count: the plain order is longest-first
+    if (amax <= 0) return FaBlock{-1, 0};
+    auto count_from = [&](int T) {                  // blocks with key count >= T (T per lane)
+        int c = 0;
+        for (int bb = 0; bb < batch; ++bb) {
+            const int Ab = __builtin_amdgcn_readlane(A, bb), nb = __builtin_amdgcn_readlane(nq, bb);
+            if (nb > 0 && Ab >= T) c += min(nb, (Ab - T) / kFaRows + 1);
+        }
+        return c;
+    };
+    // count(tmin) is every block; the largest T with count(T) > r is in [tmin, amax]
+    int lo = tmin, hi = amax;
+    if (__builtin_amdgcn_readfirstlane(count_from(tmin)) <= r) return FaBlock{-1, 0};
+    while (lo < hi) {
+        const int step = (hi - lo + 64) / 64;       // ceil((hi - lo + 1) / 64)
+        const int t = min(lo + lane * step, hi);
+        const uint64_t good = __ballot(count_from(t) > r);   // a prefix of the lanes, lane 0 in it
+        const int L = __popcll(good) - 1;
+        const int nlo = min(lo + L * step, hi);
+        hi = min(hi, nlo + step - 1);
+        lo = nlo;
+    }
+    const int T = lo;
+    // blocks above T, then the sequences with a block exactly at T, in order
+    int above = (nq > 0 && A >= T + 1) ? min(nq, (A - T - 1) / kFaRows + 1) : 0;
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) above += __shfl_xor(above, x);
+    const int rr = r - above;
+    const bool at = nq > 0 && A >= T && (A - T) % kFaRows == 0 && (A - T) / kFaRows < nq;
+    uint64_t mm = __ballot(at);
+    if (rr < 0 || rr >= __popcll(mm)) return FaBlock{-1, 0};
+    for (int i = 0; i < rr; ++i) mm &= mm - 1;
+    const int src = __ffsll(static_cast<unsigned long long>(mm)) - 1;
+    return FaBlock{src, (__shfl(A, src) - T) / kFaRows};
+}
+
 template <int D, int G, int FMT>
 __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
     const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
-    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu, int32_t hkv,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu, int32_t batch, int32_t hkv,
     int32_t num_blocks, int32_t total, int32_t max_new, float scale_log2,
     const float* __restrict__ kv_scales, uint16_t* __restrict__ out, uint32_t* __restrict__ err,
     uint32_t* __restrict__ redo_word, uint32_t gen) {
@@ -1184,21 +1274,28 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
     const int lane = tid & 63;
     const int col = lane & 31;
     const int half = lane >> 5;
-    const int g = blockIdx.y;
-    const int b = blockIdx.z;
+    // grid: KV heads x (batch x query blocks of the longest chunk); the
+    // workgroups of rank r (dispatched in order) take the r-th longest block
+    const int g = static_cast<int>(blockIdx.x) % hkv;
+    if (blockIdx.x == 0 && tid == 0) {
+        for (int bb = 0; bb < batch; ++bb) {
+            const int r0 = cu[bb], n = cu[bb + 1] - r0, c = ctx_lens[bb];
+            if (r0 < 0 || n < 0 || r0 + n > total || n > max_new || c < 0 || c + n > mbps * BS)
+                atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+        }
+    }
+    const FaBlock fb = fa_block_of_rank(static_cast<int>(blockIdx.x) / hkv, ctx_lens, cu, batch, total,
+                                        max_new, mbps, lane);
+    if (fb.b < 0) return;
+    const int b = fb.b;
+    const int qblk = fb.y;
     const int h = g * G + w;
     const int hq = hkv * G;
     const int row0 = cu[b];
     const int nnew = cu[b + 1] - row0;
     const int ctx = ctx_lens[b];
-    if (row0 < 0 || nnew < 0 || row0 + nnew > total || nnew > max_new || ctx < 0 ||
-        ctx + nnew > mbps * BS) {
-        if (blockIdx.x == 0 && g == 0 && tid == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
-        return;
-    }
     const int nqb = (nnew + kFaRows - 1) / kFaRows;
-    if (static_cast<int>(blockIdx.x) >= nqb) return;
-    const int j0 = (nqb - 1 - static_cast<int>(blockIdx.x)) * kFaRows;   // longest blocks first
+    const int j0 = (nqb - 1 - qblk) * kFaRows;   // longest blocks first
     const int p_first = ctx + j0;
     const int p_last = ctx + min(j0 + kFaRows, nnew) - 1;
     const int nks = p_last / kFaKeys + 1;       // steps holding keys 0 .. p_last
@@ -1257,12 +1354,26 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
         const int32_t id = ids_lds[pos / BS - ids_base];
         return (static_cast<size_t>(id) * hkv * BS * D + head_off + static_cast<size_t>(pos % BS) * D + 8 * piece) * ESZ;
     };
+    // K pieces: item it = tid + u NT is row it / CPR (16 consecutive lanes
+    // read one 16 * D-byte row), so the 64 lanes of a wave read rows of one
+    // cache block when NT is a multiple of 64 and CPR divides 64: the block's
+    // address is a wave-uniform base, the lane's in-block offset is fixed.
+    static_assert(64 % CPR == 0 && (BS * CPR) % 64 == 0, "a wave's K pieces lie in one cache block");
+    uint32_t koff[KPER];
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+        const int it = min(tid + u * NT, KITEMS - 1);
+        koff[u] = static_cast<uint32_t>((head_off + static_cast<size_t>((it / CPR) % BS) * D + 8 * (it % CPR)) * ESZ);
+    }
+    const size_t blk_bytes = static_cast<size_t>(hkv) * BS * D * ESZ;
     auto fetch = [&](int s, Stage& st) {
 #pragma unroll
         for (int u = 0; u < KPER; ++u) {
-            const int it = min(tid + u * NT, KITEMS - 1);
-            const int pos = min(kFaKeys * s + it / CPR, p_last);
-            st.k[u] = *reinterpret_cast<const Piece*>(kc + addr(pos, it % CPR));
+            const int it0 = min(w * 64 + u * NT, KITEMS - 1);            // the wave's first item
+            const int row = min(kFaKeys * s + it0 / CPR, p_last);
+            const int32_t id = __builtin_amdgcn_readfirstlane(ids_lds[row / BS - ids_base]);
+            const uint8_t* base = kc + static_cast<size_t>(id) * blk_bytes;
+            st.k[u] = *reinterpret_cast<const Piece*>(base + koff[u]);
         }
 #pragma unroll
         for (int u = 0; u < VPER; ++u) {
@@ -1317,7 +1428,7 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
     f32x16_t oacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16_t{};
-    float m = kNegInf, l = 0.f, top = kNegInf;
+    float m = kNegInf, l = 0.f;
 
     // One step: scores, softmax, weighted V sum from LDS buffer s % 2.
     auto compute = [&](int s) {
@@ -1363,9 +1474,7 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
         for (int t = 0; t < NH; ++t)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float a = fmaf(sc[t][i], sl2, -m);
-                top = fmaxf(top, a);
-                const float p = __builtin_amdgcn_exp2f(a);
+                const float p = __builtin_amdgcn_exp2f(fmaf(sc[t][i], sl2, -m));
                 l += p;
                 pb[2 * t + i / 8][i % 8] = static_cast<__bf16>(p);
             }
@@ -1417,7 +1526,7 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
                 *reinterpret_cast<uint2*>(oh + d0) = make_uint2(w0, w1);
             }
     }
-    if (__ballot(q_ok && !(top <= kFixedHeadroom)) != 0 && lane == 0) atomicExch(redo_word, gen);
+    if (__ballot(q_ok && !(lt <= kFixedHeadroomSum)) != 0 && lane == 0) atomicExch(redo_word, gen);
 }
 
 // Combine kernel: one workgroup per (query head, sequence). It rebuilds the
@@ -1671,10 +1780,10 @@ void launch_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
     auto fixed = f8 ? paged_prefill_fa_kernel<D, G, kFmtFp8> : paged_prefill_fa_kernel<D, G, kFmtBf16>;
     auto rescale = f8 ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQB, kPrefillRescale>
                       : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQB, kPrefillRescale>;
-    const dim3 grid_f((max_new + kFaRows - 1) / kFaRows, hkv, batch);
+    const dim3 grid_f(hkv * batch * ((max_new + kFaRows - 1) / kFaRows));
     const dim3 grid_r((max_new + BS * kPrefillQB - 1) / (BS * kPrefillQB), hkv * G, batch);
     hipLaunchKernelGGL(fixed, grid_f, dim3(64 * G), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
-                       static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, hkv, p->num_blocks,
+                       static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, batch, hkv, p->num_blocks,
                        total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err,
                        redo, gen);
     hipLaunchKernelGGL(rescale, grid_r, dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
@@ -1949,6 +2058,9 @@ extern "C" int mi_paged_prefill_attention(mi_kv_pool_t p, const uint16_t* q_rot,
     if (rc != MI_OK) return rc;
     if (total_tokens < 0 || max_new_tokens < 0 || batch > 65535) return MI_ERR_INVALID_ARG;
     if (batch == 0 || total_tokens == 0 || max_new_tokens == 0) return MI_OK;
+    if (static_cast<int64_t>(p->num_kv_heads) * batch * ((max_new_tokens + kFaRows - 1) / kFaRows) *
+            64 * (hq / p->num_kv_heads) > int64_t{0xffffffff})
+        return MI_ERR_UNSUPPORTED;                  // threads of the one-dimensional grid
     if (!q_rot || !out || !table || !ctx || !cu || q_rot == out) return MI_ERR_INVALID_ARG;
     if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(p->head_dim));
     return mikv::launch_paged_prefill(p, q_rot, out, table, mbps, ctx, cu, batch, total_tokens,

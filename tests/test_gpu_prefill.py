@@ -222,6 +222,19 @@ def test_prefill_then_decode_step():
         dev.close()
 
 
+def test_prefill_past_the_ranked_batch_limit():
+    """More than 64 sequences: the query blocks are taken in plain block-index
+    order instead of the longest-first ranking; both must cover every block."""
+    rng = np.random.default_rng(246)
+    B = 300
+    ctx = tuple(int(x) for x in rng.integers(0, 48, B))
+    n = tuple(int(x) for x in rng.integers(1, 70, B))
+    cfg = workloads.DecodeConfig("pfb", batch=B, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                                 block_size=16, num_blocks=B * 8 + 8, rope_theta=1e4,
+                                 ctx_draw="fixed", seed=17)
+    _full_check(workloads.make_prefill_case(cfg, ctx, n), "B=300")
+
+
 def test_prefill_errors_and_faults():
     cfg, ctx, n = workloads.PREFILL_CONFIGS["prefill_small"]
     case = workloads.make_prefill_case(cfg, ctx, n)
