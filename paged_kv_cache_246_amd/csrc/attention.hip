@@ -296,6 +296,7 @@ __device__ __forceinline__ int find_sequence(const int* TP, int batch, int x) {
 // weighted V sum.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -1140,9 +1141,29 @@ __global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1)
 // generation into the redo word, and the rescaling launch repeats the chunk. Keys after the block's last position are not used
 // (zero rows, so NaN bits in the cache tail never reach an MFMA); keys after
 // a query's own position are masked by selection on the diagonal steps.
-constexpr int kFaRows = 32;         // query tokens per wave
+constexpr int kFaRows = 32;         // query tokens per wave (one MFMA tile)
 constexpr int kFaKeys = 64;         // keys per step
-constexpr int kFaIdWindow = 512;    // block ids held in LDS at a time
+
+// Buffer-resource loads of one cache block: the block's base and size sit in
+// scalar registers, the lane's byte offset in the block is fixed for the whole
+// kernel, so a load carries no per-lane address arithmetic.
+typedef unsigned int fa_u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int fa_u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kFaBufferDword3 = 0x00020000;    // raw 32-bit buffer access (gfx9 family)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fa_rsrc(const uint8_t* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), static_cast<short>(0),
+                                             static_cast<int>(bytes), kFaBufferDword3);
+}
+template <typename Piece>
+__device__ __forceinline__ Piece fa_bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    if constexpr (sizeof(Piece) == 16) {
+        const fa_u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+        return Piece{t.x, t.y, t.z, t.w};
+    } else {
+        const fa_u32x2_t t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+        return Piece{t.x, t.y};
+    }
+}
 
 template <int D>
 struct FaLayout {
@@ -1160,9 +1181,9 @@ __device__ __forceinline__ int fa_vcol(int r) {
     return (r & ~15) + 8 * ((q >> 2) & 1) + (q & 3) + 4 * (q >> 3);
 }
 
-// Longest-first order of the query blocks of a chunk. Block y of sequence b
-// (y = 0 holds the chunk's last tokens) is ranked by A_b - kFaRows y, with
-// A_b = ctx_b + kFaRows nqb_b (its key count, rounded up to the block grid
+// Longest-first order of the query blocks (ROWS tokens) of a chunk. Block y
+// of sequence b (y = 0 holds the chunk's last tokens) is ranked by
+// A_b - ROWS y, with A_b = ctx_b + ROWS nqb_b (its key count, rounded up to the block grid
 // for y = 0), descending, ties in sequence order. The block of rank r is found
 // without a sort: the largest key count T with more than r blocks at or above
 // it, then the (r - count above T)-th sequence, in order, that has a block
@@ -1178,6 +1199,7 @@ struct FaBlock {
     int b, y;
 };
 constexpr int kFaRankBatch = 64;
+template <int ROWS>
 __device__ __forceinline__ FaBlock fa_block_of_rank(int r, const int32_t* __restrict__ ctx_lens,
                                                     const int32_t* __restrict__ cu, int batch, int total,
                                                     int max_new, int mbps, int lane) {
@@ -1187,8 +1209,8 @@ __device__ __forceinline__ FaBlock fa_block_of_rank(int r, const int32_t* __rest
         if (bb < batch) {
             const int row0 = cu[bb], n = cu[bb + 1] - row0, c = ctx_lens[bb];
             if (!(row0 < 0 || n < 0 || row0 + n > total || n > max_new || c < 0 || c + n > mbps * BS)) {
-                nq = (n + kFaRows - 1) / kFaRows;
-                A = c + kFaRows * nq;
+                nq = (n + ROWS - 1) / ROWS;
+                A = c + ROWS * nq;
             }
         }
     };
@@ -1207,7 +1229,7 @@ __device__ __forceinline__ FaBlock fa_block_of_rank(int r, const int32_t* __rest
         if (nb > 0) {
             amax = max(amax, Ab);
             amin = min(amin, Ab);
-            tmin = min(tmin, Ab - kFaRows * (nb - 1));
+            tmin = min(tmin, Ab - ROWS * (nb - 1));
         }
     }
     if (amax == amin) return plain();               // one key count: the plain order is longest-first
@@ -1216,7 +1238,7 @@ __device__ __forceinline__ FaBlock fa_block_of_rank(int r, const int32_t* __rest
         int c = 0;
         for (int bb = 0; bb < batch; ++bb) {
             const int Ab = __builtin_amdgcn_readlane(A, bb), nb = __builtin_amdgcn_readlane(nq, bb);
-            if (nb > 0 && Ab >= T) c += min(nb, (Ab - T) / kFaRows + 1);
+            if (nb > 0 && Ab >= T) c += min(nb, (Ab - T) / ROWS + 1);
         }
         return c;
     };
@@ -1234,16 +1256,16 @@ __device__ __forceinline__ FaBlock fa_block_of_rank(int r, const int32_t* __rest
     }
     const int T = lo;
     // blocks above T, then the sequences with a block exactly at T, in order
-    int above = (nq > 0 && A >= T + 1) ? min(nq, (A - T - 1) / kFaRows + 1) : 0;
+    int above = (nq > 0 && A >= T + 1) ? min(nq, (A - T - 1) / ROWS + 1) : 0;
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) above += __shfl_xor(above, x);
     const int rr = r - above;
-    const bool at = nq > 0 && A >= T && (A - T) % kFaRows == 0 && (A - T) / kFaRows < nq;
+    const bool at = nq > 0 && A >= T && (A - T) % ROWS == 0 && (A - T) / ROWS < nq;
     uint64_t mm = __ballot(at);
     if (rr < 0 || rr >= __popcll(mm)) return FaBlock{-1, 0};
     for (int i = 0; i < rr; ++i) mm &= mm - 1;
     const int src = __ffsll(static_cast<unsigned long long>(mm)) - 1;
-    return FaBlock{src, (__shfl(A, src) - T) / kFaRows};
+    return FaBlock{src, (__shfl(A, src) - T) / ROWS};
 }
 
 template <int D, int G, int FMT>
@@ -1255,19 +1277,20 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
     const float* __restrict__ kv_scales, uint16_t* __restrict__ out, uint32_t* __restrict__ err,
     uint32_t* __restrict__ redo_word, uint32_t gen) {
     using L = FaLayout<D>;
+    constexpr int ROWS = kFaRows;           // query tokens per workgroup (per wave and head)
     constexpr int NT = 64 * G;              // threads
     constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1;
     constexpr int CPR = D / 8;              // 8-element pieces per key row
     constexpr int KITEMS = kFaKeys * CPR;   // K pieces per step
-    constexpr int VITEMS = kFaKeys / 2 * CPR;   // V items: 8 dims of two keys
     constexpr int KPER = (KITEMS + NT - 1) / NT;
-    constexpr int VPER = (VITEMS + NT - 1) / NT;
     constexpr int NKK = D / 16;             // score MFMAs per 32-key half
     constexpr int NDT = D / 32;             // output dim tiles
     constexpr int NH = kFaKeys / 32;        // 32-key halves per step
     constexpr int BPS = kFaKeys / BS;       // cache blocks per step
+    constexpr int UPB = CPR / 8;            // V units (64 lanes: 8 key pairs x 8 pieces) per cache block
+    constexpr int VUNITS = BPS * UPB;       // V units per step
+    constexpr int VPER = (VUNITS + G - 1) / G;
     __shared__ __align__(16) char lds[2 * L::BUF];
-    __shared__ int32_t ids_lds[kFaIdWindow];
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1284,20 +1307,20 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
                 atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
         }
     }
-    const FaBlock fb = fa_block_of_rank(static_cast<int>(blockIdx.x) / hkv, ctx_lens, cu, batch, total,
-                                        max_new, mbps, lane);
+    const FaBlock fb = fa_block_of_rank<ROWS>(static_cast<int>(blockIdx.x) / hkv, ctx_lens, cu, batch,
+                                              total, max_new, mbps, lane);
     if (fb.b < 0) return;
-    const int b = fb.b;
-    const int qblk = fb.y;
+    const int b = __builtin_amdgcn_readfirstlane(fb.b);
+    const int qblk = __builtin_amdgcn_readfirstlane(fb.y);
     const int h = g * G + w;
     const int hq = hkv * G;
     const int row0 = cu[b];
     const int nnew = cu[b + 1] - row0;
     const int ctx = ctx_lens[b];
-    const int nqb = (nnew + kFaRows - 1) / kFaRows;
-    const int j0 = (nqb - 1 - qblk) * kFaRows;   // longest blocks first
+    const int nqb = (nnew + ROWS - 1) / ROWS;
+    const int j0 = (nqb - 1 - qblk) * ROWS;     // longest blocks first
     const int p_first = ctx + j0;
-    const int p_last = ctx + min(j0 + kFaRows, nnew) - 1;
+    const int p_last = ctx + min(j0 + ROWS, nnew) - 1;
     const int nks = p_last / kFaKeys + 1;       // steps holding keys 0 .. p_last
     const int ks_m = (p_first + 1) / kFaKeys;   // steps before this are unmasked for every query
     const int jq = j0 + col;                    // this lane's query token
@@ -1319,70 +1342,67 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
             qop[kk] = q_ok ? *reinterpret_cast<const uint4*>(qh + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0);
     }
 
-    // Block ids of the sequence in an LDS window of kFaIdWindow entries,
-    // refilled between barriers (range-checked when filled: a bad id is
-    // recorded and replaced by 0).
-    const int nblk_seq = p_last / BS + 1;
-    int ids_base = 0;
-    auto fill_ids = [&](int base) {
-        ids_base = base;
-        for (int i = tid; i < kFaIdWindow; i += NT) {
-            int32_t id = 0;
-            if (base + i < nblk_seq) {
-                id = table[static_cast<size_t>(b) * mbps + base + i];
-                if (id < 0 || id >= num_blocks) {
-                    atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
-                    id = 0;
-                }
-            }
-            ids_lds[i] = id;
-        }
-    };
-
-    // Copy of one step (keys 64 s .. 64 s + 63) through registers into LDS:
-    // K in 8-element pieces, V in pairs of keys (8 dims each) for the
-    // transposed store. Every load is issued (positions past p_last read
-    // p_last's row and are zeroed when stored), so the waits before the
-    // stores count exactly the loads of the older stage.
+    // Copy of one step (keys 64 s .. 64 s + 63) through registers into LDS.
+    // Each load of a wave reads one cache block: K as rows of 8-element
+    // pieces (item it = tid + u NT is row it / CPR, piece it % CPR), V in
+    // units of 8 key pairs x 8 pieces (unit c = w + G u: block c / UPB,
+    // pieces 8 (c % UPB) .. + 7; lane: pair lane & 7, piece + lane >> 3) for
+    // the transposed store. Blocks past the chunk's last key are clamped to
+    // its block; rows past p_last are read (they lie in an allocated block)
+    // and zeroed when stored. The block ids of the next fetch are read one
+    // step ahead (scalar loads, range-checked: a bad id is recorded and
+    // replaced by 0).
     typedef typename std::conditional<FMT == kFmtBf16, uint4, uint2>::type Piece;
     struct Stage {
         Piece k[KPER];
         Piece v[VPER][2];
     };
-    const size_t head_off = static_cast<size_t>(g) * BS * D;
-    auto addr = [&](int pos, int piece) {     // pos <= p_last
-        const int32_t id = ids_lds[pos / BS - ids_base];
-        return (static_cast<size_t>(id) * hkv * BS * D + head_off + static_cast<size_t>(pos % BS) * D + 8 * piece) * ESZ;
-    };
-    // K pieces: item it = tid + u NT is row it / CPR (16 consecutive lanes
-    // read one 16 * D-byte row), so the 64 lanes of a wave read rows of one
-    // cache block when NT is a multiple of 64 and CPR divides 64: the block's
-    // address is a wave-uniform base, the lane's in-block offset is fixed.
-    static_assert(64 % CPR == 0 && (BS * CPR) % 64 == 0, "a wave's K pieces lie in one cache block");
-    uint32_t koff[KPER];
+    const uint32_t blk_bytes = static_cast<uint32_t>(hkv) * BS * D * ESZ;
+    const uint32_t head_off = static_cast<uint32_t>(g) * BS * D * ESZ;
+    const int last_blk = p_last / BS;
+    const int32_t* trow = table + static_cast<size_t>(b) * mbps;
+    int jbk[KPER], jbv[VPER];                   // block of the step read by load u (wave-uniform)
+    uint32_t koff[KPER], voff[VPER];            // the lane's byte offset in that block
 #pragma unroll
     for (int u = 0; u < KPER; ++u) {
-        const int it = min(tid + u * NT, KITEMS - 1);
-        koff[u] = static_cast<uint32_t>((head_off + static_cast<size_t>((it / CPR) % BS) * D + 8 * (it % CPR)) * ESZ);
+        const int it0 = min(w * 64 + u * NT, KITEMS - 64);     // the wave's first item
+        const int it = it0 + lane;
+        jbk[u] = (it0 / CPR) / BS;
+        koff[u] = head_off + static_cast<uint32_t>(((it / CPR) % BS) * D + 8 * (it % CPR)) * ESZ;
     }
-    const size_t blk_bytes = static_cast<size_t>(hkv) * BS * D * ESZ;
-    auto fetch = [&](int s, Stage& st) {
 #pragma unroll
-        for (int u = 0; u < KPER; ++u) {
-            const int it0 = min(w * 64 + u * NT, KITEMS - 1);            // the wave's first item
-            const int row = min(kFaKeys * s + it0 / CPR, p_last);
-            const int32_t id = __builtin_amdgcn_readfirstlane(ids_lds[row / BS - ids_base]);
-            const uint8_t* base = kc + static_cast<size_t>(id) * blk_bytes;
-            st.k[u] = *reinterpret_cast<const Piece*>(base + koff[u]);
-        }
+    for (int u = 0; u < VPER; ++u) {
+        const int c = min(w + G * u, VUNITS - 1);
+        jbv[u] = c / UPB;
+        voff[u] = head_off + static_cast<uint32_t>((2 * (lane & 7)) * D + 8 * (8 * (c % UPB) + (lane >> 3))) * ESZ;
+    }
+    bool bad_id = false;                        // wave-uniform; recorded once after the loop
+    int32_t kid[KPER], vid[VPER];
+    auto load_ids = [&](int s) {               // all scalar loads first, then the checks
+        int32_t rk[KPER], rv[VPER];
+#pragma unroll
+        for (int u = 0; u < KPER; ++u) rk[u] = trow[min(BPS * s + jbk[u], last_blk)];
+#pragma unroll
+        for (int u = 0; u < VPER; ++u) rv[u] = trow[min(BPS * s + jbv[u], last_blk)];
+        auto check = [&](int32_t id) {
+            const bool ok = id >= 0 && id < num_blocks;
+            bad_id |= !ok;
+            return __builtin_amdgcn_readfirstlane(ok ? id : 0);
+        };
+#pragma unroll
+        for (int u = 0; u < KPER; ++u) kid[u] = check(rk[u]);
+#pragma unroll
+        for (int u = 0; u < VPER; ++u) vid[u] = check(rv[u]);
+    };
+    auto fetch = [&](Stage& st) {
+#pragma unroll
+        for (int u = 0; u < KPER; ++u)
+            st.k[u] = fa_bload<Piece>(fa_rsrc(kc + static_cast<size_t>(kid[u]) * blk_bytes, blk_bytes), koff[u]);
 #pragma unroll
         for (int u = 0; u < VPER; ++u) {
-            const int it = min(tid + u * NT, VITEMS - 1);
-            const int pos = kFaKeys * s + 2 * (it % (kFaKeys / 2));
-            const int piece = it / (kFaKeys / 2);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                st.v[u][e] = *reinterpret_cast<const Piece*>(vc + addr(min(pos + e, p_last), piece));
+            const __amdgpu_buffer_rsrc_t r = fa_rsrc(vc + static_cast<size_t>(vid[u]) * blk_bytes, blk_bytes);
+            st.v[u][0] = fa_bload<Piece>(r, voff[u]);
+            st.v[u][1] = fa_bload<Piece>(r, voff[u] + D * ESZ);
         }
     };
     auto widen = [&](const Piece& x) -> uint4 {       // 8 elements as bf16 (E4M3 codes widened exactly)
@@ -1393,28 +1413,42 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
                               fp8x2_to_bf16x2<false>(x.y), fp8x2_to_bf16x2<true>(x.y));
         }
     };
-    auto stash = [&](int s, const Stage& st) {
-        char* kb = lds + (s & 1) * L::BUF;
-        char* vb = kb + L::KBYTES;
+    // LDS destinations (within a stage) of the lane's K pieces and V pairs
+    uint32_t kdst[KPER], vdst[VPER];
+#pragma unroll
+    for (int u = 0; u < KPER; ++u) {
+        const int it = tid + u * NT;
+        kdst[u] = static_cast<uint32_t>((it / CPR) * L::KROW + (it % CPR) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+        const int c = min(w + G * u, VUNITS - 1);
+        const int r = BS * (c / UPB) + 2 * (lane & 7);
+        const int piece = 8 * (c % UPB) + (lane >> 3);
+        vdst[u] = static_cast<uint32_t>(L::KBYTES + (8 * piece) * L::VROW + fa_vcol(r) * 2);
+    }
+    auto stash_rows = [&](int s, const Stage& st, auto tail) {
+        constexpr bool TAIL = decltype(tail)::value;
+        char* buf = lds + (s & 1) * L::BUF;
         const int rows = p_last + 1 - kFaKeys * s;     // valid key rows of the step (1 .. 64)
 #pragma unroll
         for (int u = 0; u < KPER; ++u) {
             const int it = tid + u * NT;
-            if (it < KITEMS) {
-                const uint4 x = (it / CPR) < rows ? widen(st.k[u]) : make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4*>(kb + (it / CPR) * L::KROW + (it % CPR) * 16) = x;
+            if (KITEMS % NT == 0 || it < KITEMS) {
+                uint4 x = widen(st.k[u]);
+                if (TAIL && (it / CPR) >= rows) x = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4*>(buf + kdst[u]) = x;
             }
         }
 #pragma unroll
         for (int u = 0; u < VPER; ++u) {
-            const int it = tid + u * NT;
-            if (it < VITEMS) {
-                const int r = 2 * (it % (kFaKeys / 2));       // keys r, r + 1: adjacent columns
-                const int piece = it / (kFaKeys / 2);
-                const uint4 a = r < rows ? widen(st.v[u][0]) : make_uint4(0, 0, 0, 0);
-                const uint4 c = r + 1 < rows ? widen(st.v[u][1]) : make_uint4(0, 0, 0, 0);
+            if (VUNITS % G == 0 || w + G * u < VUNITS) {
+                const int r = BS * ((w + G * u) / UPB) + 2 * (lane & 7);
+                uint4 a = widen(st.v[u][0]), c = widen(st.v[u][1]);
+                if (TAIL && r >= rows) a = make_uint4(0, 0, 0, 0);
+                if (TAIL && r + 1 >= rows) c = make_uint4(0, 0, 0, 0);
                 const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
-                char* dst = vb + (8 * piece) * L::VROW + fa_vcol(r) * 2;
+                char* dst = buf + vdst[u];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
@@ -1423,6 +1457,10 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
                 }
             }
         }
+    };
+    auto stash = [&](int s, const Stage& st) {
+        if (p_last + 1 - kFaKeys * s >= kFaKeys) stash_rows(s, st, std::false_type{});
+        else stash_rows(s, st, std::true_type{});
     };
 
     f32x16_t oacc[NDT];
@@ -1469,15 +1507,23 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
             mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
             m = q_ok ? mx : 0.f;
         }
+        // the row sum adds the weights as they enter the MFMA (bf16), so
+        // numerator and denominator use the same rounded weights
         bf16x8_t pb[2 * NH];
 #pragma unroll
         for (int t = 0; t < NH; ++t)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sc[t][i], sl2, -m));
-                l += p;
-                pb[2 * t + i / 8][i % 8] = static_cast<__bf16>(p);
-            }
+            for (int i = 0; i < 16; ++i)
+                pb[2 * t + i / 8][i % 8] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[t][i], sl2, -m)));
+        const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+#pragma unroll
+        for (int a = 0; a < 2 * NH; ++a) {
+            const bf16x8_t x = pb[a];
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, l, false);
+        }
 #pragma unroll
         for (int a = 0; a < 2 * NH; ++a)
 #pragma unroll
@@ -1492,23 +1538,21 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
     // LDS, then stored to the other LDS buffer; one barrier per step. The
     // fetch is issued unconditionally (past the last step it reads the last
     // step again and is dropped), so every path keeps the same loads in
-    // flight.
+    // flight. The ids of step s + 2 are read while step s is computed.
     Stage st;
-    fill_ids(0);
-    __syncthreads();
-    fetch(0, st);
+    load_ids(0);
+    fetch(st);
+    load_ids(min(1, nks - 1));
     stash(0, st);
     __syncthreads();
     for (int s = 0; s < nks; ++s) {
-        if (BPS * (min(s + 1, nks - 1) + 1) - ids_base > kFaIdWindow) {   // uniform: next id window
-            fill_ids(BPS * min(s + 1, nks - 1));
-            __syncthreads();
-        }
-        fetch(min(s + 1, nks - 1), st);
+        fetch(st);                              // step s + 1 (the last step again past the end)
+        load_ids(min(s + 2, nks - 1));
         compute(s);
         if (s + 1 < nks) stash(s + 1, st);
         __syncthreads();
     }
+    if (bad_id && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
 
     const float lt = l + __shfl_xor(l, 32);
     if (q_ok) {
