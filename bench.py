@@ -112,9 +112,11 @@ def graph_of(torch, fn, reps):
     return g, side
 
 
-def run_attention_bench(args, torch, mk, workloads, kv_format="bf16"):
+def run_attention_bench(args, torch, mk, workloads, kv_format="bf16", dot=False):
     """The long-context decode step (write + attention) over a bf16 cache or an
-    8-bit (E4M3, unit scales) cache of the same workload."""
+    8-bit (E4M3, unit scales) cache of the same workload. dot: the pool takes
+    MI_POOL_DECODE_DOT (the attention on vector-ALU dot products); the
+    one-launch and flushed forms are then left out."""
     dev = "cuda:0"
     cfg = workloads.CONFIGS["qwen3_8b_long"]
     case = workloads.make_decode_case(cfg, pool="bench", kv_format=kv_format)
@@ -126,8 +128,8 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16"):
     table = torch.from_numpy(case.block_table).to(dev)
     ctx = torch.from_numpy(case.context_lens).to(dev)
     mbps, max_ctx = case.block_table.shape[1], int(case.context_lens.max())
-    pool = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp, vp,
-                              flags=mk.MI_POOL_KV_FP8 if kv_elem == 1 else 0)
+    flags = (mk.MI_POOL_KV_FP8 if kv_elem == 1 else 0) | (mk.MI_POOL_DECODE_DOT if dot else 0)
+    pool = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp, vp, flags=flags)
     ws_bytes = mk.mi_paged_gqa_decode_split_workspace_bytes(pool, B, Hq, max_ctx, args.split)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -161,7 +163,7 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16"):
 
     # The same step as one launch (mi_paged_gqa_decode_step), timed alike.
     ms_one = None
-    if not args.split:
+    if not args.split and not dot:
         ws1_bytes = mk.mi_paged_gqa_decode_workspace_bytes(pool, B, Hq, max_ctx)
         ws1 = torch.empty(ws1_bytes, dtype=torch.uint8, device=dev)
 
@@ -181,7 +183,7 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16"):
     # Flushed: single steps (write + attention), each after a fill that evicts
     # the caches; the attention launch is timed on its own inside the step.
     flushed = None
-    if not args.no_flushed:
+    if not args.no_flushed and not dot:
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
         cold_step, cold_attn = [], []
         for i in range(FLUSHED_REPS):
@@ -213,14 +215,35 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16"):
     )
 
 
-def run_prefill_bench(args, torch, mk, workloads):
-    """Prefill chunk on a Qwen3-8B-shaped layer: 4 fresh prompts of 2048 tokens
+def run_dot_compare(args, torch, mk, workloads):
+    """The long-context step's attention in its two forms, bf16 and 8-bit
+    caches: the matrix-core kernel (default) against the dot-product kernel
+    (MI_POOL_DECODE_DOT), mean launch time and algorithmic GB/s of each."""
+    res = {"workload": "qwen3-8b-shaped long-context decode attention (mi_paged_gqa_decode)"}
+    for fmt in ("bf16", "fp8"):
+        row = {}
+        for name, dot in (("mfma", False), ("dot", True)):
+            r = run_attention_bench(args, torch, mk, workloads, kv_format=fmt, dot=dot)
+            ms = float(np.mean(r["attn_ms"]))
+            row[name] = {"attention_avg_launch_ms": round(ms, 5),
+                         "GBps": round(r["attn_bytes"] / (ms * 1e-3) / 1e9, 1),
+                         "hbm_frac": round(r["attn_bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        row["dot_over_mfma_time"] = round(row["dot"]["attention_avg_launch_ms"]
+                                          / row["mfma"]["attention_avg_launch_ms"], 3)
+        res[fmt] = row
+    return res
+
+
+def run_prefill_bench(args, torch, mk, workloads, cached=False):
+    """Prefill chunk on a Qwen3-8B-shaped layer: 4 prompts of 2048 new tokens
     (packed, 8192 rows): mi_write_prefill_kv + mi_paged_prefill_attention.
-    The causal attention is a dense contraction: reported against the bf16
-    MFMA peak."""
+    Fresh prompts, or (cached) chunks after 4000/6000/2000/8000 cached tokens
+    (chunked prefill). The causal attention is a dense contraction: reported
+    against the bf16 MFMA peak."""
     dev = "cuda:0"
     cfg = workloads.PREFILL_CONFIGS["qwen3_8b_prefill"][0]
-    ctx_l, new_l = (0, 0, 0, 0), (2048, 2048, 2048, 2048)
+    ctx_l = (4000, 6000, 2000, 8000) if cached else (0, 0, 0, 0)
+    new_l = (2048, 2048, 2048, 2048)
     case = workloads.make_prefill_case(cfg, ctx_l, new_l, pool="bench")
     B, T = len(ctx_l), int(case.cu_seqlens[-1])
     Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
@@ -266,7 +289,9 @@ def run_prefill_bench(args, torch, mk, workloads):
     flops = workloads.prefill_flops(case.context_lens, case.new_lens, Hq, D)
     tflops = flops / (attn_ms * 1e-3) / 1e12
     return {
-        "workload": "qwen3-8b-shaped prefill, 4 fresh prompts x 2048 tokens (32/8 heads, D 128)",
+        "workload": ("qwen3-8b-shaped prefill, 4 chunks x 2048 tokens after 4000/6000/2000/8000 "
+                     "cached tokens (32/8 heads, D 128)" if cached else
+                     "qwen3-8b-shaped prefill, 4 fresh prompts x 2048 tokens (32/8 heads, D 128)"),
         "steps": steps,
         "ms_per_step": round(ms, 5),
         "tokens_per_s": round(T / (ms * 1e-3), 1),
@@ -764,6 +789,12 @@ def main():
                     help="skip the cache-flushed timings of the long-context step and the layer")
     ap.add_argument("--no-stream-read", action="store_true",
                     help="skip the streaming-read bandwidth measurement")
+    ap.add_argument("--no-dot", action="store_true",
+                    help="skip the dot-product form of the attention (MI_POOL_DECODE_DOT)")
+    ap.add_argument("--dot-only", action="store_true",
+                    help="time only the two attention forms, bf16 and 8-bit (for their kernel profile)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill chunks (for their kernel profile)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -798,6 +829,19 @@ def main():
         print(json.dumps({"metric": "layer-step tokens/s", "value": lay["tokens_per_s"],
                           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
                           "warmup": args.warmup, "layer_step": lay}), flush=True)
+        return
+
+    if args.dot_only:
+        print(json.dumps({"metric": "decode attention, matrix-core and dot-product forms",
+                          "steps": args.steps, "warmup": args.warmup,
+                          "decode_dot_form": run_dot_compare(args, torch, mk, workloads)}), flush=True)
+        return
+
+    if args.prefill_only:
+        print(json.dumps({"metric": "prefill chunk attention", "steps": args.steps, "warmup": args.warmup,
+                          "prefill": run_prefill_bench(args, torch, mk, workloads),
+                          "prefill_cached_prefix": run_prefill_bench(args, torch, mk, workloads,
+                                                                     cached=True)}), flush=True)
         return
 
     if args.small_only:
@@ -888,8 +932,11 @@ def main():
             "step_speedup_vs_bf16": round(ms / ms8, 3),
             "one_launch_ms_per_step": None if r8["ms_one"] is None else round(r8["ms_one"], 5),
         }
+    if not args.no_dot:
+        line["decode_dot_form"] = run_dot_compare(args, torch, mk, workloads)
     if not args.no_prefill:
         line["prefill"] = run_prefill_bench(args, torch, mk, workloads)
+        line["prefill_cached_prefix"] = run_prefill_bench(args, torch, mk, workloads, cached=True)
     if not args.no_offload:
         line["kv_offload"] = run_offload_bench(args, torch, mk, workloads)
     if not args.no_serving:

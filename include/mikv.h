@@ -88,7 +88,8 @@ enum {
 enum {
     MI_POOL_HOST_ONLY = 1u,           /* block bookkeeping only: no device memory, no kernels */
     MI_POOL_KV_FP8 = 2u,              /* 8-bit cache: E4M3 codes with per-KV-head scales */
-    MI_POOL_SWAP_STAGING = 4u         /* device staging for scattered KV swaps (mi_kv_swap_out/in) */
+    MI_POOL_SWAP_STAGING = 4u,        /* device staging for scattered KV swaps (mi_kv_swap_out/in) */
+    MI_POOL_DECODE_DOT = 8u           /* mi_paged_gqa_decode on vector-ALU dot products, not MFMA */
 };
 
 /* Static description of a status code. Never NULL. */
@@ -123,7 +124,15 @@ typedef struct mi_kv_pool_s* mi_kv_pool_t;
  *               MI_POOL_SWAP_STAGING: also allocate a device staging buffer
  *                 for KV swaps (two halves of min(64 MiB, pool bytes), freed
  *                 on destroy), with which mi_kv_swap_out/in move a run of
- *                 scattered device blocks in one transfer.
+ *                 scattered device blocks in one transfer;
+ *               MI_POOL_DECODE_DOT: mi_paged_gqa_decode computes q.k and the
+ *                 weighted V sum with packed bf16 dot products and fp32 FMAs
+ *                 on the vector ALUs (one query head at a time per tile)
+ *                 instead of the matrix cores: a second implementation of
+ *                 the same operation, kept to compare the two designs, with
+ *                 the same partition, workspace and tolerance. The other
+ *                 entry points (decode step, layer, prefill, allocation-free
+ *                 decode) are unaffected.
  * The free-block stack starts full; the first allocation returns ids 0, 1, ...
  * The current HIP device at this call is the pool's device.
  */

@@ -29,6 +29,7 @@ MI_FAULT_CONTEXT_LEN = 2
 MI_POOL_HOST_ONLY = 1
 MI_POOL_KV_FP8 = 2
 MI_POOL_SWAP_STAGING = 4
+MI_POOL_DECODE_DOT = 8
 MI_EVICT_LIFO = 0
 MI_EVICT_FIFO = 1
 MI_EVICT_LRU = 2

@@ -948,6 +948,355 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
     }
 }
 
+// ===================================== paged GQA decode, dot-product form
+// The decode attention with both contractions on the vector ALUs instead of
+// the matrix cores: the same work partition, ring of in-flight tiles and
+// partial format as the MFMA kernel above, selected for mi_paged_gqa_decode
+// by the pool flag MI_POOL_DECODE_DOT (the comparison design). Lane
+// l = LAM r + c of the wave holds key rows r, r + TPI, ... (TPI = 64 / LAM
+// rows per load instruction) of a 16-token tile and, of each row, the
+// 8-element pieces c + LAM j; q.k is a chain of packed bf16 dot products with
+// fp32 accumulation, summed over the LAM lanes of a row by DPP moves. Every
+// lane keeps a running max, sum and weighted V sum per query head over its
+// own rows; the rows are merged at the end of a segment piece. E4M3 codes are
+// widened to bf16 exactly before use; the per-head scales multiply the
+// scores and the weighted V sum, as in the MFMA kernel.
+template <int D, int LAM, int FMT>
+struct DotTile {
+    static constexpr int ESZ = FMT == kFmtBf16 ? 2 : 1;     // bytes per element
+    static constexpr int TPI = 64 / LAM;                      // key rows per load instruction
+    static constexpr int NT = BS / TPI;                       // key rows per lane per tile
+    static constexpr int NJ = D / (8 * LAM);                  // 8-element pieces per lane per row
+    static constexpr int PB = 8 * ESZ;                        // bytes per piece
+    static constexpr int ROW = D * ESZ;                       // bytes per key row
+    static_assert(NJ >= 1 && NJ * 8 * LAM == D, "head_dim / lane split");
+};
+
+// Lane sums inside a DPP row of 16 lanes (row_mask and bank_mask all on).
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7 - i within each 8
+constexpr int kDppRowMirror = 0x140;    // lane i <- lane 15 - i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the LAM consecutive lanes of one key row (LAM = 8 or 16); each of
+// them ends with the same bits (every step adds a commutative pair).
+template <int LAM>
+__device__ __forceinline__ float dot_row_sum(float x) {
+    x += dpp_move<kDppQuadSwap1>(x);
+    x += dpp_move<kDppQuadSwap2>(x);
+    x += dpp_move<kDppHalfMirror>(x);
+    if constexpr (LAM == 16) x += dpp_move<kDppRowMirror>(x);
+    return x;
+}
+
+// An 8-element piece as four bf16 pairs (E4M3 codes widened exactly).
+template <int FMT>
+__device__ __forceinline__ uint4 dot_piece(const uint32_t (&w)[FMT == kFmtBf16 ? 4 : 2]) {
+    if constexpr (FMT == kFmtBf16) {
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+        return make_uint4(fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
+                          fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1]));
+    }
+}
+
+__device__ __forceinline__ float dot8_bf16(uint4 a, uint4 b, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x),
+                                          acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y),
+                                          acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z),
+                                          acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w),
+                                          acc, false);
+    return acc;
+}
+
+// Per-wave state: the G heads' query pieces, running max (log2 units), sums
+// and weighted V sums over the lane's key rows.
+template <int D, int G, int LAM, int FMT>
+struct DotCols {
+    using TS = DotTile<D, LAM, FMT>;
+    static constexpr int NT = TS::NT;
+    static constexpr int NJ = TS::NJ;
+    static constexpr int PW = TS::PB / 4;
+    uint4 qv[G][NJ];
+    float m[G], l[G];
+    float acc[G][NJ][8];
+    float sl2;
+    int r;
+
+    // One tile: with TAIL, key rows >= valid_rows are left out by selection
+    // (their bits may be anything, NaN included).
+    template <bool TAIL>
+    __device__ __forceinline__ void consume(const uint32_t (&kw)[NT][NJ][PW], const uint32_t (&vw)[NT][NJ][PW],
+                                            int valid_rows) {
+        constexpr int TPI = TS::TPI;
+        bool valid[NT];
+        uint4 kp[NT][NJ], vp[NT][NJ];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            valid[t] = !TAIL || t * TPI + r < valid_rows;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                kp[t][j] = dot_piece<FMT>(kw[t][j]);
+                vp[t][j] = valid[t] ? dot_piece<FMT>(vw[t][j]) : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float s[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                float a = 0.f;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) a = dot8_bf16(qv[h][j], kp[t][j], a);
+                s[t] = dot_row_sum<LAM>(a) * sl2;
+                if (TAIL && !valid[t]) s[t] = kNegInf;
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int t = 1; t < NT; ++t) mx = fmaxf(mx, s[t]);
+            if (mx > m[h] + kRescaleSlack) {          // lane-local: its own rows only
+                const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
+                m[h] = mx;
+                l[h] *= alpha;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][j][e] *= alpha;
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                float p = __builtin_amdgcn_exp2f(s[t] - m[h]);
+                if (TAIL) p = valid[t] ? p : 0.f;
+                l[h] += p;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const uint32_t w4[4] = {vp[t][j].x, vp[t][j].y, vp[t][j].z, vp[t][j].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[h][j][2 * e] = fmaf(p, __uint_as_float(w4[e] << 16), acc[h][j][2 * e]);
+                        acc[h][j][2 * e + 1] = fmaf(p, __uint_as_float(w4[e] & 0xffff0000u), acc[h][j][2 * e + 1]);
+                    }
+                }
+            }
+        }
+    }
+};
+
+// Ring of PF + 1 tiles in registers (the MFMA ring's scheme: slots are
+// compile-time, every prefetch is unconditional and clamped to the last tile).
+template <int D, int LAM, int FMT, int PF>
+struct DotRing {
+    using TS = DotTile<D, LAM, FMT>;
+    static constexpr int NT = TS::NT;
+    static constexpr int NJ = TS::NJ;
+    static constexpr int PW = TS::PB / 4;
+    uint32_t kw[PF + 1][NT][NJ][PW];
+    uint32_t vw[PF + 1][NT][NJ][PW];
+    const char* kbase;
+    const char* vbase;
+    size_t blk_stride;
+    uint32_t loff[NT][NJ];
+    int32_t my_id;   // lane i holds the chunk's i-th block id
+
+    template <int S>
+    __device__ __forceinline__ void load(int tile) {
+        const int32_t id = __builtin_amdgcn_readlane(my_id, tile);
+        const char* kb = kbase + static_cast<size_t>(id) * blk_stride;
+        const char* vb = vbase + static_cast<size_t>(id) * blk_stride;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ld_words<TS::PB, true>(kb, loff[t][j], kw[S][t][j]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ld_words<TS::PB, true>(vb, loff[t][j], vw[S][t][j]);
+    }
+    template <int S>
+    __device__ __forceinline__ void prologue(int nblk) {
+        if constexpr (S < PF) {
+            load<S>(min(S, nblk - 1));
+            prologue<S + 1>(nblk);
+        }
+    }
+    template <int U, class Cols>
+    __device__ __forceinline__ void steady(int i, int nblk, Cols& cols) {
+        if constexpr (U <= PF) {
+            load<(U + PF) % (PF + 1)>(min(i + U + PF, nblk - 1));
+            cols.template consume<false>(kw[U], vw[U], BS);
+            steady<U + 1>(i, nblk, cols);
+        }
+    }
+    template <int U, class Cols>
+    __device__ __forceinline__ void rest(int i, int nblk, int valid_rows, Cols& cols) {
+        if constexpr (U <= PF) {
+            const int tile = i + U;
+            if (tile < nblk - 1 || (tile == nblk - 1 && valid_rows == BS))
+                cols.template consume<false>(kw[U], vw[U], BS);
+            else if (tile == nblk - 1)
+                cols.template consume<true>(kw[U], vw[U], valid_rows);
+            rest<U + 1>(i, nblk, valid_rows, cols);
+        }
+    }
+    template <class Cols>
+    __device__ __forceinline__ void run(int nblk, int last_rows, Cols& cols) {
+        prologue<0>(nblk);
+        int i = 0;
+        for (; i + PF + 1 < nblk; i += PF + 1) steady<0>(i, nblk, cols);
+        load<PF>(min(i + PF, nblk - 1));
+        rest<0>(i, nblk, last_rows, cols);
+    }
+};
+
+template <int D, int G, int LAM, int FMT, int PF>
+__global__ __launch_bounds__(64) void paged_attn_dot_kernel(
+    const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+    const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens, int32_t batch,
+    int32_t hkv, int32_t num_blocks, int32_t max_ctx, int32_t min_tiles, float scale_log2,
+    const float* __restrict__ kv_scales, float* __restrict__ part_acc, float2* __restrict__ part_ml,
+    uint16_t* __restrict__ out, uint32_t* __restrict__ err) {
+    using TS = DotTile<D, LAM, FMT>;
+    constexpr int NT = TS::NT;
+    constexpr int NJ = TS::NJ;
+    constexpr size_t TILE = static_cast<size_t>(BS) * TS::ROW;   // bytes per (block, head) tile
+    __shared__ int TP[kMaxBatch + 1];
+    const int w = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int r = lane / LAM;
+    const int c = lane % LAM;
+
+    bool bad_len;
+    const int T = build_tile_prefix(ctx_lens, batch, mbps, max_ctx, hkv, TP, &bad_len, lane);
+    __syncthreads();
+    if (bad_len && w == 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+    if (T == 0) return;
+    const int W = active_waves(T, gridDim.x, min_tiles);
+    if (w >= W) return;
+    const int start = range_start(w, T, W);
+    const int end = range_start(w + 1, T, W);
+
+    int pos = start;
+    int b = find_sequence(TP, batch, pos);
+    bool first_piece = true;
+    while (pos < end) {
+        while (__builtin_amdgcn_readfirstlane(TP[b + 1]) <= pos) ++b;
+        const int seg0 = __builtin_amdgcn_readfirstlane(TP[b]);
+        const int nt = (__builtin_amdgcn_readfirstlane(TP[b + 1]) - seg0) / hkv;
+        const int rel = pos - seg0;
+        const int g = rel / nt;
+        const int t0 = rel - g * nt;
+        const int t1 = min(nt, t0 + (end - pos));
+        const int L = ctx_lens[b] + 1;
+
+        DotCols<D, G, LAM, FMT> cols;
+        cols.r = r;
+        cols.sl2 = scale_log2;
+        float vscale = 1.f;
+        if constexpr (FMT == kFmtFp8) {
+            cols.sl2 *= kv_scales[g];
+            vscale = kv_scales[hkv + g];
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                cols.qv[h][j] = *reinterpret_cast<const uint4*>(
+                    q_rot + (static_cast<size_t>(b) * hkv * G + g * G + h) * D + (c + LAM * j) * 8);
+            cols.m[h] = kNegInf;
+            cols.l[h] = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cols.acc[h][j][e] = 0.f;
+        }
+
+        DotRing<D, LAM, FMT, PF> ring;
+        ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
+        ring.vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
+        ring.blk_stride = static_cast<size_t>(hkv) * TILE;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ring.loff[t][j] = (t * TS::TPI + r) * TS::ROW + (c + LAM * j) * TS::PB;
+
+        for (int s0 = t0; s0 < t1; s0 += 64) {
+            const int nblk = min(64, t1 - s0);
+            int32_t id = 0;
+            if (lane < nblk) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
+            const bool bad_id = lane < nblk && (id < 0 || id >= num_blocks);
+            if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+            ring.my_id = bad_id ? 0 : id;
+            const int last_rows = (s0 + nblk == nt) ? L - (nt - 1) * BS : BS;
+            ring.run(nblk, last_rows, cols);
+        }
+
+        // merge the TPI key-row groups (lanes c, c + LAM, ... hold the same dims)
+        const bool whole = (t0 == 0 && t1 == nt);
+        const size_t slot = 2 * static_cast<size_t>(w) + (first_piece ? 0 : 1);
+        uint16_t* o = out + (static_cast<size_t>(b) * hkv * G + g * G) * D;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float M = cols.m[h];
+#pragma unroll
+            for (int x = LAM; x < 64; x *= 2) M = fmaxf(M, __shfl_xor(M, x));
+            const float f = (cols.m[h] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(cols.m[h] - M);
+            float lt = cols.l[h] * f;
+#pragma unroll
+            for (int x = LAM; x < 64; x *= 2) lt += __shfl_xor(lt, x);
+            float red[NJ][8];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float a = cols.acc[h][j][e] * f;
+#pragma unroll
+                    for (int x = LAM; x < 64; x *= 2) a += __shfl_xor(a, x);
+                    red[j][e] = a;
+                }
+            if (r != 0) continue;
+            if (whole) {
+                const float inv = vscale / lt;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    uint32_t wd[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        wd[e] = static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e] * inv)) |
+                                (static_cast<uint32_t>(f32_to_bf16_rne(red[j][2 * e + 1] * inv)) << 16);
+                    *reinterpret_cast<uint4*>(o + h * D + (c + LAM * j) * 8) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                }
+            } else {
+                float* dst = part_acc + (slot * G + h) * D;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    float4* d4 = reinterpret_cast<float4*>(dst + (c + LAM * j) * 8);
+                    d4[0] = make_float4(red[j][0] * vscale, red[j][1] * vscale, red[j][2] * vscale, red[j][3] * vscale);
+                    d4[1] = make_float4(red[j][4] * vscale, red[j][5] * vscale, red[j][6] * vscale, red[j][7] * vscale);
+                }
+                if (c == 0) part_ml[slot * G + h] = make_float2(M, lt);
+            }
+        }
+        pos += t1 - t0;
+        first_piece = false;
+    }
+}
+
+// Lanes per key row and prefetch depth of the dot-product kernel: the
+// accumulators (G D / LAM floats per lane) and PF + 1 tiles stay in VGPRs.
+template <int D, int G>
+struct DotShape {
+    static constexpr int LAM = (D == 128 && G > 2) ? 16 : 8;
+    static constexpr int PF = (D == 128 && G > 4) ? 1 : 2;
+};
+
 // ======================================================== paged prefill
 // Causal attention of a prefill chunk (packed rows, see the PREFILL write).
 // One wave per (block of 16 QB new tokens, query head): the MFMA tile of the
@@ -1752,6 +2101,26 @@ int resident_wave_bound() {
     return cached[dev];
 }
 
+// The dot-product form (pool flag MI_POOL_DECODE_DOT) of the two-call decode.
+template <int D, int G>
+void launch_attn_dot(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, const int32_t* table,
+                     int32_t mbps, const int32_t* ctx, int32_t batch, float scale_log2, int32_t max_ctx,
+                     int32_t min_tiles, float* part_acc, float2* part_ml, hipStream_t st) {
+    constexpr int LAM = DotShape<D, G>::LAM;
+    constexpr int PF = DotShape<D, G>::PF;
+    const int hkv = p->num_kv_heads;
+    auto kern = mikv::pool_fp8(p) ? paged_attn_dot_kernel<D, G, LAM, kFmtFp8, PF>
+                                  : paged_attn_dot_kernel<D, G, LAM, kFmtBf16, PF>;
+    const int waves = mikv::attention_grid_waves(batch, hkv, max_ctx, min_tiles, attention_waves(kern));
+    hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
+                       static_cast<const uint8_t*>(p->v), table, mbps, ctx, batch, hkv, p->num_blocks, max_ctx,
+                       min_tiles, scale_log2, static_cast<const float*>(p->scales), part_acc, part_ml, out,
+                       p->err);
+    hipLaunchKernelGGL((paged_attn_combine_kernel<D, G, false>), dim3(hkv * G, batch), dim3(256), 0, st,
+                       part_acc, part_ml, ctx, batch, mbps, hkv, max_ctx, waves, min_tiles, out,
+                       static_cast<float*>(nullptr));
+}
+
 template <int D, int G, bool STEP, bool LAYER>
 void launch_attn_kernel(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                         const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
@@ -1783,6 +2152,9 @@ void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
     else if (lio)
         launch_attn_kernel<D, G, false, true>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
                                               min_tiles, part_acc, part_ml, StepToken{}, *lio, st);
+    else if (p->flags & MI_POOL_DECODE_DOT)
+        launch_attn_dot<D, G>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx, min_tiles, part_acc,
+                              part_ml, st);
     else
         launch_attn_kernel<D, G, false, false>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
                                                min_tiles, part_acc, part_ml, StepToken{}, LayerIO{}, st);

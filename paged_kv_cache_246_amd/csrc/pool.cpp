@@ -38,7 +38,8 @@ extern "C" int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t bl
     *out = nullptr;
     if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
         return MI_ERR_INVALID_ARG;
-    if (flags & ~static_cast<uint32_t>(MI_POOL_HOST_ONLY | MI_POOL_KV_FP8 | MI_POOL_SWAP_STAGING))
+    if (flags & ~static_cast<uint32_t>(MI_POOL_HOST_ONLY | MI_POOL_KV_FP8 | MI_POOL_SWAP_STAGING |
+                                       MI_POOL_DECODE_DOT))
         return MI_ERR_INVALID_ARG;
     if ((k_cache == nullptr) != (v_cache == nullptr)) return MI_ERR_INVALID_ARG;
     if ((flags & MI_POOL_HOST_ONLY) && k_cache) return MI_ERR_INVALID_ARG;

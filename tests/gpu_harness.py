@@ -29,9 +29,9 @@ def codes_to_dev(a):
 class DeviceCase:
     """A DecodeCase on the GPU with a pool over caller-owned K/V buffers. A case
     drawn with kv_format="fp8" (uint8 pools) gets an 8-bit pool with the given
-    per-head scales."""
+    per-head scales; extra_flags are further pool flags."""
 
-    def __init__(self, case, k_scales=None, v_scales=None):
+    def __init__(self, case, k_scales=None, v_scales=None, extra_flags=0):
         self.case = case
         cfg = case.cfg
         self.B = len(case.context_lens)
@@ -51,7 +51,7 @@ class DeviceCase:
         self.max_ctx = int(case.context_lens.max()) if self.B else 0
         self.pool = mk.mi_kv_pool_init(case.num_blocks, cfg.block_size, self.Hkv, self.D,
                                        self.k_pool, self.v_pool,
-                                       flags=mk.MI_POOL_KV_FP8 if self.fp8 else 0)
+                                       flags=(mk.MI_POOL_KV_FP8 if self.fp8 else 0) | extra_flags)
         if self.fp8:
             mk.mi_kv_pool_set_scales(self.pool, k_scales, v_scales)
 
