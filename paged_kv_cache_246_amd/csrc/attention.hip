@@ -27,7 +27,6 @@ namespace {
 constexpr int BS = 16;                // tokens per KV block
 constexpr float kNegInf = -INFINITY;
 constexpr float kRescaleSlack = 8.0f; // log2 units: running max may lag by 2^8
-constexpr bool kPrefillRawSoftmax = true;   // prefill softmax form (see softmax_step)
 
 // ---------------------------------------------------------------- bf16 helpers
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -343,15 +342,13 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 struct MfmaSoftmax {
     float m;      // running max of head n (log2 units), shared by its 4 lanes
     float l;      // this lane's sum of 2^(s - m)
-    float top = kNegInf;   // FIXED form: largest exponent argument s - m seen by this lane
 };
 
-// FIXED softmax form (prefill): a column's reference m is the largest score
-// of the first key tile it reads and is never raised, so no tile rescales the
-// accumulators. The weights 2^(s - m) stay finite while every later score
-// exceeds m by at most kFixedHeadroom (log2 units); a wave in which one did
-// not repeats its work with the online rescaling form.
-constexpr float kFixedHeadroom = 64.0f;
+// Fixed softmax reference (prefill, shared-tile kernel): a query's reference
+// m is the largest score of the first key step and is never raised, so no
+// step rescales the accumulators. The weights 2^(s - m) and their sum stay
+// finite while the sum stays within 2^64; a chunk in which one did not is
+// repeated with the online rescaling form.
 constexpr float kFixedHeadroomSum = 18446744073709551616.0f;   // 2^64
 
 // Operand builders of one 16-token tile.
@@ -412,11 +409,10 @@ __device__ __forceinline__ void v_operands(const uint32_t (&vr)[4][MfmaTile<D, F
 // scores and an output that is never stored.
 // With PLO the rounding remainders of the weights, bf16(p - bf16(p)), go to
 // *plo (the weighted V sum then takes p at about 16 significant bits).
-template <int NPV, bool RAW = false, bool FIXED = false, bool PLO = false>
+template <int NPV, bool RAW = false, bool PLO = false>
 __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_ok, int q4, int qlim,
                                                  bool tail, MfmaSoftmax& sm, f32x4_t (&o)[NPV],
                                                  bf16x4_t* plo = nullptr) {
-    static_assert(!FIXED || RAW, "the fixed-reference form works on raw scores");
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -425,28 +421,6 @@ __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_
             const bool ok = col_ok && (!tail || 4 * q4 + i < qlim);
             sc[i] = ok ? sc[i] : kNegInf;
         }
-    }
-    if constexpr (FIXED) {
-        // first tile of the live columns (reference still -inf): the column's
-        // largest score, shared by its 4 lanes; never raised afterwards
-        if (__ballot(sm.m == kNegInf) != 0) {
-            const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * sl2;
-            float hm = fmaxf(mx, __shfl_xor(mx, 16));
-            hm = fmaxf(hm, __shfl_xor(hm, 32));
-            if (sm.m == kNegInf) sm.m = hm;
-        }
-        float p[4];
-        float top = sm.top;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float a = fmaf(sc[i], sl2, -sm.m);
-            top = fmaxf(top, a);
-            p[i] = __builtin_amdgcn_exp2f(a);
-            sm.l += p[i];
-        }
-        sm.top = top;
-        return bf16x4_t{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
-                        static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
     }
     const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * (RAW ? sl2 : 1.0f);
     if (__ballot(mx > sm.m + kRescaleSlack) != 0) {
@@ -484,7 +458,7 @@ __device__ __forceinline__ bf16x4_t softmax_step(f32x4_t s, float sl2, bool col_
 // PAIR: the query operand is a bf16 pair, qb the rounded value and ql the
 // rounding remainder, and so are the softmax weights (about 16 significant
 // bits each); both contractions take one MFMA per half.
-template <int D, int FMT, int QB, bool RAW = false, bool FIXED = false, bool PAIR = false>
+template <int D, int FMT, int QB, bool RAW = false, bool PAIR = false>
 __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>::NKL],
                                              const uint32_t (&vr)[4][MfmaTile<D, FMT>::VW],
                                              const uint4 (&qb)[QB][MfmaTile<D, FMT>::NQK],
@@ -510,7 +484,7 @@ __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>:
                 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
                                                             __builtin_bit_cast(bf16x8_t, ql[c][j]), s, 0, 0, 0);
         }
-        pb[c] = softmax_step<TL::NPV, RAW, FIXED, PAIR>(s, sl2, col_ok[c], q4, qlim[c], tail, sm[c], o[c],
+        pb[c] = softmax_step<TL::NPV, RAW, PAIR>(s, sl2, col_ok[c], q4, qlim[c], tail, sm[c], o[c],
                                                         PAIR ? &pl[c] : nullptr);
     }
     s16x4_t vt[TL::NPV];
@@ -528,8 +502,8 @@ __device__ __forceinline__ void mfma_consume(const uint4 (&kr)[MfmaTile<D, FMT>:
 }
 
 // Per-wave state of the QB column blocks (RAW: the prefill softmax form;
-// FIXED: its fixed-reference variant; PAIR: query and weights as bf16 pairs).
-template <int D, int FMT, int QB, bool RAW = false, bool FIXED = false, bool PAIR = false>
+// PAIR: query and weights as bf16 pairs).
+template <int D, int FMT, int QB, bool RAW = false, bool PAIR = false>
 struct MfmaCols {
     using TL = MfmaTile<D, FMT>;
     uint4 qb[QB][TL::NQK];
@@ -542,7 +516,7 @@ struct MfmaCols {
 
     __device__ __forceinline__ void consume(const uint4 (&kr)[TL::NKL], const uint32_t (&vr)[4][TL::VW],
                                             const int (&qlim)[QB], int valid_rows, bool tail) {
-        mfma_consume<D, FMT, QB, RAW, FIXED, PAIR>(kr, vr, qb, ql, sl2, col_ok, q4, qlim, valid_rows, tail,
+        mfma_consume<D, FMT, QB, RAW, PAIR>(kr, vr, qb, ql, sl2, col_ok, q4, qlim, valid_rows, tail,
                                                    sm, o);
     }
     // unmasked tile, or a tile whose rows >= valid_rows are masked for every column
@@ -812,7 +786,7 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
 
         // Q^T operand: head n, the lane's 8 dims of each 32-dim slice (the
         // same dims its K row supplies)
-        MfmaCols<D, FMT, 1, false, false, LAYER> cols;
+        MfmaCols<D, FMT, 1, false, LAYER> cols;
         auto load_q = [&](size_t qoff) {
 #pragma unroll
             for (int j = 0; j < TL::NQK; ++j) {
@@ -1297,40 +1271,33 @@ struct DotShape {
     static constexpr int PF = (D == 128 && G > 4) ? 1 : 2;
 };
 
-// ======================================================== paged prefill
-// Causal attention of a prefill chunk (packed rows, see the PREFILL write).
-// One wave per (block of 16 QB new tokens, query head): the MFMA tile of the
-// decode kernel with QB column blocks taken by the block's query tokens
-// instead of the group's heads, so every K/V tile a wave loads serves 16 QB
-// queries; the loads are ordinary cached loads, since the other query blocks
-// and heads of the sequence read the same tiles. The wave streams its sequence's K/V tiles 0 .. last in logical
-// order; tiles whose keys all lie at or before the block's first position
-// are unmasked and go through the register ring, the tiles on the diagonal
-// (at most QB + 1) follow with a per-column causal limit. Blocks are issued
-// longest first (largest key range).
-// Two launches per prefill call. kPrefillFixed: the fixed-reference form;
-// a wave whose scores outgrew a column's reference by more than the headroom
-// writes the call's generation number into the pool's redo word.
-// kPrefillRescale: the online rescaling form, over every query block, only if
-// the redo word holds this call's generation (every wave exits at once
-// otherwise). Generations count the calls on a pool, so the word needs no
-// clearing between calls.
-constexpr int kPrefillFixed = 0;
-constexpr int kPrefillRescale = 1;
-constexpr int kPrefillFixedWaves = 1;   // waves per SIMD the fixed form is built for
-
-template <int D, int G, int FMT, int PF, int QB, int MODE>
-__global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1) void paged_prefill_kernel(
+// ================================================ paged prefill, rescaling form
+// Causal attention of a prefill chunk (packed rows, see the PREFILL write)
+// with the online rescaling softmax. One wave per (block of 16 QB new
+// tokens, query head): the MFMA tile of the decode kernel with QB column
+// blocks taken by the block's query tokens instead of the group's heads, so
+// every K/V tile a wave loads serves 16 QB queries; the loads are ordinary
+// cached loads, since the other query blocks and heads of the sequence read
+// the same tiles. The wave streams its sequence's K/V tiles 0 .. last in
+// logical order; tiles whose keys all lie at or before the block's first
+// position are unmasked and go through the register ring, the tiles on the
+// diagonal (at most QB + 1) follow with a per-column causal limit. Blocks
+// are issued longest first (largest key range).
+// This is the second launch of a prefill call, with the online rescaling
+// softmax: it runs over every query block only if the shared-tile kernel
+// (below) wrote this call's generation into the pool's redo word (a row sum
+// outgrew its fixed reference), and every wave exits at once otherwise.
+// Generations count the calls on a pool, so the word needs no clearing
+// between calls.
+template <int D, int G, int FMT, int PF, int QB>
+__global__ __launch_bounds__(64, 1) void paged_prefill_rescale_kernel(
     const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu, int32_t hkv,
     int32_t num_blocks, int32_t total, int32_t max_new, float scale_log2,
     const float* __restrict__ kv_scales, uint16_t* __restrict__ out, uint32_t* __restrict__ err,
     uint32_t* __restrict__ redo_word, uint32_t gen) {
-    static_assert(MODE == kPrefillRescale || kPrefillRawSoftmax, "the fixed form works on raw scores");
-    if constexpr (MODE == kPrefillRescale) {
-        if (__builtin_amdgcn_readfirstlane(*redo_word) != gen) return;
-    }
+    if (__builtin_amdgcn_readfirstlane(*redo_word) != gen) return;
     using TL = MfmaTile<D, FMT>;
     constexpr int NPV = TL::NPV;
     constexpr int QT = BS * QB;                  // query tokens per wave
@@ -1447,17 +1414,10 @@ __global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1)
         }
     };
 
-    MfmaCols<D, FMT, QB, kPrefillRawSoftmax, MODE == kPrefillFixed> cols;
+    MfmaCols<D, FMT, QB, true> cols;
     init_cols(cols);
     run_pass(cols);
     store(cols);
-    if constexpr (MODE == kPrefillFixed) {
-        float top = kNegInf;
-#pragma unroll
-        for (int c = 0; c < QB; ++c)
-            if (cols.col_ok[c]) top = fmaxf(top, cols.sm[c].top);
-        if (__ballot(!(top <= kFixedHeadroom)) != 0 && lane == 0) atomicExch(redo_word, gen);
-    }
 }
 
 // ============================================== prefill, shared-tile form
@@ -1483,13 +1443,15 @@ __global__ __launch_bounds__(64, MODE == kPrefillFixed ? kPrefillFixedWaves : 1)
 //    8 ((r / 4) % 2) + (r % 4) + 4 (r / 8), and the A operand of a lane is one
 //    16-byte read.
 // Rows of K and of V^T are padded (16 bytes) so the operand reads of 8
-// consecutive lanes fall on distinct banks. The softmax uses the fixed
-// reference of the register form (the largest score of the first step, never
-// raised). A query whose row sum ends above 2^kFixedHeadroom (which any
-// single weight above that bound forces) makes the wave write the call's
-// generation into the redo word, and the rescaling launch repeats the chunk. Keys after the block's last position are not used
-// (zero rows, so NaN bits in the cache tail never reach an MFMA); keys after
-// a query's own position are masked by selection on the diagonal steps.
+// consecutive lanes fall on distinct banks. The softmax uses a fixed
+// reference (the largest score of the first step, never raised) and the row
+// sum adds the weights as rounded for the MFMA. A query whose row sum ends
+// above kFixedHeadroomSum (which any single weight above that bound forces)
+// makes the wave write the call's generation into the redo word, and the
+// rescaling launch repeats the chunk. Keys after the block's last position
+// are not used (zero rows, so NaN bits in the cache tail never reach an
+// MFMA); keys after a query's own position are masked by selection on the
+// diagonal steps.
 constexpr int kFaRows = 32;         // query tokens per wave (one MFMA tile)
 constexpr int kFaKeys = 64;         // keys per step
 
@@ -2064,10 +2026,8 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
 constexpr int kAttnPrefetch = 1;
 constexpr int kAttnPrefetchFp8 = 2;
 constexpr int kAttnWavesPerCU = 3;
-// Query column blocks of 16 per prefill wave (the fixed-reference launch and
-// the rescaling one).
+// Query column blocks of 16 per wave of the prefill rescaling launch.
 constexpr int kPrefillQB = 3;
-constexpr int kPrefillQBFixed = 3;
 
 // Grid of the attention kernel on the current device: CUs x min(waves per
 // CU, resident workgroups per CU at the kernel's register budget), cached
@@ -2194,8 +2154,8 @@ void launch_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
     if (gen == 0) gen = ++p->prefill_gen;           // 0 is the word's initial value
     uint32_t* redo = p->err + mikv::kPrefillRedoWord;
     auto fixed = f8 ? paged_prefill_fa_kernel<D, G, kFmtFp8> : paged_prefill_fa_kernel<D, G, kFmtBf16>;
-    auto rescale = f8 ? paged_prefill_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQB, kPrefillRescale>
-                      : paged_prefill_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQB, kPrefillRescale>;
+    auto rescale = f8 ? paged_prefill_rescale_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQB>
+                      : paged_prefill_rescale_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQB>;
     const dim3 grid_f(hkv * batch * ((max_new + kFaRows - 1) / kFaRows));
     const dim3 grid_r((max_new + BS * kPrefillQB - 1) / (BS * kPrefillQB), hkv * G, batch);
     hipLaunchKernelGGL(fixed, grid_f, dim3(64 * G), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
