@@ -294,6 +294,10 @@ size_t mi_paged_gqa_decode_workspace_bytes(mi_kv_pool_t pool, int32_t batch,
  * softmax): q.K in fp32 from exact bf16 products, the softmax weights
  * exp2-based in fp32 and rounded to bf16 for the weighted sum of V (fp32
  * accumulation), partial results merged in fp32, one rounding to bf16.
+ * Short segments (max_context_len + 1 <= 384 and at most 512 (sequence, kv
+ * head) pairs, with the library's split) are split over the waves of one
+ * workgroup per pair instead and merged on chip: one launch, the workspace
+ * untouched.
  *  batch   0 .. 1024 (more: MI_ERR_UNSUPPORTED)
  *  q_rot   device bf16 [batch, num_q_heads, head_dim] (as written by
  *          mi_write_decode_kv)

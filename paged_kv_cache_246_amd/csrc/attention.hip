@@ -922,6 +922,130 @@ __global__ __launch_bounds__(64) void paged_attn_mfma_kernel(
     }
 }
 
+// ================================ paged GQA decode, per-segment form
+// Short segments (every one at most kSegWaves x kSegMaxTilesPerWave tiles,
+// few of them): one workgroup of kSegWaves waves per (KV head g,
+// sequence b). Wave w streams tiles [w nt / kSegWaves, (w + 1) nt /
+// kSegWaves) of the segment through the MFMA kernel's register ring and
+// consume step, then the waves' (m, l, acc) are merged through LDS in wave
+// order and the bf16 output is stored: the whole call is one launch, with
+// no split partials in memory and no combine launch. Same tile arithmetic
+// as the stream-K kernel; the results depend only on logical positions.
+// A sequence whose length is out of range gets NaN outputs and a recorded
+// fault, as in the stream-K path.
+// Beyond three tiles per wave the waves' serial tile round trips cost more
+// than the stream-K kernel's combine launch (segments of 65 tiles: 8.1
+// instead of 2 tiles per wave, 17-25 against 17-21 us per step).
+constexpr int kSegWaves = 8;              // waves per workgroup (two per SIMD)
+constexpr int kSegMaxTilesPerWave = 3;    // longest segment: 24 tiles (384 tokens)
+constexpr int kSegMaxSegments = 512;      // workgroups (batch x KV heads)
+
+template <int D, int G, int FMT, int PF>
+__global__ __launch_bounds__(64 * kSegWaves) void paged_attn_seg_kernel(
+    const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+    const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens, int32_t hkv,
+    int32_t num_blocks, int32_t max_ctx, float scale_log2, const float* __restrict__ kv_scales,
+    uint16_t* __restrict__ out, uint32_t* __restrict__ err) {
+    using TL = MfmaTile<D, FMT>;
+    constexpr int NPV = TL::NPV;
+    constexpr size_t TILE = static_cast<size_t>(BS) * TL::ROW;   // bytes per (block, head) tile
+    constexpr int NT = 64 * kSegWaves;
+    __shared__ float s_m[kSegWaves][G], s_l[kSegWaves][G];
+    __shared__ float s_o[kSegWaves][G][D];
+    const int g = blockIdx.x;
+    const int b = blockIdx.y;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int q4 = lane >> 4;
+    const bool head_ok = n < G;
+    uint16_t* o_seg = out + (static_cast<size_t>(b) * hkv * G + g * G) * D;
+
+    const int c = ctx_lens[b];
+    if (c < 0 || c > max_ctx || c + 1 > mbps * BS) {        // uniform over the workgroup
+        if (g == 0 && threadIdx.x == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+        for (int i = threadIdx.x; i < G * D; i += NT) o_seg[i] = 0x7fc0;
+        return;
+    }
+    const int L = c + 1;
+    const int nt = (L + BS - 1) / BS;
+    const int t0 = wv * nt / kSegWaves;
+    const int t1 = (wv + 1) * nt / kSegWaves;
+
+    MfmaCols<D, FMT, 1> cols;
+    const size_t qoff = (static_cast<size_t>(b) * hkv * G + g * G + (head_ok ? n : 0)) * D;
+#pragma unroll
+    for (int j = 0; j < TL::NQK; ++j) {
+        const int d0 = FMT == kFmtBf16 ? 32 * j + 8 * q4 : 64 * (j / 2) + 16 * q4 + 8 * (j & 1);
+        cols.qb[0][j] = head_ok ? *reinterpret_cast<const uint4*>(q_rot + qoff + d0) : make_uint4(0, 0, 0, 0);
+    }
+    cols.sl2 = scale_log2;
+    float vscale = 1.f;
+    if constexpr (FMT == kFmtFp8) {
+        cols.sl2 *= kv_scales[g];
+        vscale = kv_scales[hkv + g];
+    }
+    cols.q4 = q4;
+    cols.col_ok[0] = head_ok;
+    cols.sm[0] = MfmaSoftmax{head_ok ? kNegInf : 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < NPV; ++jj) cols.o[0][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (t0 < t1) {
+        MfmaRing<D, FMT, PF> ring;
+        ring.kbase = reinterpret_cast<const char*>(kc) + static_cast<size_t>(g) * TILE;
+        ring.vbase = reinterpret_cast<const char*>(vc) + static_cast<size_t>(g) * TILE;
+        ring.blk_stride = static_cast<size_t>(hkv) * TILE;
+#pragma unroll
+        for (int j = 0; j < TL::NKL; ++j) ring.koff[j] = n * TL::ROW + 64 * j + 16 * q4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ring.voff[r] = (4 * q4 + r) * TL::ROW + TL::VB * n;
+        for (int s0 = t0; s0 < t1; s0 += 64) {
+            const int nblk = min(64, t1 - s0);
+            int32_t id = 0;
+            if (lane < nblk) id = table[static_cast<size_t>(b) * mbps + s0 + lane];
+            const bool bad_id = lane < nblk && (id < 0 || id >= num_blocks);
+            if (__ballot(bad_id) != 0 && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+            ring.my_id = bad_id ? 0 : id;
+            const int last_rows = (s0 + nblk == nt) ? L - (nt - 1) * BS : BS;
+            ring.run(nblk, last_rows, cols);
+        }
+    }
+
+    // the wave's partial: head totals of the lane sums, the lane's D / 4 dims
+    const MfmaSoftmax& sm = cols.sm[0];
+    float lt = sm.l + __shfl_xor(sm.l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (head_ok) {
+        const int dbase = NPV * 4 * q4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int jj = 0; jj < NPV; ++jj) s_o[wv][n][dbase + NPV * r + jj] = cols.o[0][jj][r];
+        if (q4 == 0) {
+            s_m[wv][n] = sm.m;
+            s_l[wv][n] = lt;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += NT) {
+        const int h = i / D;
+        const int d = i - h * D;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, s_m[w][h]);
+        float l = 0.f, a = 0.f;
+#pragma unroll
+        for (int w = 0; w < kSegWaves; ++w) {
+            const float mw = s_m[w][h];
+            const float f = mw == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+            l = fmaf(f, s_l[w][h], l);
+            a = fmaf(f, s_o[w][h][d], a);
+        }
+        o_seg[i] = f32_to_bf16_rne(a * (vscale / l));
+    }
+}
+
 // ===================================== paged GQA decode, dot-product form
 // The decode attention with both contractions on the vector ALUs instead of
 // the matrix cores: the same work partition, ring of in-flight tiles and
@@ -2061,6 +2185,20 @@ int resident_wave_bound() {
     return cached[dev];
 }
 
+// The per-segment form of the two-call decode (no workspace, no combine).
+template <int D, int G>
+void launch_attn_seg(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, const int32_t* table,
+                     int32_t mbps, const int32_t* ctx, int32_t batch, float scale_log2, int32_t max_ctx,
+                     hipStream_t st) {
+    const int hkv = p->num_kv_heads;
+    auto kern = mikv::pool_fp8(p) ? paged_attn_seg_kernel<D, G, kFmtFp8, kAttnPrefetchFp8>
+                                  : paged_attn_seg_kernel<D, G, kFmtBf16, kAttnPrefetch>;
+    hipLaunchKernelGGL(kern, dim3(hkv, batch), dim3(64 * kSegWaves), 0, st, q_rot,
+                       static_cast<const uint8_t*>(p->k), static_cast<const uint8_t*>(p->v), table, mbps, ctx,
+                       hkv, p->num_blocks, max_ctx, scale_log2, static_cast<const float*>(p->scales), out,
+                       p->err);
+}
+
 // The dot-product form (pool flag MI_POOL_DECODE_DOT) of the two-call decode.
 template <int D, int G>
 void launch_attn_dot(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, const int32_t* table,
@@ -2105,8 +2243,10 @@ template <int D, int G>
 void launch_attn(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                  const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                  float scale_log2, int32_t max_ctx, int32_t min_tiles, float* part_acc,
-                 float2* part_ml, const StepToken* tok, const LayerIO* lio, hipStream_t st) {
-    if (tok)
+                 float2* part_ml, const StepToken* tok, const LayerIO* lio, bool seg, hipStream_t st) {
+    if (seg)
+        launch_attn_seg<D, G>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx, st);
+    else if (tok)
         launch_attn_kernel<D, G, true, false>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
                                               min_tiles, part_acc, part_ml, *tok, LayerIO{}, st);
     else if (lio)
@@ -2124,11 +2264,11 @@ template <int D>
 int dispatch_group(int G, const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                    const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                    float scale_log2, int32_t max_ctx, int32_t min_tiles, float* pa, float2* pm,
-                   const StepToken* tok, const LayerIO* lio, hipStream_t st) {
+                   const StepToken* tok, const LayerIO* lio, bool seg, hipStream_t st) {
 #define MIKV_G(GG)                                                                             \
     case GG:                                                                                   \
         launch_attn<D, GG>(p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,        \
-                           min_tiles, pa, pm, tok, lio, st);                                   \
+                           min_tiles, pa, pm, tok, lio, seg, st);                              \
         return MI_OK;
     switch (G) {
         MIKV_G(1)
@@ -2293,10 +2433,13 @@ namespace {
 // ws_waves: the wave count the workspace's partial slots are laid out for
 // (at least the grid the launch takes); 0 selects the bound the workspace
 // queries use.
+// default_split: the library's split was asked for; then a small workload of
+// the plain two-call form (no step token, not the layer, not the dot form)
+// takes the per-segment kernel.
 int launch_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, const int32_t* table,
                   int32_t mbps, const int32_t* ctx, int32_t batch, int32_t hq, float scale,
                   int32_t max_ctx, int32_t split_tokens, void* ws, const StepToken* tok,
-                  void* stream, int ws_waves = 0, const LayerIO* lio = nullptr) {
+                  void* stream, int ws_waves = 0, const LayerIO* lio = nullptr, bool default_split = false) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int G = hq / p->num_kv_heads;
     const int min_tiles = split_tokens / BS;
@@ -2308,13 +2451,16 @@ int launch_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, c
     float2* pm = reinterpret_cast<float2*>(static_cast<char*>(ws) +
                                            align_up(slots * p->head_dim * sizeof(float), 256));
     const float scale_log2 = scale * 1.4426950408889634f;
+    const bool seg = default_split && !tok && !lio && !(p->flags & MI_POOL_DECODE_DOT) &&
+                     (max_ctx + BS) / BS <= kSegWaves * kSegMaxTilesPerWave &&
+                     batch * p->num_kv_heads <= kSegMaxSegments;
     int rc;
     if (p->head_dim == 128)
         rc = dispatch_group<128>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                 min_tiles, pa, pm, tok, lio, st);
+                                 min_tiles, pa, pm, tok, lio, seg, st);
     else
         rc = dispatch_group<64>(G, p, q_rot, out, table, mbps, ctx, batch, scale_log2, max_ctx,
-                                min_tiles, pa, pm, tok, lio, st);
+                                min_tiles, pa, pm, tok, lio, seg, st);
     if (rc != MI_OK) return rc;
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
@@ -2324,9 +2470,9 @@ int launch_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out, c
 int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                             const int32_t* table, int32_t mbps, const int32_t* ctx, int32_t batch,
                             int32_t hq, float scale, int32_t max_ctx, int32_t split_tokens,
-                            void* ws, void* stream) {
+                            void* ws, void* stream, bool default_split) {
     return launch_decode(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx, split_tokens,
-                         ws, nullptr, stream);
+                         ws, nullptr, stream, 0, nullptr, default_split);
 }
 
 int launch_layer_attention(const mi_kv_pool_s* p, const uint16_t* q_hi, const uint16_t* q_lo,
@@ -2354,7 +2500,7 @@ int launch_paged_gqa_decode_noalloc(const mi_kv_pool_s* p, const uint16_t* q_rot
     const size_t need = align_up(slots * p->head_dim * sizeof(float), 256) + align_up(slots * sizeof(float2), 256);
     if (need > MI_NOALLOC_SCRATCH_BYTES) return MI_ERR_SCRATCH_TOO_SMALL;
     return launch_decode(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx,
-                         kDefaultSplitTokens, ws, nullptr, stream, waves);
+                         kDefaultSplitTokens, ws, nullptr, stream, waves, nullptr, true);
 }
 
 int launch_decode_step(const mi_kv_pool_s* p, const uint16_t* q, const uint16_t* k,
@@ -2467,6 +2613,7 @@ extern "C" int mi_paged_gqa_decode_split(mi_kv_pool_t p, const uint16_t* q_rot, 
     int rc = check_common(p, batch, hq, mbps);
     if (rc != MI_OK) return rc;
     if (max_ctx < 0 || split_tokens < 0) return MI_ERR_INVALID_ARG;
+    const bool default_split = split_tokens == 0;
     if (split_tokens == 0) split_tokens = mikv::default_split_tokens(batch, p->num_kv_heads, max_ctx);
     if (split_tokens % BS) return MI_ERR_UNSUPPORTED;
     if (batch > mikv::kMaxBatch) return MI_ERR_UNSUPPORTED;
@@ -2477,7 +2624,7 @@ extern "C" int mi_paged_gqa_decode_split(mi_kv_pool_t p, const uint16_t* q_rot, 
         return MI_ERR_WORKSPACE_TOO_SMALL;
     if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(p->head_dim));
     return mikv::launch_paged_gqa_decode(p, q_rot, out, table, mbps, ctx, batch, hq, scale, max_ctx,
-                                         split_tokens, ws, stream);
+                                         split_tokens, ws, stream, default_split);
 }
 
 extern "C" int mi_paged_gqa_decode(mi_kv_pool_t p, const uint16_t* q_rot, uint16_t* out,

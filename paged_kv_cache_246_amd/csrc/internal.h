@@ -84,10 +84,12 @@ int launch_paged_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t*
                          const int32_t* table, int32_t mbps, const int32_t* ctx, const int32_t* cu,
                          int32_t batch, int32_t total, int32_t max_new, int32_t hq, float scale,
                          void* stream);
+// default_split: the caller asked for the library's split (split_tokens 0),
+// which lets small workloads take the per-segment form (no combine launch).
 int launch_paged_gqa_decode(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
                             const int32_t* table, int32_t mbps, const int32_t* ctx,
                             int32_t batch, int32_t hq, float scale, int32_t max_ctx,
-                            int32_t split_tokens, void* ws, void* stream);
+                            int32_t split_tokens, void* ws, void* stream, bool default_split);
 // The decoder layer's attention (the default split): the query as a bf16
 // pair (q_hi + q_lo, [B, Hq, D] each), the output in float32 [B, Hq, D];
 // workspace as for launch_paged_gqa_decode.

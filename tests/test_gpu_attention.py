@@ -207,6 +207,40 @@ def test_group_sizes_head_dims_and_block_boundaries(D, Hq, Hkv):
         dc.close()
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("top", [383, 384])
+def test_per_segment_form_at_its_length_limit(top, fmt):
+    """With the library's split, contexts whose longest segment has at most 24
+    tiles (L = ctx + 1 <= 384) take the one-launch per-segment kernel (eight
+    waves per (sequence, KV head), merged in LDS); one token more takes the
+    stream-K kernel and the combine. Both sides of the limit, and the same
+    inputs through an explicit split (always stream-K), against the oracle."""
+    cfg = _custom_cfg(32, 8, 128, theta=1e6, seed=top)
+    ctx = [top, 0, 15, 16, 17, 200, top - 1, 100]
+    case = workloads.make_decode_case(cfg, pool="poison", context_lens=ctx, num_blocks=256,
+                                      kv_format=fmt)
+    if fmt == "fp8":
+        ks = np.array([1.0, 0.37, 2.0, 0.8125, 3.3, 0.5, 1.7, 0.25], np.float32)
+        vs = ks[::-1].copy()
+        ref = oatt.decode_step_fp8(case.k_pool, case.v_pool, case.q, case.k, case.v, case.block_table,
+                                   case.context_lens, 16, cfg.rope_theta, ks, vs)[0]
+        dc = DeviceCase(case, ks, vs)
+    else:
+        ref = oatt.decode_step(case.k_pool, case.v_pool, case.q, case.k, case.v, case.block_table,
+                               case.context_lens, 16, cfg.rope_theta)[0]
+        dc = DeviceCase(case)
+    try:
+        dc.write()
+        for split in (0, 32):
+            dc.attend(split_tokens=split)
+            torch.cuda.synchronize()
+            mx, rel = check_tolerance(dev_to_bits(dc.out), ref, "top=%d %s split=%d" % (top, fmt, split))
+            _say("  top %d %s split %d: max|d| %.3g relL2 %.3g" % (top, fmt, split, mx, rel))
+        assert dc.faults() == 0
+    finally:
+        dc.close()
+
+
 @pytest.mark.parametrize("B,ctx_hi", [(65, 40), (130, 200), (1024, 300)])
 def test_batches_past_one_prefix_chunk_and_at_the_maximum(B, ctx_hi):
     """The kernels build the tile prefix over the batch 64 sequences at a time
