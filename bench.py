@@ -59,9 +59,11 @@ def _pct(xs):
 
 
 def time_step(torch, stream, fn, steps, warmup, flush=None):
-    """Warm: `warmup` untimed calls, then `steps` back-to-back calls, one HIP
-    event pair (on `stream`) around each call and one around all of them:
-    ms_per_step = total / steps, plus the p10/p50/p90 of the single calls.
+    """Warm: `warmup` untimed calls, then `steps` back-to-back calls with one
+    HIP event pair (on `stream`) around all of them: ms_per_step = total /
+    steps; then `steps` more calls with an event pair around each, for the
+    p10/p50/p90 of single calls (kept apart so that the per-call event
+    packets do not enter the back-to-back figure).
     Flushed (if `flush`, a device buffer of FLUSH_BYTES, is given): the median
     (and p10/p90) of FLUSHED_REPS single calls, each after an untimed fill of
     the buffer on the same stream, which evicts the L2s and the last-level
@@ -71,14 +73,17 @@ def time_step(torch, stream, fn, steps, warmup, flush=None):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        evs = [(E(), E()) for _ in range(steps)]
         t0, t1 = E(), E()
         t0.record(stream)
+        for _ in range(steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        evs = [(E(), E()) for _ in range(steps)]
         for a, b in evs:
             a.record(stream)
             fn()
             b.record(stream)
-        t1.record(stream)
         torch.cuda.synchronize()
         per = [a.elapsed_time(b) for a, b in evs]
         res = {"ms_per_step": round(t0.elapsed_time(t1) / steps, 5), "warm_ms": _pct(per)}
@@ -144,21 +149,27 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16", dot=False)
         if ev is not None:
             ev[1].record(stream)
 
+    # Back-to-back steps with one event pair around all of them (the step
+    # rate), then as many steps again with an event pair around each
+    # attention call (its launch times; kept apart so that the event packets
+    # do not enter the step rate).
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     attn_ms = [a.elapsed_time(b) for a, b in evs]
 
     # The same step as one launch (mi_paged_gqa_decode_step), timed alike.
@@ -271,16 +282,19 @@ def run_prefill_bench(args, torch, mk, workloads, cached=False):
     steps = max(1, args.steps // 5)
     for _ in range(max(1, args.warmup // 2)):
         step()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(steps):
-        step(evs[i])
+        step()
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     faults = mk.mi_kv_pool_check_errors(pool)
     mk.mi_kv_pool_destroy(pool)
