@@ -2008,6 +2008,283 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
     if (__ballot(q_ok && !(lt <= kFixedHeadroomSum)) != 0 && lane == 0) atomicExch(redo_word, gen);
 }
 
+// ===================================== prefill, shared-tile form, bf16 DMA
+// The shared-tile kernel above for bf16 caches with the K/V copy done by
+// gfx950's direct global-to-LDS loads (`buffer_load_dwordx4 ... lds`): no
+// staging registers, no LDS stores, no permutes. A wave load writes 1 KB of
+// LDS (lane i's 16 bytes at 16 i), i.e. 1024 / (2 D) consecutive key rows of
+// one cache block; which 16-byte piece each lane fetches realises an XOR
+// swizzle of the rows' 16-byte chunks (K: chunk ^ (row & 7); V:
+// chunk ^ 2 (row & 3)), so the operand reads below are bank-conflict free.
+// V stays in key-major rows; the V^T operand of the weighted sum is read
+// with `ds_read_b64_tr_b16`, which within a group of 16 lanes hands lane l
+// element l & 3 of the 4 bf16 addressed by lane (l >> 2) + 4 e, as its
+// element e: lane j of group q (of 4) addresses key 16 a + 8 c + 4 (q >> 1)
+// + (j >> 2), dims 32 dt + 16 (q & 1) + 4 (j & 3), for call c = 0, 1, which
+// yields the 8 keys of the MFMA's k-order (the score layout's key order,
+// see fa_vcol) at dim 32 dt + l % 32. The two stages are two LDS arrays and
+// the step loop is unrolled by two, so a stage's loads and the other
+// stage's reads are known apart. V rows past the chunk's last key are
+// zeroed in LDS once the last step's loads are in (NaN bits in the cache
+// tail must not reach an MFMA); K rows there are masked by selection.
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+// 16 bytes per lane from a buffer into LDS at dst + 16 lane (dst wave-uniform).
+__device__ __forceinline__ void fa_load_lds16(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+// Transposing LDS read of 4 bf16 (see the kernel comment).
+__device__ __forceinline__ s16x4_t fa_read_tr16(const char* p) {
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
+    const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
+    const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
+    const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu, int32_t batch, int32_t hkv,
+    int32_t num_blocks, int32_t total, int32_t max_new, float scale_log2, uint16_t* __restrict__ out,
+    uint32_t* __restrict__ err, uint32_t* __restrict__ redo_word, uint32_t gen) {
+    constexpr int ROWS = kFaRows;           // query tokens per workgroup (per wave and head)
+    constexpr int NT = 64 * G;              // threads
+    constexpr int ROWB = D * 2;             // bytes per K or V row in LDS
+    constexpr int CPR16 = ROWB / 16;        // 16-byte chunks per row
+    constexpr int RPL = 1024 / ROWB;        // rows per wave load
+    constexpr int LPS = kFaKeys / RPL;      // wave loads per step (K; V alike)
+    constexpr int LPW = (LPS + G - 1) / G;  // per wave
+    constexpr int KB = kFaKeys * ROWB;      // bytes of K (and of V) per stage
+    constexpr int NKK = D / 16;             // score MFMAs per 32-key half
+    constexpr int NDT = D / 32;             // output dim tiles
+    constexpr int NH = kFaKeys / 32;        // 32-key halves per step
+    constexpr int BPS = kFaKeys / BS;       // cache blocks per step
+    static_assert(BS % RPL == 0, "a wave load stays in one cache block");
+    __shared__ __align__(1024) char stage0[2 * KB];
+    __shared__ __align__(1024) char stage1[2 * KB];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int g = static_cast<int>(blockIdx.x) % hkv;
+    if (blockIdx.x == 0 && tid == 0) {
+        for (int bb = 0; bb < batch; ++bb) {
+            const int r0 = cu[bb], n = cu[bb + 1] - r0, c = ctx_lens[bb];
+            if (r0 < 0 || n < 0 || r0 + n > total || n > max_new || c < 0 || c + n > mbps * BS)
+                atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+        }
+    }
+    const FaBlock fb = fa_block_of_rank<ROWS>(static_cast<int>(blockIdx.x) / hkv, ctx_lens, cu, batch,
+                                              total, max_new, mbps, lane);
+    if (fb.b < 0) return;
+    const int b = __builtin_amdgcn_readfirstlane(fb.b);
+    const int qblk = __builtin_amdgcn_readfirstlane(fb.y);
+    const int h = g * G + w;
+    const int hq = hkv * G;
+    const int row0 = cu[b];
+    const int nnew = cu[b + 1] - row0;
+    const int ctx = ctx_lens[b];
+    const int nqb = (nnew + ROWS - 1) / ROWS;
+    const int j0 = (nqb - 1 - qblk) * ROWS;     // longest blocks first
+    const int p_first = ctx + j0;
+    const int p_last = ctx + min(j0 + ROWS, nnew) - 1;
+    const int nks = p_last / kFaKeys + 1;       // steps holding keys 0 .. p_last
+    const int ks_m = (p_first + 1) / kFaKeys;   // steps before this are unmasked for every query
+    const int jq = j0 + col;                    // this lane's query token
+    const bool q_ok = jq < nnew;
+    const int pq = ctx + jq;
+    const float sl2 = scale_log2;
+
+    uint4 qop[NKK];
+    {
+        const uint16_t* qh = q_rot + (static_cast<size_t>(row0 + (q_ok ? jq : 0)) * hq + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            qop[kk] = q_ok ? *reinterpret_cast<const uint4*>(qh + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0);
+    }
+
+    // Wave load u of a step is load li = w + G u (if li < LPS): key rows
+    // RPL li .. + RPL - 1, in cache block (RPL li) / BS of the step.
+    const uint32_t blk_bytes = static_cast<uint32_t>(hkv) * BS * ROWB;
+    const uint32_t head_off = static_cast<uint32_t>(g) * BS * ROWB;
+    const int last_blk = p_last / BS;
+    const int32_t* trow = table + static_cast<size_t>(b) * mbps;
+    int jb[LPW];
+    uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+        const int li = min(w + G * u, LPS - 1);
+        const int r = RPL * li + lane / CPR16;              // the lane's row in the step
+        const int cp = lane % CPR16;                        // its chunk position in LDS
+        jb[u] = (RPL * li) / BS;
+        koff[u] = head_off + static_cast<uint32_t>((r % BS) * ROWB + (cp ^ (r & 7)) * 16);
+        voff[u] = head_off + static_cast<uint32_t>((r % BS) * ROWB + (cp ^ (2 * (r & 3))) * 16);
+    }
+    bool bad_id = false;
+    int32_t ids[LPW];
+    auto load_ids = [&](int s) {
+        int32_t raw[LPW];
+#pragma unroll
+        for (int u = 0; u < LPW; ++u) raw[u] = trow[min(BPS * s + jb[u], last_blk)];
+#pragma unroll
+        for (int u = 0; u < LPW; ++u) {
+            const bool ok = raw[u] >= 0 && raw[u] < num_blocks;
+            bad_id |= !ok;
+            ids[u] = __builtin_amdgcn_readfirstlane(ok ? raw[u] : 0);
+        }
+    };
+    auto dma = [&](char* buf) {
+#pragma unroll
+        for (int u = 0; u < LPW; ++u) {
+            const int li = w + G * u;
+            if (LPS % G == 0 || li < LPS) {
+                const size_t base = static_cast<size_t>(ids[u]) * blk_bytes;
+                fa_load_lds16(fa_rsrc(kc + base, blk_bytes), buf + 1024 * li, koff[u]);
+                fa_load_lds16(fa_rsrc(vc + base, blk_bytes), buf + KB + 1024 * li, voff[u]);
+            }
+        }
+    };
+    const int rows_last = p_last + 1 - kFaKeys * (nks - 1);   // valid key rows of the last step
+    auto zero_v_tail = [&](char* buf) {
+        for (int i = rows_last * CPR16 + tid; i < kFaKeys * CPR16; i += NT)
+            *reinterpret_cast<uint4*>(buf + KB + 16 * i) = make_uint4(0, 0, 0, 0);
+    };
+
+    f32x16_t oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16_t{};
+    float m = kNegInf, l = 0.f;
+    // Per-lane parts of the operand addresses that the swizzle makes
+    // non-additive; the rest (32-key halves, key groups, calls) are
+    // immediate offsets. K: row 32 t + col, chunk (2 kk + half) ^ (col & 7).
+    // V^T: key 16 a + 8 c + 4 (q >> 1) + (j >> 2) (so key & 3 = (j >> 2) & 3),
+    // 16-byte chunk (4 dt + 2 (q & 1) + (j & 3) / 2) ^ 2 (key & 3), then
+    // 8 (j & 1) bytes in.
+    const int gq = lane >> 4, jl = lane & 15;
+    uint32_t koffs[NKK], voffs[NDT];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+        koffs[kk] = static_cast<uint32_t>(col * ROWB + (((2 * kk + half) ^ (col & 7)) * 16));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        voffs[dt] = static_cast<uint32_t>((4 * (gq >> 1) + (jl >> 2)) * ROWB +
+                                          (((4 * dt + 2 * (gq & 1) + ((jl & 3) >> 1)) ^ (2 * ((jl >> 2) & 3))) * 16) +
+                                          8 * (jl & 1));
+
+    auto compute = [&](int s, const char* buf) {
+        const char* kb = buf;
+        const char* vb = buf + KB;
+        f32x16_t sacc[NH];
+#pragma unroll
+        for (int t = 0; t < NH; ++t) sacc[t] = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int t = 0; t < NH; ++t) {
+                const uint4 a = *reinterpret_cast<const uint4*>(kb + koffs[kk] + 32 * t * ROWB);
+                sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                  __builtin_bit_cast(bf16x8_t, qop[kk]), sacc[t], 0, 0, 0);
+            }
+        float sc[NH][16];
+        if (s >= ks_m) {            // diagonal step: key position <= the query's own
+#pragma unroll
+            for (int t = 0; t < NH; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kp = kFaKeys * s + 32 * t + 8 * (i / 4) + 4 * half + (i % 4);
+                    sc[t][i] = kp <= pq ? sacc[t][i] : kNegInf;
+                }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NH; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[t][i] = sacc[t][i];
+        }
+        if (s == 0) {               // the fixed reference: largest score of the first step
+            float mx = sc[0][0];
+#pragma unroll
+            for (int t = 0; t < NH; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[t][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+            m = q_ok ? mx : 0.f;
+        }
+        bf16x8_t pb[2 * NH];
+#pragma unroll
+        for (int t = 0; t < NH; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                pb[2 * t + i / 8][i % 8] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[t][i], sl2, -m)));
+        const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+#pragma unroll
+        for (int a = 0; a < 2 * NH; ++a) {
+            const bf16x8_t x = pb[a];
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), ones, l, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), ones, l, false);
+        }
+#pragma unroll
+        for (int a = 0; a < 2 * NH; ++a)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const char* vp = vb + voffs[dt] + 16 * a * ROWB;
+                const s16x4_t v0 = fa_read_tr16(vp);
+                const s16x4_t v1 = fa_read_tr16(vp + 8 * ROWB);
+                const s16x8_t v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v), pb[a],
+                                                                   oacc[dt], 0, 0, 0);
+            }
+    };
+
+    // Step s reads one stage while step s + 1 is loaded into the other; one
+    // barrier per step (after the stage's own loads are in), one more on the
+    // step before the last when its V tail needs zeroing.
+    auto step = [&](int s, const char* cur, char* nxt) {
+        if (s + 1 < nks) dma(nxt);
+        load_ids(min(s + 2, nks - 1));
+        compute(s, cur);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (s + 1 == nks - 1 && rows_last < kFaKeys) {
+            zero_v_tail(nxt);
+            __syncthreads();
+        }
+    };
+    load_ids(0);
+    dma(stage0);
+    load_ids(min(1, nks - 1));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (nks == 1 && rows_last < kFaKeys) {
+        zero_v_tail(stage0);
+        __syncthreads();
+    }
+    for (int s = 0; s < nks; s += 2) {
+        step(s, stage0, stage1);
+        if (s + 1 < nks) step(s + 1, stage1, stage0);
+    }
+    if (bad_id && lane == 0) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+
+    const float lt = l + __shfl_xor(l, 32);
+    if (q_ok) {
+        const float inv = 1.f / lt;
+        uint16_t* oh = out + (static_cast<size_t>(row0 + jq) * hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * dt + 8 * r4 + 4 * half;
+                const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * r4] * inv)) |
+                                    (static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * r4 + 1] * inv)) << 16);
+                const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * r4 + 2] * inv)) |
+                                    (static_cast<uint32_t>(f32_to_bf16_rne(oacc[dt][4 * r4 + 3] * inv)) << 16);
+                *reinterpret_cast<uint2*>(oh + d0) = make_uint2(w0, w1);
+            }
+    }
+    if (__ballot(q_ok && !(lt <= kFixedHeadroomSum)) != 0 && lane == 0) atomicExch(redo_word, gen);
+}
+
 // Combine kernel: one workgroup per (query head, sequence). It rebuilds the
 // same partition, and if the segment was cut into pieces, merges their
 // partials in range order. Thread (d, cg) folds the pieces cg, cg + NCG, ...
@@ -2293,15 +2570,20 @@ void launch_prefill(const mi_kv_pool_s* p, const uint16_t* q_rot, uint16_t* out,
     uint32_t gen = ++p->prefill_gen;
     if (gen == 0) gen = ++p->prefill_gen;           // 0 is the word's initial value
     uint32_t* redo = p->err + mikv::kPrefillRedoWord;
-    auto fixed = f8 ? paged_prefill_fa_kernel<D, G, kFmtFp8> : paged_prefill_fa_kernel<D, G, kFmtBf16>;
+    auto fixed = paged_prefill_fa_kernel<D, G, kFmtFp8>;
     auto rescale = f8 ? paged_prefill_rescale_kernel<D, G, kFmtFp8, kAttnPrefetchFp8, kPrefillQB>
                       : paged_prefill_rescale_kernel<D, G, kFmtBf16, kAttnPrefetch, kPrefillQB>;
     const dim3 grid_f(hkv * batch * ((max_new + kFaRows - 1) / kFaRows));
     const dim3 grid_r((max_new + BS * kPrefillQB - 1) / (BS * kPrefillQB), hkv * G, batch);
-    hipLaunchKernelGGL(fixed, grid_f, dim3(64 * G), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
-                       static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, batch, hkv, p->num_blocks,
-                       total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err,
-                       redo, gen);
+    if (f8)
+        hipLaunchKernelGGL(fixed, grid_f, dim3(64 * G), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
+                           static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, batch, hkv, p->num_blocks,
+                           total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err,
+                           redo, gen);
+    else
+        hipLaunchKernelGGL((paged_prefill_dma_kernel<D, G>), grid_f, dim3(64 * G), 0, st, q_rot,
+                           static_cast<const uint8_t*>(p->k), static_cast<const uint8_t*>(p->v), table, mbps,
+                           ctx, cu, batch, hkv, p->num_blocks, total, max_new, scale_log2, out, p->err, redo, gen);
     hipLaunchKernelGGL(rescale, grid_r, dim3(64), 0, st, q_rot, static_cast<const uint8_t*>(p->k),
                        static_cast<const uint8_t*>(p->v), table, mbps, ctx, cu, hkv, p->num_blocks,
                        total, max_new, scale_log2, static_cast<const float*>(p->scales), out, p->err,
