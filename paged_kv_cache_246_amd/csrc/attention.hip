@@ -2014,8 +2014,13 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
 // staging registers, no LDS stores, no permutes. A wave load writes 1 KB of
 // LDS (lane i's 16 bytes at 16 i), i.e. 1024 / (2 D) consecutive key rows of
 // one cache block; which 16-byte piece each lane fetches realises an XOR
-// swizzle of the rows' 16-byte chunks (K: chunk ^ (row & 7); V:
-// chunk ^ 2 (row & 3)), so the operand reads below are bank-conflict free.
+// swizzle of the rows' 16-byte chunks, so that the operand reads below are
+// bank-conflict free on gfx950's LDS (64 banks of 4 bytes: a 16-byte read
+// serves 16 lanes a cycle, an 8-byte read 32). With s = row / (256 / 2 D)
+// (the row's 256-byte bank line): K chunk ^ (s mod 2 D / 16), so that 16
+// consecutive key rows at one chunk fill all banks; V chunk ^ 4 (s mod
+// D / 32), so that the 4 rows x 4 chunks a transposing read touches in 32
+// lanes do.
 // V stays in key-major rows; the V^T operand of the weighted sum is read
 // with `ds_read_b64_tr_b16`, which within a group of 16 lanes hands lane l
 // element l & 3 of the 4 bf16 addressed by lane (l >> 2) + 4 e, as its
@@ -2057,7 +2062,11 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
     constexpr int NDT = D / 32;             // output dim tiles
     constexpr int NH = kFaKeys / 32;        // 32-key halves per step
     constexpr int BPS = kFaKeys / BS;       // cache blocks per step
+    constexpr int RPB = 256 / ROWB;         // rows per 256-byte bank line
     static_assert(BS % RPL == 0, "a wave load stays in one cache block");
+    static_assert(RPB >= 1 && CPR16 >= 4, "row of 64 to 256 bytes");
+    auto swz_k = [](int r) { return (r / RPB) & (CPR16 - 1); };
+    auto swz_v = [](int r) { return 4 * ((r / RPB) & (CPR16 / 4 - 1)); };
     __shared__ __align__(1024) char stage0[2 * KB];
     __shared__ __align__(1024) char stage1[2 * KB];
 
@@ -2117,8 +2126,8 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
         const int r = RPL * li + lane / CPR16;              // the lane's row in the step
         const int cp = lane % CPR16;                        // its chunk position in LDS
         jb[u] = (RPL * li) / BS;
-        koff[u] = head_off + static_cast<uint32_t>((r % BS) * ROWB + (cp ^ (r & 7)) * 16);
-        voff[u] = head_off + static_cast<uint32_t>((r % BS) * ROWB + (cp ^ (2 * (r & 3))) * 16);
+        koff[u] = head_off + static_cast<uint32_t>((r % BS) * ROWB + (cp ^ swz_k(r)) * 16);
+        voff[u] = head_off + static_cast<uint32_t>((r % BS) * ROWB + (cp ^ swz_v(r)) * 16);
     }
     bool bad_id = false;
     int32_t ids[LPW];
@@ -2156,19 +2165,19 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
     float m = kNegInf, l = 0.f;
     // Per-lane parts of the operand addresses that the swizzle makes
     // non-additive; the rest (32-key halves, key groups, calls) are
-    // immediate offsets. K: row 32 t + col, chunk (2 kk + half) ^ (col & 7).
-    // V^T: key 16 a + 8 c + 4 (q >> 1) + (j >> 2) (so key & 3 = (j >> 2) & 3),
-    // 16-byte chunk (4 dt + 2 (q & 1) + (j & 3) / 2) ^ 2 (key & 3), then
-    // 8 (j & 1) bytes in.
+    // immediate offsets. K: row 32 t + col, whose swizzle is col's. V^T: key
+    // 16 a + 8 c + 4 (q >> 1) + (j >> 2), whose swizzle is that of j >> 2
+    // (it depends on the key mod 4 only), 16-byte chunk
+    // 4 dt + 2 (q & 1) + (j & 3) / 2, then 8 (j & 1) bytes in.
     const int gq = lane >> 4, jl = lane & 15;
     uint32_t koffs[NKK], voffs[NDT];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-        koffs[kk] = static_cast<uint32_t>(col * ROWB + (((2 * kk + half) ^ (col & 7)) * 16));
+        koffs[kk] = static_cast<uint32_t>(col * ROWB + (((2 * kk + half) ^ swz_k(col)) * 16));
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
         voffs[dt] = static_cast<uint32_t>((4 * (gq >> 1) + (jl >> 2)) * ROWB +
-                                          (((4 * dt + 2 * (gq & 1) + ((jl & 3) >> 1)) ^ (2 * ((jl >> 2) & 3))) * 16) +
+                                          (((4 * dt + 2 * (gq & 1) + ((jl & 3) >> 1)) ^ swz_v(jl >> 2)) * 16) +
                                           8 * (jl & 1));
 
     auto compute = [&](int s, const char* buf) {
