@@ -2032,6 +2032,10 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_fa_kernel(
 // stage's reads are known apart. V rows past the chunk's last key are
 // zeroed in LDS once the last step's loads are in (NaN bits in the cache
 // tail must not reach an MFMA); K rows there are masked by selection.
+// Steps are 32 keys (two cache blocks): the kernel then fits in 168
+// registers and 32 KB of LDS, three waves per SIMD (64-key steps took 215
+// registers: two).
+constexpr int kFaDmaKeys = 32;
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 // 16 bytes per lane from a buffer into LDS at dst + 16 lane (dst wave-uniform).
 __device__ __forceinline__ void fa_load_lds16(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff) {
@@ -2044,24 +2048,25 @@ __device__ __forceinline__ s16x4_t fa_read_tr16(const char* p) {
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
+__global__ __launch_bounds__(64 * G, 3) void paged_prefill_dma_kernel(
     const uint16_t* __restrict__ q_rot, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, int32_t mbps,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ cu, int32_t batch, int32_t hkv,
     int32_t num_blocks, int32_t total, int32_t max_new, float scale_log2, uint16_t* __restrict__ out,
     uint32_t* __restrict__ err, uint32_t* __restrict__ redo_word, uint32_t gen) {
     constexpr int ROWS = kFaRows;           // query tokens per workgroup (per wave and head)
+    constexpr int KEYS = kFaDmaKeys;        // keys per step
     constexpr int NT = 64 * G;              // threads
     constexpr int ROWB = D * 2;             // bytes per K or V row in LDS
     constexpr int CPR16 = ROWB / 16;        // 16-byte chunks per row
     constexpr int RPL = 1024 / ROWB;        // rows per wave load
-    constexpr int LPS = kFaKeys / RPL;      // wave loads per step (K; V alike)
+    constexpr int LPS = KEYS / RPL;      // wave loads per step (K; V alike)
     constexpr int LPW = (LPS + G - 1) / G;  // per wave
-    constexpr int KB = kFaKeys * ROWB;      // bytes of K (and of V) per stage
+    constexpr int KB = KEYS * ROWB;      // bytes of K (and of V) per stage
     constexpr int NKK = D / 16;             // score MFMAs per 32-key half
     constexpr int NDT = D / 32;             // output dim tiles
-    constexpr int NH = kFaKeys / 32;        // 32-key halves per step
-    constexpr int BPS = kFaKeys / BS;       // cache blocks per step
+    constexpr int NH = KEYS / 32;        // 32-key halves per step
+    constexpr int BPS = KEYS / BS;       // cache blocks per step
     constexpr int RPB = 256 / ROWB;         // rows per 256-byte bank line
     static_assert(BS % RPL == 0, "a wave load stays in one cache block");
     static_assert(RPB >= 1 && CPR16 >= 4, "row of 64 to 256 bytes");
@@ -2097,8 +2102,8 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
     const int j0 = (nqb - 1 - qblk) * ROWS;     // longest blocks first
     const int p_first = ctx + j0;
     const int p_last = ctx + min(j0 + ROWS, nnew) - 1;
-    const int nks = p_last / kFaKeys + 1;       // steps holding keys 0 .. p_last
-    const int ks_m = (p_first + 1) / kFaKeys;   // steps before this are unmasked for every query
+    const int nks = p_last / KEYS + 1;       // steps holding keys 0 .. p_last
+    const int ks_m = (p_first + 1) / KEYS;   // steps before this are unmasked for every query
     const int jq = j0 + col;                    // this lane's query token
     const bool q_ok = jq < nnew;
     const int pq = ctx + jq;
@@ -2153,9 +2158,9 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
             }
         }
     };
-    const int rows_last = p_last + 1 - kFaKeys * (nks - 1);   // valid key rows of the last step
+    const int rows_last = p_last + 1 - KEYS * (nks - 1);   // valid key rows of the last step
     auto zero_v_tail = [&](char* buf) {
-        for (int i = rows_last * CPR16 + tid; i < kFaKeys * CPR16; i += NT)
+        for (int i = rows_last * CPR16 + tid; i < KEYS * CPR16; i += NT)
             *reinterpret_cast<uint4*>(buf + KB + 16 * i) = make_uint4(0, 0, 0, 0);
     };
 
@@ -2200,7 +2205,7 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
             for (int t = 0; t < NH; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int kp = kFaKeys * s + 32 * t + 8 * (i / 4) + 4 * half + (i % 4);
+                    const int kp = KEYS * s + 32 * t + 8 * (i / 4) + 4 * half + (i % 4);
                     sc[t][i] = kp <= pq ? sacc[t][i] : kNegInf;
                 }
         } else {
@@ -2255,7 +2260,7 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
         compute(s, cur);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (s + 1 == nks - 1 && rows_last < kFaKeys) {
+        if (s + 1 == nks - 1 && rows_last < KEYS) {
             zero_v_tail(nxt);
             __syncthreads();
         }
@@ -2265,7 +2270,7 @@ __global__ __launch_bounds__(64 * G, 2) void paged_prefill_dma_kernel(
     load_ids(min(1, nks - 1));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (nks == 1 && rows_last < kFaKeys) {
+    if (nks == 1 && rows_last < KEYS) {
         zero_v_tail(stage0);
         __syncthreads();
     }
