@@ -36,13 +36,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
-// float64 -> bf16, nearest-even, a single rounding: truncate to float32 with a
-// sticky bit (round-to-odd keeps 16 guard bits), then round that to bf16.
+// float64 -> bf16, nearest-even, a single rounding: float32 rounded to odd
+// (16 guard bits and a sticky bit), then rounded to bf16. Round-to-odd is the
+// value truncated toward zero with its last bit set when inexact; truncation is
+// the nearest-even float32 stepped one unit toward zero when that nearest
+// value lies farther from zero than x (the two differ by at most one unit, and
+// the hardware conversion rounds to nearest, so no emulated truncation is
+// needed).
 __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
     if (x != x) return 0x7fc0;
-    const float f = __double2float_rz(x);
+    const float f = static_cast<float>(x);
+    const double back = static_cast<double>(f);
     uint32_t u = __float_as_uint(f);
-    if (static_cast<double>(f) != x) u |= 1u;
+    if (back != x) {
+        if (fabs(back) > fabs(x)) u -= 1u;
+        u |= 1u;
+    }
     u += 0x7fffu + ((u >> 16) & 1u);
     return static_cast<uint16_t>(u >> 16);
 }
@@ -52,47 +61,27 @@ __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
 }
 
 // ============================================================== write_decode_kv
-// Per row (grid.x): rotation threads, each owning pair (i, i + D/2) of one
-// head (decode) or of every (kRotThreads / (D/2))-th head (prefill), q heads
-// first, then the new k heads; then 16-byte pieces of the V copy; workgroups
-// of 256 threads tile that index space (grid.y). The angle pos * theta^(-2i/D) (inverse
-// frequencies from the host table), its sine and cosine and the rotation are
-// float64 with separately rounded products, rounded once to bf16. An 8-bit
-// cache (FMT = kFmtFp8) stores the E4M3 codes of that bf16 K and of v under
-// the head's scales.
+// Per decode row (grid.x = sequence): rotation threads, each owning pair
+// (i, i + D/2) of one head, q heads first, then the new k heads; then 16-byte
+// pieces of the V copy; workgroups of 256 threads tile that index space
+// (grid.y). The angle pos * theta^(-2i/D) (inverse frequencies from the host
+// table), its sine and cosine and the rotation are float64 with separately
+// rounded products, rounded once to bf16. An 8-bit cache (FMT = kFmtFp8)
+// stores the E4M3 codes of that bf16 K and of v under the head's scales.
 constexpr int kFmtBf16 = 0;
 constexpr int kFmtFp8 = 1;
-// Rotation threads per prefill row of write_decode_kv: 256 (each angle shared
-// by a quarter of the heads at D = 128) measured fastest on MI355X (512: +1 %,
-// 1024: +4 % on a 4 x 2048-token prefill step).
-constexpr int kRotThreads = 256;
 
-// With PREFILL the rows of q, k, v are the packed new tokens of a prefill
-// chunk (grid.x = total tokens): row i belongs to the sequence b with
-// cu[b] <= i < cu[b + 1] and sits at position ctx_b + i - cu[b].
-template <int D, int FMT, bool PREFILL>
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* q_rot, void* __restrict__ kc, void* __restrict__ vc,
     const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ cu, int32_t batch, int32_t hq, int32_t hkv, int32_t num_blocks,
-    mikv::RopeTable rope, const float* __restrict__ kv_scales, uint32_t* __restrict__ err) {
+    int32_t hq, int32_t hkv, int32_t num_blocks, mikv::RopeTable rope,
+    const float* __restrict__ kv_scales, uint32_t* __restrict__ err) {
     constexpr int H2 = D / 2;
-    const int row = blockIdx.x;               // row of q, k, v
-    int b = row;
-    int pos = 0;
-    if constexpr (PREFILL) {
-        int lo = 0, hi = batch - 1;           // last b with cu[b] <= row
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cu[mid] <= row) lo = mid;
-            else hi = mid - 1;
-        }
-        b = lo;
-        pos = ctx_lens[b] + row - cu[b];
-    } else {
-        pos = ctx_lens[b];
-    }
+    const int row = blockIdx.x;               // row of q, k, v = sequence
+    const int b = row;
+    const int pos = ctx_lens[b];
     const bool pos_ok = pos >= 0 && pos / BS < mbps;
     const int32_t blk = pos_ok ? table[static_cast<size_t>(b) * mbps + pos / BS] : -1;
     const bool blk_ok = pos_ok && blk >= 0 && blk < num_blocks;
@@ -102,62 +91,41 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
     }
     if (!pos_ok) return;
     const int off = pos % BS;
-    // Rotation threads: thread (grp, i) owns pair i of the heads grp, grp + NG,
-    // grp + 2 NG, ... (q heads, then the new k heads) and computes their
-    // angle's float64 sine and cosine once; its heads go in batches of 8 whose
-    // loads are issued before any store. A decode row (few rows, latency
-    // bound) takes one head per thread (NG = all heads); a prefill row (many
-    // rows, bound by the sines and cosines) shares each angle over
-    // (Hq + Hkv) / NG heads, NG = kRotThreads / (D/2).
+    // Rotation threads: thread (h, i) owns pair i of head h (q heads, then
+    // the new k heads) and computes its angle's float64 sine and cosine (a
+    // decode row is latency bound: one head per thread).
     const int nh = hq + hkv;
-    const int NG = PREFILL ? kRotThreads / H2 : nh;
-    const int n_rot = NG * H2;
+    const int n_rot = nh * H2;
     const int idx = blockIdx.y * blockDim.x + threadIdx.x;
     if (idx < n_rot) {
-        const int grp = idx / H2;
-        const int i = idx - grp * H2;
-        if (grp >= nh) return;
+        const int h = idx / H2;
+        const int i = idx - h * H2;
+        const uint16_t* src = h < hq ? q + (static_cast<size_t>(row) * hq + h) * D
+                                     : k + (static_cast<size_t>(row) * hkv + (h - hq)) * D;
+        const uint16_t in1 = src[i], in2 = src[i + H2];
+        if (h >= hq && !blk_ok) return;
         double sn, cs;
         sincos(static_cast<double>(pos) * rope.inv_freq[i], &sn, &cs);
-        for (int h0 = grp; h0 < nh; h0 += 8 * NG) {
-            uint16_t in1[8], in2[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int h = h0 + NG * t;
-                in1[t] = in2[t] = 0;
-                if (h < nh) {
-                    const uint16_t* src = h < hq ? q + (static_cast<size_t>(row) * hq + h) * D
-                                                 : k + (static_cast<size_t>(row) * hkv + (h - hq)) * D;
-                    in1[t] = src[i];
-                    in2[t] = src[i + H2];
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int h = h0 + NG * t;
-                if (h >= nh || (h >= hq && !blk_ok)) continue;
-                const double x1 = bf16_to_f64(in1[t]);
-                const double x2 = bf16_to_f64(in2[t]);
-                const uint16_t r1 = f64_to_bf16_rne(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
-                const uint16_t r2 = f64_to_bf16_rne(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
-                if (h < hq) {
-                    uint16_t* dst = q_rot + (static_cast<size_t>(row) * hq + h) * D;
-                    dst[i] = r1;
-                    dst[i + H2] = r2;
-                } else {
-                    const int g = h - hq;
-                    const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
-                    if constexpr (FMT == kFmtBf16) {
-                        uint16_t* dst = static_cast<uint16_t*>(kc) + at;
-                        dst[i] = r1;
-                        dst[i + H2] = r2;
-                    } else {
-                        uint8_t* dst = static_cast<uint8_t*>(kc) + at;
-                        const float sc = kv_scales[g];
-                        dst[i] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, sc));
-                        dst[i + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, sc));
-                    }
-                }
+        const double x1 = bf16_to_f64(in1);
+        const double x2 = bf16_to_f64(in2);
+        const uint16_t r1 = f64_to_bf16_rne(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
+        const uint16_t r2 = f64_to_bf16_rne(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
+        if (h < hq) {
+            uint16_t* dst = q_rot + (static_cast<size_t>(row) * hq + h) * D;
+            dst[i] = r1;
+            dst[i + H2] = r2;
+        } else {
+            const int g = h - hq;
+            const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + off) * D;
+            if constexpr (FMT == kFmtBf16) {
+                uint16_t* dst = static_cast<uint16_t*>(kc) + at;
+                dst[i] = r1;
+                dst[i + H2] = r2;
+            } else {
+                uint8_t* dst = static_cast<uint8_t*>(kc) + at;
+                const float sc = kv_scales[g];
+                dst[i] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r1, sc));
+                dst[i + H2] = static_cast<uint8_t>(mikv_dev::e4m3_quantize_bf16(r2, sc));
             }
         }
     } else if (blk_ok) {
@@ -173,6 +141,172 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
         else
             *reinterpret_cast<uint2*>(static_cast<uint8_t*>(vc) + at) =
                 mikv_dev::e4m3_quantize_bf16x8(val, kv_scales[hkv + g]);
+    }
+}
+
+// ====================================================== prompt KV write (prefill)
+// The packed rows of a prefill chunk (row i of sequence b: cu[b] <= i <
+// cu[b + 1], position ctx_b + i - cu[b]) with the same arithmetic as
+// write_decode_kv: the float64 angle, sine and cosine, a float64 rotation with
+// separately rounded products and one rounding to bf16 (an 8-bit cache stores
+// the E4M3 codes of that bf16 K and of v). Shaped for bandwidth: a workgroup
+// takes kWpRows rows; every access is a 16-byte piece (8 dims of one head and
+// the 8 dims D/2 further, which are their rotation partners, or 8 dims of v),
+// consecutive threads take consecutive pieces of a row, and each thread
+// loads all of its pieces of a pass before it rotates and stores any. The
+// rows' sines and cosines (kWpRows x D/2, one per thread) sit in LDS. Rows with a bad position write nothing (fault bit); rows whose
+// block id is bad write q_rot only.
+constexpr int kWpRows = 2;          // prompt rows per workgroup
+constexpr int kWpItems = 4;         // 16-byte pieces per thread per pass
+template <int D, int FMT>
+__global__ __launch_bounds__(256) void write_prefill_kv_kernel(
+    const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* q_rot, void* __restrict__ kc, void* __restrict__ vc,
+    const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ cu, int32_t batch, int32_t tokens, int32_t hq, int32_t hkv,
+    int32_t num_blocks, mikv::RopeTable rope, const float* __restrict__ kv_scales,
+    uint32_t* __restrict__ err) {
+    constexpr int H2 = D / 2;
+    constexpr int PC = H2 / 8;          // rotation pieces per head (each with its partner piece)
+    constexpr int VC = D / 8;           // v pieces per head
+    constexpr int R = kWpRows;
+    constexpr int NT = 256;
+    __shared__ int s_pos[R], s_blk[R];  // s_pos < 0: row not written; s_blk < 0: no K/V
+    __shared__ double s_cs[R][H2], s_sn[R][H2];
+    const int tid = threadIdx.x;
+    const int row0 = static_cast<int>(blockIdx.x) * R;
+    const int nh = hq + hkv;
+    const int per_rot = nh * PC, per_v = hkv * VC;
+    const int n_rot = R * per_rot;
+    const int total = n_rot + R * per_v;
+    // piece it: rotation pieces (row, head, j) first, then v pieces (row, kv head, e)
+    struct Piece {
+        uint4 lo, hi;
+    };
+    auto fetch = [&](int it) __attribute__((always_inline)) {
+        Piece pc{make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+        if (it < n_rot) {
+            const int r = it / per_rot, rem = it - r * per_rot;
+            const int h = rem / PC, j = rem - h * PC;
+            const int row = row0 + r;
+            if (row < tokens) {
+                const uint16_t* src = h < hq ? q + (static_cast<size_t>(row) * hq + h) * D
+                                             : k + (static_cast<size_t>(row) * hkv + (h - hq)) * D;
+                pc.lo = *reinterpret_cast<const uint4*>(src + 8 * j);
+                pc.hi = *reinterpret_cast<const uint4*>(src + H2 + 8 * j);
+            }
+        } else if (it < total) {
+            const int iv = it - n_rot;
+            const int r = iv / per_v, rem = iv - r * per_v;
+            const int g = rem / VC, e = (rem - g * VC) * 8;
+            const int row = row0 + r;
+            if (row < tokens)
+                pc.lo = *reinterpret_cast<const uint4*>(v + (static_cast<size_t>(row) * hkv + g) * D + e);
+        }
+        return pc;
+    };
+    auto put = [&](int it, const Piece& pc) __attribute__((always_inline)) {
+        if (it < n_rot) {
+            const int r = it / per_rot, rem = it - r * per_rot;
+            const int h = rem / PC, j = rem - h * PC;
+            const int pos = s_pos[r], blk = s_blk[r];
+            if (pos >= 0 && (h < hq || blk >= 0)) {
+                const uint32_t a[4] = {pc.lo.x, pc.lo.y, pc.lo.z, pc.lo.w};
+                const uint32_t c[4] = {pc.hi.x, pc.hi.y, pc.hi.z, pc.hi.w};
+                uint32_t o1[4], o2[4];
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) {
+                    uint32_t p1 = 0, p2 = 0;
+#pragma unroll
+                    for (int sh = 0; sh < 2; ++sh) {
+                        const int d = 8 * j + 2 * w2 + sh;
+                        const double x1 = bf16_to_f64(static_cast<uint16_t>(a[w2] >> (16 * sh)));
+                        const double x2 = bf16_to_f64(static_cast<uint16_t>(c[w2] >> (16 * sh)));
+                        const double cs = s_cs[r][d], sn = s_sn[r][d];
+                        const uint32_t r1 = f64_to_bf16_rne(__dsub_rn(__dmul_rn(x1, cs), __dmul_rn(x2, sn)));
+                        const uint32_t r2 = f64_to_bf16_rne(__dadd_rn(__dmul_rn(x2, cs), __dmul_rn(x1, sn)));
+                        p1 |= r1 << (16 * sh);
+                        p2 |= r2 << (16 * sh);
+                    }
+                    o1[w2] = p1;
+                    o2[w2] = p2;
+                }
+                const uint4 v1 = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+                const uint4 v2 = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+                const int row = row0 + r;
+                if (h < hq) {
+                    uint16_t* dst = q_rot + (static_cast<size_t>(row) * hq + h) * D;
+                    *reinterpret_cast<uint4*>(dst + 8 * j) = v1;
+                    *reinterpret_cast<uint4*>(dst + H2 + 8 * j) = v2;
+                } else {
+                    const int g = h - hq;
+                    const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + pos % BS) * D;
+                    if constexpr (FMT == kFmtBf16) {
+                        uint16_t* dst = static_cast<uint16_t*>(kc) + at;
+                        *reinterpret_cast<uint4*>(dst + 8 * j) = v1;
+                        *reinterpret_cast<uint4*>(dst + H2 + 8 * j) = v2;
+                    } else {
+                        uint8_t* dst = static_cast<uint8_t*>(kc) + at;
+                        const float sc = kv_scales[g];
+                        *reinterpret_cast<uint2*>(dst + 8 * j) = mikv_dev::e4m3_quantize_bf16x8(v1, sc);
+                        *reinterpret_cast<uint2*>(dst + H2 + 8 * j) = mikv_dev::e4m3_quantize_bf16x8(v2, sc);
+                    }
+                }
+            }
+        } else if (it < total) {
+            const int iv = it - n_rot;
+            const int r = iv / per_v, rem = iv - r * per_v;
+            const int g = rem / VC, e = (rem - g * VC) * 8;
+            const int pos = s_pos[r], blk = s_blk[r];
+            if (pos >= 0 && blk >= 0) {
+                const size_t at = ((static_cast<size_t>(blk) * hkv + g) * BS + pos % BS) * D + e;
+                if constexpr (FMT == kFmtBf16)
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(vc) + at) = pc.lo;
+                else
+                    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(vc) + at) =
+                        mikv_dev::e4m3_quantize_bf16x8(pc.lo, kv_scales[hkv + g]);
+            }
+        }
+    };
+    if (tid < R) {                      // row -> sequence, position, block (faults recorded per row)
+        const int row = row0 + tid;
+        int pos = -1, blk = -1;
+        if (row < tokens) {
+            int lo_b = 0, hi_b = batch - 1;     // last b with cu[b] <= row
+            while (lo_b < hi_b) {
+                const int mid = (lo_b + hi_b + 1) >> 1;
+                if (cu[mid] <= row) lo_b = mid;
+                else hi_b = mid - 1;
+            }
+            const int b = lo_b;
+            pos = ctx_lens[b] + row - cu[b];
+            const bool pos_ok = pos >= 0 && pos / BS < mbps;
+            blk = pos_ok ? table[static_cast<size_t>(b) * mbps + pos / BS] : -1;
+            const bool blk_ok = pos_ok && blk >= 0 && blk < num_blocks;
+            if (!pos_ok) atomicOr(err, static_cast<uint32_t>(MI_FAULT_CONTEXT_LEN));
+            else if (!blk_ok) atomicOr(err, static_cast<uint32_t>(MI_FAULT_BLOCK_ID));
+            if (!pos_ok) pos = -1;
+            if (!blk_ok) blk = -1;
+        }
+        s_pos[tid] = pos;
+        s_blk[tid] = blk;
+    }
+    __syncthreads();
+    for (int a2 = tid; a2 < R * H2; a2 += NT) {
+        const int r = a2 / H2, i = a2 - r * H2;
+        const int pos = s_pos[r];
+        double sn = 0.0, cs = 1.0;
+        if (pos >= 0) sincos(static_cast<double>(pos) * rope.inv_freq[i], &sn, &cs);
+        s_cs[r][i] = cs;
+        s_sn[r][i] = sn;
+    }
+    __syncthreads();
+    for (int base = 0; base < total; base += NT * kWpItems) {
+        Piece pc[kWpItems];
+#pragma unroll
+        for (int u = 0; u < kWpItems; ++u) pc[u] = fetch(base + u * NT + tid);
+#pragma unroll
+        for (int u = 0; u < kWpItems; ++u) put(base + u * NT + tid, pc[u]);
     }
 }
 
@@ -1396,7 +1530,7 @@ struct DotShape {
 };
 
 // ================================================ paged prefill, rescaling form
-// Causal attention of a prefill chunk (packed rows, see the PREFILL write)
+// Causal attention of a prefill chunk (packed rows, see the prompt KV write)
 // with the online rescaling softmax. One wave per (block of 16 QB new
 // tokens, query head): the MFMA tile of the decode kernel with QB column
 // blocks taken by the block's query tokens instead of the group's heads, so
@@ -1546,7 +1680,9 @@ __global__ __launch_bounds__(64, 1) void paged_prefill_rescale_kernel(
 
 // ============================================== prefill, shared-tile form
 // Causal attention of a prefill chunk with the K/V tiles shared by the query
-// heads of a KV group. One workgroup per (KV head g, sequence, 32-token query
+// heads of a KV group; this register-staged form serves 8-bit caches (the
+// copy widens the codes), bf16 caches take paged_prefill_dma_kernel below.
+// One workgroup per (KV head g, sequence, 32-token query
 // block), one wave per query head of the group (G waves); the blocks with the
 // longest key ranges are dispatched first across the whole chunk
 // (fa_block_of_rank). A sequence with a bad length or chunk is recorded as a
@@ -1566,8 +1702,8 @@ __global__ __launch_bounds__(64, 1) void paged_prefill_rescale_kernel(
 //    of each group in the matching order: key 16a + r sits at column 16a +
 //    8 ((r / 4) % 2) + (r % 4) + 4 (r / 8), and the A operand of a lane is one
 //    16-byte read.
-// Rows of K and of V^T are padded (16 bytes) so the operand reads of 8
-// consecutive lanes fall on distinct banks. The softmax uses a fixed
+// Rows of K and of V^T are padded (16 bytes) so the 16 lanes a 16-byte
+// operand read serves per cycle fall on distinct banks. The softmax uses a fixed
 // reference (the largest score of the first step, never raised) and the row
 // sum adds the weights as rounded for the MFMA. A query whose row sum ends
 // above kFixedHeadroomSum (which any single weight above that bound forces)
@@ -2662,11 +2798,10 @@ int launch_write_decode_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint1
     const RopeTable rope = make_rope_table(theta, p->head_dim);
     const bool f8 = pool_fp8(p);
     auto kern = p->head_dim == 128
-                    ? (f8 ? write_decode_kv_kernel<128, kFmtFp8, false> : write_decode_kv_kernel<128, kFmtBf16, false>)
-                    : (f8 ? write_decode_kv_kernel<64, kFmtFp8, false> : write_decode_kv_kernel<64, kFmtBf16, false>);
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, k, v, q_rot, p->k, p->v, table, mbps, ctx,
-                       static_cast<const int32_t*>(nullptr), batch, hq, hkv, p->num_blocks, rope,
-                       static_cast<const float*>(p->scales), p->err);
+                    ? (f8 ? write_decode_kv_kernel<128, kFmtFp8> : write_decode_kv_kernel<128, kFmtBf16>)
+                    : (f8 ? write_decode_kv_kernel<64, kFmtFp8> : write_decode_kv_kernel<64, kFmtBf16>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, k, v, q_rot, p->k, p->v, table, mbps, ctx, hq, hkv,
+                       p->num_blocks, rope, static_cast<const float*>(p->scales), p->err);
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 
@@ -2676,15 +2811,15 @@ int launch_write_prefill_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint
                             int32_t hq, double theta, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int hkv = p->num_kv_heads;
-    const int items = kRotThreads + hkv * (p->head_dim / 8);
-    const dim3 grid(tokens, (items + 255) / 256);
+    const dim3 grid((tokens + kWpRows - 1) / kWpRows);
     const RopeTable rope = make_rope_table(theta, p->head_dim);
     const bool f8 = pool_fp8(p);
     auto kern = p->head_dim == 128
-                    ? (f8 ? write_decode_kv_kernel<128, kFmtFp8, true> : write_decode_kv_kernel<128, kFmtBf16, true>)
-                    : (f8 ? write_decode_kv_kernel<64, kFmtFp8, true> : write_decode_kv_kernel<64, kFmtBf16, true>);
+                    ? (f8 ? write_prefill_kv_kernel<128, kFmtFp8> : write_prefill_kv_kernel<128, kFmtBf16>)
+                    : (f8 ? write_prefill_kv_kernel<64, kFmtFp8> : write_prefill_kv_kernel<64, kFmtBf16>);
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, k, v, q_rot, p->k, p->v, table, mbps, ctx, cu,
-                       batch, hq, hkv, p->num_blocks, rope, static_cast<const float*>(p->scales), p->err);
+                       batch, tokens, hq, hkv, p->num_blocks, rope, static_cast<const float*>(p->scales),
+                       p->err);
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
 

@@ -55,11 +55,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     u += 0x7fffu + ((u >> 16) & 1u);
     return static_cast<uint16_t>(u >> 16);
 }
+// float64 -> bf16 with one nearest-even rounding: float32 rounded to odd (the
+// nearest-even float32, stepped one unit toward zero when it lies farther
+// from zero than x, with the last bit set when inexact), then to bf16.
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
     if (x != x) return 0x7fc0;
-    const float f = __double2float_rz(x);
+    const float f = static_cast<float>(x);
+    const double back = static_cast<double>(f);
     uint32_t u = __float_as_uint(f);
-    if (static_cast<double>(f) != x) u |= 1u;
+    if (back != x) {
+        if (fabs(back) > fabs(x)) u -= 1u;
+        u |= 1u;
+    }
     u += 0x7fffu + ((u >> 16) & 1u);
     return static_cast<uint16_t>(u >> 16);
 }
