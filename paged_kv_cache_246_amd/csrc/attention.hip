@@ -156,10 +156,11 @@ __global__ __launch_bounds__(256) void write_decode_kv_kernel(
 // loads all of its pieces of a pass before it rotates and stores any. The
 // rows' sines and cosines (kWpRows x D/2, one per thread) sit in LDS. Rows with a bad position write nothing (fault bit); rows whose
 // block id is bad write q_rot only.
-constexpr int kWpRows = 2;          // prompt rows per workgroup
-constexpr int kWpItems = 4;         // 16-byte pieces per thread per pass
+constexpr int kWpRows = 1;          // prompt rows per workgroup
+constexpr int kWpItems = 2;         // 16-byte pieces per thread per pass
+constexpr int kWpThreads = 256;
 template <int D, int FMT>
-__global__ __launch_bounds__(256) void write_prefill_kv_kernel(
+__global__ __launch_bounds__(kWpThreads) void write_prefill_kv_kernel(
     const uint16_t* q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* q_rot, void* __restrict__ kc, void* __restrict__ vc,
     const int32_t* __restrict__ table, int32_t mbps, const int32_t* __restrict__ ctx_lens,
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256) void write_prefill_kv_kernel(
     constexpr int PC = H2 / 8;          // rotation pieces per head (each with its partner piece)
     constexpr int VC = D / 8;           // v pieces per head
     constexpr int R = kWpRows;
-    constexpr int NT = 256;
+    constexpr int NT = kWpThreads;
     __shared__ int s_pos[R], s_blk[R];  // s_pos < 0: row not written; s_blk < 0: no K/V
     __shared__ double s_cs[R][H2], s_sn[R][H2];
     const int tid = threadIdx.x;
@@ -2817,8 +2818,8 @@ int launch_write_prefill_kv(const mi_kv_pool_s* p, const uint16_t* q, const uint
     auto kern = p->head_dim == 128
                     ? (f8 ? write_prefill_kv_kernel<128, kFmtFp8> : write_prefill_kv_kernel<128, kFmtBf16>)
                     : (f8 ? write_prefill_kv_kernel<64, kFmtFp8> : write_prefill_kv_kernel<64, kFmtBf16>);
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, k, v, q_rot, p->k, p->v, table, mbps, ctx, cu,
-                       batch, tokens, hq, hkv, p->num_blocks, rope, static_cast<const float*>(p->scales),
+    hipLaunchKernelGGL(kern, grid, dim3(kWpThreads), 0, st, q, k, v, q_rot, p->k, p->v, table, mbps, ctx,
+                       cu, batch, tokens, hq, hkv, p->num_blocks, rope, static_cast<const float*>(p->scales),
                        p->err);
     return hipGetLastError() == hipSuccess ? MI_OK : MI_ERR_HIP;
 }
