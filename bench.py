@@ -269,33 +269,29 @@ def run_prefill_bench(args, torch, mk, workloads, cached=False):
     stream = torch.cuda.current_stream()
     st = stream.cuda_stream
 
-    def step(ev=None):
+    def write():
         mk.mi_write_prefill_kv(pool, q, k, v, q_rot, table, mbps, ctx, cu, B, T, Hq,
                                cfg.rope_theta, st)
-        if ev is not None:
-            ev[0].record(stream)
+
+    def attention():
         mk.mi_paged_prefill_attention(pool, q_rot, out, table, mbps, ctx, cu, B, T, max_new, Hq,
                                       0.0, st)
-        if ev is not None:
-            ev[1].record(stream)
 
+    def step():
+        write()
+        attention()
+
+    # The step (write + attention) back to back; then the attention alone:
+    # back to back under one event pair (its average launch duration, the
+    # roofline's) and with an event pair per call (percentiles). The calls
+    # repeat the same work on the same inputs.
     steps = max(1, args.steps // 5)
-    for _ in range(max(1, args.warmup // 2)):
-        step()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    warm = max(1, args.warmup // 2)
+    t_step = time_step(torch, stream, step, steps, warm)
+    t_attn = time_step(torch, stream, attention, steps, warm)
+    t_write = time_step(torch, stream, write, steps, warm)
+    ms = t_step["ms_per_step"]
+    attn_ms = t_attn["ms_per_step"]
     faults = mk.mi_kv_pool_check_errors(pool)
     mk.mi_kv_pool_destroy(pool)
     if faults:
@@ -310,6 +306,8 @@ def run_prefill_bench(args, torch, mk, workloads, cached=False):
         "ms_per_step": round(ms, 5),
         "tokens_per_s": round(T / (ms * 1e-3), 1),
         "attention_avg_launch_ms": round(attn_ms, 5),
+        "attention_per_call_ms": t_attn["warm_ms"],
+        "write_avg_launch_ms": t_write["ms_per_step"],
         "attention_flops": int(flops),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
