@@ -34,6 +34,12 @@ there are no infinities; the largest finite magnitude is 448.
   float32 operation (the precision the device computes it in), then a
   single rounding to E4M3.
 * ``dequantize``: decode(code) * s in float64 (exact).
+* ``calibrate_scales``: static per-head scales from sample rows of k and v
+  (for example a prefill chunk). The article's section 2.2 scales a group by
+  its largest magnitude (127 / max|x| for int8): the largest value maps to
+  the largest code. For E4M3 that reads s = max|x| / 448, here with a
+  caller's margin factor (a margin above 1 leaves room for later values
+  above the sample's maximum, which would otherwise saturate).
 """
 import numpy as np
 
@@ -101,3 +107,30 @@ def quantize(bf16_values, scale):
 def dequantize(codes, scale):
     """Values an attention reads back: decode(code) * scale (float64, exact)."""
     return decode(codes) * float(np.float32(scale))
+
+
+def calibrate_scales(k_bits, v_bits, margin=1.0):
+    """Per-KV-head scales from sample rows: k_bits, v_bits are bf16 bit
+    patterns [rows, num_kv_heads, head_dim]. For each head and each of K and
+    V, a = the largest |x| over the head's finite values; the scale is
+    float32(float32(a * margin) / 448) (two float32 operations, the precision
+    the device computes in), or 1.0 when that is not a positive finite value
+    (no finite nonzero sample). Returns (k_scales, v_scales), float32 arrays
+    [num_kv_heads]."""
+    m = np.float32(margin)
+
+    def per_head(bits):
+        b = np.asarray(bits, dtype=np.uint16)
+        x = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        hkv = x.shape[1]
+        out = np.empty(hkv, dtype=np.float32)
+        for g in range(hkv):
+            vals = x[:, g, :]
+            fin = vals[np.isfinite(vals)]
+            a = np.float32(np.max(np.abs(fin))) if fin.size else np.float32(0.0)
+            with np.errstate(over="ignore"):
+                s = np.float32(np.float32(a * m) / np.float32(MAX_FINITE))
+            out[g] = s if (np.isfinite(s) and s > 0) else np.float32(1.0)
+        return out
+
+    return per_head(k_bits), per_head(v_bits)

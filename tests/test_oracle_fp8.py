@@ -203,3 +203,59 @@ def test_fp8_workload_codes_are_finite_and_normal_like():
     d = fp8.decode(c)
     assert np.all(np.isfinite(d))
     assert 0.6 < np.std(d) < 1.4 and abs(np.mean(d)) < 0.02
+
+
+# ---------------------------------------------------------------- calibration
+
+def _bits(x):
+    return bf16.encode(np.asarray(x, dtype=np.float64))
+
+
+def test_calibrated_scale_maps_each_heads_largest_value_to_448():
+    """margin 1: the largest |x| of every head stores as +-448 (code 0x7E or
+    0xFE) and nothing saturates; the scale of a head with a negative maximum
+    comes from its magnitude."""
+    rng = np.random.default_rng(31)
+    k = rng.standard_normal((40, 3, 16))
+    v = rng.standard_normal((40, 3, 16)) * np.array([1.0, 20.0, 0.01])[None, :, None]
+    k[7, 2, 5] = -9.5                                  # head 2's largest magnitude, negative
+    kb, vb = _bits(k), _bits(v)
+    ks, vs = fp8.calibrate_scales(kb, vb)
+    for bits, sc in ((kb, ks), (vb, vs)):
+        x = bf16.decode(bits)
+        for g in range(3):
+            codes = fp8.quantize(x[:, g, :], sc[g])
+            mag = codes & 0x7F
+            i = np.unravel_index(np.argmax(np.abs(x[:, g, :])), x[:, g, :].shape)
+            assert mag[i] == 0x7E
+            assert mag.max() == 0x7E and (mag == 0x7E).sum() >= 1
+    # per head, not per pool: head 1 of v is 20x head 0 and 2000x head 2
+    assert 10 < vs[1] / vs[0] < 40 and 1000 < vs[1] / vs[2] < 4000
+    # K and V calibrated separately
+    assert not np.array_equal(ks, vs)
+    assert np.isclose(ks[2], 9.5 / 448, rtol=1e-6)
+
+
+def test_calibration_skips_non_finite_values_and_defaults_to_one():
+    k = np.zeros((8, 2, 16))
+    v = np.ones((8, 2, 16))
+    k[:, 1, :] = 0.5
+    kb, vb = _bits(k), _bits(v)
+    kb[3, 1, 4] = 0x7F80                 # +inf
+    kb[4, 1, 4] = 0x7FC0                 # NaN
+    vb[:, 0, :] = 0x7F80                 # a head of infinities only
+    ks, vs = fp8.calibrate_scales(kb, vb)
+    assert ks[0] == np.float32(1.0)      # all zeros
+    assert ks[1] == np.float32(np.float32(0.5) / np.float32(448))
+    assert vs[0] == np.float32(1.0)      # no finite value
+    assert vs[1] == np.float32(np.float32(1.0) / np.float32(448))
+
+
+def test_calibration_margin_scales_exactly():
+    rng = np.random.default_rng(32)
+    k = _bits(rng.standard_normal((16, 4, 8)))
+    v = _bits(rng.standard_normal((16, 4, 8)))
+    k1, v1 = fp8.calibrate_scales(k, v, 1.0)
+    k2, v2 = fp8.calibrate_scales(k, v, 2.0)
+    np.testing.assert_array_equal(k2, 2 * k1)          # a power of two: exact
+    np.testing.assert_array_equal(v2, 2 * v1)
