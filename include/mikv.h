@@ -154,6 +154,13 @@ int mi_kv_pool_init(mi_kv_pool_t* out, int32_t num_blocks, int32_t block_size,
 int mi_kv_pool_set_scales(mi_kv_pool_t pool, const float* k_scales, const float* v_scales);
 
 /*
+ * Read back the per-KV-head scales of an 8-bit pool (as set or calibrated)
+ * into host arrays [num_kv_heads]; either may be NULL. Synchronises the
+ * device. MI_ERR_INVALID_ARG for a bf16 or host-only pool or two NULLs.
+ */
+int mi_kv_pool_get_scales(mi_kv_pool_t pool, float* k_scales, float* v_scales);
+
+/*
  * Quantise whole bf16 caches into an 8-bit pool: k_src, v_src are device
  * bf16 pools of the same [num_blocks, num_kv_heads, 16, head_dim] shape
  * (e.g. filled by a bf16 prefill); every element is stored as its code under
@@ -162,6 +169,28 @@ int mi_kv_pool_set_scales(mi_kv_pool_t pool, const float* k_scales, const float*
  */
 int mi_kv_pool_quantize(mi_kv_pool_t pool, const uint16_t* k_src, const uint16_t* v_src,
                         void* stream);
+
+/*
+ * Calibrate the per-KV-head scales of an 8-bit pool from sample rows, e.g. a
+ * prefill chunk (nxmr.cn inference-techniques article, section 2.2: a group
+ * is scaled by its largest magnitude so that this value maps to the largest
+ * code; read here for E4M3 and static per-head scales). For each KV head and
+ * each of K and V:
+ *     s = (a * margin) / 448      (two float32 operations)
+ * where a is the largest |x| over the head's finite sample values; s = 1.0
+ * when that is not positive and finite (no finite nonzero sample).
+ *  k, v    device bf16 [rows, num_kv_heads, head_dim] (the layout of
+ *          mi_write_prefill_kv's k and v), 16-byte aligned, rows >= 1
+ *  margin  finite and > 0. At 1 the sample's largest value stores as +-448;
+ *          above 1 leaves headroom for larger later values, which would
+ *          otherwise saturate.
+ * The new scales replace the pool's on `stream` (asynchronous). Calibrate
+ * before anything is written, as with mi_kv_pool_set_scales.
+ * MI_ERR_INVALID_ARG for a bf16 or host-only pool, NULL inputs, rows < 1 or
+ * a bad margin (nothing launched).
+ */
+int mi_kv_pool_calibrate_scales(mi_kv_pool_t pool, const uint16_t* k, const uint16_t* v, int32_t rows,
+                                float margin, void* stream);
 
 /* Free the handle, library-owned pools and the error word. NULL is a no-op. */
 int mi_kv_pool_destroy(mi_kv_pool_t pool);

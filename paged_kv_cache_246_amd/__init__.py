@@ -48,6 +48,8 @@ SIGNATURES = {
     "mi_kv_pool_destroy": (_c.c_int, [_vp]),
     "mi_kv_pool_set_scales": (_c.c_int, [_vp, _vp, _vp]),
     "mi_kv_pool_quantize": (_c.c_int, [_vp, _vp, _vp, _vp]),
+    "mi_kv_pool_calibrate_scales": (_c.c_int, [_vp, _vp, _vp, _i32, _c.c_float, _vp]),
+    "mi_kv_pool_get_scales": (_c.c_int, [_vp, _vp, _vp]),
     "mi_kv_pool_get": (_c.c_int, [_vp, _c.POINTER(_vp), _c.POINTER(_vp)]),
     "mi_kv_pool_shape": (_c.c_int, [_vp, _c.POINTER(_i32), _c.POINTER(_i32), _c.POINTER(_i32),
                                     _c.POINTER(_i32)]),
@@ -184,6 +186,19 @@ def mi_kv_pool_set_scales(pool, k_scales=None, v_scales=None):
 def mi_kv_pool_quantize(pool, k_src, v_src, stream=None):
     return _check("mi_kv_pool_quantize", lib().mi_kv_pool_quantize(
         pool, _ptr(k_src), _ptr(v_src), _stream(stream)))
+
+
+def mi_kv_pool_calibrate_scales(pool, k, v, rows, margin=1.0, stream=None):
+    return _check("mi_kv_pool_calibrate_scales", lib().mi_kv_pool_calibrate_scales(
+        pool, _ptr(k), _ptr(v), rows, margin, _stream(stream)))
+
+
+def mi_kv_pool_get_scales(pool):
+    """(k_scales, v_scales) of an 8-bit pool as lists of floats."""
+    hkv = mi_kv_pool_shape(pool)[2]
+    ks, vs = (ctypes.c_float * hkv)(), (ctypes.c_float * hkv)()
+    _check("mi_kv_pool_get_scales", lib().mi_kv_pool_get_scales(pool, ks, vs))
+    return list(ks), list(vs)
 
 
 def mi_kv_pool_get(pool):

@@ -132,6 +132,21 @@ extern "C" int mi_kv_pool_set_scales(mi_kv_pool_t p, const float* k_scales, cons
     return MI_OK;
 }
 
+extern "C" int mi_kv_pool_get_scales(mi_kv_pool_t p, float* k_scales, float* v_scales) {
+    if (!p || !mikv::pool_fp8(p) || !mikv::pool_has_device(p) || (!k_scales && !v_scales))
+        return MI_ERR_INVALID_ARG;
+    const int hkv = p->num_kv_heads;
+    std::vector<float> s(2 * static_cast<size_t>(hkv));
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(s.data(), p->scales, s.size() * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess)
+        return MI_ERR_HIP;
+    for (int g = 0; g < hkv; ++g) {
+        if (k_scales) k_scales[g] = s[g];
+        if (v_scales) v_scales[g] = s[hkv + g];
+    }
+    return MI_OK;
+}
+
 extern "C" int mi_kv_pool_destroy(mi_kv_pool_t p) {
     if (!p) return MI_OK;
     int st = MI_OK;

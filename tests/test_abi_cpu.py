@@ -163,6 +163,16 @@ def test_fp8_pool_scales_validation_on_host_only_pools():
         with pytest.raises(mk.MikvError) as e:          # no device buffers to quantise into
             mk.mi_kv_pool_quantize(p8, 1, 1, stream=0)
         assert e.value.status == mk.MI_ERR_INVALID_ARG
+        # calibration and read-back need device scales; arguments are checked
+        # before anything is launched
+        for pool, rows, margin in ((p8, 4, 1.0), (p16, 4, 1.0)):
+            with pytest.raises(mk.MikvError) as e:
+                mk.mi_kv_pool_calibrate_scales(pool, 16, 16, rows, margin, stream=0)
+            assert e.value.status == mk.MI_ERR_INVALID_ARG
+        for pool in (p8, p16):
+            with pytest.raises(mk.MikvError) as e:
+                mk.mi_kv_pool_get_scales(pool)
+            assert e.value.status == mk.MI_ERR_INVALID_ARG
     finally:
         mk.mi_kv_pool_destroy(p8)
         mk.mi_kv_pool_destroy(p16)

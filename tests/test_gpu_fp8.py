@@ -83,6 +83,50 @@ def test_quantize_every_bf16_pattern_bit_exact():
         assert nk == 0 and nv == 0
 
 
+def test_calibrated_scales_match_the_oracle_and_drive_the_quantisation():
+    """mi_kv_pool_calibrate_scales on prompt rows whose KV heads have different
+    ranges (one head of v all zeros, an infinity and a NaN planted in k) gives
+    the oracle's scales bit for bit at margins 1 and 1.5; a whole-pool
+    quantisation under the calibrated scales then stores the oracle's codes,
+    and the rows' largest value of each head stores as +-448 at margin 1."""
+    rows, Hkv, D = 300, 4, 128
+    rng = np.random.default_rng(77)
+    k = rng.standard_normal((rows, Hkv, D)) * np.array([1.0, 30.0, 0.02, 1.0])[None, :, None]
+    v = rng.standard_normal((rows, Hkv, D)) * np.array([2.0, 1.0, 1.0, 0.0])[None, :, None]
+    kb, vb = obf16.encode(k), obf16.encode(v)
+    kb[5, 3, 7] = 0x7F80                                   # +inf
+    kb[9, 3, 1] = 0xFFC0                                   # NaN
+    N = 8
+    src_k = obf16.encode(rng.standard_normal((N, Hkv, 16, D)) * 4.0)
+    src_v = obf16.encode(rng.standard_normal((N, Hkv, 16, D)) * 4.0)
+    kd = torch.zeros((N, Hkv, 16, D), dtype=torch.uint8, device=DEV)
+    vd = torch.zeros_like(kd)
+    pool = mk.mi_kv_pool_init(N, 16, Hkv, D, kd, vd, flags=mk.MI_POOL_KV_FP8)
+    try:
+        for margin in (1.0, 1.5):
+            mk.mi_kv_pool_calibrate_scales(pool, bits_to_dev(kb), bits_to_dev(vb), rows, margin)
+            ks, vs = (np.array(x, dtype=np.float32) for x in mk.mi_kv_pool_get_scales(pool))
+            oks, ovs = ofp8.calibrate_scales(kb, vb, margin)
+            _say("margin", margin, "k scales", ks, "v scales", vs)
+            assert np.array_equal(ks, oks) and np.array_equal(vs, ovs)
+        mk.mi_kv_pool_calibrate_scales(pool, bits_to_dev(kb), bits_to_dev(vb), rows, 1.0)
+        mk.mi_kv_pool_quantize(pool, bits_to_dev(src_k), bits_to_dev(src_v))
+        torch.cuda.synchronize()
+        gk, gv = _codes(kd), _codes(vd)
+        faults = mk.mi_kv_pool_check_errors(pool)
+    finally:
+        mk.mi_kv_pool_destroy(pool)
+    assert faults == 0
+    oks, ovs = ofp8.calibrate_scales(kb, vb, 1.0)
+    assert ovs[3] == np.float32(1.0)                       # the all-zero head
+    for g in range(Hkv):
+        assert np.array_equal(gk[:, g], ofp8.quantize(obf16.decode(src_k[:, g]), oks[g]))
+        assert np.array_equal(gv[:, g], ofp8.quantize(obf16.decode(src_v[:, g]), ovs[g]))
+        x = obf16.decode(kb[:, g, :])
+        top = np.max(np.abs(x[np.isfinite(x)]))
+        assert (ofp8.quantize(np.array([top]), oks[g])[0] & 0x7F) == 0x7E
+
+
 def _check_write_fp8(case, dc, ks, vs, oracle_write=None):
     """Codes after the GPU write vs the oracle's: V codes bit-exact; K codes
     equal except where the bf16 RoPE value itself may differ by one ulp
