@@ -117,28 +117,63 @@ def graph_of(torch, fn, reps):
     return g, side
 
 
+CALIB_BLOCKS = 4096     # cache blocks (65,536 tokens) the 8-bit scales are calibrated on
+
+
 def run_attention_bench(args, torch, mk, workloads, kv_format="bf16", dot=False):
     """The long-context decode step (write + attention) over a bf16 cache or an
-    8-bit (E4M3, unit scales) cache of the same workload. dot: the pool takes
+    8-bit (E4M3) cache of the same workload. The 8-bit cache is the bf16 one
+    quantised under per-head scales calibrated on its first CALIB_BLOCKS blocks
+    (mi_kv_pool_calibrate_scales, margin 1), and the step's output is compared
+    with the same step over the bf16 cache. dot: the pool takes
     MI_POOL_DECODE_DOT (the attention on vector-ALU dot products); the
     one-launch and flushed forms are then left out."""
     dev = "cuda:0"
     cfg = workloads.CONFIGS["qwen3_8b_long"]
-    case = workloads.make_decode_case(cfg, pool="bench", kv_format=kv_format)
-    kv_elem = 1 if kv_format == "fp8" else 2
+    case = workloads.make_decode_case(cfg, pool="bench", kv_format="bf16")
+    fp8 = kv_format == "fp8"
+    kv_elem = 1 if fp8 else 2
     B, Hq, Hkv, D = len(case.context_lens), cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
-    kp, vp = _dev(case.k_pool, torch, dev), _dev(case.v_pool, torch, dev)
+    kp16, vp16 = _dev(case.k_pool, torch, dev), _dev(case.v_pool, torch, dev)
     q, k, v = _dev(case.q, torch, dev), _dev(case.k, torch, dev), _dev(case.v, torch, dev)
     q_rot, out = torch.empty_like(q), torch.empty_like(q)
     table = torch.from_numpy(case.block_table).to(dev)
     ctx = torch.from_numpy(case.context_lens).to(dev)
     mbps, max_ctx = case.block_table.shape[1], int(case.context_lens.max())
-    flags = (mk.MI_POOL_KV_FP8 if kv_elem == 1 else 0) | (mk.MI_POOL_DECODE_DOT if dot else 0)
-    pool = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp, vp, flags=flags)
-    ws_bytes = mk.mi_paged_gqa_decode_split_workspace_bytes(pool, B, Hq, max_ctx, args.split)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     st = stream.cuda_stream
+    out16, calib = None, None
+    if fp8:
+        # the same step over the bf16 cache, for the 8-bit output's error
+        out16 = torch.empty_like(q)
+        p16 = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp16, vp16)
+        try:
+            w16 = mk.mi_paged_gqa_decode_workspace_bytes(p16, B, Hq, max_ctx)
+            ws16 = torch.empty(w16, dtype=torch.uint8, device=dev)
+            mk.mi_write_decode_kv(p16, q, k, v, q_rot, table, mbps, ctx, B, Hq, cfg.rope_theta, st)
+            mk.mi_paged_gqa_decode(p16, q_rot, out16, table, mbps, ctx, B, Hq, 0.0, max_ctx, ws16, w16, st)
+            torch.cuda.synchronize()
+        finally:
+            mk.mi_kv_pool_destroy(p16)
+        kp = torch.zeros(kp16.shape, dtype=torch.uint8, device=dev)
+        vp = torch.zeros_like(kp)
+    else:
+        kp, vp = kp16, vp16
+    flags = (mk.MI_POOL_KV_FP8 if fp8 else 0) | (mk.MI_POOL_DECODE_DOT if dot else 0)
+    pool = mk.mi_kv_pool_init(case.num_blocks, 16, Hkv, D, kp, vp, flags=flags)
+    if fp8:
+        nb = min(case.num_blocks, CALIB_BLOCKS)
+        rows_k = kp16[:nb].permute(0, 2, 1, 3).reshape(nb * 16, Hkv, D).contiguous()
+        rows_v = vp16[:nb].permute(0, 2, 1, 3).reshape(nb * 16, Hkv, D).contiguous()
+        mk.mi_kv_pool_calibrate_scales(pool, rows_k, rows_v, nb * 16, 1.0, st)
+        mk.mi_kv_pool_quantize(pool, kp16, vp16, st)
+        torch.cuda.synchronize()
+        ks, vs = mk.mi_kv_pool_get_scales(pool)
+        calib = {"sample_tokens": nb * 16, "k_scales": [round(min(ks), 6), round(max(ks), 6)],
+                 "v_scales": [round(min(vs), 6), round(max(vs), 6)]}
+        del rows_k, rows_v, kp16, vp16
+    ws_bytes = mk.mi_paged_gqa_decode_split_workspace_bytes(pool, B, Hq, max_ctx, args.split)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         mk.mi_write_decode_kv(pool, q, k, v, q_rot, table, mbps, ctx, B, Hq, cfg.rope_theta, st)
@@ -213,6 +248,12 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16", dot=False)
     mk.mi_kv_pool_destroy(pool)
     if faults:
         raise RuntimeError("device fault bits %#x during the benchmark" % faults)
+    vs_bf16 = None
+    if out16 is not None:
+        a = out.view(torch.bfloat16).float()
+        b = out16.view(torch.bfloat16).float()
+        vs_bf16 = {"max_abs": round(float((a - b).abs().max()), 5),
+                   "rel_l2": round(float((a - b).norm() / b.norm()), 5)}
 
     ctx_np = case.context_lens
     attn_bytes = workloads.attention_bytes(ctx_np, Hq, Hkv, D, 16, kv_elem_bytes=kv_elem)
@@ -223,6 +264,7 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16", dot=False)
         attn_bytes=attn_bytes, step_bytes=attn_bytes + write_bytes,
         tokens=int(ctx_np.sum()) + B,
         split=args.split or None,
+        calib=calib, vs_bf16=vs_bf16,
     )
 
 
@@ -933,7 +975,10 @@ def main():
         ms8 = r8["ms_step"]
         attn8 = float(np.mean(r8["attn_ms"]))
         line["kv_fp8"] = {
-            "workload": "same step over an 8-bit E4M3 cache (unit per-head scales)",
+            "workload": ("same step over an 8-bit E4M3 cache: the bf16 cache quantised under "
+                         "per-head scales calibrated on its first %d tokens" % r8["calib"]["sample_tokens"]),
+            "calibrated_scales_min_max": {"k": r8["calib"]["k_scales"], "v": r8["calib"]["v_scales"]},
+            "output_vs_bf16_cache": r8["vs_bf16"],
             "ms_per_step": round(ms8, 5),
             "algorithmic_bytes_per_step": int(r8["step_bytes"]),
             "GBps": round(r8["step_bytes"] / (ms8 * 1e-3) / 1e9, 1),
