@@ -143,6 +143,34 @@ def test_prefill_score_far_above_the_first_tile_takes_the_rescaling_pass(D):
         dev.close()
 
 
+def test_prefill_rescaling_pass_at_qwen3_8b_heads():
+    """The rescaling launch at Qwen3-8B-shaped heads (32/8, D 128) with
+    chunks of 700, 300 and 50 tokens after 0, 100 and 16 cached: 15 query
+    blocks x 32 heads x 3 sequences = 1,440 waves. A key of 30 u in every
+    sequence (all queries u) sends the call through that launch, and the whole
+    output must match the oracle on two calls in a row."""
+    cfg = workloads.PREFILL_CONFIGS["qwen3_8b_prefill"][0]
+    case = workloads.make_prefill_case(cfg, (0, 100, 16), (700, 300, 50))
+    u = case.q[0, 0].copy()
+    case.q[:] = u
+    big = obf16.encode(30.0 * obf16.decode(u))
+    for b, pos in enumerate((5, 60, 10)):   # new-token index of the large key
+        case.k[case.cu_seqlens[b] + pos] = big
+    ref, kn, vn, qb = oatt.prefill_step(case.k_pool, case.v_pool, case.q, case.k, case.v,
+                                        case.block_table, case.context_lens, case.cu_seqlens, 16,
+                                        case.cfg.rope_theta)
+    dev = PrefillOnDevice(case)
+    try:
+        for call in range(2):
+            dev.out.fill_(0)
+            dev.run()
+            _check_write(case, dev, kn, vn, qb)
+            check_tolerance(dev_to_bits(dev.out), ref, "qwen3_8b rescaling call %d" % call)
+        assert mk.mi_kv_pool_check_errors(dev.pool) == 0
+    finally:
+        dev.close()
+
+
 def test_prefill_qwen3_8b_shape_full():
     """Qwen3-8B-shaped chunk (32/8 heads, D 128): a 1000-token prompt, a 700-token
     chunk after 600 cached tokens and a 64-token chunk after 3000; the whole
