@@ -588,9 +588,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Waves per workgroup of a projection: the largest divisor of the K batches
 // that keeps the workgroup within its wave bound and the LDS cap, and the
 // projection within the target wave count.
-// down (256 workgroups at hidden 4096) takes up to 16 waves each: with the
-// one-load fp32 activations a wave fits in 76 registers, and 16 waves per
-// workgroup measured faster than 8 or 12 on MI355X.
+// down (256 workgroups at hidden 4096) may take up to 16 waves each: with
+// the one-load fp32 activations a wave fits in 76 registers. At 4 K steps
+// per batch the LDS cap (4352 bytes per wave) then allows 15, so it runs the
+// largest divisor of its 96 batches below that, 12; 6 and 8 waves, and 2 K
+// steps per batch, measured within run-to-run spread of it on MI355X.
 constexpr int kProjTargetWavesDown = 4096;
 template <int MT, int NW, int KB, int ACT, int EPI, bool HALF>
 int proj_waves(int wgs, int K) {
