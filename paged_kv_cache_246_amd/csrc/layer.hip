@@ -591,8 +591,9 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // down (256 workgroups at hidden 4096) may take up to 16 waves each: with
 // the one-load fp32 activations a wave fits in 76 registers. At 4 K steps
 // per batch the LDS cap (4352 bytes per wave) then allows 15, so it runs the
-// largest divisor of its 96 batches below that, 12; 6 and 8 waves, and 2 K
-// steps per batch, measured within run-to-run spread of it on MI355X.
+// largest divisor of its 96 batches below that, 12. On MI355X 8 waves, and
+// 2 K steps per batch, measured within run-to-run spread of it; 6 waves was
+// 1-2 us slower per layer.
 constexpr int kProjTargetWavesDown = 4096;
 template <int MT, int NW, int KB, int ACT, int EPI, bool HALF>
 int proj_waves(int wgs, int K) {
