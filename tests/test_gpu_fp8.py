@@ -127,6 +127,41 @@ def test_calibrated_scales_match_the_oracle_and_drive_the_quantisation():
         assert (ofp8.quantize(np.array([top]), oks[g])[0] & 0x7F) == 0x7E
 
 
+def test_calibrated_scales_at_the_benchmark_sample_size():
+    """Calibration over 65,536 rows of 8 KV heads x 128 dims (the sample the
+    long-context benchmark calibrates on): N(0, 1) bf16 values, one head of k
+    scaled by 40 and a single outlier of 1000 planted in one head of v. The
+    scales equal the oracle's bit for bit. (The random inputs are cast to
+    bf16 by torch on the CPU; only the oracle computes the expected scales.)"""
+    rows, Hkv, D = 65536, 8, 128
+    rng = np.random.default_rng(2024)
+
+    def bits(x):
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    k = rng.standard_normal((rows, Hkv, D), dtype=np.float32)
+    k[:, 5, :] *= 40.0
+    v = rng.standard_normal((rows, Hkv, D), dtype=np.float32)
+    v[40000, 2, 17] = 1000.0
+    kb, vb = bits(k), bits(v)
+    del k, v
+    kd = torch.zeros((4, Hkv, 16, D), dtype=torch.uint8, device=DEV)
+    vd = torch.zeros_like(kd)
+    pool = mk.mi_kv_pool_init(4, 16, Hkv, D, kd, vd, flags=mk.MI_POOL_KV_FP8)
+    try:
+        mk.mi_kv_pool_calibrate_scales(pool, bits_to_dev(kb), bits_to_dev(vb), rows, 1.0)
+        ks, vs = (np.array(x, dtype=np.float32) for x in mk.mi_kv_pool_get_scales(pool))
+        faults = mk.mi_kv_pool_check_errors(pool)
+    finally:
+        mk.mi_kv_pool_destroy(pool)
+    oks, ovs = ofp8.calibrate_scales(kb, vb, 1.0)
+    _say("k scales", ks, "v scales", vs)
+    assert faults == 0
+    assert np.array_equal(ks, oks) and np.array_equal(vs, ovs)
+    assert ovs[2] == np.float32(np.float32(1000.0) / np.float32(448.0))
+
+
 def _check_write_fp8(case, dc, ks, vs, oracle_write=None):
     """Codes after the GPU write vs the oracle's: V codes bit-exact; K codes
     equal except where the bf16 RoPE value itself may differ by one ulp
