@@ -186,8 +186,8 @@ int mi_kv_pool_quantize(mi_kv_pool_t pool, const uint16_t* k_src, const uint16_t
  *          otherwise saturate.
  * The new scales replace the pool's on `stream` (asynchronous). Calibrate
  * before anything is written, as with mi_kv_pool_set_scales.
- * MI_ERR_INVALID_ARG for a bf16 or host-only pool, NULL inputs, rows < 1 or
- * a bad margin (nothing launched).
+ * MI_ERR_INVALID_ARG for a bf16 or host-only pool, NULL or misaligned
+ * inputs, rows < 1 or a bad margin (nothing launched).
  */
 int mi_kv_pool_calibrate_scales(mi_kv_pool_t pool, const uint16_t* k, const uint16_t* v, int32_t rows,
                                 float margin, void* stream);

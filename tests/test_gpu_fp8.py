@@ -162,6 +162,33 @@ def test_calibrated_scales_at_the_benchmark_sample_size():
     assert ovs[2] == np.float32(np.float32(1000.0) / np.float32(448.0))
 
 
+def test_calibration_rejects_bad_arguments_and_keeps_the_scales():
+    """On a device 8-bit pool, rows < 1, a margin that is not finite and
+    positive, and inputs off 16-byte alignment are refused with
+    MI_ERR_INVALID_ARG before anything is launched; the scales set before stay."""
+    Hkv, D, rows = 2, 128, 32
+    kd = torch.zeros((4, Hkv, 16, D), dtype=torch.uint8, device=DEV)
+    vd = torch.zeros_like(kd)
+    src = torch.ones((rows + 8, Hkv, D), dtype=torch.int16, device=DEV)
+    pool = mk.mi_kv_pool_init(4, 16, Hkv, D, kd, vd, flags=mk.MI_POOL_KV_FP8)
+    try:
+        mk.mi_kv_pool_set_scales(pool, [0.25, 0.5], [2.0, 4.0])
+        odd = src.view(-1)[1:1 + rows * Hkv * D]           # 2 bytes past an aligned start
+        cases = [(src, src, 0, 1.0), (src, src, -3, 1.0), (src, src, rows, 0.0),
+                 (src, src, rows, -1.0), (src, src, rows, float("nan")), (src, src, rows, float("inf")),
+                 (odd, src, rows, 1.0), (src, odd, rows, 1.0)]
+        for k, v, r, margin in cases:
+            with pytest.raises(mk.MikvError) as e:
+                mk.mi_kv_pool_calibrate_scales(pool, k, v, r, margin)
+            assert e.value.status == mk.MI_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        ks, vs = mk.mi_kv_pool_get_scales(pool)
+        assert list(ks) == [0.25, 0.5] and list(vs) == [2.0, 4.0]
+        assert mk.mi_kv_pool_check_errors(pool) == 0
+    finally:
+        mk.mi_kv_pool_destroy(pool)
+
+
 def _check_write_fp8(case, dc, ks, vs, oracle_write=None):
     """Codes after the GPU write vs the oracle's: V codes bit-exact; K codes
     equal except where the bf16 RoPE value itself may differ by one ulp
