@@ -226,6 +226,20 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16", dot=False)
         t1.record(stream)
         torch.cuda.synchronize()
         ms_one = t0.elapsed_time(t1) / args.steps
+    # The two calls replayed from a HIP graph of 20 captured steps, the way a
+    # serving loop launches its decode steps.
+    ms_graph = None
+    if not dot:
+        def step_on(s):
+            mk.mi_write_decode_kv(pool, q, k, v, q_rot, table, mbps, ctx, B, Hq, cfg.rope_theta,
+                                  s.cuda_stream)
+            mk.mi_paged_gqa_decode_split(pool, q_rot, out, table, mbps, ctx, B, Hq, 0.0, max_ctx,
+                                         args.split, ws, ws_bytes, s.cuda_stream)
+
+        g, side = graph_of(torch, step_on, 20)
+        tg = time_step(torch, side, g.replay, max(3, args.steps // 20), 2)
+        ms_graph = tg["ms_per_step"] / 20
+        del g
     # Flushed: single steps (write + attention), each after a fill that evicts
     # the caches; the attention launch is timed on its own inside the step.
     flushed = None
@@ -259,7 +273,7 @@ def run_attention_bench(args, torch, mk, workloads, kv_format="bf16", dot=False)
     attn_bytes = workloads.attention_bytes(ctx_np, Hq, Hkv, D, 16, kv_elem_bytes=kv_elem)
     write_bytes = workloads.write_bytes(B, Hq, Hkv, D, kv_elem_bytes=kv_elem)
     return dict(
-        case=case, cfg=cfg, ms_step=ms_step, ms_one=ms_one, wall=wall, attn_ms=attn_ms,
+        case=case, cfg=cfg, ms_step=ms_step, ms_one=ms_one, ms_graph=ms_graph, wall=wall, attn_ms=attn_ms,
         flushed=flushed,
         attn_bytes=attn_bytes, step_bytes=attn_bytes + write_bytes,
         tokens=int(ctx_np.sum()) + B,
@@ -954,6 +968,11 @@ def main():
             "ms_per_step": round(r["ms_one"], 5),
             "GBps": round(r["step_bytes"] / (r["ms_one"] * 1e-3) / 1e9, 1),
         },
+        "decode_step_graph": None if r["ms_graph"] is None else {
+            "what": "the two calls replayed from a HIP graph of 20 captured steps",
+            "ms_per_step": round(r["ms_graph"], 5),
+            "GBps": round(r["step_bytes"] / (r["ms_graph"] * 1e-3) / 1e9, 1),
+        },
         "attention_launch_ms": _pct(r["attn_ms"]),
     }
     if r["flushed"] is not None:
@@ -988,6 +1007,7 @@ def main():
             "attention_hbm_frac": round(r8["attn_bytes"] / (attn8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "step_speedup_vs_bf16": round(ms / ms8, 3),
             "one_launch_ms_per_step": None if r8["ms_one"] is None else round(r8["ms_one"], 5),
+            "graph_ms_per_step": None if r8["ms_graph"] is None else round(r8["ms_graph"], 5),
         }
     if not args.no_dot:
         line["decode_dot_form"] = run_dot_compare(args, torch, mk, workloads)
